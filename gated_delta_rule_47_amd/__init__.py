@@ -1,0 +1,216 @@
+"""Python binding of libgdn2 (Gated DeltaNet-2 core recurrence on MI355X).
+
+Thin ctypes marshalling over the C ABI declared in include/libgdn2.h: the
+gdn2_* functions take raw device pointers and sizes exactly like their C
+counterparts; chunk_fwd() and step() accept torch tensors, allocate outputs and
+the workspace with torch, and pass torch's current stream.  Every step of the
+computation runs in the HIP library; if libgdn2.so is missing, loading fails
+with an error (there is no fallback).
+"""
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgdn2.so")
+
+GDN2_OK = 0
+GDN2_ERR_INVALID_ARGUMENT = 1
+GDN2_ERR_UNSUPPORTED = 2
+GDN2_ERR_WORKSPACE = 3
+GDN2_ERR_HIP = 4
+GDN2_F32 = 0
+GDN2_BF16 = 1
+CHUNK = 64
+
+GDN2_STAGE_PLAN = 1
+GDN2_STAGE_FACTORS = 2
+GDN2_STAGE_PROPAGATE = 4
+GDN2_STAGE_ALL = 7
+
+EXPORTED = ("gdn2_abi_version", "gdn2_status_string", "gdn2_chunk_fwd_workspace_bytes",
+            "gdn2_chunk_fwd_workspace_layout", "gdn2_chunk_fwd", "gdn2_chunk_fwd_stages",
+            "gdn2_step")
+
+
+class Gdn2Error(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__("%s failed: %s" % (where, gdn2_status_string(status)))
+
+
+class WorkspaceLayout(ctypes.Structure):
+    _fields_ = [("total_bytes", ctypes.c_size_t), ("max_chunks", ctypes.c_int),
+                ("off_Tinv", ctypes.c_size_t), ("off_W", ctypes.c_size_t),
+                ("off_Qhat", ctypes.c_size_t), ("off_KhatT", ctypes.c_size_t),
+                ("off_M", ctypes.c_size_t), ("off_gamma_last", ctypes.c_size_t),
+                ("off_plan", ctypes.c_size_t)]
+
+
+_lib = None
+
+
+def load_library(path=LIB_PATH):
+    """Load libgdn2.so (once).  Raises if the library has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError("libgdn2.so not found at %s; build it with "
+                          "`python -m gated_delta_rule_47_amd.build`" % path)
+    lib = ctypes.CDLL(path)
+    P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.gdn2_abi_version.restype = I
+    lib.gdn2_abi_version.argtypes = []
+    lib.gdn2_status_string.restype = ctypes.c_char_p
+    lib.gdn2_status_string.argtypes = [I]
+    lib.gdn2_chunk_fwd_workspace_bytes.restype = Z
+    lib.gdn2_chunk_fwd_workspace_bytes.argtypes = [I] * 8
+    lib.gdn2_chunk_fwd_workspace_layout.restype = I
+    lib.gdn2_chunk_fwd_workspace_layout.argtypes = [I] * 8 + [ctypes.POINTER(WorkspaceLayout)]
+    lib.gdn2_chunk_fwd.restype = I
+    lib.gdn2_chunk_fwd.argtypes = [P] * 10 + [I] * 7 + [P, Z, P]
+    lib.gdn2_chunk_fwd_stages.restype = I
+    lib.gdn2_chunk_fwd_stages.argtypes = [P] * 10 + [I] * 7 + [P, Z, P, I]
+    lib.gdn2_step.restype = I
+    lib.gdn2_step.argtypes = [P] * 8 + [I] * 5 + [P]
+    _lib = lib
+    return lib
+
+
+# ---------------------------------------------------------------------------
+# Raw C-ABI wrappers (same names and arguments as the C functions)
+# ---------------------------------------------------------------------------
+
+def gdn2_abi_version():
+    return load_library().gdn2_abi_version()
+
+
+def gdn2_status_string(status):
+    return load_library().gdn2_status_string(int(status)).decode()
+
+
+def gdn2_chunk_fwd_workspace_bytes(N, B, T, H, Dk, Dv, io, varlen):
+    return load_library().gdn2_chunk_fwd_workspace_bytes(N, B, T, H, Dk, Dv, io, int(varlen))
+
+
+def gdn2_chunk_fwd_workspace_layout(N, B, T, H, Dk, Dv, io, varlen):
+    out = WorkspaceLayout()
+    st = load_library().gdn2_chunk_fwd_workspace_layout(N, B, T, H, Dk, Dv, io, int(varlen),
+                                                        ctypes.byref(out))
+    if st != GDN2_OK:
+        raise Gdn2Error(st, "gdn2_chunk_fwd_workspace_layout")
+    return out
+
+
+def gdn2_chunk_fwd(q, k, v, log_alpha, b, w, S0, o, S_final, cu_seqlens, N, B, T, H, Dk, Dv,
+                   io, workspace, workspace_bytes, stream):
+    """Raw call: every pointer argument is an int (device address) or None."""
+    return load_library().gdn2_chunk_fwd(q, k, v, log_alpha, b, w, S0, o, S_final, cu_seqlens,
+                                          N, B, T, H, Dk, Dv, io, workspace, workspace_bytes,
+                                          stream)
+
+
+def gdn2_chunk_fwd_stages(q, k, v, log_alpha, b, w, S0, o, S_final, cu_seqlens, N, B, T, H, Dk,
+                          Dv, io, workspace, workspace_bytes, stream, stages):
+    """Raw call of a subset of the chunk-forward stages (GDN2_STAGE_* bits)."""
+    return load_library().gdn2_chunk_fwd_stages(q, k, v, log_alpha, b, w, S0, o, S_final,
+                                                 cu_seqlens, N, B, T, H, Dk, Dv, io, workspace,
+                                                 workspace_bytes, stream, stages)
+
+
+def gdn2_step(q, k, v, log_alpha, b, w, S, o, B, H, Dk, Dv, io, stream):
+    """Raw call: every pointer argument is an int (device address) or None."""
+    return load_library().gdn2_step(q, k, v, log_alpha, b, w, S, o, B, H, Dk, Dv, io, stream)
+
+
+# ---------------------------------------------------------------------------
+# torch-tensor marshalling
+# ---------------------------------------------------------------------------
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _io_of(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return GDN2_BF16
+    if t.dtype == torch.float32:
+        return GDN2_F32
+    raise TypeError("q/k/v must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _check(t, name, dtype=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+
+
+def chunk_fwd(q, k, v, log_alpha, b, w, S0=None, cu_seqlens=None, o=None, S_final=None,
+              output_final_state=True, workspace=None, stream=None, stages=GDN2_STAGE_ALL):
+    """Chunk-parallel forward.  Shapes: q, k, log_alpha, b [B,T,H,Dk]; v, w [B,T,H,Dv].
+
+    cu_seqlens (int32 device tensor [N+1]) selects a packed call (B must be 1).
+    stages (GDN2_STAGE_* bits) runs only part of the forward, see the header.
+    Returns (o [B,T,H,Dv] in q's dtype, S_final [N,H,Dk,Dv] float32 or None).
+    """
+    import torch
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    io = _io_of(q)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check(t, name, q.dtype)
+    for name, t in (("log_alpha", log_alpha), ("b", b), ("w", w), ("S0", S0)):
+        _check(t, name, torch.float32)
+    _check(cu_seqlens, "cu_seqlens", torch.int32)
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    if o is None:
+        o = torch.empty((B, T, H, Dv), dtype=q.dtype, device=q.device)
+    if S_final is None and output_final_state:
+        S_final = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=q.device)
+    varlen = cu_seqlens is not None
+    nbytes = gdn2_chunk_fwd_workspace_bytes(N, B, T, H, Dk, Dv, io, varlen)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(S0), _ptr(o),
+            _ptr(S_final), _ptr(cu_seqlens), N, B, T, H, Dk, Dv, io, _ptr(workspace),
+            workspace.numel(), _stream(stream))
+    if stages == GDN2_STAGE_ALL:
+        st = gdn2_chunk_fwd(*args)
+    else:
+        st = gdn2_chunk_fwd_stages(*args, stages)
+    if st != GDN2_OK:
+        raise Gdn2Error(st, "gdn2_chunk_fwd")
+    return o, S_final
+
+
+def step(q, k, v, log_alpha, b, w, S, o=None, stream=None):
+    """One decode token: q, k, log_alpha, b [B,H,Dk]; v, w [B,H,Dv]; S [B,H,Dk,Dv] f32 in place."""
+    import torch
+    B, H, Dk = q.shape
+    Dv = v.shape[-1]
+    io = _io_of(q)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check(t, name, q.dtype)
+    for name, t in (("log_alpha", log_alpha), ("b", b), ("w", w), ("S", S)):
+        _check(t, name, torch.float32)
+    if o is None:
+        o = torch.empty((B, H, Dv), dtype=q.dtype, device=q.device)
+    st = gdn2_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(S), _ptr(o),
+                   B, H, Dk, Dv, io, _stream(stream))
+    if st != GDN2_OK:
+        raise Gdn2Error(st, "gdn2_step")
+    return o

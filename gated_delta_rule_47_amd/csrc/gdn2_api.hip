@@ -1,0 +1,219 @@
+// C ABI of libgdn2: argument validation, workspace carving and launches.
+// The declarations and their contracts are in include/libgdn2.h.
+
+#include <stdlib.h>
+#include <string.h>
+
+#include <climits>
+
+#include "gdn2_device.h"
+#include "gdn2_internal.h"
+#include "libgdn2.h"
+
+using namespace gdn2;
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool debug_sync() {
+    static const bool on = [] {
+        const char *e = getenv("GDN2_DEBUG_SYNC");
+        return e && e[0] == '1';
+    }();
+    return on;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+bool supported_dims(int Dk, int Dv) { return Dk == Dv && (Dk == 64 || Dk == 128); }
+
+int finish(hipError_t launch_err, hipStream_t stream) {
+    if (launch_err != hipSuccess) return GDN2_ERR_HIP;
+    if (debug_sync()) {
+        if (hipStreamSynchronize(stream) != hipSuccess) return GDN2_ERR_HIP;
+        if (hipGetLastError() != hipSuccess) return GDN2_ERR_HIP;
+    }
+    return GDN2_OK;
+}
+
+}  // namespace
+
+namespace gdn2 {
+
+bool workspace_layout(int N, int B, int T, int H, int Dk, int Dv, size_t io_bytes, bool varlen,
+                      WorkspaceLayout *out) {
+    if (N < 0 || B < 0 || T < 0 || H < 0 || !supported_dims(Dk, Dv)) return false;
+    const long long nc_seq = (T + kChunk - 1) / kChunk;
+    long long max_chunks = varlen ? nc_seq + N : (long long)B * nc_seq;
+    if (max_chunks > INT_MAX / 2) return false;
+    const size_t chd = (size_t)max_chunks * (size_t)H;  // chunk-heads
+    if (H > 0 && chd / (size_t)H != (size_t)max_chunks) return false;
+    WorkspaceLayout L;
+    L.max_chunks = (int)max_chunks;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off = align_up(off + bytes);
+        return at;
+    };
+    L.off_T = take(chd * kChunk * kChunk * io_bytes);
+    L.off_W = take(chd * kChunk * Dk * io_bytes);
+    L.off_Qh = take(chd * kChunk * Dk * io_bytes);
+    L.off_KhT = take(chd * Dk * kChunk * io_bytes);
+    L.off_M = take(chd * kChunk * kChunk * io_bytes);
+    L.off_gl = take(chd * Dk * sizeof(float));
+    L.plan_ints = varlen ? (size_t)N + 1 + 3 * (size_t)max_chunks : 0;
+    L.off_plan = take(L.plan_ints * sizeof(int32_t));
+    L.total = off;
+    *out = L;
+    return true;
+}
+
+}  // namespace gdn2
+
+extern "C" {
+
+int gdn2_abi_version(void) { return kAbiVersion; }
+
+const char *gdn2_status_string(int status) {
+    switch (status) {
+        case GDN2_OK: return "GDN2_OK";
+        case GDN2_ERR_INVALID_ARGUMENT: return "GDN2_ERR_INVALID_ARGUMENT";
+        case GDN2_ERR_UNSUPPORTED: return "GDN2_ERR_UNSUPPORTED";
+        case GDN2_ERR_WORKSPACE: return "GDN2_ERR_WORKSPACE";
+        case GDN2_ERR_HIP: return "GDN2_ERR_HIP";
+        default: return "GDN2_ERR_UNKNOWN";
+    }
+}
+
+static size_t io_size(int io) { return io == GDN2_BF16 ? 2 : 4; }
+
+size_t gdn2_chunk_fwd_workspace_bytes(int N, int B, int T, int H, int Dk, int Dv, int io,
+                                      int varlen) {
+    if (io != GDN2_F32 && io != GDN2_BF16) return 0;
+    WorkspaceLayout L;
+    if (!workspace_layout(N, B, T, H, Dk, Dv, io_size(io), varlen != 0, &L)) return 0;
+    return L.total;
+}
+
+int gdn2_chunk_fwd_workspace_layout(int N, int B, int T, int H, int Dk, int Dv, int io,
+                                    int varlen, gdn2_workspace_layout *out) {
+    if (!out) return GDN2_ERR_INVALID_ARGUMENT;
+    if (io != GDN2_F32 && io != GDN2_BF16) return GDN2_ERR_INVALID_ARGUMENT;
+    if (!supported_dims(Dk, Dv)) return GDN2_ERR_UNSUPPORTED;
+    WorkspaceLayout L;
+    if (!workspace_layout(N, B, T, H, Dk, Dv, io_size(io), varlen != 0, &L))
+        return GDN2_ERR_INVALID_ARGUMENT;
+    out->total_bytes = L.total;
+    out->max_chunks = L.max_chunks;
+    out->off_Tinv = L.off_T;
+    out->off_W = L.off_W;
+    out->off_Qhat = L.off_Qh;
+    out->off_KhatT = L.off_KhT;
+    out->off_M = L.off_M;
+    out->off_gamma_last = L.off_gl;
+    out->off_plan = L.off_plan;
+    return GDN2_OK;
+}
+
+int gdn2_chunk_fwd_stages(const void *q, const void *k, const void *v, const float *log_alpha,
+                          const float *b, const float *w, const float *S0, void *o,
+                          float *S_final, const int32_t *cu_seqlens, int N, int B, int T, int H,
+                          int Dk, int Dv, int io, void *workspace, size_t workspace_bytes,
+                          void *stream_ptr, int stages) {
+    if (stages & ~GDN2_STAGE_ALL) return GDN2_ERR_INVALID_ARGUMENT;
+    if (io != GDN2_F32 && io != GDN2_BF16) return GDN2_ERR_INVALID_ARGUMENT;
+    if (N < 0 || B < 0 || T < 0 || H < 0 || Dk <= 0 || Dv <= 0) return GDN2_ERR_INVALID_ARGUMENT;
+    if (!supported_dims(Dk, Dv)) return GDN2_ERR_UNSUPPORTED;
+    const bool varlen = cu_seqlens != nullptr;
+    if (varlen ? B != 1 : N != B) return GDN2_ERR_INVALID_ARGUMENT;
+    if (N == 0 || H == 0) return GDN2_OK;  // nothing to compute
+    // Dense sizes must fit the int indexing of the kernels.
+    if ((long long)B * T > INT_MAX / 2) return GDN2_ERR_UNSUPPORTED;
+    const bool need_tokens = T > 0;
+    const void *tok_ptrs[] = {q, k, v, log_alpha, b, w, o};
+    for (const void *p : tok_ptrs) {
+        if (need_tokens && !p) return GDN2_ERR_INVALID_ARGUMENT;
+        if (p && !aligned16(p)) return GDN2_ERR_INVALID_ARGUMENT;
+    }
+    if ((S0 && !aligned16(S0)) || (S_final && !aligned16(S_final)) ||
+        (cu_seqlens && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3)))
+        return GDN2_ERR_INVALID_ARGUMENT;
+    if ((const void *)o == (const void *)S0 || (const void *)o == (const void *)S_final)
+        return GDN2_ERR_INVALID_ARGUMENT;
+
+    WorkspaceLayout L;
+    if (!workspace_layout(N, B, T, H, Dk, Dv, io_size(io), varlen, &L))
+        return GDN2_ERR_INVALID_ARGUMENT;
+    if (L.total > 0 && (!workspace || workspace_bytes < L.total)) return GDN2_ERR_WORKSPACE;
+    if (workspace && (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)))
+        return GDN2_ERR_WORKSPACE;
+
+    hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+    char *ws = static_cast<char *>(workspace);
+    ChunkArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.log_alpha = log_alpha;
+    a.b = b;
+    a.w = w;
+    a.S0 = S0;
+    a.o = o;
+    a.S_final = S_final;
+    a.cu_seqlens = cu_seqlens;
+    a.N = N;
+    a.B = B;
+    a.T = T;
+    a.H = H;
+    a.NC = (T + kChunk - 1) / kChunk;
+    a.max_chunks = L.max_chunks;
+    a.plan = varlen ? reinterpret_cast<int32_t *>(ws + L.off_plan) : nullptr;
+    a.ws_T = ws + L.off_T;
+    a.ws_W = ws + L.off_W;
+    a.ws_Qh = ws + L.off_Qh;
+    a.ws_KhT = ws + L.off_KhT;
+    a.ws_M = ws + L.off_M;
+    a.ws_gl = reinterpret_cast<float *>(ws + L.off_gl);
+    const bool bf = io == GDN2_BF16;
+
+    hipError_t err = hipSuccess;
+    if (varlen && (stages & GDN2_STAGE_PLAN)) err = launch_plan(a, stream);
+    if (err == hipSuccess && (stages & GDN2_STAGE_FACTORS) && L.max_chunks > 0)
+        err = launch_chunk_prep(a, Dk, bf, stream);
+    if (err == hipSuccess && (stages & GDN2_STAGE_PROPAGATE) && (S_final || L.max_chunks > 0))
+        err = launch_chunk_prop(a, Dk, bf, stream);
+    return finish(err, stream);
+}
+
+int gdn2_chunk_fwd(const void *q, const void *k, const void *v, const float *log_alpha,
+                   const float *b, const float *w, const float *S0, void *o, float *S_final,
+                   const int32_t *cu_seqlens, int N, int B, int T, int H, int Dk, int Dv, int io,
+                   void *workspace, size_t workspace_bytes, void *stream_ptr) {
+    return gdn2_chunk_fwd_stages(q, k, v, log_alpha, b, w, S0, o, S_final, cu_seqlens, N, B, T, H,
+                                 Dk, Dv, io, workspace, workspace_bytes, stream_ptr,
+                                 GDN2_STAGE_ALL);
+}
+
+int gdn2_step(const void *q, const void *k, const void *v, const float *log_alpha, const float *b,
+              const float *w, float *S, void *o, int B, int H, int Dk, int Dv, int io,
+              void *stream_ptr) {
+    if (io != GDN2_F32 && io != GDN2_BF16) return GDN2_ERR_INVALID_ARGUMENT;
+    if (B < 0 || H < 0 || Dk <= 0 || Dv <= 0) return GDN2_ERR_INVALID_ARGUMENT;
+    if (!supported_dims(Dk, Dv)) return GDN2_ERR_UNSUPPORTED;
+    if (B == 0 || H == 0) return GDN2_OK;
+    if ((long long)B * H > INT_MAX) return GDN2_ERR_UNSUPPORTED;
+    const void *ptrs[] = {q, k, v, log_alpha, b, w, S, o};
+    for (const void *p : ptrs)
+        if (!p || !aligned16(p)) return GDN2_ERR_INVALID_ARGUMENT;
+    if ((const void *)o == (const void *)S) return GDN2_ERR_INVALID_ARGUMENT;
+    StepArgs a{q, k, v, log_alpha, b, w, S, o, B, H};
+    hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+    return finish(launch_step(a, Dk, io == GDN2_BF16, stream), stream);
+}
+
+}  // extern "C"

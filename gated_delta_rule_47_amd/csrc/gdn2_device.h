@@ -1,0 +1,123 @@
+// Device-side building blocks shared by the libgdn2 kernels (gfx950 only).
+//
+// MFMA conventions used throughout (v_mfma_f32_16x16x32_bf16 and
+// v_mfma_f32_16x16x4_f32, wave64):
+//   D[m][n] += sum_k A[m][k] * B[n][k]          ("NT" form)
+// Operands are read from row-major tiles with k contiguous:
+//   lane l supplies A[m0 + l%16][k0 + KPL*(l/16) .. + KPL-1] and the same for B,
+// where KPL = 8 (bf16) or 1 (f32).  The 16x16 fp32 result is held as
+//   lane l: D[4*(l/16) + r][l%16], r = 0..3.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn2 {
+
+constexpr int kChunk = 64;        // tokens per chunk
+constexpr int kThreads = 256;     // threads per workgroup of the chunk kernels (4 waves)
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return static_cast<float>(x); }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return static_cast<bf16>(x); }
+
+// ---------------------------------------------------------------------------
+// MFMA traits: one 16x16 output tile per instruction, K = KS per instruction.
+// ---------------------------------------------------------------------------
+template <typename E> struct Mma;
+
+template <> struct Mma<bf16> {
+    using elem = bf16;
+    typedef bf16x8 frag;
+    static constexpr int KS = 32;
+    static constexpr int KPL = 8;
+    static __device__ __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ frag zero() {
+        frag z;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) z[i] = static_cast<bf16>(0.0f);
+        return z;
+    }
+};
+
+template <> struct Mma<float> {
+    using elem = float;
+    typedef float frag;
+    static constexpr int KS = 4;
+    static constexpr int KPL = 1;
+    static __device__ __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ frag zero() { return 0.0f; }
+};
+
+// Operand fragment of a row-major tile (rows r0.., k0..) with leading dim ld.
+template <typename E>
+__device__ __forceinline__ typename Mma<E>::frag load_frag(const E *tile, int ld, int lane) {
+    using M = Mma<E>;
+    return *reinterpret_cast<const typename M::frag *>(tile + (lane & 15) * ld + M::KPL * (lane >> 4));
+}
+
+// acc += A[16 x K] * B[16 x K]^T, both row-major with k contiguous.
+template <typename E, int K>
+__device__ __forceinline__ f32x4 mma_tile(f32x4 acc, const E *A, int lda, const E *B, int ldb,
+                                          int lane) {
+    using M = Mma<E>;
+#pragma unroll
+    for (int kk = 0; kk < K; kk += M::KS)
+        acc = M::mma(load_frag<E>(A + kk, lda, lane), load_frag<E>(B + kk, ldb, lane), acc);
+    return acc;
+}
+
+// Same with a runtime K (a multiple of KS).
+template <typename E>
+__device__ __forceinline__ f32x4 mma_tile_k(f32x4 acc, const E *A, int lda, const E *B, int ldb,
+                                            int K, int lane) {
+    using M = Mma<E>;
+    for (int kk = 0; kk < K; kk += M::KS)
+        acc = M::mma(load_frag<E>(A + kk, lda, lane), load_frag<E>(B + kk, ldb, lane), acc);
+    return acc;
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.0f, 0.0f, 0.0f, 0.0f}; }
+
+// Store the 4 results a lane holds as 4 consecutive elements of row (l%16)
+// of a row-major destination: dst[(l%16)*ld + 4*(l/16) + r] = acc[r].
+// (This writes the TRANSPOSE of the D tile: Dt[n][m].)
+template <typename E>
+__device__ __forceinline__ void store_tile_t(E *dst, int ld, f32x4 acc, int lane) {
+    E *p = dst + (lane & 15) * ld + 4 * (lane >> 4);
+    if constexpr (sizeof(E) == 2) {
+        bf16x4 v;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = static_cast<bf16>(acc[r]);
+        *reinterpret_cast<bf16x4 *>(p) = v;
+    } else {
+        *reinterpret_cast<f32x4 *>(p) = acc;
+    }
+}
+
+// Store the D tile in its natural orientation: dst[(4*(l/16)+r)*ld + l%16] = acc[r].
+template <typename E>
+__device__ __forceinline__ void store_tile(E *dst, int ld, f32x4 acc, int lane) {
+    E *p = dst + (4 * (lane >> 4)) * ld + (lane & 15);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p[r * ld] = from_f32<E>(acc[r]);
+}
+
+}  // namespace gdn2

@@ -1,0 +1,190 @@
+/*
+ * libgdn2 — Gated DeltaNet-2 core recurrence on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (per sequence and head; state S is Dk x Dv, rows = key channels):
+ *
+ *   S_t = (I - k_t (b_t * k_t)^T) Diag(alpha_t) S_{t-1} + k_t (w_t * v_t)^T
+ *   o_t = S_t^T q_t
+ *
+ * with alpha_t = exp(log_alpha_t) a per-key-channel decay, b_t an erase gate on
+ * the key axis and w_t a write gate on the value axis.  Sources: the state
+ * update equation of the gist.science summary of arXiv 2605.22791 (technical
+ * summary, part "1. Gated Delta Rule-2") and of the zubnet.ai news item (first
+ * paragraph); the order decay -> read with b*k -> write, and the query reading
+ * the UPDATED state, from the iplexlaw blog digest (section "Decisiones
+ * independientes en dos ejes").  No query scale is applied.
+ *
+ * Conventions shared by every call
+ *   - All tensor pointers are DEVICE pointers, allocated and owned by the
+ *     caller.  Compute calls allocate nothing; intermediates of the chunk
+ *     forward live in a caller-supplied device workspace.
+ *   - Layouts are dense, row-major, last dimension fastest.  Every tensor
+ *     pointer must be 16-byte aligned.
+ *   - `io` selects the element type of q, k, v and o (GDN2_BF16 or GDN2_F32).
+ *     log_alpha, b, w and all states are always float32.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls enqueue work
+ *     and return; results are valid once the stream has been synchronised.
+ *     With the environment variable GDN2_DEBUG_SYNC=1 each call synchronises
+ *     its stream and reports asynchronous failures as GDN2_ERR_HIP.
+ *   - Errors are reported only through the returned status.  Arguments are
+ *     validated on the host before anything is launched; on a non-OK status
+ *     nothing has been enqueued (except GDN2_ERR_HIP, which reports a failed
+ *     launch).  Device faults surface at the caller's next synchronisation.
+ *   - Supported head sizes: Dk == Dv, either 64 or 128
+ *     (others return GDN2_ERR_UNSUPPORTED).
+ *   - Calls keep no state between invocations and are reentrant; two calls
+ *     may run concurrently on different streams if they share no outputs or
+ *     workspace.  Results are bitwise reproducible for identical inputs.
+ */
+#ifndef LIBGDN2_H
+#define LIBGDN2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gdn2_status {
+    GDN2_OK = 0,
+    GDN2_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, bad size or dtype */
+    GDN2_ERR_UNSUPPORTED = 2,      /* valid request this build does not implement */
+    GDN2_ERR_WORKSPACE = 3,        /* workspace missing or smaller than required */
+    GDN2_ERR_HIP = 4               /* a HIP launch or runtime call failed */
+} gdn2_status;
+
+typedef enum gdn2_dtype {
+    GDN2_F32 = 0,
+    GDN2_BF16 = 1
+} gdn2_dtype;
+
+/* Version of this interface; bumped on any incompatible change. */
+int gdn2_abi_version(void);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char *gdn2_status_string(int status);
+
+/*
+ * Workspace bytes gdn2_chunk_fwd needs for a call with these sizes.
+ * varlen != 0 sizes it for a packed call with N sequences and T total tokens
+ * (B must then be 1).  Returns 0 for unsupported or invalid sizes.
+ */
+size_t gdn2_chunk_fwd_workspace_bytes(int N, int B, int T, int H, int Dk, int Dv,
+                                      int io, int varlen);
+
+/*
+ * Chunk-parallel forward over whole sequences.
+ *
+ * The sequence is processed in 64-token chunks (the WY chunk form of the
+ * iplexlaw digest, section "Procesamiento del token y entrenamiento
+ * paralelo", and of the gist.science summary, part "3. Efficient chunkwise
+ * parallel training"): per chunk the cumulative log-decay is taken in fp32,
+ * the strictly lower-triangular interaction matrix A of the decayed,
+ * erase-modulated keys against the keys is formed and T = (I + A)^-1 is
+ * solved in fp32, the chunk's auxiliaries (W = T (gamma*b*k), the causal
+ * query-key matrix, the decayed queries and keys) are formed with bf16 (or
+ * fp32 for io = GDN2_F32) MFMA contractions, and one sequential pass per
+ * (sequence, head) carries the fp32 state across chunks and writes o.
+ *
+ * Dense call (cu_seqlens == NULL): N must equal B; each of the B rows is one
+ * sequence of T tokens.
+ *   q, k       [B, T, H, Dk]  io dtype        log_alpha, b [B, T, H, Dk] f32
+ *   v          [B, T, H, Dv]  io dtype        w            [B, T, H, Dv] f32
+ *   o          [B, T, H, Dv]  io dtype (output)
+ *   S0         [N, H, Dk, Dv] f32, or NULL for a zero initial state
+ *   S_final    [N, H, Dk, Dv] f32 (output), or NULL to skip it; may alias S0.
+ * Packed variable-length call (cu_seqlens != NULL): B must be 1 and T is the
+ * total token count; cu_seqlens is a DEVICE int32 array of N+1 offsets with
+ * cu_seqlens[0] == 0, non-decreasing, cu_seqlens[N] == T.  Sequence n owns
+ * tokens [cu_seqlens[n], cu_seqlens[n+1]), starts from S0[n] (or zero), is
+ * chunked from its own first token (its last chunk may be shorter than 64)
+ * and writes S_final[n].  Offsets are clamped into [0, T] on the device, so
+ * malformed offsets give undefined values but no out-of-bounds access.
+ *
+ * The workspace (device memory, >= gdn2_chunk_fwd_workspace_bytes(...) bytes,
+ * 256-byte aligned) holds the per-chunk intermediates; its layout is
+ * described by gdn2_chunk_fwd_workspace_layout.  T == 0 or N == 0 is allowed:
+ * then S_final = S0 (or zero) and o is untouched.
+ *
+ * Precondition on the decay: within one 64-token chunk, the decay of any key
+ * channel must stay below about 170 nats (half of it must be representable
+ * as an fp32 exponent).  Larger decays overflow the scaled factors.
+ */
+int gdn2_chunk_fwd(const void *q, const void *k, const void *v,
+                   const float *log_alpha, const float *b, const float *w,
+                   const float *S0, void *o, float *S_final,
+                   const int32_t *cu_seqlens, int N,
+                   int B, int T, int H, int Dk, int Dv, int io,
+                   void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * The stages of gdn2_chunk_fwd, for profiling each kernel on its own and for
+ * inspecting the intermediates.  gdn2_chunk_fwd == gdn2_chunk_fwd_stages(...,
+ * GDN2_STAGE_ALL).  A later call with the same arguments and workspace may run
+ * the remaining stages: the workspace carries the chunk table and the chunk
+ * factors between calls.  Running a stage whose inputs were never produced in
+ * this workspace gives undefined values (but no out-of-bounds access).
+ */
+#define GDN2_STAGE_PLAN 1       /* packed calls: build the chunk table on the device */
+#define GDN2_STAGE_FACTORS 2    /* per-chunk cumulative decay, A, T = (I+A)^-1, W, M, Qhat, Khat */
+#define GDN2_STAGE_PROPAGATE 4  /* sequential state propagation: U, U_eff, o, S_final */
+#define GDN2_STAGE_ALL 7
+
+int gdn2_chunk_fwd_stages(const void *q, const void *k, const void *v,
+                          const float *log_alpha, const float *b, const float *w,
+                          const float *S0, void *o, float *S_final,
+                          const int32_t *cu_seqlens, int N,
+                          int B, int T, int H, int Dk, int Dv, int io,
+                          void *workspace, size_t workspace_bytes, void *stream, int stages);
+
+/*
+ * Where gdn2_chunk_fwd keeps its per-chunk intermediates inside the
+ * workspace, for inspection by tests.  Offsets are in bytes from the
+ * workspace start; every array is indexed by (chunk id c, head h) as
+ * [c][h][...], with chunk ids numbered sequence by sequence (dense: chunk c
+ * of row n has id n * ceil(T/64) + c).  Element type is the io dtype unless
+ * stated.  For a chunk shorter than 64 tokens, the rows past its length are
+ * zero in W, M and Qhat, the matching columns of M and KhatT are zero, and T
+ * is the identity on those rows and columns.
+ *   Tinv   [64][64]  (I + A)^-1, row-major
+ *   W      [64][Dk]  T (gamma * b * k), token-major
+ *   Qhat   [64][Dk]  gamma * q, token-major
+ *   KhatT  [Dk][64]  (exp(g_last - g) * k)^T, channel-major
+ *   M      [64][64]  lower incl. diagonal, M_ij = sum_c q_i k_j exp(g_i - g_j)
+ *   gamma_last [Dk]  f32, exp(g_last)
+ *   plan   int32: for packed calls, [0..N] first chunk id of each sequence
+ *          followed by 3 ints (sequence, first token, length) per chunk.
+ * Returns GDN2_OK and fills the fields, or an error status.
+ */
+typedef struct gdn2_workspace_layout {
+    size_t total_bytes;
+    int max_chunks;          /* chunk-id capacity */
+    size_t off_Tinv, off_W, off_Qhat, off_KhatT, off_M, off_gamma_last, off_plan;
+} gdn2_workspace_layout;
+
+int gdn2_chunk_fwd_workspace_layout(int N, int B, int T, int H, int Dk, int Dv,
+                                    int io, int varlen, gdn2_workspace_layout *out);
+
+/*
+ * One recurrent decode token for B independent sequences (constant-memory
+ * decoding: the gist.science summary, "Problem statement").  The state is
+ * read once and written once, in place:
+ *   r = sum_c alpha_c b_c k_c S[c,:],  p = sum_c alpha_c q_c S[c,:]
+ *   o = p + (q . k) (w*v - r),         S[c,:] <- alpha_c S[c,:] + k_c (w*v - r)
+ * which equals the update above followed by o = S_t^T q_t.
+ *   q, k   [B, H, Dk] io dtype      log_alpha, b [B, H, Dk] f32
+ *   v      [B, H, Dv] io dtype      w            [B, H, Dv] f32
+ *   S      [B, H, Dk, Dv] f32, updated in place
+ *   o      [B, H, Dv] io dtype (output); must not alias S or any input.
+ */
+int gdn2_step(const void *q, const void *k, const void *v,
+              const float *log_alpha, const float *b, const float *w,
+              float *S, void *o, int B, int H, int Dk, int Dv, int io,
+              void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBGDN2_H */

@@ -1,0 +1,212 @@
+"""GPU parity of gdn2_chunk_fwd against the fp64 oracle: end to end, per stage
+(the chunk intermediates kept in the workspace), varlen, edge cases and the
+full-size workloads on sampled (sequence, head) pairs."""
+
+import numpy as np
+import pytest
+
+import gated_delta_rule_47_amd as g
+import oracle as O
+import workloads as W
+from gpu_util import dev, gpu_slices, host, log, oracle_sampled, tol, upload_chunk
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(inp, d=None, workspace=None):
+    import torch
+    d = d or upload_chunk(inp)
+    o, S = g.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], S0=d["S0"],
+                       cu_seqlens=d["cu_seqlens"], workspace=workspace)
+    torch.cuda.synchronize()
+    return o, S
+
+
+def _check_all(inp, label):
+    o, S = _run(inp)
+    args = [inp[x] for x in ("q", "k", "v", "log_alpha", "b", "w")]
+    o_ref, S_ref = O.recurrence(*args, S0=inp["S0"], cu_seqlens=inp["cu_seqlens"])
+    eo, es = O.rel_max_err(host(o), o_ref), O.rel_max_err(host(S), S_ref)
+    log("%s: err_o %.3e err_S %.3e" % (label, eo, es))
+    assert eo <= tol(inp["io"]) and es <= tol(inp["io"])
+    return o, S
+
+
+def test_tiny_fp32_workload_full():
+    """B=1, H=2, T=256, d=64, all fp32, S0 = 0: whole output against the oracle."""
+    _check_all(W.make_chunk_inputs(W.TINY_F32), "tiny_f32")
+
+
+@pytest.mark.parametrize("io,D", [(W.BF16, 128), (W.BF16, 64), (W.F32, 128), (W.F32, 64)])
+def test_dense_ragged_with_state(io, D):
+    """Several chunks and a ragged tail (T = 200 = 3*64 + 8), nonzero S0."""
+    wl = W.ChunkWorkload("dense_test", 2, 200, 3, D, D, io, 555 + D, with_S0=True)
+    _check_all(W.make_chunk_inputs(wl), "dense io=%s D=%d" % (io, D))
+
+
+@pytest.mark.parametrize("io", [W.BF16, W.F32])
+def test_varlen_edge_lengths(io):
+    """Packed sequences of lengths 1, 63, 64, 65, 130, 0 and 7 with S0."""
+    wl = W.ChunkWorkload("varlen_test", 1, 0, 2, 128, 128, io, 777, with_S0=True, n_seqs=7)
+    _check_all(W.make_chunk_inputs(wl, lengths=[1, 63, 64, 65, 130, 0, 7]), "varlen io=%s" % io)
+
+
+def test_erase_gate_range_zero_to_two():
+    """The kernels do not assume b <= 1 (widened [0, 2] erase range)."""
+    wl = W.ChunkWorkload("b2_test", 1, 192, 2, 128, 128, W.BF16, 888, with_S0=True)
+    _check_all(W.make_chunk_inputs(wl, b_scale=2.0), "b in [0,2]")
+
+
+def test_empty_sequence_returns_initial_state():
+    import torch
+    wl = W.ChunkWorkload("empty_test", 2, 64, 2, 128, 128, W.BF16, 999, with_S0=True)
+    inp = W.make_chunk_inputs(wl)
+    d = upload_chunk(inp)
+    z = d["q"][:, :0].contiguous()
+    zf = d["log_alpha"][:, :0].contiguous()
+    o, S = g.chunk_fwd(z, z, z, zf, zf, zf, S0=d["S0"])
+    torch.cuda.synchronize()
+    assert o.shape[1] == 0
+    assert torch.equal(S, d["S0"])
+
+
+def test_deterministic_bitwise():
+    import torch
+    inp = W.make_chunk_inputs(W.SEQ_4K, T=300, H=4)
+    d = upload_chunk(inp)
+    o1, S1 = _run(inp, d)
+    o2, S2 = _run(inp, d)
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+def test_state_passing_split_sequence():
+    """run(x1 || x2) == run(x2, S0 = run(x1).S_final) on the GPU (resume)."""
+    import torch
+    wl = W.ChunkWorkload("split_test", 2, 320, 2, 128, 128, W.BF16, 1234, with_S0=True)
+    inp = W.make_chunk_inputs(wl)
+    d = upload_chunk(inp)
+    o, S = _run(inp, d)
+    keys = ("q", "k", "v", "log_alpha", "b", "w")
+    d1 = {k_: d[k_][:, :128].contiguous() for k_ in keys}
+    d2 = {k_: d[k_][:, 128:].contiguous() for k_ in keys}
+    o1, S1 = g.chunk_fwd(*(d1[k_] for k_ in keys), S0=d["S0"])
+    o2, S2 = g.chunk_fwd(*(d2[k_] for k_ in keys), S0=S1)
+    torch.cuda.synchronize()
+    assert O.rel_max_err(host(torch.cat([o1, o2], 1)), host(o)) <= 2e-2
+    assert O.rel_max_err(host(S2), host(S)) <= 2e-2
+
+
+def test_final_state_aliases_initial_state():
+    import torch
+    wl = W.ChunkWorkload("alias_test", 1, 130, 2, 128, 128, W.BF16, 4321, with_S0=True)
+    inp = W.make_chunk_inputs(wl)
+    d = upload_chunk(inp)
+    o_ref, S_ref = _run(inp, d)
+    S_io = d["S0"].clone()
+    g.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], S0=S_io, S_final=S_io)
+    torch.cuda.synchronize()
+    assert torch.equal(S_io, S_ref)
+
+
+# ---------------------------------------------------------------------------
+# Per-stage parity: the intermediates the chunk-factor kernel leaves in the
+# workspace (cumulative decay via Qhat/Khat/gamma_last, the solved T, W, M)
+# ---------------------------------------------------------------------------
+
+def _ws_view(ws, off, count, dtype, shape):
+    import torch
+    esz = 2 if dtype == torch.bfloat16 else 4
+    return ws[off:off + count * esz].view(dtype).reshape(shape)
+
+
+@pytest.mark.parametrize("io,D,lengths", [(W.F32, 64, None), (W.BF16, 128, None),
+                                          (W.BF16, 128, [70, 5, 64])])
+def test_chunk_factors_in_workspace(io, D, lengths):
+    import torch
+    if lengths is None:
+        wl = W.ChunkWorkload("factors_test", 1, 200, 2, D, D, io, 2468)
+        inp = W.make_chunk_inputs(wl)
+    else:
+        wl = W.ChunkWorkload("factors_vl", 1, 0, 2, D, D, io, 2469, n_seqs=len(lengths))
+        inp = W.make_chunk_inputs(wl, lengths=lengths)
+    varlen = inp["cu_seqlens"] is not None
+    N, B, T, H = inp["N"], inp["B"], inp["T"], inp["H"]
+    ioc = g.GDN2_BF16 if io == W.BF16 else g.GDN2_F32
+    L = g.gdn2_chunk_fwd_workspace_layout(N, B, T, H, D, D, ioc, varlen)
+    ws = torch.zeros(L.total_bytes, dtype=torch.uint8, device="cuda")
+    _run(inp, workspace=ws)
+    tdt = torch.bfloat16 if io == W.BF16 else torch.float32
+    nch = L.max_chunks
+    Tw = host(_ws_view(ws, L.off_Tinv, nch * H * 4096, tdt, (nch, H, 64, 64)))
+    Ww = host(_ws_view(ws, L.off_W, nch * H * 64 * D, tdt, (nch, H, 64, D)))
+    Qw = host(_ws_view(ws, L.off_Qhat, nch * H * 64 * D, tdt, (nch, H, 64, D)))
+    Kw = host(_ws_view(ws, L.off_KhatT, nch * H * 64 * D, tdt, (nch, H, D, 64)))
+    Mw = host(_ws_view(ws, L.off_M, nch * H * 4096, tdt, (nch, H, 64, 64)))
+    Gw = host(_ws_view(ws, L.off_gamma_last, nch * H * D, torch.float32, (nch, H, D)))
+    # chunk list in id order: (row, first token, length)
+    chunks = []
+    if varlen:
+        cu = inp["cu_seqlens"]
+        for n in range(N):
+            for t0 in range(int(cu[n]), int(cu[n + 1]), 64):
+                chunks.append((0, t0, min(64, int(cu[n + 1]) - t0)))
+    else:
+        for n in range(B):
+            for t0 in range(0, T, 64):
+                chunks.append((n, t0, min(64, T - t0)))
+    bound = 1e-2 if io == W.BF16 else 1e-5
+    worst = {}
+    for cid, (row, t0, ln) in enumerate(chunks):
+        for h in range(H):
+            sl = (row, slice(t0, t0 + ln), h)
+            f = O.chunk_factors(*(inp[x][sl] for x in ("q", "k", "v", "log_alpha", "b", "w")))
+            pairs = {"Tinv": (Tw[cid, h, :ln, :ln], f["Tinv"]),
+                     "W": (Ww[cid, h, :ln], f["W"]),
+                     "Qhat": (Qw[cid, h, :ln], f["Qhat"]),
+                     "KhatT": (Kw[cid, h, :, :ln], f["Khat"].T),
+                     "M": (Mw[cid, h, :ln, :ln], f["M"]),
+                     "gamma_last": (Gw[cid, h], f["gamma_last"])}
+            for name, (got, ref) in pairs.items():
+                worst[name] = max(worst.get(name, 0.0), O.rel_max_err(got, ref))
+            # padding rows/columns past the chunk's length
+            assert np.all(Ww[cid, h, ln:] == 0) and np.all(Qw[cid, h, ln:] == 0)
+            assert np.all(Kw[cid, h, :, ln:] == 0) and np.all(Mw[cid, h, ln:] == 0)
+            assert np.all(Mw[cid, h, :, ln:] == 0)
+            np.testing.assert_array_equal(Tw[cid, h, ln:, ln:], np.eye(64 - ln))
+            assert np.all(Tw[cid, h, :ln, ln:] == 0) and np.all(Tw[cid, h, ln:, :ln] == 0)
+    log("factors io=%s D=%d: %s" % (io, D, " ".join("%s %.2e" % kv for kv in worst.items())))
+    for name, e in worst.items():
+        assert e <= bound, (name, e)
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads, oracle on sampled (sequence, head) pairs
+# ---------------------------------------------------------------------------
+
+def _check_sampled(wl, pairs):
+    inp = W.make_chunk_inputs(wl)
+    log("%s: T=%d N=%d generated" % (wl.name, inp["T"], inp["N"]))
+    o, S = _run(inp)
+    ref = oracle_sampled(inp, pairs)
+    worst_o = worst_S = 0.0
+    for (n, h), (o_r, S_r) in ref.items():
+        o_g, S_g = gpu_slices(inp, o, S, n, h)
+        worst_o = max(worst_o, O.rel_max_err(o_g, o_r))
+        worst_S = max(worst_S, O.rel_max_err(S_g, S_r))
+    log("%s: sampled %s err_o %.3e err_S %.3e" % (wl.name, pairs, worst_o, worst_S))
+    assert worst_o <= tol(wl.io) and worst_S <= tol(wl.io)
+    assert np.isfinite(host(S)).all()
+
+
+def test_seq_4k_workload_sampled_heads():
+    _check_sampled(W.SEQ_4K, [(0, 0), (0, 9), (0, 15)])
+
+
+def test_batch_4k_workload_sampled_pairs():
+    _check_sampled(W.BATCH_4K, [(0, 0), (3, 11), (7, 15)])
+
+
+def test_varlen_workload_sampled_sequences():
+    lens = W.varlen_lengths(W.VARLEN)
+    longest = int(np.argmax(lens))
+    _check_sampled(W.VARLEN, [(0, 0), (longest, 6), (31, 15)])

@@ -10,7 +10,8 @@ Shapes stand in for a 1.3B-parameter token-mixer layer with 16 heads and a
 128 x 128 state per head (iplexlaw blog, "Condiciones de comparación": 16
 heads, 128 x 128 state, 262,144 state values per layer and batch element;
 4K training context).  Distributions:
-  q, k ~ N(0, 1), then L2-normalised per (token, head) in float64;
+  q, k ~ N(0, 1), then L2-normalised per (token, head) (norm accumulated in
+  float64, scaling in float32);
   v ~ N(0, 1);
   log alpha ~ U[-0.2, -0.001] per key channel;
   b = sigmoid(N(0, 1)) over d_k;  w = sigmoid(N(0, 1)) over d_v;
@@ -74,9 +75,13 @@ CHUNK_WORKLOADS = (TINY_F32, SEQ_4K, BATCH_4K, VARLEN)
 def bf16_bits(x):
     """float32 array -> uint16 bfloat16 bit patterns, round-to-nearest-even."""
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
-    nan = (u & 0x7FFFFFFF) > 0x7F800000
-    rounded = u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))
-    out = (rounded >> np.uint32(16)).astype(np.uint16)
+    nan = (u & np.uint32(0x7FFFFFFF)) > np.uint32(0x7F800000)
+    r = u >> np.uint32(16)
+    r &= np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u
+    r >>= np.uint32(16)
+    out = r.astype(np.uint16)
     if nan.any():
         out[nan] = 0x7FC0
     return out
@@ -93,12 +98,17 @@ def bf16_round(x):
 
 
 def _sigmoid(x):
-    return (1.0 / (1.0 + np.exp(-np.asarray(x, dtype=np.float64)))).astype(np.float32)
+    x = np.asarray(x, dtype=np.float32)
+    out = np.exp(-x)
+    out += np.float32(1.0)
+    np.reciprocal(out, out=out)
+    return out
 
 
 def _l2norm(x):
-    x64 = np.asarray(x, dtype=np.float64)
-    return (x64 / np.linalg.norm(x64, axis=-1, keepdims=True)).astype(np.float32)
+    x = np.asarray(x, dtype=np.float32)
+    inv = 1.0 / np.sqrt(np.einsum("...i,...i->...", x, x, dtype=np.float64))
+    return (x * inv[..., None].astype(np.float32)).astype(np.float32)
 
 
 def _io_cast(x, io):
