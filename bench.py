@@ -59,10 +59,13 @@ def parse():
 # ---------------------------------------------------------------------------
 
 def chunk_alg_bytes(n_tok_heads, n_states, d, io_bytes):
-    """Per kernel: factors reads q, k, log_alpha, b; propagation reads v, w and
-    the initial state and writes o and the final state."""
-    factors = n_tok_heads * (2 * d * io_bytes + 2 * d * 4)
-    prop = n_tok_heads * (d * io_bytes + d * 4 + d * io_bytes) + n_states * 2 * d * d * 4
+    """Algorithmic bytes, split by the kernel that moves them: the chunk-factor
+    kernel reads every per-token input (q, k, v in the io type; log_alpha, b,
+    w in fp32); the propagation kernel reads the initial state and writes o
+    and the final state.  The chunk factors passed between the two kernels
+    through the workspace are not algorithmic bytes."""
+    factors = n_tok_heads * (3 * d * io_bytes + 3 * d * 4)
+    prop = n_tok_heads * d * io_bytes + n_states * 2 * d * d * 4
     return factors, prop
 
 

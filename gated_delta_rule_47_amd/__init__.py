@@ -27,6 +27,7 @@ GDN2_STAGE_PLAN = 1
 GDN2_STAGE_FACTORS = 2
 GDN2_STAGE_PROPAGATE = 4
 GDN2_STAGE_ALL = 7
+GDN2_STAGE_STORE_T = 8
 
 EXPORTED = ("gdn2_abi_version", "gdn2_status_string", "gdn2_chunk_fwd_workspace_bytes",
             "gdn2_chunk_fwd_workspace_layout", "gdn2_chunk_fwd", "gdn2_chunk_fwd_stages",
@@ -43,7 +44,8 @@ class WorkspaceLayout(ctypes.Structure):
     _fields_ = [("total_bytes", ctypes.c_size_t), ("max_chunks", ctypes.c_int),
                 ("off_Tinv", ctypes.c_size_t), ("off_W", ctypes.c_size_t),
                 ("off_Qhat", ctypes.c_size_t), ("off_KhatT", ctypes.c_size_t),
-                ("off_M", ctypes.c_size_t), ("off_gamma_last", ctypes.c_size_t),
+                ("off_M", ctypes.c_size_t), ("off_U", ctypes.c_size_t),
+                ("off_gamma_last", ctypes.c_size_t),
                 ("off_plan", ctypes.c_size_t)]
 
 

@@ -65,6 +65,7 @@ bool workspace_layout(int N, int B, int T, int H, int Dk, int Dv, size_t io_byte
     L.off_Qh = take(chd * kChunk * Dk * io_bytes);
     L.off_KhT = take(chd * Dk * kChunk * io_bytes);
     L.off_M = take(chd * kChunk * kChunk * io_bytes);
+    L.off_U = take(chd * kChunk * Dv * io_bytes);
     L.off_gl = take(chd * Dk * sizeof(float));
     L.plan_ints = varlen ? (size_t)N + 1 + 3 * (size_t)max_chunks : 0;
     L.off_plan = take(L.plan_ints * sizeof(int32_t));
@@ -115,6 +116,7 @@ int gdn2_chunk_fwd_workspace_layout(int N, int B, int T, int H, int Dk, int Dv, 
     out->off_Qhat = L.off_Qh;
     out->off_KhatT = L.off_KhT;
     out->off_M = L.off_M;
+    out->off_U = L.off_U;
     out->off_gamma_last = L.off_gl;
     out->off_plan = L.off_plan;
     return GDN2_OK;
@@ -125,7 +127,7 @@ int gdn2_chunk_fwd_stages(const void *q, const void *k, const void *v, const flo
                           float *S_final, const int32_t *cu_seqlens, int N, int B, int T, int H,
                           int Dk, int Dv, int io, void *workspace, size_t workspace_bytes,
                           void *stream_ptr, int stages) {
-    if (stages & ~GDN2_STAGE_ALL) return GDN2_ERR_INVALID_ARGUMENT;
+    if (stages & ~(GDN2_STAGE_ALL | GDN2_STAGE_STORE_T)) return GDN2_ERR_INVALID_ARGUMENT;
     if (io != GDN2_F32 && io != GDN2_BF16) return GDN2_ERR_INVALID_ARGUMENT;
     if (N < 0 || B < 0 || T < 0 || H < 0 || Dk <= 0 || Dv <= 0) return GDN2_ERR_INVALID_ARGUMENT;
     if (!supported_dims(Dk, Dv)) return GDN2_ERR_UNSUPPORTED;
@@ -154,6 +156,7 @@ int gdn2_chunk_fwd_stages(const void *q, const void *k, const void *v, const flo
         return GDN2_ERR_WORKSPACE;
 
     hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+    (void)hipGetLastError();  // a stale error left by other code is not ours to report
     char *ws = static_cast<char *>(workspace);
     ChunkArgs a{};
     a.q = q;
@@ -178,6 +181,8 @@ int gdn2_chunk_fwd_stages(const void *q, const void *k, const void *v, const flo
     a.ws_Qh = ws + L.off_Qh;
     a.ws_KhT = ws + L.off_KhT;
     a.ws_M = ws + L.off_M;
+    a.ws_U = ws + L.off_U;
+    a.store_T = (stages & GDN2_STAGE_STORE_T) ? 1 : 0;
     a.ws_gl = reinterpret_cast<float *>(ws + L.off_gl);
     const bool bf = io == GDN2_BF16;
 
@@ -213,6 +218,7 @@ int gdn2_step(const void *q, const void *k, const void *v, const float *log_alph
     if ((const void *)o == (const void *)S) return GDN2_ERR_INVALID_ARGUMENT;
     StepArgs a{q, k, v, log_alpha, b, w, S, o, B, H};
     hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+    (void)hipGetLastError();  // a stale error left by other code is not ours to report
     return finish(launch_step(a, Dk, io == GDN2_BF16, stream), stream);
 }
 

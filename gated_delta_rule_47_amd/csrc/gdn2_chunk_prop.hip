@@ -2,9 +2,8 @@
 //
 // For each (sequence, head) the fp32 state is carried across the chunks of
 // the sequence in order.  With the chunk factors of the chunk-factor kernel
-// (T = (I + A)^-1, W, Qhat, Khat, M, gamma_last) and Z = w * v, one chunk is
+// (U = T (w*v), W, Qhat, Khat, M, gamma_last), one chunk is
 //
-//   U     = T Z                      write-side auxiliary
 //   U_eff = U - W S                  per-token corrected values
 //   O     = Qhat S + M U_eff         the query reads the updated state
 //   S    <- Diag(gamma_last) S + Khat^T U_eff
@@ -14,10 +13,14 @@
 // axis) independently, so each (sequence, head) is split into Dv / DVS
 // column slabs, one workgroup per slab.  The slab's fp32 state lives in MFMA
 // accumulator registers for the whole sequence; a bf16 (or fp32) copy of it,
-// transposed, is kept in LDS as the MFMA operand.  Workgroup ids are mapped
+// transposed and double-buffered, is kept in LDS as the MFMA operand.  All
+// loads of chunk c+1 (operand fragments straight from the workspace into
+// registers) are issued before chunk c is computed.  Workgroup ids are mapped
 // so that all slabs of one (sequence, head) land on the same XCD (ids are
 // dispatched round-robin over the 8 XCDs), where they share the chunk
 // factors through that XCD's L2.
+
+#include <type_traits>
 
 #include "gdn2_device.h"
 #include "gdn2_internal.h"
@@ -28,23 +31,94 @@ template <typename E, int DK, int DVS>
 struct PropCfg {
     static constexpr int PAD = (sizeof(E) == 2) ? 8 : 4;
     static constexpr int LDS_ = DK + PAD;       // S^T     [DVS][LDS_]
-    static constexpr int LDZ = kChunk + PAD;    // Z^T, U_eff^T [DVS][LDZ]
+    static constexpr int LDU = kChunk + PAD;    // U_eff^T [DVS][LDU]
     static constexpr int NCB = DVS / 16;        // 16-column blocks of the slab
     static constexpr int NKB = DK / 16;         // 16-row blocks of the state
     static constexpr int S_TPW = NKB * NCB / 4; // state tiles per wave
-    static constexpr size_t SMEM = (size_t(DVS) * LDS_ + 2 * size_t(DVS) * LDZ) * sizeof(E);
-    static_assert(S_TPW * 4 == NKB * NCB, "state tiles split over 4 waves");
+    static constexpr int KB_W = NKB / 4;        // state row blocks per wave
+    static constexpr size_t SZ_S = size_t(DVS) * LDS_ * sizeof(E);
+    static constexpr size_t SMEM = 2 * SZ_S + size_t(DVS) * LDU * sizeof(E);
+    static_assert(S_TPW * 4 == NKB * NCB && KB_W * 4 == NKB, "state tiles split over 4 waves");
 };
+
+// Everything one wave reads from memory for one chunk: the operand fragments of
+// its row blocks (W, Qhat, M, the state rows of Khat^T, gamma_last) and its U
+// tiles (already in accumulator order).
+template <typename E, int DK, int DVS>
+struct ChunkFrags {
+    using M = Mma<E>;
+    using C = PropCfg<E, DK, DVS>;
+    using V4 = typename std::conditional<sizeof(E) == 2, bf16x4, f32x4>::type;
+    static constexpr int NK64 = kChunk / M::KS;
+    static constexpr int NKD = DK / M::KS;
+    typename M::frag w[NKD], qh[NKD], m[NK64], kh[C::KB_W][NK64];
+    V4 u[C::NCB];
+    f32x4 gl[C::KB_W];
+    int tok0, len;
+};
+
+template <typename E, int DK, int DV, int DVS>
+__device__ __forceinline__ void load_chunk(ChunkFrags<E, DK, DVS> &f, const ChunkArgs &a, int n,
+                                           int h, int cid, int cbeg, int col0, int wave,
+                                           int lane) {
+    using M = Mma<E>;
+    using C = PropCfg<E, DK, DVS>;
+    using F = ChunkFrags<E, DK, DVS>;
+    if (a.plan) {
+        // Entries are clamped so that a stale or malformed table stays in bounds.
+        const int32_t *e = a.plan + a.N + 1 + 3 * (size_t)cid;
+        f.tok0 = min(max(e[1], 0), a.T);
+        f.len = min(max(e[2], 0), min(kChunk, a.T - f.tok0));
+    } else {
+        const int c = cid - cbeg;
+        f.tok0 = n * a.T + c * kChunk;
+        f.len = min(kChunk, a.T - c * kChunk);
+    }
+    const size_t ch = (size_t)cid * a.H + h;
+    // W, Qhat, M and Khat^T are stored in fragment order (see frag_index).
+    const E *Wg = reinterpret_cast<const E *>(a.ws_W) + ch * kChunk * DK;
+    const E *Qg = reinterpret_cast<const E *>(a.ws_Qh) + ch * kChunk * DK;
+    const E *Mg = reinterpret_cast<const E *>(a.ws_M) + ch * kChunk * kChunk;
+    const E *Kg = reinterpret_cast<const E *>(a.ws_KhT) + ch * DK * kChunk;
+    const E *Ug = reinterpret_cast<const E *>(a.ws_U) + ch * kChunk * DV +
+                  ((wave * (DV / 16) + col0 / 16) * 64 + lane) * 4;
+    const float *gl = a.ws_gl + ch * DK;
+#pragma unroll
+    for (int cb = 0; cb < C::NCB; ++cb)
+        f.u[cb] = *reinterpret_cast<const typename F::V4 *>(Ug + cb * 64 * 4);
+#pragma unroll
+    for (int kk = 0; kk < F::NKD; ++kk) f.w[kk] = load_frag_packed<E>(Wg, DK, wave, kk, lane);
+#pragma unroll
+    for (int kk = 0; kk < F::NK64; ++kk) f.m[kk] = load_frag_packed<E>(Mg, kChunk, wave, kk, lane);
+#pragma unroll
+    for (int kk = 0; kk < F::NKD; ++kk) f.qh[kk] = load_frag_packed<E>(Qg, DK, wave, kk, lane);
+#pragma unroll
+    for (int b = 0; b < C::KB_W; ++b) {
+        const int cblk = wave * C::KB_W + b;
+#pragma unroll
+        for (int kk = 0; kk < F::NK64; ++kk)
+            f.kh[b][kk] = load_frag_packed<E>(Kg, kChunk, cblk, kk, lane);
+        f.gl[b] = *reinterpret_cast<const f32x4 *>(gl + 16 * cblk + 4 * (lane >> 4));
+    }
+}
+
+template <typename E, typename V4>
+__device__ __forceinline__ f32x4 to_f32x4(V4 x) {
+    return f32x4{to_f32(x[0]), to_f32(x[1]), to_f32(x[2]), to_f32(x[3])};
+}
 
 template <typename E, int DK, int DV, int DVS>
 __global__ __launch_bounds__(kThreads, 2) void chunk_prop_kernel(ChunkArgs a) {
     using C = PropCfg<E, DK, DVS>;
     using M = Mma<E>;
-    constexpr int NS = DV / DVS, LDS_ = C::LDS_, LDZ = C::LDZ, NCB = C::NCB;
+    using F = ChunkFrags<E, DK, DVS>;
+    constexpr int NS = DV / DVS, LDS_ = C::LDS_, LDU = C::LDU, NCB = C::NCB;
+    // Double-buffer the fragments in registers for bf16; fp32 fragments are
+    // 4x larger, so the fp32 path loads each chunk just before using it.
+    constexpr bool kPrefetch = sizeof(E) == 2;
     __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
-    E *sS = reinterpret_cast<E *>(smem);   // S^T of the slab
-    E *sZ = sS + DVS * LDS_;               // Z^T
-    E *sU = sZ + DVS * LDZ;                // U_eff^T
+    E *sS0 = reinterpret_cast<E *>(smem);               // S^T of the slab, two buffers
+    E *sU = reinterpret_cast<E *>(smem + 2 * C::SZ_S);   // U_eff^T
 
     const int H = a.H;
     const int x = blockIdx.x, xcd = x & 7, rest = x >> 3;
@@ -63,86 +137,62 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prop_kernel(ChunkArgs a) {
         cend = cbeg + a.NC;
     }
 
+    F cur, nxt;
+    if (cbeg < cend) load_chunk<E, DK, DV, DVS>(cur, a, n, h, cbeg, cbeg, col0, wave, lane);
+
     // Initial state (fp32 accumulators) and its operand copy.
     f32x4 Sacc[C::S_TPW];
 #pragma unroll
     for (int u = 0; u < C::S_TPW; ++u) {
-        const int t = wave * C::S_TPW + u, cblk = t / NCB, colb = t % NCB;
+        const int cblk = wave * C::KB_W + u / NCB, colb = u % NCB;
         const int col = col0 + 16 * colb + (lane & 15);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int c = 16 * cblk + 4 * (lane >> 4) + r;
             Sacc[u][r] = a.S0 ? a.S0[((size_t)chain * DK + c) * DV + col] : 0.0f;
         }
-        store_tile_t<E>(sS + 16 * colb * LDS_ + 16 * cblk, LDS_, Sacc[u], lane);
+        store_tile_t<E>(sS0 + 16 * colb * LDS_ + 16 * cblk, LDS_, Sacc[u], lane);
     }
+    __syncthreads();
 
-    const E *vin = reinterpret_cast<const E *>(a.v);
     E *out = reinterpret_cast<E *>(a.o);
-    constexpr int ZC = DVS / 4;  // columns of Z per thread
-    const int zi = tid & 63, zc0 = (tid >> 6) * ZC;
-
+    int buf = 0;
     for (int cid = cbeg; cid < cend; ++cid) {
-        int tok0, len;
-        if (a.plan) {
-            const int32_t *e = a.plan + a.N + 1 + 3 * (size_t)cid;
-            tok0 = min(max(e[1], 0), a.T);
-            len = min(max(e[2], 0), min(kChunk, a.T - tok0));
-        } else {
-            const int c = cid - cbeg;
-            tok0 = n * a.T + c * kChunk;
-            len = min(kChunk, a.T - c * kChunk);
+        if constexpr (kPrefetch) {
+            if (cid + 1 < cend)
+                load_chunk<E, DK, DV, DVS>(nxt, a, n, h, cid + 1, cbeg, col0, wave, lane);
         }
-        const size_t ch = (size_t)cid * H + h;
-        const E *Tg = reinterpret_cast<const E *>(a.ws_T) + ch * kChunk * kChunk;
-        const E *Wg = reinterpret_cast<const E *>(a.ws_W) + ch * kChunk * DK;
-        const E *Qg = reinterpret_cast<const E *>(a.ws_Qh) + ch * kChunk * DK;
-        const E *Kg = reinterpret_cast<const E *>(a.ws_KhT) + ch * DK * kChunk;
-        const E *Mg = reinterpret_cast<const E *>(a.ws_M) + ch * kChunk * kChunk;
-        const float *gl = a.ws_gl + ch * DK;
+        const E *sS = sS0 + buf * (DVS * LDS_);
+        E *sSn = sS0 + (buf ^ 1) * (DVS * LDS_);
 
-        // Z^T = (w * v)^T of the slab (zero past the chunk's length).
-        {
-            float zv[ZC];
-            if (zi < len) {
-                const size_t off = ((size_t)(tok0 + zi) * H + h) * DV + col0 + zc0;
+        // U_eff rows of block `wave`:  U - W S.
 #pragma unroll
-                for (int j = 0; j < ZC; ++j) zv[j] = a.w[off + j] * to_f32(vin[off + j]);
-            } else {
+        for (int cb = 0; cb < NCB; ++cb) {
+            f32x4 ws = zero4();
 #pragma unroll
-                for (int j = 0; j < ZC; ++j) zv[j] = 0.0f;
-            }
-#pragma unroll
-            for (int j = 0; j < ZC; ++j) sZ[(zc0 + j) * LDZ + zi] = from_f32<E>(zv[j]);
-        }
-        __syncthreads();
-
-        // U_eff rows of block `wave`:  T Z - W S.
-        {
-            const int KT = ((16 * (wave + 1) + M::KS - 1) / M::KS) * M::KS;
-#pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) {
-                f32x4 u = mma_tile_k<E>(zero4(), Tg + 16 * wave * kChunk, kChunk,
-                                        sZ + 16 * cb * LDZ, LDZ, KT, lane);
-                f32x4 ws = mma_tile<E, DK>(zero4(), Wg + 16 * wave * DK, DK,
-                                           sS + 16 * cb * LDS_, LDS_, lane);
-                store_tile_t<E>(sU + 16 * cb * LDZ + 16 * wave, LDZ, u - ws, lane);
-            }
+            for (int kk = 0; kk < F::NKD; ++kk)
+                ws = M::mma(cur.w[kk], load_frag<E>(sS + 16 * cb * LDS_ + kk * M::KS, LDS_, lane),
+                            ws);
+            store_tile_t<E>(sU + 16 * cb * LDU + 16 * wave, LDU, to_f32x4<E>(cur.u[cb]) - ws, lane);
         }
         __syncthreads();
 
         // O^T rows of block `wave`:  D[col][i] = S^T Qhat^T + U_eff^T M^T.
         {
-            const int KM = ((16 * (wave + 1) + M::KS - 1) / M::KS) * M::KS;
             const int i = 16 * wave + (lane & 15);
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) {
-                f32x4 acc = mma_tile<E, DK>(zero4(), sS + 16 * cb * LDS_, LDS_,
-                                            Qg + 16 * wave * DK, DK, lane);
-                acc = mma_tile_k<E>(acc, sU + 16 * cb * LDZ, LDZ, Mg + 16 * wave * kChunk, kChunk,
-                                    KM, lane);
-                if (i < len) {
-                    E *dst = out + ((size_t)(tok0 + i) * H + h) * DV + col0 + 16 * cb +
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int kk = 0; kk < F::NKD; ++kk)
+                    acc = M::mma(load_frag<E>(sS + 16 * cb * LDS_ + kk * M::KS, LDS_, lane),
+                                 cur.qh[kk], acc);
+#pragma unroll
+                for (int kk = 0; kk < F::NK64; ++kk)
+                    acc = M::mma(load_frag<E>(sU + 16 * cb * LDU + kk * M::KS, LDU, lane),
+                                 cur.m[kk], acc);
+                if (i < cur.len) {
+                    E *dst = out + ((size_t)(cur.tok0 + i) * H + h) * DV + col0 + 16 * cb +
                              4 * (lane >> 4);
                     if constexpr (sizeof(E) == 2) {
                         bf16x4 ov;
@@ -155,27 +205,33 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prop_kernel(ChunkArgs a) {
                 }
             }
         }
-        // S <- Diag(gamma_last) S + Khat^T U_eff.
+        // S <- Diag(gamma_last) S + Khat^T U_eff, and its operand copy for the next chunk.
 #pragma unroll
         for (int u = 0; u < C::S_TPW; ++u) {
-            const int t = wave * C::S_TPW + u, cblk = t / NCB, colb = t % NCB;
-            const f32x4 g = *reinterpret_cast<const f32x4 *>(gl + 16 * cblk + 4 * (lane >> 4));
-            const f32x4 d = mma_tile<E, kChunk>(zero4(), Kg + 16 * cblk * kChunk, kChunk,
-                                                sU + 16 * colb * LDZ, LDZ, lane);
-            Sacc[u] = g * Sacc[u] + d;
+            const int b = u / NCB, colb = u % NCB;
+            f32x4 d = zero4();
+#pragma unroll
+            for (int kk = 0; kk < F::NK64; ++kk)
+                d = M::mma(cur.kh[b][kk], load_frag<E>(sU + 16 * colb * LDU + kk * M::KS, LDU, lane),
+                           d);
+            Sacc[u] = cur.gl[b] * Sacc[u] + d;
+            const int cblk = wave * C::KB_W + b;
+            store_tile_t<E>(sSn + 16 * colb * LDS_ + 16 * cblk, LDS_, Sacc[u], lane);
         }
         __syncthreads();
-#pragma unroll
-        for (int u = 0; u < C::S_TPW; ++u) {
-            const int t = wave * C::S_TPW + u, cblk = t / NCB, colb = t % NCB;
-            store_tile_t<E>(sS + 16 * colb * LDS_ + 16 * cblk, LDS_, Sacc[u], lane);
+        buf ^= 1;
+        if constexpr (kPrefetch) {
+            cur = nxt;
+        } else {
+            if (cid + 1 < cend)
+                load_chunk<E, DK, DV, DVS>(cur, a, n, h, cid + 1, cbeg, col0, wave, lane);
         }
     }
 
     if (a.S_final) {
 #pragma unroll
         for (int u = 0; u < C::S_TPW; ++u) {
-            const int t = wave * C::S_TPW + u, cblk = t / NCB, colb = t % NCB;
+            const int cblk = wave * C::KB_W + u / NCB, colb = u % NCB;
             const int col = col0 + 16 * colb + (lane & 15);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -186,10 +242,13 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prop_kernel(ChunkArgs a) {
     }
 }
 
-// Slab width: the widest of 64/32/16 columns that still gives >= 512 workgroups.
+// Slab width.  Every slab workgroup of a (sequence, head) reads all of that
+// chunk's factors through its CU's vector memory path, which bounds the time
+// per chunk; wide slabs cut that re-reading, narrow slabs give parallelism
+// when there are few (sequence, head) chains.
 static int choose_dvs(int chains, int Dv) {
-    for (int dvs = 64; dvs >= 16; dvs >>= 1)
-        if (dvs <= Dv && (long long)chains * (Dv / dvs) >= 512) return dvs;
+    if (Dv >= 64 && chains >= 128) return 64;
+    if (Dv >= 32 && chains >= 64) return 32;
     return 16;
 }
 

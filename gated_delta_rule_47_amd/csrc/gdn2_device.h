@@ -96,6 +96,40 @@ __device__ __forceinline__ f32x4 mma_tile_k(f32x4 acc, const E *A, int lda, cons
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.0f, 0.0f, 0.0f, 0.0f}; }
 
+// Operand-fragment order of a matrix X with K columns (used for the chunk
+// factors kept in the workspace): 16-row blocks by KS-column blocks, each
+// block stored as 64 lanes x KPL elements exactly as load_frag would gather
+// it, so that one wave reads a fragment as one contiguous 64*KPL-element run.
+template <typename E>
+__device__ __forceinline__ size_t frag_index(int r, int k, int K) {
+    using M = Mma<E>;
+    return ((size_t)(r >> 4) * (K / M::KS) + k / M::KS) * (64 * M::KPL) +
+           ((r & 15) + 16 * ((k % M::KS) / M::KPL)) * M::KPL + (k % M::KPL);
+}
+
+// Fragment (row block rb, column block kb) of a matrix stored in fragment order.
+template <typename E>
+__device__ __forceinline__ typename Mma<E>::frag load_frag_packed(const E *X, int K, int rb, int kb,
+                                                                   int lane) {
+    using M = Mma<E>;
+    return *reinterpret_cast<const typename M::frag *>(
+        X + ((size_t)rb * (K / M::KS) + kb) * (64 * M::KPL) + lane * M::KPL);
+}
+
+// X[r][k..k+3] = v (k a multiple of 4) into fragment order.
+template <typename E>
+__device__ __forceinline__ void store4_frag(E *X, int K, int r, int k, f32x4 v) {
+    if constexpr (sizeof(E) == 2) {  // the 4 values are adjacent within a lane's 8
+        bf16x4 b;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b[j] = static_cast<bf16>(v[j]);
+        *reinterpret_cast<bf16x4 *>(X + frag_index<E>(r, k, K)) = b;
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) X[frag_index<E>(r, k + j, K)] = v[j];
+    }
+}
+
 // Store the 4 results a lane holds as 4 consecutive elements of row (l%16)
 // of a row-major destination: dst[(l%16)*ld + 4*(l/16) + r] = acc[r].
 // (This writes the TRANSPOSE of the D tile: Dt[n][m].)

@@ -13,7 +13,8 @@ namespace gdn2 {
 struct WorkspaceLayout {
     size_t total = 0;
     int max_chunks = 0;
-    size_t off_T = 0, off_W = 0, off_Qh = 0, off_KhT = 0, off_M = 0, off_gl = 0, off_plan = 0;
+    size_t off_T = 0, off_W = 0, off_Qh = 0, off_KhT = 0, off_M = 0, off_U = 0, off_gl = 0,
+           off_plan = 0;
     size_t plan_ints = 0;
 };
 
@@ -32,8 +33,9 @@ struct ChunkArgs {
     int NC;               // dense: chunks per sequence
     int max_chunks;       // chunk-id capacity (grid of the chunk-factor kernel)
     int32_t *plan;        // packed calls: chunk table (nullptr for dense calls)
-    void *ws_T, *ws_W, *ws_Qh, *ws_KhT, *ws_M;
+    void *ws_T, *ws_W, *ws_Qh, *ws_KhT, *ws_M, *ws_U;
     float *ws_gl;
+    int store_T;          // the chunk-factor kernel also stores T = (I + A)^-1
 };
 
 struct StepArgs {

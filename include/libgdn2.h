@@ -127,9 +127,10 @@ int gdn2_chunk_fwd(const void *q, const void *k, const void *v,
  * this workspace gives undefined values (but no out-of-bounds access).
  */
 #define GDN2_STAGE_PLAN 1       /* packed calls: build the chunk table on the device */
-#define GDN2_STAGE_FACTORS 2    /* per-chunk cumulative decay, A, T = (I+A)^-1, W, M, Qhat, Khat */
-#define GDN2_STAGE_PROPAGATE 4  /* sequential state propagation: U, U_eff, o, S_final */
+#define GDN2_STAGE_FACTORS 2    /* per chunk: cumulative decay, A, T = (I+A)^-1, W, U, M, Qhat, Khat */
+#define GDN2_STAGE_PROPAGATE 4  /* sequential state propagation: U_eff, o, S_final */
 #define GDN2_STAGE_ALL 7
+#define GDN2_STAGE_STORE_T 8    /* with FACTORS: also store T in the workspace (inspection only) */
 
 int gdn2_chunk_fwd_stages(const void *q, const void *k, const void *v,
                           const float *log_alpha, const float *b, const float *w,
@@ -145,13 +146,19 @@ int gdn2_chunk_fwd_stages(const void *q, const void *k, const void *v,
  * [c][h][...], with chunk ids numbered sequence by sequence (dense: chunk c
  * of row n has id n * ceil(T/64) + c).  Element type is the io dtype unless
  * stated.  For a chunk shorter than 64 tokens, the rows past its length are
- * zero in W, M and Qhat, the matching columns of M and KhatT are zero, and T
- * is the identity on those rows and columns.
- *   Tinv   [64][64]  (I + A)^-1, row-major
- *   W      [64][Dk]  T (gamma * b * k), token-major
- *   Qhat   [64][Dk]  gamma * q, token-major
- *   KhatT  [Dk][64]  (exp(g_last - g) * k)^T, channel-major
+ * zero in W, U, M and Qhat, the matching columns of M and KhatT are zero, and
+ * T is the identity on those rows and columns.
+ *   Tinv   [64][64]  (I + A)^-1, row-major; written only when the stages
+ *                    include GDN2_STAGE_STORE_T
+ *   W      [64][Dk]  T (gamma * b * k)                  } in fragment order,
+ *   Qhat   [64][Dk]  gamma * q                          } see below
+ *   KhatT  [Dk][64]  (exp(g_last - g) * k)^T            }
  *   M      [64][64]  lower incl. diagonal, M_ij = sum_c q_i k_j exp(g_i - g_j)
+ *          Fragment order of an R x K matrix X: X[r][k] is element
+ *            ((r/16)*(K/KS) + k/KS)*64*KPL + ((r%16) + 16*((k%KS)/KPL))*KPL + k%KPL
+ *          with (KS, KPL) = (32, 8) for bf16 and (4, 1) for f32.
+ *   U      [4][Dv/16][64][4]  T (w * v) in MFMA accumulator order: element
+ *                    [I][cb][l][r] is U[16 I + 4 (l / 16) + r][16 cb + l % 16]
  *   gamma_last [Dk]  f32, exp(g_last)
  *   plan   int32: for packed calls, [0..N] first chunk id of each sequence
  *          followed by 3 ints (sequence, first token, length) per chunk.
@@ -160,7 +167,7 @@ int gdn2_chunk_fwd_stages(const void *q, const void *k, const void *v,
 typedef struct gdn2_workspace_layout {
     size_t total_bytes;
     int max_chunks;          /* chunk-id capacity */
-    size_t off_Tinv, off_W, off_Qhat, off_KhatT, off_M, off_gamma_last, off_plan;
+    size_t off_Tinv, off_W, off_Qhat, off_KhatT, off_M, off_U, off_gamma_last, off_plan;
 } gdn2_workspace_layout;
 
 int gdn2_chunk_fwd_workspace_layout(int N, int B, int T, int H, int Dk, int Dv,

@@ -13,11 +13,11 @@ from gpu_util import dev, gpu_slices, host, log, oracle_sampled, tol, upload_chu
 pytestmark = pytest.mark.gpu
 
 
-def _run(inp, d=None, workspace=None):
+def _run(inp, d=None, workspace=None, stages=g.GDN2_STAGE_ALL):
     import torch
     d = d or upload_chunk(inp)
     o, S = g.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], S0=d["S0"],
-                       cu_seqlens=d["cu_seqlens"], workspace=workspace)
+                       cu_seqlens=d["cu_seqlens"], workspace=workspace, stages=stages)
     torch.cuda.synchronize()
     return o, S
 
@@ -119,6 +119,21 @@ def _ws_view(ws, off, count, dtype, shape):
     return ws[off:off + count * esz].view(dtype).reshape(shape)
 
 
+def _frag_order(R, K, bf16):
+    """Flat index of X[r][k] for an R x K matrix stored in MFMA fragment order
+    (the layout the header documents)."""
+    KS, KPL = (32, 8) if bf16 else (4, 1)
+    r = np.arange(R)[:, None]
+    k = np.arange(K)[None, :]
+    return ((r // 16) * (K // KS) + k // KS) * 64 * KPL + ((r % 16) + 16 * ((k % KS) // KPL)) * KPL \
+        + k % KPL
+
+
+def _unfrag(flat, R, K, bf16):
+    """[..., R*K] in fragment order -> [..., R, K]."""
+    return flat[..., _frag_order(R, K, bf16)]
+
+
 @pytest.mark.parametrize("io,D,lengths", [(W.F32, 64, None), (W.BF16, 128, None),
                                           (W.BF16, 128, [70, 5, 64])])
 def test_chunk_factors_in_workspace(io, D, lengths):
@@ -134,15 +149,19 @@ def test_chunk_factors_in_workspace(io, D, lengths):
     ioc = g.GDN2_BF16 if io == W.BF16 else g.GDN2_F32
     L = g.gdn2_chunk_fwd_workspace_layout(N, B, T, H, D, D, ioc, varlen)
     ws = torch.zeros(L.total_bytes, dtype=torch.uint8, device="cuda")
-    _run(inp, workspace=ws)
+    _run(inp, workspace=ws, stages=g.GDN2_STAGE_ALL | g.GDN2_STAGE_STORE_T)
     tdt = torch.bfloat16 if io == W.BF16 else torch.float32
     nch = L.max_chunks
     Tw = host(_ws_view(ws, L.off_Tinv, nch * H * 4096, tdt, (nch, H, 64, 64)))
-    Ww = host(_ws_view(ws, L.off_W, nch * H * 64 * D, tdt, (nch, H, 64, D)))
-    Qw = host(_ws_view(ws, L.off_Qhat, nch * H * 64 * D, tdt, (nch, H, 64, D)))
-    Kw = host(_ws_view(ws, L.off_KhatT, nch * H * 64 * D, tdt, (nch, H, D, 64)))
-    Mw = host(_ws_view(ws, L.off_M, nch * H * 4096, tdt, (nch, H, 64, 64)))
+    bf = io == W.BF16
+    Ww = _unfrag(host(_ws_view(ws, L.off_W, nch * H * 64 * D, tdt, (nch, H, 64 * D))), 64, D, bf)
+    Qw = _unfrag(host(_ws_view(ws, L.off_Qhat, nch * H * 64 * D, tdt, (nch, H, 64 * D))), 64, D, bf)
+    Kw = _unfrag(host(_ws_view(ws, L.off_KhatT, nch * H * 64 * D, tdt, (nch, H, 64 * D))), D, 64, bf)
+    Mw = _unfrag(host(_ws_view(ws, L.off_M, nch * H * 4096, tdt, (nch, H, 4096))), 64, 64, bf)
     Gw = host(_ws_view(ws, L.off_gamma_last, nch * H * D, torch.float32, (nch, H, D)))
+    # U is stored in MFMA accumulator order: [I][cb][lane][r] -> U[16I + 4(lane/16) + r][16cb + lane%16]
+    Us = host(_ws_view(ws, L.off_U, nch * H * 64 * D, tdt, (nch, H, 4, D // 16, 4, 16, 4)))
+    Uw = Us.transpose(0, 1, 2, 4, 6, 3, 5).reshape(nch, H, 64, D)
     # chunk list in id order: (row, first token, length)
     chunks = []
     if varlen:
@@ -162,6 +181,7 @@ def test_chunk_factors_in_workspace(io, D, lengths):
             f = O.chunk_factors(*(inp[x][sl] for x in ("q", "k", "v", "log_alpha", "b", "w")))
             pairs = {"Tinv": (Tw[cid, h, :ln, :ln], f["Tinv"]),
                      "W": (Ww[cid, h, :ln], f["W"]),
+                     "U": (Uw[cid, h, :ln], f["U"]),
                      "Qhat": (Qw[cid, h, :ln], f["Qhat"]),
                      "KhatT": (Kw[cid, h, :, :ln], f["Khat"].T),
                      "M": (Mw[cid, h, :ln, :ln], f["M"]),
@@ -170,6 +190,7 @@ def test_chunk_factors_in_workspace(io, D, lengths):
                 worst[name] = max(worst.get(name, 0.0), O.rel_max_err(got, ref))
             # padding rows/columns past the chunk's length
             assert np.all(Ww[cid, h, ln:] == 0) and np.all(Qw[cid, h, ln:] == 0)
+            assert np.all(Uw[cid, h, ln:] == 0)
             assert np.all(Kw[cid, h, :, ln:] == 0) and np.all(Mw[cid, h, ln:] == 0)
             assert np.all(Mw[cid, h, :, ln:] == 0)
             np.testing.assert_array_equal(Tw[cid, h, ln:, ln:], np.eye(64 - ln))
