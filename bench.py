@@ -47,7 +47,7 @@ def parse():
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--only", choices=["all", "chunk", "decode", "varlen"], default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-rows", type=int, default=2,
+    ap.add_argument("--cpu-sample-rows", type=int, default=8,
                     help="batch rows (4096 tokens x 16 heads each) the oracle runs on")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a plain device copy of 1 GiB (5 times) and exit")
@@ -298,9 +298,15 @@ def main():
         wl = W.DECODE
         wall, mean_ms, med_ms = time_decode(a.decode_steps)
         nbytes = decode_alg_bytes(wl.B, wl.H, wl.Dk, 2)
+        ddig = source_digest("gdn2_step.hip", "gdn2_device.h")
         dec = {"workload": wl.name, "steps": a.decode_steps, "us_per_step": mean_ms * 1e3,
                "GBps": nbytes / (mean_ms * 1e-3) / 1e9,
                "hbm_frac": nbytes / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+               "roofline": {"bound": "hbm", "kernel": "decode_step",
+                            "achieved": nbytes / (mean_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                            "unit": "GB/s", "frac": nbytes / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                            "traffic": stored_traffic("decode_step", wl.name, ddig),
+                            "alg_bytes_per_launch": nbytes, "avg_launch_ms": mean_ms},
                "alg_bytes_per_step": nbytes, "loop_wall_s": wall,
                "tokens_per_s": wl.B * a.decode_steps / wall}
         out["decode"] = dec
