@@ -25,8 +25,11 @@
 //
 // Work split (256 threads = 4 waves): thread (qd, tg) owns channels 4qd..4qd+3
 // of tokens tg*TPG .. tg*TPG+TPG-1, so each wave load instruction reads whole
-// token rows of one head.  LDS is reused phase by phase (about 52 KB for bf16
-// with 128-wide heads; two workgroups per CU).
+// token rows of one head.  LDS is reused phase by phase (68 KB for bf16 with
+// 128-wide heads; two workgroups per CU).  W, M and U leave the accumulators
+// as 512 contiguous bytes per wave store; Qhat and Khat^T, whose fragment order
+// does not match the thread map, go through an LDS image and leave in 1 KiB
+// contiguous wave stores.
 
 #include <type_traits>
 
@@ -55,10 +58,41 @@ struct PrepCfg {
     static constexpr size_t R1 = 2 * SZ_TILE > R1_SOLVE ? 2 * SZ_TILE : R1_SOLVE;
     // Region 2: channel-major (gamma b k)^T, later (w v)^T.
     static constexpr size_t SZ_ET = size_t(DK) * LDC * sizeof(E);
-    static constexpr size_t SMEM = R1 + SZ_ET;
+    // Region 3: fragment-order image of Khat^T, then of Qhat, copied out in
+    // 16-byte granules (NG of them).
+    static constexpr size_t SZ_STG = size_t(kChunk) * DK * sizeof(E);
+    static constexpr int NG = int(SZ_STG / 16);
+    static constexpr size_t SMEM = R1 + SZ_ET + SZ_STG;
     static_assert(NTG * NQUAD == kThreads && TPG * NTG == kChunk && TPG % 4 == 0, "thread map");
     static_assert(size_t(NTG) * DK * 4 <= R1, "group totals fit in region 1");
+    static_assert(NG % kThreads == 0 && SMEM <= 160 * 1024, "staging image");
 };
+
+// The staging image keeps the fragment order in 16-byte granules, with granule
+// g held at slot g ^ ((g/16 ^ g/128) mod 16).  The XOR only permutes the slots
+// inside each aligned run of 16 granules (one pass over all LDS banks), so the
+// contiguous copy-out reads without bank conflicts, and it spreads the
+// scattered writes of the thread map below over distinct banks.
+__device__ __forceinline__ int stage_slot(int g) { return g ^ (((g >> 4) ^ (g >> 7)) & 15); }
+
+template <typename E>
+__device__ __forceinline__ E *stage_ptr(E *img, size_t e) {  // element e of the fragment order
+    constexpr int G = 16 / sizeof(E);
+    return img + (size_t)stage_slot(int(e / G)) * G + e % G;
+}
+
+// Copy the whole image to its fragment-ordered destination: each wave store
+// instruction writes 1 KiB of consecutive bytes.
+template <typename E, int NG>
+__device__ __forceinline__ void stage_copy_out(E *dst, const E *img, int tid) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const char *src = reinterpret_cast<const char *>(img);
+    char *d = reinterpret_cast<char *>(dst);
+#pragma unroll
+    for (int t = tid; t < NG; t += kThreads)
+        *reinterpret_cast<u32x4 *>(d + (size_t)t * 16) =
+            *reinterpret_cast<const u32x4 *>(src + (size_t)stage_slot(t) * 16);
+}
 
 // acc += X[16x16] * Y[16x16], fp32, X row-major; Y[k][n] read at Y[k*ysk + n*ysn].
 __device__ __forceinline__ f32x4 mma16_f32(f32x4 acc, const float *X, int ldx, const float *Y,
@@ -167,6 +201,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(ChunkArgs a) {
     E *sTb = reinterpret_cast<E *>(smem + C::SZ_A);        // [64][LDC] T as E, row-major
     float *sS = reinterpret_cast<float *>(smem + C::SZ_A + C::SZ_TB);  // [4][16][LDX]
     E *sEt = reinterpret_cast<E *>(smem + C::R1);          // [DK][LDC] (gamma b k)^T, then (w v)^T
+    E *sStg = reinterpret_cast<E *>(smem + C::R1 + C::SZ_ET);  // Khat^T, then Qhat image
 
     // Heads vary fastest across workgroup ids, so that workgroups running at the
     // same time read neighbouring head slices of the same token rows.
@@ -238,7 +273,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(ChunkArgs a) {
     // ---- scaled tiles --------------------------------------------------------
     E *Qh = reinterpret_cast<E *>(a.ws_Qh) + ch * kChunk * DK;
     E *KhT = reinterpret_cast<E *>(a.ws_KhT) + ch * DK * kChunk;
-    Vec4<E> qp[TPG];
+    Vec4<E> qp[TPG], qh[TPG];
 #pragma unroll
     for (int j = 0; j < TPG; ++j) {
         const int i = tg * TPG + j;
@@ -255,24 +290,46 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(ChunkArgs a) {
         store4<E>(sKp + i * LDT + c0, kf * ei);
         // gamma = e^{g} = e^{g-g_r} e^{g_r};  e^{g_last-g} = e^{g_r-g} e^{g_r}
         const f32x4 gm = ex * egr;
-        store4_frag<E>(Qh, DK, i, c0, qf * gm);
+        qh[j] = pack4<E>(qf * gm);    // Qhat, staged once the image region is free
         qp[j] = pack4<E>(qf * ex);    // q e^{g-g_r}, kept for M
         bk[j] *= gm;                  // gamma b k, stored channel-major below
-        g[j] = kf * ei * egr;         // e^{g_last-g} k, stored channel-major below
+        g[j] = kf * ei * egr;         // e^{g_last-g} k, staged below
     }
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-        float et[TPG], kh[TPG];
+        float et[TPG];
 #pragma unroll
-        for (int j = 0; j < TPG; ++j) {
-            et[j] = bk[j][c];
-            kh[j] = g[j][c];
-        }
+        for (int j = 0; j < TPG; ++j) et[j] = bk[j][c];
         store_run<E, TPG>(sEt + (c0 + c) * LDC + tg * TPG, et);
+    }
+    // Khat^T image: row = channel, column = token.
+    if constexpr (sizeof(E) == 2) {  // a granule is 8 tokens of one channel
 #pragma unroll
-        for (int m = 0; m < TPG; m += 4)
-            store4_frag<E>(KhT, kChunk, c0 + c, tg * TPG + m,
-                           f32x4{kh[m], kh[m + 1], kh[m + 2], kh[m + 3]});
+        for (int c = 0; c < 4; ++c) {
+            float kh[TPG];
+#pragma unroll
+            for (int j = 0; j < TPG; ++j) kh[j] = g[j][c];
+            if constexpr (TPG % 8 == 0) {
+#pragma unroll
+                for (int m = 0; m < TPG; m += 8) {
+                    bf16x8 x;
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) x[u] = static_cast<bf16>(kh[m + u]);
+                    *reinterpret_cast<bf16x8 *>(
+                        stage_ptr(sStg, frag_index<E>(c0 + c, tg * TPG + m, kChunk))) = x;
+                }
+            } else {
+#pragma unroll
+                for (int m = 0; m < TPG; m += 4)
+                    store4<E>(stage_ptr(sStg, frag_index<E>(c0 + c, tg * TPG + m, kChunk)),
+                              f32x4{kh[m], kh[m + 1], kh[m + 2], kh[m + 3]});
+            }
+        }
+    } else {  // a granule is 4 channels of one token
+#pragma unroll
+        for (int j = 0; j < TPG; ++j)
+            *reinterpret_cast<f32x4 *>(stage_ptr(sStg, frag_index<E>(c0, tg * TPG + j, kChunk))) =
+                g[j];
     }
     if (tg == 0) {
         f32x4 gl;
@@ -285,6 +342,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(ChunkArgs a) {
     // ---- stage 2a: A (then M) by MFMA over the channels -------------------
     // Tile (I, J), I >= J, is formed transposed: D[j][i] = sum_c Kp[j][c] Y[i][c],
     // so each lane ends up with 4 consecutive columns j of one row i.
+    stage_copy_out<E, C::NG>(KhT, sStg, tid);
     f32x4 accA[3];
 #pragma unroll
     for (int u = 0; u < 3; ++u) {
@@ -304,10 +362,23 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(ChunkArgs a) {
             accA[u] = acc;
         }
     }
-    __syncthreads();  // Ep is dead: X now receives q e^{g-g_r}
+    __syncthreads();  // Ep and the Khat^T image are dead: X receives q e^{g-g_r}, the image Qhat
 #pragma unroll
     for (int j = 0; j < TPG; ++j) *reinterpret_cast<Vec4<E> *>(sX + (tg * TPG + j) * LDT + c0) = qp[j];
+    if constexpr (sizeof(E) == 2) {  // a granule is 8 channels of one token
+#pragma unroll
+        for (int j = 0; j < TPG; ++j)
+            *reinterpret_cast<Vec4<E> *>(stage_ptr(sStg, frag_index<E>(tg * TPG + j, c0, DK))) = qh[j];
+    } else {  // a granule is 4 tokens of one channel
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int m = 0; m < TPG; m += 4)
+                *reinterpret_cast<f32x4 *>(stage_ptr(sStg, frag_index<E>(tg * TPG + m, c0 + c, DK))) =
+                    f32x4{qh[m][c], qh[m + 1][c], qh[m + 2][c], qh[m + 3][c]};
+    }
     __syncthreads();
+    stage_copy_out<E, C::NG>(Qh, sStg, tid);
     E *Mg = reinterpret_cast<E *>(a.ws_M) + ch * kChunk * kChunk;
 #pragma unroll
     for (int u = 0; u < 3; ++u) {

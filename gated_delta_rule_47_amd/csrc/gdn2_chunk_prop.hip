@@ -13,12 +13,14 @@
 // axis) independently, so each (sequence, head) is split into Dv / DVS
 // column slabs, one workgroup per slab.  The slab's fp32 state lives in MFMA
 // accumulator registers for the whole sequence; a bf16 (or fp32) copy of it,
-// transposed and double-buffered, is kept in LDS as the MFMA operand.  All
-// loads of chunk c+1 (operand fragments straight from the workspace into
-// registers) are issued before chunk c is computed.  Workgroup ids are mapped
+// transposed, is kept in LDS as the MFMA operand.  Workgroup ids are mapped
 // so that all slabs of one (sequence, head) land on the same XCD (ids are
 // dispatched round-robin over the 8 XCDs), where they share the chunk
 // factors through that XCD's L2.
+//
+// Two implementations: for bf16, 4 compute waves fed through LDS by 4 loader
+// waves (chunk_prop_ws_kernel); for fp32, whose fragments are twice as large,
+// 4 waves that load their own operand fragments (chunk_prop_kernel).
 
 #include <type_traits>
 
@@ -242,6 +244,293 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prop_kernel(ChunkArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 path with producer waves.
+//
+// A compute wave that issues its own prefetch stalls in the issue of those
+// loads for as long as the memory pipeline takes to return earlier ones, and
+// cannot do MFMA work meanwhile.  Here each workgroup has 4 compute waves and
+// 4 loader waves.  The loader waves copy the fragment-ordered W, Qhat, M and
+// Khat^T of a chunk (a byte-for-byte image of the workspace, so every fragment
+// is one conflict-free 16-byte-per-lane LDS read) into one of two LDS stages,
+// two chunks ahead: during chunk c they write chunk c+1 (loaded during chunk
+// c-1) into the free stage and then issue the loads of chunk c+2.  The compute
+// waves read the factors from the stage and load only their own U tiles and
+// gamma_last.  Qhat S does not depend on U_eff, so it is formed before the
+// mid-chunk barrier, together with W S.
+// ---------------------------------------------------------------------------
+template <int DK, int DVS>
+struct WsCfg {
+    static constexpr int PAD = 8;
+    static constexpr int LDS_ = DK + PAD;       // S^T     [DVS][LDS_]
+    static constexpr int LDU = kChunk + PAD;    // U_eff^T [DVS][LDU]
+    static constexpr int NCB = DVS / 16;
+    static constexpr int NKB = DK / 16;
+    static constexpr int S_TPW = NKB * NCB / 4;
+    static constexpr int KB_W = NKB / 4;
+    static constexpr int NG_W = kChunk * DK * 2 / 16;      // 16-byte granules of W, Qhat, Khat^T
+    static constexpr int NG_M = kChunk * kChunk * 2 / 16;  // of M
+    static constexpr int NG = 3 * NG_W + NG_M;             // one chunk's stage: W | Qhat | M | Khat^T
+    static constexpr int NJ = NG / kThreads;               // loads per loader thread
+    static constexpr size_t SZ_STAGE = size_t(NG) * 16;
+    static constexpr size_t SZ_S = size_t(DVS) * LDS_ * 2;
+    static constexpr size_t SMEM = 2 * SZ_STAGE + SZ_S + size_t(DVS) * LDU * 2;
+    static_assert(NG % kThreads == 0 && NG_W % kThreads == 0 && NG_M % kThreads == 0, "loader split");
+    static_assert(S_TPW * 4 == NKB * NCB && KB_W * 4 == NKB, "state tiles split over 4 waves");
+    static_assert(SMEM <= 160 * 1024, "LDS");
+};
+
+typedef unsigned int granule_t __attribute__((ext_vector_type(4)));
+
+template <int NJ>
+struct StageRegs {
+    granule_t v[NJ];
+};
+
+// Loader thread t (0..255) moves granules t, t+256, ... of a chunk's stage;
+// load j covers granules 256j .. 256j+255, which lie in one of the four arrays.
+template <int DK, int DVS, int J>
+__device__ __forceinline__ granule_t ws_load(const ChunkArgs &a, size_t ch, int t) {
+    using C = WsCfg<DK, DVS>;
+    constexpr int g = J * kThreads;
+    if constexpr (g < C::NG_W)
+        return reinterpret_cast<const granule_t *>(a.ws_W)[ch * C::NG_W + g + t];
+    else if constexpr (g < 2 * C::NG_W)
+        return reinterpret_cast<const granule_t *>(a.ws_Qh)[ch * C::NG_W + g - C::NG_W + t];
+    else if constexpr (g < 2 * C::NG_W + C::NG_M)
+        return reinterpret_cast<const granule_t *>(a.ws_M)[ch * C::NG_M + g - 2 * C::NG_W + t];
+    else
+        return reinterpret_cast<const granule_t *>(a.ws_KhT)[ch * C::NG_W + g - 2 * C::NG_W - C::NG_M + t];
+}
+
+// Loads J .. J1-1: store each register of the chunk already loaded into
+// `stage`, then reuse it for the same load of chunk-head `ch_next`, so that the
+// loads stay in flight one after another.  The sequence has no branches, which
+// lets every store wait for its own load only.
+template <int DK, int DVS, int J, int J1>
+__device__ __forceinline__ void ws_pipe(StageRegs<WsCfg<DK, DVS>::NJ> &buf, char *stage,
+                                        const ChunkArgs &a, size_t ch_next, int t) {
+    if constexpr (J < J1) {
+        *reinterpret_cast<granule_t *>(stage + ((size_t)J * kThreads + t) * 16) = buf.v[J];
+        buf.v[J] = ws_load<DK, DVS, J>(a, ch_next, t);
+        ws_pipe<DK, DVS, J + 1, J1>(buf, stage, a, ch_next, t);
+    }
+}
+
+template <int DK, int DV, int DVS>
+__global__ __launch_bounds__(2 * kThreads, 1) void chunk_prop_ws_kernel(ChunkArgs a) {
+    using C = WsCfg<DK, DVS>;
+    using M = Mma<bf16>;
+    constexpr int NS = DV / DVS, LDS_ = C::LDS_, LDU = C::LDU, NCB = C::NCB;
+    constexpr int NKD = DK / M::KS, NK64 = kChunk / M::KS;
+    __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
+    // S^T as the MFMA operand: read only before the mid-chunk barrier and
+    // rewritten only after it, so one buffer serves.
+    bf16 *sS = reinterpret_cast<bf16 *>(smem + 2 * C::SZ_STAGE);
+    bf16 *sU = reinterpret_cast<bf16 *>(smem + 2 * C::SZ_STAGE + C::SZ_S);  // U_eff^T
+
+    const int H = a.H;
+    const int x = blockIdx.x, xcd = x & 7, rest = x >> 3;
+    const int slab = rest % NS, chain = (rest / NS) * 8 + xcd;
+    if (chain >= a.N * H) return;  // uniform over the workgroup
+    const int n = chain / H, h = chain % H;
+    const int col0 = slab * DVS;
+    const int tid = threadIdx.x;
+
+    int cbeg, cend;
+    if (a.plan) {
+        cbeg = min(max(a.plan[n], 0), a.max_chunks);
+        cend = min(max(a.plan[n + 1], cbeg), a.max_chunks);
+    } else {
+        cbeg = n * a.NC;
+        cend = cbeg + a.NC;
+    }
+
+    if (cbeg == cend) {  // nothing to propagate: S_final = S0, no barriers in either role
+        if (tid >= kThreads || !a.S_final) return;
+        for (int e = tid; e < DK * DVS; e += kThreads) {
+            const size_t o = ((size_t)chain * DK + e / DVS) * DV + col0 + e % DVS;
+            a.S_final[o] = a.S0 ? a.S0[o] : 0.0f;
+        }
+        return;
+    }
+
+    if (tid >= kThreads) {
+        // ---- loader waves ----------------------------------------------------
+        // Step `it` (0 .. n+1 for n chunks) stores the registers of chunk
+        // cbeg+it-1 into its stage and loads chunk cbeg+it (clamped to the
+        // last chunk; stages written past the end are never read).  Step it
+        // runs beside the compute of chunk it-2, with the same two barriers.
+        // Everything happens inside the one loop, so the loads in flight at
+        // its head always come in the same order and each store waits only
+        // for its own load.
+        constexpr int NJ = C::NJ, NJ2 = NJ / 2;
+        const int t = tid - kThreads;
+        StageRegs<NJ> buf;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) buf.v[j] = granule_t{0u, 0u, 0u, 0u};
+        for (int it = 0; it < cend - cbeg + 2; ++it) {
+            char *st = smem + ((it + 1) & 1) * C::SZ_STAGE;  // stage of chunk cbeg+it-1
+            const size_t chn = (size_t)min(cbeg + it, cend - 1) * H + h;
+            ws_pipe<DK, DVS, 0, NJ2>(buf, st, a, chn, t);
+            __syncthreads();
+            ws_pipe<DK, DVS, NJ2, NJ>(buf, st, a, chn, t);
+            __syncthreads();
+        }
+        return;
+    }
+
+    // ---- compute waves ----------------------------------------------------
+    const int lane = tid & 63, wave = tid >> 6;
+    // Per chunk: this wave's U tiles (accumulator order), gamma_last of its
+    // state rows, and the chunk's token span.
+    struct Own {
+        bf16x4 u[NCB];
+        f32x4 gl[C::KB_W];
+        int tok0, len;
+    };
+    auto load_own = [&](Own &f, int cid) {
+        if (a.plan) {
+            const int32_t *e = a.plan + a.N + 1 + 3 * (size_t)cid;
+            f.tok0 = min(max(e[1], 0), a.T);
+            f.len = min(max(e[2], 0), min(kChunk, a.T - f.tok0));
+        } else {
+            const int c = cid - cbeg;
+            f.tok0 = n * a.T + c * kChunk;
+            f.len = min(kChunk, a.T - c * kChunk);
+        }
+        const size_t ch = (size_t)cid * H + h;
+        const bf16 *Ug = reinterpret_cast<const bf16 *>(a.ws_U) + ch * kChunk * DV +
+                         ((wave * (DV / 16) + col0 / 16) * 64 + lane) * 4;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) f.u[cb] = *reinterpret_cast<const bf16x4 *>(Ug + cb * 64 * 4);
+#pragma unroll
+        for (int b = 0; b < C::KB_W; ++b)
+            f.gl[b] = *reinterpret_cast<const f32x4 *>(a.ws_gl + ch * DK + 16 * (wave * C::KB_W + b) +
+                                                       4 * (lane >> 4));
+    };
+    Own cur, nxt;
+    load_own(cur, cbeg);
+
+    f32x4 Sacc[C::S_TPW];
+#pragma unroll
+    for (int u = 0; u < C::S_TPW; ++u) {
+        const int cblk = wave * C::KB_W + u / NCB, colb = u % NCB;
+        const int col = col0 + 16 * colb + (lane & 15);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int c = 16 * cblk + 4 * (lane >> 4) + r;
+            Sacc[u][r] = a.S0 ? a.S0[((size_t)chain * DK + c) * DV + col] : 0.0f;
+        }
+        store_tile_t<bf16>(sS + 16 * colb * LDS_ + 16 * cblk, LDS_, Sacc[u], lane);
+    }
+    // The loader's steps 0 and 1 (the first chunk reaches stage 0).
+#pragma unroll
+    for (int j = 0; j < 4; ++j) __syncthreads();
+
+    bf16 *out = reinterpret_cast<bf16 *>(a.o);
+    for (int cid = cbeg; cid < cend; ++cid) {
+        if (cid + 1 < cend) load_own(nxt, cid + 1);
+        const bf16 *stage = reinterpret_cast<const bf16 *>(smem + ((cid - cbeg) & 1) * C::SZ_STAGE);
+        const bf16 *Wf = stage;
+        const bf16 *Qf = stage + C::NG_W * 8;
+        const bf16 *Mf = stage + 2 * C::NG_W * 8;
+        const bf16 *Kf = stage + (2 * C::NG_W + C::NG_M) * 8;
+
+        // Phase 1: U_eff rows of block `wave` (U - W S) and the state part of
+        // O^T (S^T Qhat^T).  All operands are read first, then the products run
+        // as 2*NCB independent accumulation chains.
+        f32x4 oacc[NCB];
+        {
+            M::frag wf[NKD], qf[NKD], sf[NCB][NKD];
+#pragma unroll
+            for (int kk = 0; kk < NKD; ++kk) {
+                wf[kk] = load_frag_packed<bf16>(Wf, DK, wave, kk, lane);
+                qf[kk] = load_frag_packed<bf16>(Qf, DK, wave, kk, lane);
+            }
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                for (int kk = 0; kk < NKD; ++kk)
+                    sf[cb][kk] = load_frag<bf16>(sS + 16 * cb * LDS_ + kk * M::KS, LDS_, lane);
+            f32x4 ws[NCB];
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) ws[cb] = oacc[cb] = zero4();
+#pragma unroll
+            for (int kk = 0; kk < NKD; ++kk)
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) {
+                    ws[cb] = M::mma(wf[kk], sf[cb][kk], ws[cb]);
+                    oacc[cb] = M::mma(sf[cb][kk], qf[kk], oacc[cb]);
+                }
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+                store_tile_t<bf16>(sU + 16 * cb * LDU + 16 * wave, LDU,
+                                   to_f32x4<bf16>(cur.u[cb]) - ws[cb], lane);
+        }
+        __syncthreads();  // U_eff complete; S^T is no longer read this chunk
+
+        // Phase 2: O^T += U_eff^T M^T;  S <- Diag(gamma_last) S + Khat^T U_eff.
+        {
+            M::frag uf[NCB][NK64], mf[NK64], kf[C::KB_W][NK64];
+#pragma unroll
+            for (int kk = 0; kk < NK64; ++kk) {
+                mf[kk] = load_frag_packed<bf16>(Mf, kChunk, wave, kk, lane);
+#pragma unroll
+                for (int b = 0; b < C::KB_W; ++b)
+                    kf[b][kk] = load_frag_packed<bf16>(Kf, kChunk, wave * C::KB_W + b, kk, lane);
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb)
+                    uf[cb][kk] = load_frag<bf16>(sU + 16 * cb * LDU + kk * M::KS, LDU, lane);
+            }
+            f32x4 d[C::S_TPW];
+#pragma unroll
+            for (int u = 0; u < C::S_TPW; ++u) d[u] = zero4();
+#pragma unroll
+            for (int kk = 0; kk < NK64; ++kk) {
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) oacc[cb] = M::mma(uf[cb][kk], mf[kk], oacc[cb]);
+#pragma unroll
+                for (int u = 0; u < C::S_TPW; ++u)
+                    d[u] = M::mma(kf[u / NCB][kk], uf[u % NCB][kk], d[u]);
+            }
+            const int i = 16 * wave + (lane & 15);
+            if (i < cur.len) {
+                bf16 *dst = out + ((size_t)(cur.tok0 + i) * H + h) * DV + col0 + 4 * (lane >> 4);
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) {
+                    bf16x4 ov;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) ov[r] = static_cast<bf16>(oacc[cb][r]);
+                    *reinterpret_cast<bf16x4 *>(dst + 16 * cb) = ov;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < C::S_TPW; ++u) {
+                const int b = u / NCB, colb = u % NCB;
+                Sacc[u] = cur.gl[b] * Sacc[u] + d[u];
+                store_tile_t<bf16>(sS + 16 * colb * LDS_ + 16 * (wave * C::KB_W + b), LDS_, Sacc[u],
+                                   lane);
+            }
+        }
+        __syncthreads();
+        cur = nxt;
+    }
+
+    if (a.S_final) {
+#pragma unroll
+        for (int u = 0; u < C::S_TPW; ++u) {
+            const int cblk = wave * C::KB_W + u / NCB, colb = u % NCB;
+            const int col = col0 + 16 * colb + (lane & 15);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int c = 16 * cblk + 4 * (lane >> 4) + r;
+                a.S_final[((size_t)chain * DK + c) * DV + col] = Sacc[u][r];
+            }
+        }
+    }
+}
+
 // Slab width.  Every slab workgroup of a (sequence, head) reads all of that
 // chunk's factors through its CU's vector memory path, which bounds the time
 // per chunk; wide slabs cut that re-reading, narrow slabs give parallelism
@@ -256,16 +545,28 @@ template <typename E, int D>
 static void launch_prop_d(const ChunkArgs &a, int dvs, hipStream_t stream) {
     const int chains = a.N * a.H;
     const int groups = (chains + 7) / 8;
-    const dim3 block(kThreads);
-    if (dvs == 64) {
-        hipLaunchKernelGGL((chunk_prop_kernel<E, D, D, 64>), dim3(groups * 8 * (D / 64)), block, 0,
-                           stream, a);
-    } else if (dvs == 32) {
-        hipLaunchKernelGGL((chunk_prop_kernel<E, D, D, 32>), dim3(groups * 8 * (D / 32)), block, 0,
-                           stream, a);
+    if constexpr (sizeof(E) == 2) {  // compute + loader waves
+        const dim3 block(2 * kThreads);
+        if (dvs == 64)
+            hipLaunchKernelGGL((chunk_prop_ws_kernel<D, D, 64>), dim3(groups * 8 * (D / 64)), block, 0,
+                               stream, a);
+        else if (dvs == 32)
+            hipLaunchKernelGGL((chunk_prop_ws_kernel<D, D, 32>), dim3(groups * 8 * (D / 32)), block, 0,
+                               stream, a);
+        else
+            hipLaunchKernelGGL((chunk_prop_ws_kernel<D, D, 16>), dim3(groups * 8 * (D / 16)), block, 0,
+                               stream, a);
     } else {
-        hipLaunchKernelGGL((chunk_prop_kernel<E, D, D, 16>), dim3(groups * 8 * (D / 16)), block, 0,
-                           stream, a);
+        const dim3 block(kThreads);
+        if (dvs == 64)
+            hipLaunchKernelGGL((chunk_prop_kernel<E, D, D, 64>), dim3(groups * 8 * (D / 64)), block, 0,
+                               stream, a);
+        else if (dvs == 32)
+            hipLaunchKernelGGL((chunk_prop_kernel<E, D, D, 32>), dim3(groups * 8 * (D / 32)), block, 0,
+                               stream, a);
+        else
+            hipLaunchKernelGGL((chunk_prop_kernel<E, D, D, 16>), dim3(groups * 8 * (D / 16)), block, 0,
+                               stream, a);
     }
 }
 
