@@ -274,7 +274,11 @@ struct WsCfg {
     static constexpr int NJ = NG / kThreads;               // loads per loader thread
     static constexpr size_t SZ_STAGE = size_t(NG) * 16;
     static constexpr size_t SZ_S = size_t(DVS) * LDS_ * 2;
-    static constexpr size_t SMEM = 2 * SZ_STAGE + SZ_S + size_t(DVS) * LDU * 2;
+    static constexpr int LDO = DVS + 8;         // O staging [64][LDO]
+    static constexpr int GPR_O = DVS / 8;       // 16-byte granules per token row of O
+    static constexpr size_t SZ_U = size_t(DVS) * LDU * 2;
+    static constexpr size_t SZ_O = size_t(kChunk) * LDO * 2;
+    static constexpr size_t SMEM = 2 * SZ_STAGE + SZ_S + SZ_U + SZ_O;
     static_assert(NG % kThreads == 0 && NG_W % kThreads == 0 && NG_M % kThreads == 0, "loader split");
     static_assert(S_TPW * 4 == NKB * NCB && KB_W * 4 == NKB, "state tiles split over 4 waves");
     static_assert(SMEM <= 160 * 1024, "LDS");
@@ -317,6 +321,33 @@ __device__ __forceinline__ void ws_pipe(StageRegs<WsCfg<DK, DVS>::NJ> &buf, char
     }
 }
 
+// Loader side: the O rows of chunk `cid` (staged in LDS by the compute waves)
+// to global memory, 16 bytes per lane, the slab's part of each token row
+// contiguous.
+template <int DK, int DV, int DVS>
+__device__ __forceinline__ void ws_store_o(const ChunkArgs &a, const bf16 *sO, int n, int h, int cbeg,
+                                           int cid, int col0, int t) {
+    using C = WsCfg<DK, DVS>;
+    int tok0, len;
+    if (a.plan) {
+        const int32_t *e = a.plan + a.N + 1 + 3 * (size_t)cid;
+        tok0 = min(max(e[1], 0), a.T);
+        len = min(max(e[2], 0), min(kChunk, a.T - tok0));
+    } else {
+        const int c = cid - cbeg;
+        tok0 = n * a.T + c * kChunk;
+        len = min(kChunk, a.T - c * kChunk);
+    }
+    bf16 *out = reinterpret_cast<bf16 *>(a.o);
+#pragma unroll
+    for (int g = t; g < kChunk * C::GPR_O; g += kThreads) {
+        const int row = g / C::GPR_O, piece = g % C::GPR_O;
+        if (row < len)
+            *reinterpret_cast<granule_t *>(out + ((size_t)(tok0 + row) * a.H + h) * DV + col0 + 8 * piece) =
+                *reinterpret_cast<const granule_t *>(sO + row * C::LDO + 8 * piece);
+    }
+}
+
 template <int DK, int DV, int DVS>
 __global__ __launch_bounds__(2 * kThreads, 1) void chunk_prop_ws_kernel(ChunkArgs a) {
     using C = WsCfg<DK, DVS>;
@@ -328,6 +359,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_prop_ws_kernel(ChunkArg
     // rewritten only after it, so one buffer serves.
     bf16 *sS = reinterpret_cast<bf16 *>(smem + 2 * C::SZ_STAGE);
     bf16 *sU = reinterpret_cast<bf16 *>(smem + 2 * C::SZ_STAGE + C::SZ_S);  // U_eff^T
+    bf16 *sO = reinterpret_cast<bf16 *>(smem + 2 * C::SZ_STAGE + C::SZ_S + C::SZ_U);  // O, row-major
 
     const int H = a.H;
     const int x = blockIdx.x, xcd = x & 7, rest = x >> 3;
@@ -357,19 +389,21 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_prop_ws_kernel(ChunkArg
 
     if (tid >= kThreads) {
         // ---- loader waves ----------------------------------------------------
-        // Step `it` (0 .. n+1 for n chunks) stores the registers of chunk
-        // cbeg+it-1 into its stage and loads chunk cbeg+it (clamped to the
-        // last chunk; stages written past the end are never read).  Step it
-        // runs beside the compute of chunk it-2, with the same two barriers.
-        // Everything happens inside the one loop, so the loads in flight at
-        // its head always come in the same order and each store waits only
-        // for its own load.
+        // Step `it` (0 .. n+1 for n chunks) runs beside the compute of chunk
+        // cbeg+it-2, with the same two barriers.  It first writes out the O
+        // rows of chunk cbeg+it-3 (staged by the compute waves in the previous
+        // step), then stores the registers of chunk cbeg+it-1 into its stage
+        // and loads chunk cbeg+it (clamped to the last chunk; stages written
+        // past the end are never read).  The stage traffic stays inside the
+        // one loop, so the loads in flight at its head always come in the
+        // same order and each store waits only for its own load.
         constexpr int NJ = C::NJ, NJ2 = NJ / 2;
-        const int t = tid - kThreads;
+        const int t = tid - kThreads, col0_ = col0;
         StageRegs<NJ> buf;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) buf.v[j] = granule_t{0u, 0u, 0u, 0u};
         for (int it = 0; it < cend - cbeg + 2; ++it) {
+            if (it >= 3) ws_store_o<DK, DV, DVS>(a, sO, n, h, cbeg, cbeg + it - 3, col0_, t);
             char *st = smem + ((it + 1) & 1) * C::SZ_STAGE;  // stage of chunk cbeg+it-1
             const size_t chn = (size_t)min(cbeg + it, cend - 1) * H + h;
             ws_pipe<DK, DVS, 0, NJ2>(buf, st, a, chn, t);
@@ -377,28 +411,19 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_prop_ws_kernel(ChunkArg
             ws_pipe<DK, DVS, NJ2, NJ>(buf, st, a, chn, t);
             __syncthreads();
         }
+        ws_store_o<DK, DV, DVS>(a, sO, n, h, cbeg, cend - 1, col0_, t);  // the last chunk
         return;
     }
 
     // ---- compute waves ----------------------------------------------------
     const int lane = tid & 63, wave = tid >> 6;
-    // Per chunk: this wave's U tiles (accumulator order), gamma_last of its
-    // state rows, and the chunk's token span.
+    // Per chunk: this wave's U tiles (accumulator order) and gamma_last of its
+    // state rows, loaded two chunks ahead.
     struct Own {
         bf16x4 u[NCB];
         f32x4 gl[C::KB_W];
-        int tok0, len;
     };
     auto load_own = [&](Own &f, int cid) {
-        if (a.plan) {
-            const int32_t *e = a.plan + a.N + 1 + 3 * (size_t)cid;
-            f.tok0 = min(max(e[1], 0), a.T);
-            f.len = min(max(e[2], 0), min(kChunk, a.T - f.tok0));
-        } else {
-            const int c = cid - cbeg;
-            f.tok0 = n * a.T + c * kChunk;
-            f.len = min(kChunk, a.T - c * kChunk);
-        }
         const size_t ch = (size_t)cid * H + h;
         const bf16 *Ug = reinterpret_cast<const bf16 *>(a.ws_U) + ch * kChunk * DV +
                          ((wave * (DV / 16) + col0 / 16) * 64 + lane) * 4;
@@ -409,8 +434,9 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_prop_ws_kernel(ChunkArg
             f.gl[b] = *reinterpret_cast<const f32x4 *>(a.ws_gl + ch * DK + 16 * (wave * C::KB_W + b) +
                                                        4 * (lane >> 4));
     };
-    Own cur, nxt;
+    Own cur, nxt, nxt2;
     load_own(cur, cbeg);
+    load_own(nxt, min(cbeg + 1, cend - 1));
 
     f32x4 Sacc[C::S_TPW];
 #pragma unroll
@@ -428,9 +454,8 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_prop_ws_kernel(ChunkArg
 #pragma unroll
     for (int j = 0; j < 4; ++j) __syncthreads();
 
-    bf16 *out = reinterpret_cast<bf16 *>(a.o);
     for (int cid = cbeg; cid < cend; ++cid) {
-        if (cid + 1 < cend) load_own(nxt, cid + 1);
+        load_own(nxt2, min(cid + 2, cend - 1));
         const bf16 *stage = reinterpret_cast<const bf16 *>(smem + ((cid - cbeg) & 1) * C::SZ_STAGE);
         const bf16 *Wf = stage;
         const bf16 *Qf = stage + C::NG_W * 8;
@@ -494,16 +519,14 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_prop_ws_kernel(ChunkArg
                 for (int u = 0; u < C::S_TPW; ++u)
                     d[u] = M::mma(kf[u / NCB][kk], uf[u % NCB][kk], d[u]);
             }
-            const int i = 16 * wave + (lane & 15);
-            if (i < cur.len) {
-                bf16 *dst = out + ((size_t)(cur.tok0 + i) * H + h) * DV + col0 + 4 * (lane >> 4);
+            // O rows to the staging buffer; the loader waves write them out.
 #pragma unroll
-                for (int cb = 0; cb < NCB; ++cb) {
-                    bf16x4 ov;
+            for (int cb = 0; cb < NCB; ++cb) {
+                bf16x4 ov;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) ov[r] = static_cast<bf16>(oacc[cb][r]);
-                    *reinterpret_cast<bf16x4 *>(dst + 16 * cb) = ov;
-                }
+                for (int r = 0; r < 4; ++r) ov[r] = static_cast<bf16>(oacc[cb][r]);
+                *reinterpret_cast<bf16x4 *>(sO + (16 * wave + (lane & 15)) * C::LDO + 16 * cb +
+                                            4 * (lane >> 4)) = ov;
             }
 #pragma unroll
             for (int u = 0; u < C::S_TPW; ++u) {
@@ -515,6 +538,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_prop_ws_kernel(ChunkArg
         }
         __syncthreads();
         cur = nxt;
+        nxt = nxt2;
     }
 
     if (a.S_final) {
