@@ -321,23 +321,13 @@ __device__ __forceinline__ void ws_pipe(StageRegs<WsCfg<DK, DVS>::NJ> &buf, char
     }
 }
 
-// Loader side: the O rows of chunk `cid` (staged in LDS by the compute waves)
+// Loader side: the O rows of one chunk (staged in LDS by the compute waves)
 // to global memory, 16 bytes per lane, the slab's part of each token row
 // contiguous.
 template <int DK, int DV, int DVS>
-__device__ __forceinline__ void ws_store_o(const ChunkArgs &a, const bf16 *sO, int n, int h, int cbeg,
-                                           int cid, int col0, int t) {
+__device__ __forceinline__ void ws_store_o(const ChunkArgs &a, const bf16 *sO, int h, int tok0, int len,
+                                           int col0, int t) {
     using C = WsCfg<DK, DVS>;
-    int tok0, len;
-    if (a.plan) {
-        const int32_t *e = a.plan + a.N + 1 + 3 * (size_t)cid;
-        tok0 = min(max(e[1], 0), a.T);
-        len = min(max(e[2], 0), min(kChunk, a.T - tok0));
-    } else {
-        const int c = cid - cbeg;
-        tok0 = n * a.T + c * kChunk;
-        len = min(kChunk, a.T - c * kChunk);
-    }
     bf16 *out = reinterpret_cast<bf16 *>(a.o);
 #pragma unroll
     for (int g = t; g < kChunk * C::GPR_O; g += kThreads) {
@@ -389,29 +379,55 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_prop_ws_kernel(ChunkArg
 
     if (tid >= kThreads) {
         // ---- loader waves ----------------------------------------------------
-        // Step `it` (0 .. n+1 for n chunks) runs beside the compute of chunk
-        // cbeg+it-2, with the same two barriers.  It first writes out the O
-        // rows of chunk cbeg+it-3 (staged by the compute waves in the previous
-        // step), then stores the registers of chunk cbeg+it-1 into its stage
-        // and loads chunk cbeg+it (clamped to the last chunk; stages written
-        // past the end are never read).  The stage traffic stays inside the
-        // one loop, so the loads in flight at its head always come in the
-        // same order and each store waits only for its own load.
+        // Step `it` runs beside the compute of chunk cbeg+it-2, with the same
+        // two barriers.  It first writes out the O rows of chunk cbeg+it-3
+        // (staged by the compute waves during the previous step), then stores
+        // the registers holding chunk cbeg+it-1 into that chunk's stage and
+        // reuses them for chunk cbeg+it+1 (clamped to the last chunk; stages
+        // written past the end are never read).  Two register sets alternate,
+        // so a chunk's loads have two steps to arrive.  The loop is unrolled
+        // by two and always runs an even number of steps; the stage traffic
+        // has no branches, so the loads in flight at its head always come in
+        // the same order and each store waits only for its own load.
         constexpr int NJ = C::NJ, NJ2 = NJ / 2;
-        const int t = tid - kThreads, col0_ = col0;
-        StageRegs<NJ> buf;
+        const int t = tid - kThreads, col0_ = col0, nch = cend - cbeg;
+        // Token span of chunk k of this sequence, from its first token and end.
+        int tok_first, seq_end;
+        if (a.plan) {
+            const int32_t *e0 = a.plan + a.N + 1 + 3 * (size_t)cbeg;
+            const int32_t *e1 = a.plan + a.N + 1 + 3 * (size_t)(cend - 1);
+            tok_first = min(max(e0[1], 0), a.T);
+            seq_end = min(max(e1[1] + e1[2], tok_first), a.T);
+        } else {
+            tok_first = n * a.T;
+            seq_end = tok_first + a.T;
+        }
+        auto store_o = [&](int k) {
+            const int tok0 = min(tok_first + k * kChunk, a.T * (a.plan ? 1 : a.N));
+            ws_store_o<DK, DV, DVS>(a, sO, h, tok0, min(kChunk, seq_end - tok0), col0_, t);
+        };
+        auto chunk_head = [&](int k) { return (size_t)(cbeg + min(k, nch - 1)) * H + h; };
+        StageRegs<NJ> buf0, buf1;
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) buf.v[j] = granule_t{0u, 0u, 0u, 0u};
-        for (int it = 0; it < cend - cbeg + 2; ++it) {
-            if (it >= 3) ws_store_o<DK, DV, DVS>(a, sO, n, h, cbeg, cbeg + it - 3, col0_, t);
-            char *st = smem + ((it + 1) & 1) * C::SZ_STAGE;  // stage of chunk cbeg+it-1
-            const size_t chn = (size_t)min(cbeg + it, cend - 1) * H + h;
-            ws_pipe<DK, DVS, 0, NJ2>(buf, st, a, chn, t);
+        for (int j = 0; j < NJ; ++j) buf0.v[j] = granule_t{0u, 0u, 0u, 0u};
+        // chunk 0 into buf1 (stored at step 1); buf0 receives chunk 1 at step 0
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) buf1.v[j] = granule_t{0u, 0u, 0u, 0u};
+        ws_pipe<DK, DVS, 0, NJ>(buf1, smem + C::SZ_STAGE, a, chunk_head(0), t);
+        const int nsteps = (nch + 3) & ~1;  // nch + 2, rounded up to even
+        for (int it = 0; it < nsteps; it += 2) {
+            if (it >= 3 && it - 3 < nch) store_o(it - 3);
+            ws_pipe<DK, DVS, 0, NJ2>(buf0, smem + C::SZ_STAGE, a, chunk_head(it + 1), t);
             __syncthreads();
-            ws_pipe<DK, DVS, NJ2, NJ>(buf, st, a, chn, t);
+            ws_pipe<DK, DVS, NJ2, NJ>(buf0, smem + C::SZ_STAGE, a, chunk_head(it + 1), t);
+            __syncthreads();
+            if (it + 1 >= 3 && it - 2 < nch) store_o(it - 2);
+            ws_pipe<DK, DVS, 0, NJ2>(buf1, smem, a, chunk_head(it + 2), t);
+            __syncthreads();
+            ws_pipe<DK, DVS, NJ2, NJ>(buf1, smem, a, chunk_head(it + 2), t);
             __syncthreads();
         }
-        ws_store_o<DK, DV, DVS>(a, sO, n, h, cbeg, cend - 1, col0_, t);  // the last chunk
+        if (nsteps - 3 < nch) store_o(nch - 1);  // the last chunk when no step after it remained
         return;
     }
 
@@ -539,6 +555,10 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_prop_ws_kernel(ChunkArg
         __syncthreads();
         cur = nxt;
         nxt = nxt2;
+    }
+    if ((cend - cbeg) & 1) {  // the loader's padding step
+        __syncthreads();
+        __syncthreads();
     }
 
     if (a.S_final) {
