@@ -213,6 +213,157 @@ def chunked(q, k, v, log_alpha, b, w, S0=None, cu_seqlens=None, chunk=CHUNK):
 
 
 # ---------------------------------------------------------------------------
+# Backward: gradients of the recurrence
+# ---------------------------------------------------------------------------
+#
+# The pages name a gate-aware backward as one of the method's contributions
+# ([gist-3], item on the backward pass: the channel-wise gates b and w enter
+# the gradients of the auxiliary matrices directly; [iplexlaw], "El artículo
+# y su pregunta": gradients that include the gates) but print no formulas.
+# The gradient of the recurrence has a plain definition, the chain rule taken
+# backwards through the token steps, which recurrence_bwd writes out.
+
+def recurrence_bwd(q, k, v, log_alpha, b, w, do, S0=None, dS_final=None, cu_seqlens=None):
+    """Reverse-mode gradients of recurrence() for upstream gradients do
+    (of o) and dS_final (of S_final; None means zero).
+
+    Returns a dict of float64 arrays: dq, dk, dv, dlog_alpha, db, dw (shapes
+    of the inputs) and dS0 [N, H, Dk, Dv].
+
+    One token of the forward (see step) is  Sbar = Diag(alpha) S_prev,
+    r = Sbar^T e, u = z - r, S = Sbar + k u^T, o = S^T q  with e = b*k and
+    z = w*v.  Going backwards with G = dL/dS (the output gradient folded in):
+        G     += q do^T,        dq = S do
+        du     = G^T k,         dk = G u
+        dSbar  = G - e du^T,    de = -Sbar du        (u = z - Sbar^T e)
+        dlog_alpha = rowsum(dSbar * Sbar),   G_prev = Diag(alpha) dSbar
+        db = de * k,  dk += de * b,  dw = du * v,  dv = du * w.
+    """
+    q, k, v, log_alpha, b, w, do, S0, dS_final = map(
+        _f64, (q, k, v, log_alpha, b, w, do, S0, dS_final))
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    N = B if cu_seqlens is None else len(cu_seqlens) - 1
+    out = dict(dq=np.zeros_like(q), dk=np.zeros_like(k), dv=np.zeros_like(v),
+               dlog_alpha=np.zeros_like(log_alpha), db=np.zeros_like(b), dw=np.zeros_like(w),
+               dS0=np.zeros((N, H, Dk, Dv)))
+    for n, row, t0, t1 in _sequences(B, T, cu_seqlens):
+        for h in range(H):
+            S = np.zeros((Dk, Dv)) if S0 is None else S0[n, h].copy()
+            states = [S]                               # states[i] = S after i tokens
+            for t in range(t0, t1):
+                _, S = step(q[row, t, h], k[row, t, h], v[row, t, h], log_alpha[row, t, h],
+                            b[row, t, h], w[row, t, h], S)
+                states.append(S)
+            G = np.zeros((Dk, Dv)) if dS_final is None else dS_final[n, h].copy()
+            for t in range(t1 - 1, t0 - 1, -1):
+                i = t - t0
+                S_prev, S_t = states[i], states[i + 1]
+                qt, kt, vt = q[row, t, h], k[row, t, h], v[row, t, h]
+                bt, wt = b[row, t, h], w[row, t, h]
+                alpha = np.exp(log_alpha[row, t, h])
+                S_bar = alpha[:, None] * S_prev
+                e, z = bt * kt, wt * vt
+                u = z - S_bar.T @ e
+                G = G + np.outer(qt, do[row, t, h])
+                out["dq"][row, t, h] = S_t @ do[row, t, h]
+                du = G.T @ kt
+                dk = G @ u
+                dS_bar = G - np.outer(e, du)
+                de = -(S_bar @ du)
+                out["dlog_alpha"][row, t, h] = np.sum(dS_bar * S_bar, axis=1)
+                G = alpha[:, None] * dS_bar
+                out["db"][row, t, h] = de * kt
+                out["dk"][row, t, h] = dk + de * bt
+                out["dw"][row, t, h] = du * vt
+                out["dv"][row, t, h] = du * wt
+            out["dS0"][n, h] = G
+    return out
+
+
+def chunk_bwd(f, q, k, v, b, w, S_in, dO, dS_out):
+    """Gradients of one chunk (fp64, explicit inverse), given its factors f
+    (chunk_factors), the incoming state S_in, the output gradient dO [L, Dv]
+    and the gradient dS_out of the outgoing state.
+
+    This is the chain rule applied to the chunk form (chunk_factors and
+    chunk_apply), written factor by factor; the unit tests check it against
+    recurrence_bwd.  Returns (grads dict for the chunk's tokens, dS_in) with
+    dlog_alpha already accumulated over the chunk's cumulative sum.
+    """
+    q, k, v, b, w, S_in, dO, dS_out = map(_f64, (q, k, v, b, w, S_in, dO, dS_out))
+    g = f["g"]
+    gamma = np.exp(g)
+    gl = f["gamma_last"]
+    E = gamma * b * k                                  # erase side (W = Tinv E)
+    Kt = k / gamma                                     # key side of A and M
+    Z = w * v
+    T_ = f["Tinv"]
+    U_eff = f["U"] - f["W"] @ S_in
+    # chunk_apply:  O = Qhat S + M U_eff,  S_out = Diag(gl) S + Khat^T U_eff
+    dU_eff = f["M"].T @ dO + f["Khat"] @ dS_out
+    dS_in = f["Qhat"].T @ dO + gl[:, None] * dS_out - f["W"].T @ dU_eff
+    dQhat = dO @ S_in.T
+    dM = np.tril(dO @ U_eff.T)
+    dKhat = U_eff @ dS_out.T
+    dgl = np.sum(dS_out * S_in, axis=1)
+    dW = -dU_eff @ S_in.T
+    dU = dU_eff
+    # W = Tinv E,  U = Tinv Z,  Tinv = (I + A)^-1:  dA = -Tinv^T dTinv Tinv^T,
+    # and Tinv^T (dU Z^T + dW E^T) Tinv^T = dZ U^T + dE W^T.
+    dZ = T_.T @ dU
+    dE = T_.T @ dW
+    dA = -np.tril(dZ @ f["U"].T + dE @ f["W"].T, -1)
+    # A = tril(E Kt^T, -1),  M = tril(Qhat Kt^T),  Khat = gl * Kt
+    dE = dE + dA @ Kt
+    dKt = dA.T @ E + dM.T @ f["Qhat"] + gl * dKhat
+    dQhat = dQhat + dM @ Kt
+    dgl = dgl + np.sum(Kt * dKhat, axis=0)
+    # E = gamma b k,  Qhat = gamma q,  Kt = k / gamma,  Z = w v
+    grads = dict(dq=gamma * dQhat, db=gamma * k * dE, dk=gamma * b * dE + dKt / gamma,
+                 dw=v * dZ, dv=w * dZ)
+    dg = E * dE + f["Qhat"] * dQhat - Kt * dKt          # d/dg_i of the token-i factors
+    dg_last = gl * dgl                                  # gamma_last = exp(g_last)
+    # g_i = sum_{j<=i} log_alpha_j:  dlog_alpha_j = sum_{i>=j} dg_i  (+ dg_last for all j)
+    grads["dlog_alpha"] = np.cumsum(dg[::-1], axis=0)[::-1] + dg_last[None, :]
+    return grads, dS_in
+
+
+def chunked_bwd(q, k, v, log_alpha, b, w, do, S0=None, dS_final=None, cu_seqlens=None,
+                chunk=CHUNK):
+    """Same result as recurrence_bwd, by the chunk form: a forward pass that
+    keeps each chunk's incoming state, then the chunks in reverse with
+    chunk_bwd carrying the state gradient."""
+    q, k, v, log_alpha, b, w, do, S0, dS_final = map(
+        _f64, (q, k, v, log_alpha, b, w, do, S0, dS_final))
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    N = B if cu_seqlens is None else len(cu_seqlens) - 1
+    out = dict(dq=np.zeros_like(q), dk=np.zeros_like(k), dv=np.zeros_like(v),
+               dlog_alpha=np.zeros_like(log_alpha), db=np.zeros_like(b), dw=np.zeros_like(w),
+               dS0=np.zeros((N, H, Dk, Dv)))
+    for n, row, t0, t1 in _sequences(B, T, cu_seqlens):
+        for h in range(H):
+            S = np.zeros((Dk, Dv)) if S0 is None else S0[n, h].copy()
+            spans, fs, S_ins = [], [], []
+            for c0 in range(t0, t1, chunk):
+                c1 = min(c0 + chunk, t1)
+                sl = (row, slice(c0, c1), h)
+                f = chunk_factors(q[sl], k[sl], v[sl], log_alpha[sl], b[sl], w[sl])
+                spans.append(sl)
+                fs.append(f)
+                S_ins.append(S)
+                _, S = chunk_apply(f, S)
+            dS = np.zeros((Dk, Dv)) if dS_final is None else dS_final[n, h].copy()
+            for sl, f, S_in in zip(spans[::-1], fs[::-1], S_ins[::-1]):
+                grads, dS = chunk_bwd(f, q[sl], k[sl], v[sl], b[sl], w[sl], S_in, do[sl], dS)
+                for name, val in grads.items():
+                    out[name][sl] = val
+            out["dS0"][n, h] = dS
+    return out
+
+
+# ---------------------------------------------------------------------------
 # Error metric used by every parity check
 # ---------------------------------------------------------------------------
 
