@@ -2,7 +2,7 @@
 
 Thin ctypes marshalling over the C ABI declared in include/libgdn2.h: the
 gdn2_* functions take raw device pointers and sizes exactly like their C
-counterparts; chunk_fwd() and step() accept torch tensors, allocate outputs and
+counterparts; chunk_fwd(), chunk_bwd() and step() accept torch tensors, allocate outputs and
 the workspace with torch, and pass torch's current stream.  Every step of the
 computation runs in the HIP library; if libgdn2.so is missing, loading fails
 with an error (there is no fallback).
@@ -31,7 +31,7 @@ GDN2_STAGE_STORE_T = 8
 
 EXPORTED = ("gdn2_abi_version", "gdn2_status_string", "gdn2_chunk_fwd_workspace_bytes",
             "gdn2_chunk_fwd_workspace_layout", "gdn2_chunk_fwd", "gdn2_chunk_fwd_stages",
-            "gdn2_step")
+            "gdn2_chunk_bwd_workspace_bytes", "gdn2_chunk_bwd", "gdn2_step")
 
 
 class Gdn2Error(RuntimeError):
@@ -74,6 +74,10 @@ def load_library(path=LIB_PATH):
     lib.gdn2_chunk_fwd.argtypes = [P] * 10 + [I] * 7 + [P, Z, P]
     lib.gdn2_chunk_fwd_stages.restype = I
     lib.gdn2_chunk_fwd_stages.argtypes = [P] * 10 + [I] * 7 + [P, Z, P, I]
+    lib.gdn2_chunk_bwd_workspace_bytes.restype = Z
+    lib.gdn2_chunk_bwd_workspace_bytes.argtypes = [I] * 8
+    lib.gdn2_chunk_bwd.restype = I
+    lib.gdn2_chunk_bwd.argtypes = [P] * 17 + [I] * 7 + [P, Z, P]
     lib.gdn2_step.restype = I
     lib.gdn2_step.argtypes = [P] * 8 + [I] * 5 + [P]
     _lib = lib
@@ -119,6 +123,18 @@ def gdn2_chunk_fwd_stages(q, k, v, log_alpha, b, w, S0, o, S_final, cu_seqlens, 
     return load_library().gdn2_chunk_fwd_stages(q, k, v, log_alpha, b, w, S0, o, S_final,
                                                  cu_seqlens, N, B, T, H, Dk, Dv, io, workspace,
                                                  workspace_bytes, stream, stages)
+
+
+def gdn2_chunk_bwd_workspace_bytes(N, B, T, H, Dk, Dv, io, varlen):
+    return load_library().gdn2_chunk_bwd_workspace_bytes(N, B, T, H, Dk, Dv, io, int(varlen))
+
+
+def gdn2_chunk_bwd(q, k, v, log_alpha, b, w, S0, dout, dS_final, dq, dk, dv, dlog_alpha, db, dw,
+                   dS0, cu_seqlens, N, B, T, H, Dk, Dv, io, workspace, workspace_bytes, stream):
+    """Raw call: every pointer argument is an int (device address) or None."""
+    return load_library().gdn2_chunk_bwd(q, k, v, log_alpha, b, w, S0, dout, dS_final, dq, dk,
+                                          dv, dlog_alpha, db, dw, dS0, cu_seqlens, N, B, T, H,
+                                          Dk, Dv, io, workspace, workspace_bytes, stream)
 
 
 def gdn2_step(q, k, v, log_alpha, b, w, S, o, B, H, Dk, Dv, io, stream):
@@ -216,3 +232,40 @@ def step(q, k, v, log_alpha, b, w, S, o=None, stream=None):
     if st != GDN2_OK:
         raise Gdn2Error(st, "gdn2_step")
     return o
+
+
+def chunk_bwd(q, k, v, log_alpha, b, w, dout, S0=None, dS_final=None, cu_seqlens=None,
+              need_dS0=True, workspace=None, stream=None):
+    """Gradients of chunk_fwd for upstream gradients dout (of o) and dS_final
+    (of S_final, None = zero).  Same shapes as chunk_fwd; bfloat16 q/k/v only.
+    Returns a dict: dq, dk, dv (q's dtype), dlog_alpha, db, dw (float32) and
+    dS0 ([N,H,Dk,Dv] float32, or None when need_dS0 is False).
+    """
+    import torch
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    io = _io_of(q)
+    for name, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
+        _check(t, name, q.dtype)
+    for name, t in (("log_alpha", log_alpha), ("b", b), ("w", w), ("S0", S0),
+                    ("dS_final", dS_final)):
+        _check(t, name, torch.float32)
+    _check(cu_seqlens, "cu_seqlens", torch.int32)
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+               dlog_alpha=torch.empty_like(log_alpha), db=torch.empty_like(b),
+               dw=torch.empty_like(w),
+               dS0=torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=q.device)
+               if need_dS0 else None)
+    varlen = cu_seqlens is not None
+    nbytes = gdn2_chunk_bwd_workspace_bytes(N, B, T, H, Dk, Dv, io, varlen)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    st = gdn2_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(S0),
+                        _ptr(dout), _ptr(dS_final), _ptr(out["dq"]), _ptr(out["dk"]),
+                        _ptr(out["dv"]), _ptr(out["dlog_alpha"]), _ptr(out["db"]),
+                        _ptr(out["dw"]), _ptr(out["dS0"]), _ptr(cu_seqlens), N, B, T, H, Dk, Dv,
+                        io, _ptr(workspace), workspace.numel(), _stream(stream))
+    if st != GDN2_OK:
+        raise Gdn2Error(st, "gdn2_chunk_bwd")
+    return out

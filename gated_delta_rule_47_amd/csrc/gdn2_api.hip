@@ -74,6 +74,30 @@ bool workspace_layout(int N, int B, int T, int H, int Dk, int Dv, size_t io_byte
     return true;
 }
 
+bool bwd_layout(int N, int B, int T, int H, int Dk, int Dv, size_t io_bytes, bool varlen,
+                BwdLayout *out) {
+    BwdLayout L;
+    if (!workspace_layout(N, B, T, H, Dk, Dv, io_bytes, varlen, &L.fwd)) return false;
+    const size_t chd = (size_t)L.fwd.max_chunks * (size_t)H;
+    size_t off = align_up(L.fwd.total);
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off = align_up(off + bytes);
+        return at;
+    };
+    L.off_Sc = take(chd * Dk * Dv * sizeof(float));
+    L.off_dSc = take(chd * Dk * Dv * sizeof(float));
+    L.off_dQh = take(chd * kChunk * Dk * sizeof(float));
+    L.off_dW = take(chd * kChunk * Dk * sizeof(float));
+    L.off_dKh = take(chd * kChunk * Dk * sizeof(float));
+    L.off_dM = take(chd * kChunk * kChunk * sizeof(float));
+    L.off_dAp = take(chd * kChunk * kChunk * sizeof(float));
+    L.off_dG = take(chd * Dk * sizeof(float));
+    L.total = off;
+    *out = L;
+    return true;
+}
+
 }  // namespace gdn2
 
 extern "C" {
@@ -202,6 +226,114 @@ int gdn2_chunk_fwd(const void *q, const void *k, const void *v, const float *log
     return gdn2_chunk_fwd_stages(q, k, v, log_alpha, b, w, S0, o, S_final, cu_seqlens, N, B, T, H,
                                  Dk, Dv, io, workspace, workspace_bytes, stream_ptr,
                                  GDN2_STAGE_ALL);
+}
+
+size_t gdn2_chunk_bwd_workspace_bytes(int N, int B, int T, int H, int Dk, int Dv, int io,
+                                      int varlen) {
+    if (io != GDN2_F32 && io != GDN2_BF16) return 0;
+    BwdLayout L;
+    if (!bwd_layout(N, B, T, H, Dk, Dv, io_size(io), varlen != 0, &L)) return 0;
+    return L.total;
+}
+
+int gdn2_chunk_bwd(const void *q, const void *k, const void *v, const float *log_alpha,
+                   const float *b, const float *w, const float *S0, const void *dout,
+                   const float *dS_final, void *dq, void *dk, void *dv, float *dlog_alpha,
+                   float *db, float *dw, float *dS0, const int32_t *cu_seqlens, int N, int B, int T,
+                   int H, int Dk, int Dv, int io, void *workspace, size_t workspace_bytes,
+                   void *stream_ptr) {
+    if (io != GDN2_F32 && io != GDN2_BF16) return GDN2_ERR_INVALID_ARGUMENT;
+    if (N < 0 || B < 0 || T < 0 || H < 0 || Dk <= 0 || Dv <= 0) return GDN2_ERR_INVALID_ARGUMENT;
+    if (!supported_dims(Dk, Dv) || io != GDN2_BF16) return GDN2_ERR_UNSUPPORTED;
+    const bool varlen = cu_seqlens != nullptr;
+    if (varlen ? B != 1 : N != B) return GDN2_ERR_INVALID_ARGUMENT;
+    if (N == 0 || H == 0) return GDN2_OK;
+    if ((long long)B * T > INT_MAX / 2) return GDN2_ERR_UNSUPPORTED;
+    const void *ins[] = {q, k, v, log_alpha, b, w, dout};
+    const void *outs[] = {dq, dk, dv, dlog_alpha, db, dw};
+    for (const void *p : ins) {
+        if (T > 0 && !p) return GDN2_ERR_INVALID_ARGUMENT;
+        if (p && !aligned16(p)) return GDN2_ERR_INVALID_ARGUMENT;
+    }
+    for (const void *p : outs) {
+        if (T > 0 && !p) return GDN2_ERR_INVALID_ARGUMENT;
+        if (p && !aligned16(p)) return GDN2_ERR_INVALID_ARGUMENT;
+    }
+    if ((S0 && !aligned16(S0)) || (dS_final && !aligned16(dS_final)) || (dS0 && !aligned16(dS0)) ||
+        (cu_seqlens && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3)))
+        return GDN2_ERR_INVALID_ARGUMENT;
+    // Outputs must be distinct from each other and from every input.
+    const void *all_out[] = {dq, dk, dv, dlog_alpha, db, dw, dS0};
+    const void *all_in[] = {q, k, v, log_alpha, b, w, dout, S0, dS_final, cu_seqlens};
+    for (int i = 0; i < 7; ++i) {
+        if (!all_out[i]) continue;
+        for (int j = i + 1; j < 7; ++j)
+            if (all_out[i] == all_out[j]) return GDN2_ERR_INVALID_ARGUMENT;
+        for (const void *p : all_in)
+            if (all_out[i] == p) return GDN2_ERR_INVALID_ARGUMENT;
+    }
+
+    BwdLayout L;
+    if (!bwd_layout(N, B, T, H, Dk, Dv, io_size(io), varlen, &L)) return GDN2_ERR_INVALID_ARGUMENT;
+    if (!workspace || workspace_bytes < L.total) return GDN2_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) return GDN2_ERR_WORKSPACE;
+
+    hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+    (void)hipGetLastError();  // a stale error left by other code is not ours to report
+    char *ws = static_cast<char *>(workspace);
+    const WorkspaceLayout &F = L.fwd;
+    BwdArgs ba{};
+    ChunkArgs &a = ba.c;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.log_alpha = log_alpha;
+    a.b = b;
+    a.w = w;
+    a.S0 = S0;
+    a.o = nullptr;
+    a.S_final = nullptr;
+    a.cu_seqlens = cu_seqlens;
+    a.N = N;
+    a.B = B;
+    a.T = T;
+    a.H = H;
+    a.NC = (T + kChunk - 1) / kChunk;
+    a.max_chunks = F.max_chunks;
+    a.plan = varlen ? reinterpret_cast<int32_t *>(ws + F.off_plan) : nullptr;
+    a.ws_T = ws + F.off_T;
+    a.ws_W = ws + F.off_W;
+    a.ws_Qh = ws + F.off_Qh;
+    a.ws_KhT = ws + F.off_KhT;
+    a.ws_M = ws + F.off_M;
+    a.ws_U = ws + F.off_U;
+    a.ws_gl = reinterpret_cast<float *>(ws + F.off_gl);
+    a.store_T = 1;
+    a.ws_Sc = reinterpret_cast<float *>(ws + L.off_Sc);
+    ba.dout = dout;
+    ba.dS_final = dS_final;
+    ba.dq = dq;
+    ba.dk = dk;
+    ba.dv = dv;
+    ba.dla = dlog_alpha;
+    ba.db = db;
+    ba.dw = dw;
+    ba.dS0 = dS0;
+    ba.Sc = a.ws_Sc;
+    ba.dSc = reinterpret_cast<float *>(ws + L.off_dSc);
+    ba.dQh = reinterpret_cast<float *>(ws + L.off_dQh);
+    ba.dW = reinterpret_cast<float *>(ws + L.off_dW);
+    ba.dKh = reinterpret_cast<float *>(ws + L.off_dKh);
+    ba.dM = reinterpret_cast<float *>(ws + L.off_dM);
+    ba.dAp = reinterpret_cast<float *>(ws + L.off_dAp);
+    ba.dG = reinterpret_cast<float *>(ws + L.off_dG);
+
+    hipError_t err = hipSuccess;
+    if (varlen) err = launch_plan(a, stream);
+    if (err == hipSuccess && F.max_chunks > 0) err = launch_chunk_prep(a, Dk, true, stream);
+    if (err == hipSuccess && F.max_chunks > 0) err = launch_chunk_prop(a, Dk, true, stream);
+    if (err == hipSuccess) err = launch_chunk_bwd(ba, Dk, stream);
+    return finish(err, stream);
 }
 
 int gdn2_step(const void *q, const void *k, const void *v, const float *log_alpha, const float *b,

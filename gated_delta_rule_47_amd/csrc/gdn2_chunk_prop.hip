@@ -338,7 +338,9 @@ __device__ __forceinline__ void ws_store_o(const ChunkArgs &a, const bf16 *sO, i
     }
 }
 
-template <int DK, int DV, int DVS>
+// kStates: also store every chunk's incoming state in a.ws_Sc (for the
+// backward) and write no o.
+template <int DK, int DV, int DVS, bool kStates>
 __global__ __launch_bounds__(2 * kThreads, 1) void chunk_prop_ws_kernel(ChunkArgs a) {
     using C = WsCfg<DK, DVS>;
     using M = Mma<bf16>;
@@ -403,8 +405,10 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_prop_ws_kernel(ChunkArg
             seq_end = tok_first + a.T;
         }
         auto store_o = [&](int k) {
-            const int tok0 = min(tok_first + k * kChunk, a.T * (a.plan ? 1 : a.N));
-            ws_store_o<DK, DV, DVS>(a, sO, h, tok0, min(kChunk, seq_end - tok0), col0_, t);
+            if constexpr (!kStates) {
+                const int tok0 = min(tok_first + k * kChunk, a.T * (a.plan ? 1 : a.N));
+                ws_store_o<DK, DV, DVS>(a, sO, h, tok0, min(kChunk, seq_end - tok0), col0_, t);
+            }
         };
         auto chunk_head = [&](int k) { return (size_t)(cbeg + min(k, nch - 1)) * H + h; };
         StageRegs<NJ> buf0, buf1;
@@ -471,6 +475,17 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_prop_ws_kernel(ChunkArg
     for (int j = 0; j < 4; ++j) __syncthreads();
 
     for (int cid = cbeg; cid < cend; ++cid) {
+        if constexpr (kStates) {  // the incoming state of this chunk, fp32 [Dk][Dv]
+            float *Sc = a.ws_Sc + ((size_t)cid * H + h) * DK * DV;
+#pragma unroll
+            for (int u = 0; u < C::S_TPW; ++u) {
+                const int cblk = wave * C::KB_W + u / NCB, colb = u % NCB;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    Sc[(size_t)(16 * cblk + 4 * (lane >> 4) + r) * DV + col0 + 16 * colb + (lane & 15)] =
+                        Sacc[u][r];
+            }
+        }
         load_own(nxt2, min(cid + 2, cend - 1));
         const bf16 *stage = reinterpret_cast<const bf16 *>(smem + ((cid - cbeg) & 1) * C::SZ_STAGE);
         const bf16 *Wf = stage;
@@ -591,15 +606,26 @@ static void launch_prop_d(const ChunkArgs &a, int dvs, hipStream_t stream) {
     const int groups = (chains + 7) / 8;
     if constexpr (sizeof(E) == 2) {  // compute + loader waves
         const dim3 block(2 * kThreads);
-        if (dvs == 64)
-            hipLaunchKernelGGL((chunk_prop_ws_kernel<D, D, 64>), dim3(groups * 8 * (D / 64)), block, 0,
-                               stream, a);
-        else if (dvs == 32)
-            hipLaunchKernelGGL((chunk_prop_ws_kernel<D, D, 32>), dim3(groups * 8 * (D / 32)), block, 0,
-                               stream, a);
-        else
-            hipLaunchKernelGGL((chunk_prop_ws_kernel<D, D, 16>), dim3(groups * 8 * (D / 16)), block, 0,
-                               stream, a);
+        if (a.ws_Sc) {
+            if (dvs == 64)
+                hipLaunchKernelGGL((chunk_prop_ws_kernel<D, D, 64, true>), dim3(groups * 8 * (D / 64)),
+                                   block, 0, stream, a);
+            else if (dvs == 32)
+                hipLaunchKernelGGL((chunk_prop_ws_kernel<D, D, 32, true>), dim3(groups * 8 * (D / 32)),
+                                   block, 0, stream, a);
+            else
+                hipLaunchKernelGGL((chunk_prop_ws_kernel<D, D, 16, true>), dim3(groups * 8 * (D / 16)),
+                                   block, 0, stream, a);
+        } else if (dvs == 64) {
+            hipLaunchKernelGGL((chunk_prop_ws_kernel<D, D, 64, false>), dim3(groups * 8 * (D / 64)), block,
+                               0, stream, a);
+        } else if (dvs == 32) {
+            hipLaunchKernelGGL((chunk_prop_ws_kernel<D, D, 32, false>), dim3(groups * 8 * (D / 32)), block,
+                               0, stream, a);
+        } else {
+            hipLaunchKernelGGL((chunk_prop_ws_kernel<D, D, 16, false>), dim3(groups * 8 * (D / 16)), block,
+                               0, stream, a);
+        }
     } else {
         const dim3 block(kThreads);
         if (dvs == 64)

@@ -36,6 +36,32 @@ struct ChunkArgs {
     void *ws_T, *ws_W, *ws_Qh, *ws_KhT, *ws_M, *ws_U;
     float *ws_gl;
     int store_T;          // the chunk-factor kernel also stores T = (I + A)^-1
+    float *ws_Sc;         // if set, the propagation stores every chunk's incoming
+                          // state here ([chunk id][head][Dk][Dv]) and writes no o
+};
+
+// The backward's workspace: the forward's layout (T always stored) followed
+// by fp32 arrays indexed [chunk id][head][...]: every chunk's incoming state
+// Sc and the gradient dSc of its outgoing state ([Dk][Dv]); the state-side
+// partial gradients dQh, dW, dKh ([64][Dk]), dM and dAp ([64][64], dAp =
+// dZ U^T) and dG ([Dk], the gradient of gamma_last through the state).
+struct BwdLayout {
+    WorkspaceLayout fwd;
+    size_t off_Sc = 0, off_dSc = 0, off_dQh = 0, off_dW = 0, off_dKh = 0, off_dM = 0,
+           off_dAp = 0, off_dG = 0;
+    size_t total = 0;
+};
+
+bool bwd_layout(int N, int B, int T, int H, int Dk, int Dv, size_t io_bytes, bool varlen,
+                BwdLayout *out);
+
+struct BwdArgs {
+    ChunkArgs c;          // forward arguments and chunk factors (c.o unused)
+    const void *dout;
+    const float *dS_final;
+    void *dq, *dk, *dv;
+    float *dla, *db, *dw, *dS0;
+    float *Sc, *dSc, *dQh, *dW, *dKh, *dM, *dAp, *dG;
 };
 
 struct StepArgs {
@@ -51,5 +77,7 @@ hipError_t launch_plan(const ChunkArgs &a, hipStream_t stream);
 hipError_t launch_chunk_prep(const ChunkArgs &a, int Dk, bool bf16_io, hipStream_t stream);
 hipError_t launch_chunk_prop(const ChunkArgs &a, int Dk, bool bf16_io, hipStream_t stream);
 hipError_t launch_step(const StepArgs &a, int Dk, bool bf16_io, hipStream_t stream);
+// Backward (bf16 only): reverse state-gradient pass, then the two per-chunk kernels.
+hipError_t launch_chunk_bwd(const BwdArgs &a, int Dk, hipStream_t stream);
 
 }  // namespace gdn2

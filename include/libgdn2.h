@@ -174,6 +174,49 @@ int gdn2_chunk_fwd_workspace_layout(int N, int B, int T, int H, int Dk, int Dv,
                                     int io, int varlen, gdn2_workspace_layout *out);
 
 /*
+ * Workspace bytes gdn2_chunk_bwd needs for a call with these sizes (same
+ * meaning of the arguments as gdn2_chunk_fwd_workspace_bytes).  Returns 0 for
+ * unsupported or invalid sizes.
+ */
+size_t gdn2_chunk_bwd_workspace_bytes(int N, int B, int T, int H, int Dk, int Dv,
+                                      int io, int varlen);
+
+/*
+ * Gradients of gdn2_chunk_fwd: the gate-aware chunkwise backward (the
+ * gist.science summary, part "3. Efficient chunkwise parallel training", item
+ * on the backward pass: the channel-wise gates b and w enter the gradients of
+ * the chunk's auxiliary matrices; the iplexlaw digest, section "El artículo y
+ * su pregunta").  Given the upstream gradients dout = dL/do and dS_final =
+ * dL/dS_final, it returns dL/d of every input: the exact chain rule of the
+ * recurrence above, taken through the same 64-token chunk form as the forward
+ * (the forward is recomputed inside the call; nothing from an earlier
+ * gdn2_chunk_fwd is needed).
+ *
+ * Same sizes, layouts, dense/packed conventions and decay precondition as
+ * gdn2_chunk_fwd.  Inputs:
+ *   q, k, v, log_alpha, b, w, S0    as for gdn2_chunk_fwd (S0 may be NULL)
+ *   dout      [B, T, H, Dv]  io dtype
+ *   dS_final  [N, H, Dk, Dv] f32, or NULL for zero
+ * Outputs (all written in full; every gradient of a token of the call):
+ *   dq, dk    [B, T, H, Dk]  io dtype       dlog_alpha, db [B, T, H, Dk] f32
+ *   dv        [B, T, H, Dv]  io dtype       dw             [B, T, H, Dv] f32
+ *   dS0       [N, H, Dk, Dv] f32, or NULL to skip it
+ * Outputs must not alias each other or any input.  The workspace (>=
+ * gdn2_chunk_bwd_workspace_bytes(...) bytes, 256-byte aligned) holds the
+ * chunk factors, every chunk's incoming state and state gradient, and the
+ * per-chunk partial gradients.  Only io = GDN2_BF16 is implemented;
+ * GDN2_F32 returns GDN2_ERR_UNSUPPORTED.
+ */
+int gdn2_chunk_bwd(const void *q, const void *k, const void *v,
+                   const float *log_alpha, const float *b, const float *w,
+                   const float *S0, const void *dout, const float *dS_final,
+                   void *dq, void *dk, void *dv,
+                   float *dlog_alpha, float *db, float *dw, float *dS0,
+                   const int32_t *cu_seqlens, int N,
+                   int B, int T, int H, int Dk, int Dv, int io,
+                   void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * One recurrent decode token for B independent sequences (constant-memory
  * decoding: the gist.science summary, "Problem statement").  The state is
  * read once and written once, in place:

@@ -1,0 +1,90 @@
+"""GPU parity of gdn2_chunk_bwd against the fp64 oracle's reverse recurrence
+(oracle.recurrence_bwd): every gradient, dense and packed calls, ragged tails,
+with and without initial state and final-state gradient."""
+
+import numpy as np
+import pytest
+
+import gated_delta_rule_47_amd as g
+import oracle as O
+import workloads as W
+from gpu_util import dev, host, log, upload_chunk
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("dq", "dk", "dv", "dlog_alpha", "db", "dw", "dS0")
+# bf16 I/O: the forward's bf16 factors and the bf16 gradient outputs bound the
+# agreement at a few 1e-3 of the largest value; the bound leaves headroom.
+TOL = 3e-2
+
+
+def _run_bwd(inp, grads):
+    import torch
+    d = upload_chunk(inp)
+    dout = dev(grads["dout"], inp["io"])
+    dSf = dev(grads["dS_final"])
+    out = g.chunk_bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], dout, S0=d["S0"],
+                      dS_final=dSf, cu_seqlens=d["cu_seqlens"])
+    torch.cuda.synchronize()
+    return out
+
+
+def _check(inp, grads, label):
+    out = _run_bwd(inp, grads)
+    ref = O.recurrence_bwd(*(inp[x] for x in ("q", "k", "v", "log_alpha", "b", "w")),
+                           grads["dout"], inp["S0"], grads["dS_final"], inp["cu_seqlens"])
+    errs = {n: O.rel_max_err(host(out[n]), ref[n]) for n in NAMES}
+    log("%s: %s" % (label, " ".join("%s %.2e" % kv for kv in errs.items())))
+    for n, e in errs.items():
+        assert e <= TOL, (n, e)
+    return out
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_bwd_dense_ragged(D):
+    """T = 150 (two full chunks and a 22-token tail), S0 and dS_final nonzero."""
+    wl = W.ChunkWorkload("bwd_dense", 2, 150, 2, D, D, W.BF16, 4242 + D, with_S0=True)
+    inp = W.make_chunk_inputs(wl)
+    _check(inp, W.make_chunk_grads(inp, 11 + D), "bwd dense D=%d" % D)
+
+
+def test_bwd_no_state_no_final_grad():
+    """S0 = NULL and dS_final = NULL (zero), a single short chunk."""
+    wl = W.ChunkWorkload("bwd_nostate", 1, 40, 2, 128, 128, W.BF16, 4343)
+    inp = W.make_chunk_inputs(wl)
+    _check(inp, W.make_chunk_grads(inp, 12, with_dS_final=False), "bwd no state")
+
+
+def test_bwd_varlen_edge_lengths():
+    """Packed sequences of lengths 1, 63, 64, 65, 130, 0 and 7."""
+    wl = W.ChunkWorkload("bwd_varlen", 1, 0, 2, 128, 128, W.BF16, 4444, with_S0=True, n_seqs=7)
+    inp = W.make_chunk_inputs(wl, lengths=[1, 63, 64, 65, 130, 0, 7])
+    _check(inp, W.make_chunk_grads(inp, 13), "bwd varlen")
+
+
+def test_bwd_erase_gate_to_two():
+    wl = W.ChunkWorkload("bwd_b2", 1, 128, 2, 128, 128, W.BF16, 4545, with_S0=True)
+    inp = W.make_chunk_inputs(wl, b_scale=2.0)
+    _check(inp, W.make_chunk_grads(inp, 14), "bwd b in [0,2]")
+
+
+def test_bwd_deterministic_bitwise():
+    import torch
+    wl = W.ChunkWorkload("bwd_det", 2, 200, 3, 128, 128, W.BF16, 4646, with_S0=True)
+    inp = W.make_chunk_inputs(wl)
+    grads = W.make_chunk_grads(inp, 15)
+    a = _run_bwd(inp, grads)
+    b = _run_bwd(inp, grads)
+    for n in NAMES:
+        assert torch.equal(a[n], b[n]), n
+
+
+def test_bwd_f32_unsupported():
+    import torch
+    wl = W.ChunkWorkload("bwd_f32", 1, 64, 1, 64, 64, W.F32, 4747)
+    inp = W.make_chunk_inputs(wl)
+    d = upload_chunk(inp)
+    dout = torch.zeros_like(d["q"])
+    with pytest.raises(g.Gdn2Error) as e:
+        g.chunk_bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], dout)
+    assert e.value.status == g.GDN2_ERR_UNSUPPORTED

@@ -183,6 +183,18 @@ def make_chunk_inputs(wl: ChunkWorkload, lengths=None, T: Optional[int] = None,
                 B=B_, T=T_, H=H, Dk=Dk, Dv=Dv, N=N, io=wl.io)
 
 
+def make_chunk_grads(inp, seed: int, with_dS_final: bool = True):
+    """Upstream gradients for a backward call on `inp` (a make_chunk_inputs
+    result), from their own PCG64 stream: dout ~ N(0, 1) [B, T, H, Dv] in the
+    io dtype and dS_final ~ N(0, 1) [N, H, Dk, Dv] float32 (or None)."""
+    rng = np.random.Generator(np.random.PCG64([seed, 7]))
+    dout = _io_cast(_normal(rng, (inp["B"], inp["T"], inp["H"], inp["Dv"])), inp["io"])
+    dSf = None
+    if with_dS_final:
+        dSf = _normal(rng, (inp["N"], inp["H"], inp["Dk"], inp["Dv"])).astype(np.float32)
+    return dict(dout=dout, dS_final=dSf)
+
+
 # ---------------------------------------------------------------------------
 # Decode inputs
 # ---------------------------------------------------------------------------
