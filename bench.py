@@ -45,7 +45,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-steps", type=int, default=1024)
-    ap.add_argument("--only", choices=["all", "chunk", "decode", "varlen"], default="all")
+    ap.add_argument("--only", choices=["all", "chunk", "decode", "varlen", "bwd"], default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=8,
                     help="batch rows (4096 tokens x 16 heads each) the oracle runs on")
@@ -229,6 +229,39 @@ def cpu_baseline(inp, rows):
     return n_tokens / dt, dt, n_tokens
 
 
+def bwd_alg_bytes(n_th, chains, D, io_bytes):
+    """Backward: reads q, k, v, dout (io) and log_alpha, b, w (fp32), writes dq, dk, dv (io)
+    and dlog_alpha, db, dw (fp32), per token-head; S0 and dS_final in, dS0 out per chain."""
+    per_th = D * (7 * io_bytes + 6 * 4)
+    return n_th * per_th + chains * 3 * D * D * 4
+
+
+def time_bwd(d, inp, steps, warmup):
+    """Time `steps` gdn2_chunk_bwd calls (events on the launch stream)."""
+    import torch
+    import gated_delta_rule_47_amd as g
+    import workloads as W
+    B, T, H, D, N = inp["B"], inp["T"], inp["H"], inp["Dk"], inp["N"]
+    gr = W.make_chunk_grads(inp, 1)
+    dout = torch.from_numpy(W.bf16_bits(gr["dout"]).view(np.int16)).to("cuda").view(torch.bfloat16)
+    dSf = torch.from_numpy(gr["dS_final"]).to("cuda")
+    varlen = d["cu_seqlens"] is not None
+    ws = torch.empty(g.gdn2_chunk_bwd_workspace_bytes(N, B, T, H, D, D, g.GDN2_BF16, varlen),
+                     dtype=torch.uint8, device="cuda")
+    x = (d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], dout)
+    kw = dict(S0=d["S0"], dS_final=dSf, cu_seqlens=d["cu_seqlens"], workspace=ws)
+    for _ in range(warmup):
+        g.chunk_bwd(*x, **kw)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        g.chunk_bwd(*x, **kw)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps, ws.numel()
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -292,6 +325,26 @@ def main():
                                              "(%d tokens x 16 heads, S0 as in the workload), one "
                                              "process, %.1f s" % (rows - 1, n, dt)}
             log("cpu oracle: %.1f tokens/s (%d tokens in %.1f s)" % (tps, n, dt))
+        del d, inp
+
+    if a.only in ("all", "bwd"):
+        wl = W.BATCH_4K
+        log("generating %s (backward)" % wl.name)
+        inp = W.make_chunk_inputs(wl)
+        d = upload(inp)
+        ms, ws_bytes = time_bwd(d, inp, max(3, a.steps // 4), 2)
+        tokens = inp["B"] * inp["T"]
+        nb = bwd_alg_bytes(tokens * inp["H"], inp["N"] * inp["H"], inp["Dk"], 2)
+        out["backward"] = {"workload": wl.name, "entry": "gdn2_chunk_bwd", "ms": ms,
+                           "tokens_per_s": tokens / (ms * 1e-3), "alg_bytes": nb,
+                           "alg_GBps": nb / (ms * 1e-3) / 1e9,
+                           "hbm_frac": nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                           "workspace_bytes": ws_bytes}
+        log("backward: %.3f ms -> %.3e tokens/s (%.1f%% of HBM by algorithmic bytes)"
+            % (ms, tokens / (ms * 1e-3), 100 * out["backward"]["hbm_frac"]))
+        if "value" not in out:
+            out.update({"value": tokens / (ms * 1e-3), "ms_per_step": ms,
+                        "config": {"workload": wl.name, "pass": "backward"}})
         del d, inp
 
     if a.only in ("all", "decode"):

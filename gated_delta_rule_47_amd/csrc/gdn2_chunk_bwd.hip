@@ -235,24 +235,59 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_rev_kernel(BwdArgs ba) 
 
 // ---------------------------------------------------------------------------
 // State side, one workgroup per (chunk, head): the products with S and dS',
-// taken over 32-column slabs of the value axis.  Wave w owns token rows
-// 16w .. 16w+15 of every 64-row result.
+// taken over 32-column slabs of the value axis with bf16 MFMA (16x16x32).
+// Every operand is staged in LDS in the orientation its fragment load wants
+// (k contiguous), transposing on the way in where needed.  Wave w owns token
+// rows 16w .. 16w+15 of every 64-row result.
 // ---------------------------------------------------------------------------
 template <int DK>
+struct StateCfg {
+    static constexpr int DV = DK, SW = 32, NSL = DV / SW, NKB = DK / 16;
+    static constexpr int LSW = SW + 8;     // [..][SW] bf16 rows
+    static constexpr int LDKP = DK + 8;    // [..][DK] bf16 rows
+    static constexpr int L64 = kChunk + 8; // [..][64] bf16 rows
+};
+
+// Scatter 8 consecutive elements of row r (columns k..k+7) of a fragment-ordered
+// source into a transposed LDS array: dst[(k + t) * ld + r].
+__device__ __forceinline__ void scatter_t8(bf16 *dst, int ld, int r, int k, granule_t g8) {
+    const bf16x8 v = *reinterpret_cast<const bf16x8 *>(&g8);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) dst[(k + t) * ld + r] = v[t];
+}
+
+// Row and first column of granule `gi` (8 elements) of a fragment-ordered bf16
+// matrix with K columns.
+__device__ __forceinline__ void frag_granule_pos(int gi, int K, int &r, int &k) {
+    const int blk = gi >> 6, lp = gi & 63, nkb = K / 32;
+    r = (blk / nkb) * 16 + (lp & 15);
+    k = (blk % nkb) * 32 + (lp >> 4) * 8;
+}
+
+template <int DK>
 __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_state_kernel(BwdArgs ba) {
-    constexpr int DV = DK, SW = 32, NSL = DV / SW, LD = 48, NKB = DK / 16;
+    using C = StateCfg<DK>;
+    using MB = Mma<bf16>;
+    constexpr int DV = C::DV, SW = C::SW, NKB = C::NKB, LSW = C::LSW, LDKP = C::LDKP, L64 = C::L64;
+    constexpr int NKD = DK / 32;
     const ChunkArgs &a = ba.c;
-    __shared__ __attribute__((aligned(16))) bf16 sW[kChunk * DK];
-    __shared__ __attribute__((aligned(16))) bf16 sM[kChunk * kChunk];
-    __shared__ __attribute__((aligned(16))) bf16 sK[DK * kChunk];
-    __shared__ __attribute__((aligned(16))) bf16 sT[kChunk * kChunk];
-    __shared__ __attribute__((aligned(16))) float sS[DK * LD];
-    __shared__ __attribute__((aligned(16))) float sdS[DK * LD];
-    __shared__ __attribute__((aligned(16))) float sdO[kChunk * LD];
-    __shared__ __attribute__((aligned(16))) float sUs[kChunk * LD];
-    __shared__ __attribute__((aligned(16))) float sUe[kChunk * LD];
-    __shared__ __attribute__((aligned(16))) float sdU[kChunk * LD];
-    __shared__ __attribute__((aligned(16))) float sdZ[kChunk * LD];
+    // persistent
+    __shared__ __attribute__((aligned(16))) bf16 sW[kChunk * DK];    // W, fragment order
+    __shared__ __attribute__((aligned(16))) bf16 sMt[kChunk * L64];  // [i][j] = M[j][i]
+    __shared__ __attribute__((aligned(16))) bf16 sKh[kChunk * LDKP]; // [i][c] = Khat[i][c]
+    __shared__ __attribute__((aligned(16))) bf16 sTt[kChunk * L64];  // [i][j] = T[j][i]
+    // per slab
+    __shared__ __attribute__((aligned(16))) bf16 sSt[SW * LDKP];     // [v][c] = S[c][v]
+    __shared__ __attribute__((aligned(16))) bf16 sS[DK * LSW];       // [c][v]
+    __shared__ __attribute__((aligned(16))) bf16 sdSt[SW * LDKP];    // [v][c] = dS'[c][v]
+    __shared__ __attribute__((aligned(16))) bf16 sdS[DK * LSW];      // [c][v]
+    __shared__ __attribute__((aligned(16))) bf16 sdOt[SW * L64];     // [v][j] = dO[j][v]
+    __shared__ __attribute__((aligned(16))) bf16 sdO[kChunk * LSW];  // [i][v]
+    __shared__ __attribute__((aligned(16))) bf16 sU[kChunk * LSW];   // [j][v] = U[j][v]
+    __shared__ __attribute__((aligned(16))) bf16 sUe[kChunk * LSW];  // [i][v] = U_eff
+    __shared__ __attribute__((aligned(16))) bf16 sdUt[SW * L64];     // [v][i] = dU_eff[i][v]
+    __shared__ __attribute__((aligned(16))) bf16 sdU[kChunk * LSW];  // [i][v]
+    __shared__ __attribute__((aligned(16))) bf16 sdZ[kChunk * LSW];  // [i][v]
 
     const int H = a.H, cid = blockIdx.x / H, h = blockIdx.x % H;
     if (a.plan && cid >= a.plan[a.N]) return;
@@ -265,73 +300,113 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_state_kernel(BwdArgs ba
     const bf16 *Ug = reinterpret_cast<const bf16 *>(a.ws_U) + ch * kChunk * DV;
     bf16 *dv = reinterpret_cast<bf16 *>(ba.dv);
 
+    // ---- persistent operands ---------------------------------------------
     copy16(sW, reinterpret_cast<const bf16 *>(a.ws_W) + ch * kChunk * DK, kChunk * DK * 2, tid, kThreads);
-    copy16(sM, reinterpret_cast<const bf16 *>(a.ws_M) + ch * kChunk * kChunk, kChunk * kChunk * 2, tid,
-           kThreads);
-    copy16(sK, reinterpret_cast<const bf16 *>(a.ws_KhT) + ch * DK * kChunk, DK * kChunk * 2, tid, kThreads);
-    copy16(sT, reinterpret_cast<const bf16 *>(a.ws_T) + ch * kChunk * kChunk, kChunk * kChunk * 2, tid,
-           kThreads);
+    {
+        const granule_t *Mg = reinterpret_cast<const granule_t *>(a.ws_M) + ch * (kChunk * kChunk / 8);
+        for (int gi = tid; gi < kChunk * kChunk / 8; gi += kThreads) {
+            int r, k;
+            frag_granule_pos(gi, kChunk, r, k);   // M[r][k..k+7] -> sMt[k+t][r]
+            scatter_t8(sMt, L64, r, k, Mg[gi]);
+        }
+        const granule_t *Kg = reinterpret_cast<const granule_t *>(a.ws_KhT) + ch * (DK * kChunk / 8);
+        for (int gi = tid; gi < DK * kChunk / 8; gi += kThreads) {
+            int r, k;
+            frag_granule_pos(gi, kChunk, r, k);   // KhT[c = r][i = k..k+7] -> sKh[i][c]
+            scatter_t8(sKh, LDKP, r, k, Kg[gi]);
+        }
+        const granule_t *Tg = reinterpret_cast<const granule_t *>(a.ws_T) + ch * (kChunk * kChunk / 8);
+        for (int gi = tid; gi < kChunk * kChunk / 8; gi += kThreads)  // T row-major [j][i..i+7]
+            scatter_t8(sTt, L64, gi / 8, 8 * (gi % 8), Tg[gi]);
+    }
 
     f32x4 dQh[NKB], dWt[NKB], dKh[NKB], dMa[4], dAp[4];
 #pragma unroll
     for (int j = 0; j < NKB; ++j) dQh[j] = dWt[j] = dKh[j] = zero4();
 #pragma unroll
     for (int j = 0; j < 4; ++j) dMa[j] = dAp[j] = zero4();
-    float dG = 0.0f;
     const float *Sc = ba.Sc + ch * DK * DV;
     const float *dSc = ba.dSc + ch * DK * DV;
 
-    for (int sl = 0; sl < NSL; ++sl) {
+    for (int sl = 0; sl < C::NSL; ++sl) {
         const int v0 = sl * SW;
+        // S and dS' columns v0..v0+SW: [c][v] and transposed [v][c].
         for (int e = tid; e < DK * SW / 4; e += kThreads) {
-            const int c = e / (SW / 4), c4 = 4 * (e % (SW / 4));
-            *reinterpret_cast<f32x4 *>(sS + c * LD + c4) =
-                *reinterpret_cast<const f32x4 *>(Sc + (size_t)c * DV + v0 + c4);
-            *reinterpret_cast<f32x4 *>(sdS + c * LD + c4) =
-                *reinterpret_cast<const f32x4 *>(dSc + (size_t)c * DV + v0 + c4);
+            const int c = e / (SW / 4), v4 = 4 * (e % (SW / 4));
+            const f32x4 s4 = *reinterpret_cast<const f32x4 *>(Sc + (size_t)c * DV + v0 + v4);
+            const f32x4 d4 = *reinterpret_cast<const f32x4 *>(dSc + (size_t)c * DV + v0 + v4);
+            bf16x4 sb, db;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                sb[t] = static_cast<bf16>(s4[t]);
+                db[t] = static_cast<bf16>(d4[t]);
+                sSt[(v4 + t) * LDKP + c] = sb[t];
+                sdSt[(v4 + t) * LDKP + c] = db[t];
+            }
+            *reinterpret_cast<bf16x4 *>(sS + c * LSW + v4) = sb;
+            *reinterpret_cast<bf16x4 *>(sdS + c * LSW + v4) = db;
         }
-        for (int e = tid; e < kChunk * SW; e += kThreads) {
-            const int i = e / SW, vv = e % SW, col = v0 + vv;
-            sdO[i * LD + vv] = i < len ? static_cast<float>(dout[((size_t)(tok0 + i) * H + h) * DV + col])
-                                       : 0.0f;
+        // dO rows (zero past the chunk) and U, [i][v] and transposed.
+        for (int e = tid; e < kChunk * SW / 4; e += kThreads) {
+            const int i = e / (SW / 4), v4 = 4 * (e % (SW / 4));
+            bf16x4 o4;
+            if (i < len) {
+                o4 = *reinterpret_cast<const bf16x4 *>(dout + ((size_t)(tok0 + i) * H + h) * DV + v0 + v4);
+            } else {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) o4[t] = static_cast<bf16>(0.0f);
+            }
+            *reinterpret_cast<bf16x4 *>(sdO + i * LSW + v4) = o4;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) sdOt[(v4 + t) * L64 + i] = o4[t];
             // U in accumulator order: [I][cb][lane][r] = U[16I + 4(lane/16) + r][16cb + lane%16]
-            const int ul = 16 * ((i & 15) >> 2) + (col & 15);
-            sUs[i * LD + vv] =
-                static_cast<float>(Ug[(((size_t)(i >> 4) * (DV / 16) + (col >> 4)) * 64 + ul) * 4 + (i & 3)]);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int col = v0 + v4 + t, ul = 16 * ((i & 15) >> 2) + (col & 15);
+                sU[i * LSW + v4 + t] = Ug[(((size_t)(i >> 4) * (DV / 16) + (col >> 4)) * 64 + ul) * 4 + (i & 3)];
+            }
         }
         __syncthreads();
 
-        // U_eff = U - W S and dU_eff = M^T dO + Khat dS' on this slab.
+        // U_eff = U - W S and dU_eff = M^T dO + Khat dS' on this slab (rows of block I).
 #pragma unroll
         for (int cb = 0; cb < SW / 16; ++cb) {
-            const f32x4 ws = mma_f32<DK>(
-                zero4(), lane, [&](int m, int k) { return fe(sW, DK, 16 * I + m, k); },
-                [&](int nn, int k) { return sS[k * LD + 16 * cb + nn]; });
-            f32x4 du = mma_f32<kChunk>(
-                zero4(), lane, [&](int m, int k) { return fe(sM, kChunk, k, 16 * I + m); },
-                [&](int nn, int k) { return sdO[k * LD + 16 * cb + nn]; });
-            du = mma_f32<DK>(
-                du, lane, [&](int m, int k) { return fe(sK, kChunk, k, 16 * I + m); },
-                [&](int nn, int k) { return sdS[k * LD + 16 * cb + nn]; });
+            f32x4 ws = zero4(), du = zero4();
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int o = (16 * I + 4 * (lane >> 4) + r) * LD + 16 * cb + (lane & 15);
-                sUe[o] = sUs[o] - ws[r];
-                sdU[o] = du[r];
+            for (int kk = 0; kk < NKD; ++kk) {
+                ws = MB::mma(load_frag_packed<bf16>(sW, DK, I, kk, lane),
+                             load_frag<bf16>(sSt + 16 * cb * LDKP + 32 * kk, LDKP, lane), ws);
+                du = MB::mma(load_frag<bf16>(sKh + 16 * I * LDKP + 32 * kk, LDKP, lane),
+                             load_frag<bf16>(sdSt + 16 * cb * LDKP + 32 * kk, LDKP, lane), du);
             }
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+                du = MB::mma(load_frag<bf16>(sMt + 16 * I * L64 + 32 * kk, L64, lane),
+                             load_frag<bf16>(sdOt + 16 * cb * L64 + 32 * kk, L64, lane), du);
+            // U tile in accumulator order straight from the workspace.
+            const bf16x4 u4 = *reinterpret_cast<const bf16x4 *>(
+                Ug + (((size_t)I * (DV / 16) + (v0 / 16 + cb)) * 64 + lane) * 4);
+            f32x4 ue;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) ue[r] = static_cast<float>(u4[r]) - ws[r];
+            store_tile<bf16>(sUe + 16 * I * LSW + 16 * cb, LSW, ue, lane);
+            store_tile<bf16>(sdU + 16 * I * LSW + 16 * cb, LSW, du, lane);
+            store_tile_t<bf16>(sdUt + 16 * cb * L64 + 16 * I, L64, du, lane);
         }
         __syncthreads();
 
         // dZ = T^T dU_eff; dv = w dZ, dw = v dZ.
 #pragma unroll
         for (int cb = 0; cb < SW / 16; ++cb) {
-            const f32x4 dz = mma_f32<kChunk>(
-                zero4(), lane, [&](int m, int k) { return static_cast<float>(sT[k * kChunk + 16 * I + m]); },
-                [&](int nn, int k) { return sdU[k * LD + 16 * cb + nn]; });
+            f32x4 dz = zero4();
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+                dz = MB::mma(load_frag<bf16>(sTt + 16 * I * L64 + 32 * kk, L64, lane),
+                             load_frag<bf16>(sdUt + 16 * cb * L64 + 32 * kk, L64, lane), dz);
+            store_tile<bf16>(sdZ + 16 * I * LSW + 16 * cb, LSW, dz, lane);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = 16 * I + 4 * (lane >> 4) + r, vv = 16 * cb + (lane & 15);
-                sdZ[i * LD + vv] = dz[r];
                 if (i < len) {
                     const size_t o = ((size_t)(tok0 + i) * H + h) * DV + v0 + vv;
                     dv[o] = static_cast<bf16>(a.w[o] * dz[r]);
@@ -339,27 +414,29 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_state_kernel(BwdArgs ba
                 }
             }
         }
-        // Products accumulated over the slabs (k runs over the slab's columns).
+        // Products accumulated over the slabs (k = the slab's 32 columns).
+        {
+            const MB::frag fdO = load_frag<bf16>(sdO + 16 * I * LSW, LSW, lane);
+            const MB::frag fdU = load_frag<bf16>(sdU + 16 * I * LSW, LSW, lane);
+            const MB::frag fUe = load_frag<bf16>(sUe + 16 * I * LSW, LSW, lane);
 #pragma unroll
-        for (int cb = 0; cb < NKB; ++cb) {
-            dQh[cb] = mma_f32<SW>(dQh[cb], lane, [&](int m, int k) { return sdO[(16 * I + m) * LD + k]; },
-                                  [&](int nn, int k) { return sS[(16 * cb + nn) * LD + k]; });
-            dWt[cb] = mma_f32<SW>(dWt[cb], lane, [&](int m, int k) { return sdU[(16 * I + m) * LD + k]; },
-                                  [&](int nn, int k) { return sS[(16 * cb + nn) * LD + k]; });
-            dKh[cb] = mma_f32<SW>(dKh[cb], lane, [&](int m, int k) { return sUe[(16 * I + m) * LD + k]; },
-                                  [&](int nn, int k) { return sdS[(16 * cb + nn) * LD + k]; });
+            for (int cb = 0; cb < NKB; ++cb) {
+                const MB::frag fS = load_frag<bf16>(sS + 16 * cb * LSW, LSW, lane);
+                dQh[cb] = MB::mma(fdO, fS, dQh[cb]);
+                dWt[cb] = MB::mma(fdU, fS, dWt[cb]);
+                dKh[cb] = MB::mma(fUe, load_frag<bf16>(sdS + 16 * cb * LSW, LSW, lane), dKh[cb]);
+            }
+#pragma unroll
+            for (int J = 0; J < 4; ++J)
+                dMa[J] = MB::mma(fdO, load_frag<bf16>(sUe + 16 * J * LSW, LSW, lane), dMa[J]);
         }
-#pragma unroll
-        for (int J = 0; J < 4; ++J)
-            dMa[J] = mma_f32<SW>(dMa[J], lane, [&](int m, int k) { return sdO[(16 * I + m) * LD + k]; },
-                                 [&](int nn, int k) { return sUe[(16 * J + nn) * LD + k]; });
-        if (tid < DK)
-            for (int vv = 0; vv < SW; ++vv) dG += sdS[tid * LD + vv] * sS[tid * LD + vv];
         __syncthreads();  // dZ complete
+        {
+            const MB::frag fdZ = load_frag<bf16>(sdZ + 16 * I * LSW, LSW, lane);
 #pragma unroll
-        for (int J = 0; J < 4; ++J)
-            dAp[J] = mma_f32<SW>(dAp[J], lane, [&](int m, int k) { return sdZ[(16 * I + m) * LD + k]; },
-                                 [&](int nn, int k) { return sUs[(16 * J + nn) * LD + k]; });
+            for (int J = 0; J < 4; ++J)
+                dAp[J] = MB::mma(fdZ, load_frag<bf16>(sU + 16 * J * LSW, LSW, lane), dAp[J]);
+        }
         __syncthreads();  // before the next slab is staged
     }
 
@@ -382,7 +459,6 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_state_kernel(BwdArgs ba
             oA[i * kChunk + j] = dAp[J][r];
         }
     }
-    if (tid < DK) ba.dG[ch * DK + tid] = dG;
 }
 
 // ---------------------------------------------------------------------------
@@ -616,7 +692,26 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_factor_kernel(BwdArgs b
         if (t > tg) after += *reinterpret_cast<const f32x4 *>(sRed + t * DK + c0);
         kdk_all += *reinterpret_cast<const f32x4 *>(sRed + (C::NTG + t) * DK + c0);
     }
-    const f32x4 dG = *reinterpret_cast<const f32x4 *>(ba.dG + ch * DK + c0);
+    // dgl[c] = sum_v dS'[c][v] S[c][v]: this thread takes v in [tg*DV/NTG, ..), the
+    // group partials meet in LDS.
+    {
+        constexpr int VPT = DK / C::NTG;
+        const float *Sc = ba.Sc + ch * DK * DK, *dSc = ba.dSc + ch * DK * DK;
+        f32x4 part = zero4();
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            for (int v = tg * VPT; v < (tg + 1) * VPT; v += 4) {
+                const f32x4 s4 = *reinterpret_cast<const f32x4 *>(Sc + (size_t)(c0 + c) * DK + v);
+                const f32x4 d4 = *reinterpret_cast<const f32x4 *>(dSc + (size_t)(c0 + c) * DK + v);
+                part[c] += s4[0] * d4[0] + s4[1] * d4[1] + s4[2] * d4[2] + s4[3] * d4[3];
+            }
+        __syncthreads();  // the totals above have been read
+        *reinterpret_cast<f32x4 *>(sRed + tg * DK + c0) = part;
+    }
+    __syncthreads();
+    f32x4 dG = zero4();
+#pragma unroll
+    for (int t = 0; t < C::NTG; ++t) dG += *reinterpret_cast<const f32x4 *>(sRed + t * DK + c0);
     f32x4 dglast;
 #pragma unroll
     for (int c = 0; c < 4; ++c) dglast[c] = __expf(glast[c]) * dG[c] + kdk_all[c];

@@ -88,3 +88,24 @@ def test_bwd_f32_unsupported():
     with pytest.raises(g.Gdn2Error) as e:
         g.chunk_bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], dout)
     assert e.value.status == g.GDN2_ERR_UNSUPPORTED
+
+
+def test_bwd_full_batch_workload_sampled():
+    """B=8, H=16, T=4096, d=128 (the batch workload) in the launch configuration
+    the benchmark times; sampled (sequence, head) pairs against the oracle's
+    chunk-form backward (pinned to the reverse recurrence on the CPU)."""
+    inp = W.make_chunk_inputs(W.BATCH_4K)
+    grads = W.make_chunk_grads(inp, 1)
+    out = _run_bwd(inp, grads)
+    for n, h in [(0, 0), (5, 9), (7, 15)]:
+        sl = (slice(n, n + 1), slice(None), slice(h, h + 1))
+        ref = O.chunked_bwd(*(inp[x][sl] for x in ("q", "k", "v", "log_alpha", "b", "w")),
+                            grads["dout"][sl], inp["S0"][n:n + 1, h:h + 1],
+                            grads["dS_final"][n:n + 1, h:h + 1])
+        errs = {}
+        for name in NAMES:
+            got = out[name][n:n + 1, h:h + 1] if name == "dS0" else out[name][sl]
+            errs[name] = O.rel_max_err(host(got), ref[name])
+        log("bwd batch (%d,%d): %s" % (n, h, " ".join("%s %.2e" % kv for kv in errs.items())))
+        for name, e in errs.items():
+            assert e <= TOL, (name, e)
