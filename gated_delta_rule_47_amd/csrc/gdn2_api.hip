@@ -85,6 +85,10 @@ bool bwd_layout(int N, int B, int T, int H, int Dk, int Dv, size_t io_bytes, boo
         off = align_up(off + bytes);
         return at;
     };
+    L.off_Mt = take(chd * kChunk * kChunk * io_bytes);
+    L.off_Kh = take(chd * kChunk * Dk * io_bytes);
+    L.off_Qt = take(chd * Dk * kChunk * io_bytes);
+    L.off_Wt = take(chd * Dk * kChunk * io_bytes);
     L.off_Sc = take(chd * Dk * Dv * sizeof(float));
     L.off_dSc = take(chd * Dk * Dv * sizeof(float));
     L.off_dQh = take(chd * kChunk * Dk * sizeof(float));
@@ -92,7 +96,6 @@ bool bwd_layout(int N, int B, int T, int H, int Dk, int Dv, size_t io_bytes, boo
     L.off_dKh = take(chd * kChunk * Dk * sizeof(float));
     L.off_dM = take(chd * kChunk * kChunk * sizeof(float));
     L.off_dAp = take(chd * kChunk * kChunk * sizeof(float));
-    L.off_dG = take(chd * Dk * sizeof(float));
     L.total = off;
     *out = L;
     return true;
@@ -310,6 +313,10 @@ int gdn2_chunk_bwd(const void *q, const void *k, const void *v, const float *log
     a.ws_gl = reinterpret_cast<float *>(ws + F.off_gl);
     a.store_T = 1;
     a.ws_Sc = reinterpret_cast<float *>(ws + L.off_Sc);
+    a.ws_Mt = ws + L.off_Mt;
+    a.ws_Kh = ws + L.off_Kh;
+    a.ws_Qt = ws + L.off_Qt;
+    a.ws_Wt = ws + L.off_Wt;
     ba.dout = dout;
     ba.dS_final = dS_final;
     ba.dq = dq;
@@ -326,7 +333,6 @@ int gdn2_chunk_bwd(const void *q, const void *k, const void *v, const float *log
     ba.dKh = reinterpret_cast<float *>(ws + L.off_dKh);
     ba.dM = reinterpret_cast<float *>(ws + L.off_dM);
     ba.dAp = reinterpret_cast<float *>(ws + L.off_dAp);
-    ba.dG = reinterpret_cast<float *>(ws + L.off_dG);
 
     hipError_t err = hipSuccess;
     if (varlen) err = launch_plan(a, stream);

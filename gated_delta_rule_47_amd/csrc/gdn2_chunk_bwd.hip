@@ -104,29 +104,28 @@ __device__ __forceinline__ void dense_span(const ChunkArgs &a, int cid, int &tok
 
 // ---------------------------------------------------------------------------
 // Reverse pass: one workgroup per (sequence, head, DVS-column slab), the
-// chunks of the sequence from last to first.  dS' lives in accumulators:
-// wave w owns state rows 16 (w*KB_W + b) .. of the slab, like the forward.
+// chunks of the sequence from last to first, bf16 MFMA.  dS' lives in fp32
+// accumulators (wave w owns state rows 16 (w*KB_W + b) .. of the slab, like
+// the forward); its bf16 transpose in LDS is the operand of Khat dS'.  The
+// factors are the transposed copies the chunk-factor kernel writes for
+// backward calls (M^T, Khat, Qhat^T, W^T), loaded as fragments.
 // ---------------------------------------------------------------------------
 template <int DK, int DVS>
 struct RevCfg {
     static constexpr int DV = DK, NS = DV / DVS, NCB = DVS / 16, NKB = DK / 16;
     static constexpr int KB_W = NKB / 4, S_TPW = KB_W * NCB;
-    static constexpr int LDD = (DVS == 16) ? 16 : DVS + 16;  // column reads hit distinct banks
+    static constexpr int LDKP = DK + 8, L64 = kChunk + 8;
 };
 
 template <int DK, int DVS>
 __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_rev_kernel(BwdArgs ba) {
     using C = RevCfg<DK, DVS>;
-    constexpr int DV = C::DV, NCB = C::NCB, LDD = C::LDD;
+    using MB = Mma<bf16>;
+    constexpr int DV = C::DV, NCB = C::NCB, LDKP = C::LDKP, L64 = C::L64, NKD = DK / 32;
     const ChunkArgs &a = ba.c;
-    __shared__ __attribute__((aligned(16))) float sdS[DK * LDD];  // dS' of the chunk, this slab
-    __shared__ __attribute__((aligned(16))) float sdO[kChunk * LDD];
-    __shared__ __attribute__((aligned(16))) float sdU[kChunk * LDD];
-    __shared__ __attribute__((aligned(16))) bf16 sM[kChunk * kChunk];
-    __shared__ __attribute__((aligned(16))) bf16 sK[DK * kChunk];
-    __shared__ __attribute__((aligned(16))) bf16 sQ[kChunk * DK];
-    __shared__ __attribute__((aligned(16))) bf16 sW[kChunk * DK];
-    __shared__ float sgl[DK];
+    __shared__ __attribute__((aligned(16))) bf16 sdSt[DVS * LDKP];  // [v][c] = dS'[c][v]
+    __shared__ __attribute__((aligned(16))) bf16 sdOt[DVS * L64];   // [v][i] = dO[i][v]
+    __shared__ __attribute__((aligned(16))) bf16 sdUt[DVS * L64];   // [v][i] = dU_eff[i][v]
 
     const int H = a.H;
     const int x = blockIdx.x, xcd = x & 7, rest = x >> 3;
@@ -152,71 +151,79 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_rev_kernel(BwdArgs ba) 
         const size_t ch = (size_t)cid * H + h;
         int tok0, len;
         chunk_span_of(a, cid, cbeg, n, tok0, len);
-        // dS' of this chunk: to the workspace (for the per-chunk kernels) and to LDS.
+        // Fragments of this chunk: M^T and Khat rows of block `wave`, Qhat^T
+        // and W^T rows of this wave's state row blocks; gamma_last.
+        const bf16 *Mt = reinterpret_cast<const bf16 *>(a.ws_Mt) + ch * kChunk * kChunk;
+        const bf16 *Kh = reinterpret_cast<const bf16 *>(a.ws_Kh) + ch * kChunk * DK;
+        const bf16 *Qt = reinterpret_cast<const bf16 *>(a.ws_Qt) + ch * DK * kChunk;
+        const bf16 *Wt = reinterpret_cast<const bf16 *>(a.ws_Wt) + ch * DK * kChunk;
+        MB::frag fM[2], fK[NKD], fQ[C::KB_W][2], fW[C::KB_W][2];
+        f32x4 gl[C::KB_W];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) fM[kk] = load_frag_packed<bf16>(Mt, kChunk, wave, kk, lane);
+#pragma unroll
+        for (int kk = 0; kk < NKD; ++kk) fK[kk] = load_frag_packed<bf16>(Kh, DK, wave, kk, lane);
+#pragma unroll
+        for (int b = 0; b < C::KB_W; ++b) {
+            const int cblk = wave * C::KB_W + b;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                fQ[b][kk] = load_frag_packed<bf16>(Qt, kChunk, cblk, kk, lane);
+                fW[b][kk] = load_frag_packed<bf16>(Wt, kChunk, cblk, kk, lane);
+            }
+            gl[b] = *reinterpret_cast<const f32x4 *>(a.ws_gl + ch * DK + 16 * cblk + 4 * (lane >> 4));
+        }
+        // dS' of this chunk: to the workspace (fp32, for the per-chunk kernels)
+        // and, transposed, to LDS.
         float *dSc = ba.dSc + ch * DK * DV;
 #pragma unroll
         for (int u = 0; u < C::S_TPW; ++u) {
             const int cblk = wave * C::KB_W + u / NCB, colb = u % NCB;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = 16 * cblk + 4 * (lane >> 4) + r, c = 16 * colb + (lane & 15);
-                dSc[(size_t)row * DV + col0 + c] = dS[u][r];
-                sdS[row * LDD + c] = dS[u][r];
-            }
+            for (int r = 0; r < 4; ++r)
+                dSc[(size_t)(16 * cblk + 4 * (lane >> 4) + r) * DV + col0 + 16 * colb + (lane & 15)] = dS[u][r];
+            store_tile_t<bf16>(sdSt + 16 * colb * LDKP + 16 * cblk, LDKP, dS[u], lane);
         }
+        // dO rows of the chunk (zero past its end), transposed.
         for (int e = tid; e < kChunk * DVS / 4; e += kThreads) {
             const int i = e / (DVS / 4), c4 = 4 * (e % (DVS / 4));
-            f32x4 x4 = zero4();
+            bf16x4 v4;
             if (i < len) {
-                const bf16x4 v4 = *reinterpret_cast<const bf16x4 *>(
-                    dout + ((size_t)(tok0 + i) * H + h) * DV + col0 + c4);
-                x4 = f32x4{static_cast<float>(v4[0]), static_cast<float>(v4[1]),
-                           static_cast<float>(v4[2]), static_cast<float>(v4[3])};
+                v4 = *reinterpret_cast<const bf16x4 *>(dout + ((size_t)(tok0 + i) * H + h) * DV + col0 + c4);
+            } else {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) v4[t] = static_cast<bf16>(0.0f);
             }
-            *reinterpret_cast<f32x4 *>(sdO + i * LDD + c4) = x4;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) sdOt[(c4 + t) * L64 + i] = v4[t];
         }
-        copy16(sM, reinterpret_cast<const bf16 *>(a.ws_M) + ch * kChunk * kChunk, kChunk * kChunk * 2,
-               tid, kThreads);
-        copy16(sK, reinterpret_cast<const bf16 *>(a.ws_KhT) + ch * DK * kChunk, DK * kChunk * 2, tid,
-               kThreads);
-        copy16(sQ, reinterpret_cast<const bf16 *>(a.ws_Qh) + ch * kChunk * DK, kChunk * DK * 2, tid,
-               kThreads);
-        copy16(sW, reinterpret_cast<const bf16 *>(a.ws_W) + ch * kChunk * DK, kChunk * DK * 2, tid,
-               kThreads);
-        for (int c = tid; c < DK; c += kThreads) sgl[c] = a.ws_gl[ch * DK + c];
         __syncthreads();
 
         // dU_eff rows of block `wave`:  M^T dO + Khat dS'.
-        {
-            const int I = wave;
 #pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) {
-                f32x4 acc = mma_f32<kChunk>(
-                    zero4(), lane, [&](int m, int k) { return fe(sM, kChunk, k, 16 * I + m); },
-                    [&](int nn, int k) { return sdO[k * LDD + 16 * cb + nn]; });
-                acc = mma_f32<DK>(
-                    acc, lane, [&](int m, int k) { return fe(sK, kChunk, k, 16 * I + m); },
-                    [&](int nn, int k) { return sdS[k * LDD + 16 * cb + nn]; });
+        for (int cb = 0; cb < NCB; ++cb) {
+            f32x4 acc = zero4();
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    sdU[(16 * I + 4 * (lane >> 4) + r) * LDD + 16 * cb + (lane & 15)] = acc[r];
-            }
+            for (int kk = 0; kk < 2; ++kk)
+                acc = MB::mma(fM[kk], load_frag<bf16>(sdOt + 16 * cb * L64 + 32 * kk, L64, lane), acc);
+#pragma unroll
+            for (int kk = 0; kk < NKD; ++kk)
+                acc = MB::mma(fK[kk], load_frag<bf16>(sdSt + 16 * cb * LDKP + 32 * kk, LDKP, lane), acc);
+            store_tile_t<bf16>(sdUt + 16 * cb * L64 + 16 * wave, L64, acc, lane);
         }
         __syncthreads();
 
         // dS <- Diag(gl) dS' + Qhat^T dO - W^T dU_eff.
 #pragma unroll
         for (int u = 0; u < C::S_TPW; ++u) {
-            const int cblk = wave * C::KB_W + u / NCB, colb = u % NCB;
-            const f32x4 q = mma_f32<kChunk>(
-                zero4(), lane, [&](int m, int k) { return fe(sQ, DK, k, 16 * cblk + m); },
-                [&](int nn, int k) { return sdO[k * LDD + 16 * colb + nn]; });
-            const f32x4 wu = mma_f32<kChunk>(
-                zero4(), lane, [&](int m, int k) { return fe(sW, DK, k, 16 * cblk + m); },
-                [&](int nn, int k) { return sdU[k * LDD + 16 * colb + nn]; });
+            const int b = u / NCB, colb = u % NCB;
+            f32x4 q = zero4(), wu = zero4();
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                dS[u][r] = sgl[16 * cblk + 4 * (lane >> 4) + r] * dS[u][r] + q[r] - wu[r];
+            for (int kk = 0; kk < 2; ++kk) {
+                q = MB::mma(fQ[b][kk], load_frag<bf16>(sdOt + 16 * colb * L64 + 32 * kk, L64, lane), q);
+                wu = MB::mma(fW[b][kk], load_frag<bf16>(sdUt + 16 * colb * L64 + 32 * kk, L64, lane), wu);
+            }
+            dS[u] = gl[b] * dS[u] + q - wu;
         }
         __syncthreads();
     }

@@ -188,7 +188,9 @@ __device__ __forceinline__ void chunk_span(const ChunkArgs &a, int cid, int &tok
     }
 }
 
-template <typename E, int DK>
+// kBwd: also write the transposed factors a backward call needs (a.ws_Mt,
+// ws_Kh, ws_Qt, ws_Wt).
+template <typename E, int DK, bool kBwd>
 __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(ChunkArgs a) {
     using C = PrepCfg<E, DK>;
     using M = Mma<E>;
@@ -302,6 +304,19 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(ChunkArgs a) {
         for (int j = 0; j < TPG; ++j) et[j] = bk[j][c];
         store_run<E, TPG>(sEt + (c0 + c) * LDC + tg * TPG, et);
     }
+    if constexpr (kBwd) {  // backward calls: Khat token-major and Qhat^T, fragment order
+        E *KhG = reinterpret_cast<E *>(a.ws_Kh) + ch * kChunk * DK;
+        E *QtG = reinterpret_cast<E *>(a.ws_Qt) + ch * DK * kChunk;
+#pragma unroll
+        for (int j = 0; j < TPG; ++j) store4_frag<E>(KhG, DK, tg * TPG + j, c0, g[j]);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int m = 0; m < TPG; m += 4)
+                store4_frag<E>(QtG, kChunk, c0 + c, tg * TPG + m,
+                               f32x4{elem<E>(qh[m], c), elem<E>(qh[m + 1], c), elem<E>(qh[m + 2], c),
+                                     elem<E>(qh[m + 3], c)});
+    }
     // Khat^T image: row = channel, column = token.
     if constexpr (sizeof(E) == 2) {  // a granule is 8 tokens of one channel
 #pragma unroll
@@ -395,6 +410,14 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(ChunkArgs a) {
                 acc[r] = j <= i ? acc[r] : 0.0f;
             }
             store4_frag<E>(Mg, kChunk, i, 16 * J + 4 * (lane >> 4), acc);
+            if constexpr (kBwd) {  // M^T[j][i] = M[i][j]: the same tile with the operands swapped
+                f32x4 t = mma_tile<E, DK>(zero4(), sX + 16 * I * LDT, LDT, sKp + 16 * J * LDT, LDT, lane);
+                const int jj = 16 * J + (lane & 15);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) t[r] = jj <= 16 * I + 4 * (lane >> 4) + r ? t[r] : 0.0f;
+                store4_frag<E>(reinterpret_cast<E *>(a.ws_Mt) + ch * kChunk * kChunk, kChunk, jj,
+                               16 * I + 4 * (lane >> 4), t);
+            }
         }
     }
 #pragma unroll
@@ -404,6 +427,9 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(ChunkArgs a) {
             int I, J;
             upper_tile(t, I, J);
             store4_frag<E>(Mg, kChunk, 16 * I + (lane & 15), 16 * J + 4 * (lane >> 4), zero4());
+            if constexpr (kBwd)  // the zero lower blocks of M^T
+                store4_frag<E>(reinterpret_cast<E *>(a.ws_Mt) + ch * kChunk * kChunk, kChunk,
+                               16 * J + (lane & 15), 16 * I + 4 * (lane >> 4), zero4());
         }
     }
     __syncthreads();  // the token-major tiles are dead: region 1 becomes the solve buffers
@@ -493,6 +519,12 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(ChunkArgs a) {
                 f32x4 acc = mma_tile_k<E>(zero4(), sEt + 16 * cblk * LDC, LDC, sTb + 16 * I * LDC,
                                           LDC, K, lane);
                 store4_frag<E>(Wg, DK, 16 * I + (lane & 15), 16 * cblk + 4 * (lane >> 4), acc);
+                if constexpr (kBwd) {  // W^T: the same tile with the operands swapped
+                    const f32x4 t = mma_tile_k<E>(zero4(), sTb + 16 * I * LDC, LDC, sEt + 16 * cblk * LDC,
+                                                  LDC, K, lane);
+                    store4_frag<E>(reinterpret_cast<E *>(a.ws_Wt) + ch * DK * kChunk, kChunk,
+                                   16 * cblk + (lane & 15), 16 * I + 4 * (lane >> 4), t);
+                }
             }
         }
     }
@@ -527,12 +559,15 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(ChunkArgs a) {
 
 hipError_t launch_chunk_prep(const ChunkArgs &a, int Dk, bool bf16_io, hipStream_t stream) {
     const dim3 grid((unsigned)((size_t)a.max_chunks * a.H)), block(kThreads);
-    if (bf16_io) {
-        if (Dk == 128) hipLaunchKernelGGL((chunk_prep_kernel<bf16, 128>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((chunk_prep_kernel<bf16, 64>), grid, block, 0, stream, a);
+    if (bf16_io && a.ws_Mt) {  // backward calls (bf16 only)
+        if (Dk == 128) hipLaunchKernelGGL((chunk_prep_kernel<bf16, 128, true>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((chunk_prep_kernel<bf16, 64, true>), grid, block, 0, stream, a);
+    } else if (bf16_io) {
+        if (Dk == 128) hipLaunchKernelGGL((chunk_prep_kernel<bf16, 128, false>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((chunk_prep_kernel<bf16, 64, false>), grid, block, 0, stream, a);
     } else {
-        if (Dk == 128) hipLaunchKernelGGL((chunk_prep_kernel<float, 128>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((chunk_prep_kernel<float, 64>), grid, block, 0, stream, a);
+        if (Dk == 128) hipLaunchKernelGGL((chunk_prep_kernel<float, 128, false>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((chunk_prep_kernel<float, 64, false>), grid, block, 0, stream, a);
     }
     return hipGetLastError();
 }

@@ -38,17 +38,21 @@ struct ChunkArgs {
     int store_T;          // the chunk-factor kernel also stores T = (I + A)^-1
     float *ws_Sc;         // if set, the propagation stores every chunk's incoming
                           // state here ([chunk id][head][Dk][Dv]) and writes no o
+    // If set (backward calls), the chunk-factor kernel also writes, in fragment
+    // order: M^T [64][64], Khat [64][Dk], Qhat^T [Dk][64] and W^T [Dk][64].
+    void *ws_Mt, *ws_Kh, *ws_Qt, *ws_Wt;
 };
 
-// The backward's workspace: the forward's layout (T always stored) followed
-// by fp32 arrays indexed [chunk id][head][...]: every chunk's incoming state
-// Sc and the gradient dSc of its outgoing state ([Dk][Dv]); the state-side
-// partial gradients dQh, dW, dKh ([64][Dk]), dM and dAp ([64][64], dAp =
-// dZ U^T) and dG ([Dk], the gradient of gamma_last through the state).
+// The backward's workspace: the forward's layout (T always stored), the
+// transposed chunk factors (io dtype, fragment order), then fp32 arrays
+// indexed [chunk id][head][...]: every chunk's incoming state Sc and the
+// gradient dSc of its outgoing state ([Dk][Dv]); the state-side partial
+// gradients dQh, dW, dKh ([64][Dk]), dM and dAp ([64][64], dAp = dZ U^T).
 struct BwdLayout {
     WorkspaceLayout fwd;
+    size_t off_Mt = 0, off_Kh = 0, off_Qt = 0, off_Wt = 0;
     size_t off_Sc = 0, off_dSc = 0, off_dQh = 0, off_dW = 0, off_dKh = 0, off_dM = 0,
-           off_dAp = 0, off_dG = 0;
+           off_dAp = 0;
     size_t total = 0;
 };
 
@@ -61,7 +65,7 @@ struct BwdArgs {
     const float *dS_final;
     void *dq, *dk, *dv;
     float *dla, *db, *dw, *dS0;
-    float *Sc, *dSc, *dQh, *dW, *dKh, *dM, *dAp, *dG;
+    float *Sc, *dSc, *dQh, *dW, *dKh, *dM, *dAp;
 };
 
 struct StepArgs {
