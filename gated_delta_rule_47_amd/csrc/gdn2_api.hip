@@ -89,13 +89,15 @@ bool bwd_layout(int N, int B, int T, int H, int Dk, int Dv, size_t io_bytes, boo
     L.off_Kh = take(chd * kChunk * Dk * io_bytes);
     L.off_Qt = take(chd * Dk * kChunk * io_bytes);
     L.off_Wt = take(chd * Dk * kChunk * io_bytes);
-    L.off_Sc = take(chd * Dk * Dv * sizeof(float));
-    L.off_dSc = take(chd * Dk * Dv * sizeof(float));
-    L.off_dQh = take(chd * kChunk * Dk * sizeof(float));
-    L.off_dW = take(chd * kChunk * Dk * sizeof(float));
+    L.off_Tt = take(chd * kChunk * kChunk * io_bytes);
+    L.off_Sc = take(chd * Dk * Dv * 2);
+    L.off_dSc = take(chd * Dk * Dv * 2);
     L.off_dKh = take(chd * kChunk * Dk * sizeof(float));
-    L.off_dM = take(chd * kChunk * kChunk * sizeof(float));
+    L.off_dWt = take(chd * Dk * kChunk * 2);
+    L.off_dM = take(chd * kChunk * kChunk * 2);
+    L.off_dMt = take(chd * kChunk * kChunk * 2);
     L.off_dAp = take(chd * kChunk * kChunk * sizeof(float));
+    L.off_dG = take(chd * Dk * sizeof(float));
     L.total = off;
     *out = L;
     return true;
@@ -312,11 +314,12 @@ int gdn2_chunk_bwd(const void *q, const void *k, const void *v, const float *log
     a.ws_U = ws + F.off_U;
     a.ws_gl = reinterpret_cast<float *>(ws + F.off_gl);
     a.store_T = 1;
-    a.ws_Sc = reinterpret_cast<float *>(ws + L.off_Sc);
+    a.ws_Sc = reinterpret_cast<bf16_t *>(ws + L.off_Sc);
     a.ws_Mt = ws + L.off_Mt;
     a.ws_Kh = ws + L.off_Kh;
     a.ws_Qt = ws + L.off_Qt;
     a.ws_Wt = ws + L.off_Wt;
+    a.ws_Tt = ws + L.off_Tt;
     ba.dout = dout;
     ba.dS_final = dS_final;
     ba.dq = dq;
@@ -327,12 +330,13 @@ int gdn2_chunk_bwd(const void *q, const void *k, const void *v, const float *log
     ba.dw = dw;
     ba.dS0 = dS0;
     ba.Sc = a.ws_Sc;
-    ba.dSc = reinterpret_cast<float *>(ws + L.off_dSc);
-    ba.dQh = reinterpret_cast<float *>(ws + L.off_dQh);
-    ba.dW = reinterpret_cast<float *>(ws + L.off_dW);
+    ba.dSc = reinterpret_cast<bf16_t *>(ws + L.off_dSc);
     ba.dKh = reinterpret_cast<float *>(ws + L.off_dKh);
-    ba.dM = reinterpret_cast<float *>(ws + L.off_dM);
+    ba.dWt = reinterpret_cast<bf16_t *>(ws + L.off_dWt);
+    ba.dM = reinterpret_cast<bf16_t *>(ws + L.off_dM);
+    ba.dMt = reinterpret_cast<bf16_t *>(ws + L.off_dMt);
     ba.dAp = reinterpret_cast<float *>(ws + L.off_dAp);
+    ba.dG = reinterpret_cast<float *>(ws + L.off_dG);
 
     hipError_t err = hipSuccess;
     if (varlen) err = launch_plan(a, stream);

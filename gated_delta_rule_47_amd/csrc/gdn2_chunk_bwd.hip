@@ -24,14 +24,16 @@
 //   dg = E dE + Ep dEp + Qhat dQhat + Qp dQp - Kp dKp - Khat dKhat,
 //   dlog_alpha_j = sum_{i>=j} dg_i + gl dgl + sum_i Khat_i dKhat_i.
 //
-// Three kernels after the forward (chunk factors with T, and the propagation
-// storing every chunk's incoming state):
+// Three kernels after the forward (chunk factors with T and, for backward
+// calls, their transposes M^T, Khat, Qhat^T, W^T, T^T; the propagation storing
+// every chunk's incoming state):
 //   chunk_bwd_rev_kernel     sequential over the chunks of a sequence, in
 //                            reverse: dU_eff and dS, storing each chunk's dS'
 //   chunk_bwd_state_kernel   per chunk: the state-side products, dv and dw
 //   chunk_bwd_factor_kernel  per chunk: the factor side, dq, dk, db, dlog_alpha
-// The products are fp32 MFMA (16x16x4) with operands read element by element
-// from LDS, so every operand can keep the layout it was stored in.
+// All products are bf16 MFMA (16x16x32) with fp32 accumulation; each operand is
+// either a fragment-ordered factor from the workspace or staged in LDS with its
+// contraction index contiguous.
 
 #include "gdn2_device.h"
 #include "gdn2_internal.h"
@@ -41,29 +43,6 @@ namespace gdn2 {
 namespace {
 
 typedef unsigned int granule_t __attribute__((ext_vector_type(4)));
-
-// Element (r, k) of a fragment-ordered bf16 matrix with K columns.
-__device__ __forceinline__ float fe(const bf16 *X, int K, int r, int k) {
-    return static_cast<float>(X[frag_index<bf16>(r, k, K)]);
-}
-
-// acc += A B^T over K (a multiple of 4) for one 16x16 tile with fp32 MFMA:
-// a(m, k) = A[m][k], b(n, k) = B[n][k] for the tile's rows m and columns n.
-template <int K, class FA, class FB>
-__device__ __forceinline__ f32x4 mma_f32(f32x4 acc, int lane, const FA &a, const FB &b) {
-    const int m = lane & 15, kq = lane >> 4;
-#pragma unroll 8
-    for (int kk = 0; kk < K; kk += 4)
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a(m, kk + kq), b(m, kk + kq), acc, 0, 0, 0);
-    return acc;
-}
-
-// Copy `bytes` (a multiple of 16) from global to LDS, 16 bytes per thread.
-__device__ __forceinline__ void copy16(void *dst, const void *src, int bytes, int tid, int nthr) {
-    const granule_t *s = reinterpret_cast<const granule_t *>(src);
-    granule_t *d = reinterpret_cast<granule_t *>(dst);
-    for (int i = tid; i < bytes / 16; i += nthr) d[i] = s[i];
-}
 
 __device__ __forceinline__ void chunk_span_of(const ChunkArgs &a, int cid, int cbeg, int n, int &tok0,
                                               int &len) {
@@ -173,15 +152,16 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_rev_kernel(BwdArgs ba) 
             }
             gl[b] = *reinterpret_cast<const f32x4 *>(a.ws_gl + ch * DK + 16 * cblk + 4 * (lane >> 4));
         }
-        // dS' of this chunk: to the workspace (fp32, for the per-chunk kernels)
+        // dS' of this chunk: to the workspace (bf16, for the per-chunk kernels)
         // and, transposed, to LDS.
-        float *dSc = ba.dSc + ch * DK * DV;
+        bf16 *dSc = ba.dSc + ch * DK * DV;
 #pragma unroll
         for (int u = 0; u < C::S_TPW; ++u) {
             const int cblk = wave * C::KB_W + u / NCB, colb = u % NCB;
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                dSc[(size_t)(16 * cblk + 4 * (lane >> 4) + r) * DV + col0 + 16 * colb + (lane & 15)] = dS[u][r];
+                dSc[(size_t)(16 * cblk + 4 * (lane >> 4) + r) * DV + col0 + 16 * colb + (lane & 15)] =
+                    static_cast<bf16>(dS[u][r]);
             store_tile_t<bf16>(sdSt + 16 * colb * LDKP + 16 * cblk, LDKP, dS[u], lane);
         }
         // dO rows of the chunk (zero past its end), transposed.
@@ -241,7 +221,8 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_rev_kernel(BwdArgs ba) 
 }
 
 // ---------------------------------------------------------------------------
-// State side, one workgroup per (chunk, head): the products with S and dS',
+// State side, one workgroup per (chunk, head): the products with S and dS'
+// (except dQhat = dO S^T, which the factor side forms),
 // taken over 32-column slabs of the value axis with bf16 MFMA (16x16x32).
 // Every operand is staged in LDS in the orientation its fragment load wants
 // (k contiguous), transposing on the way in where needed.  Wave w owns token
@@ -255,35 +236,14 @@ struct StateCfg {
     static constexpr int L64 = kChunk + 8; // [..][64] bf16 rows
 };
 
-// Scatter 8 consecutive elements of row r (columns k..k+7) of a fragment-ordered
-// source into a transposed LDS array: dst[(k + t) * ld + r].
-__device__ __forceinline__ void scatter_t8(bf16 *dst, int ld, int r, int k, granule_t g8) {
-    const bf16x8 v = *reinterpret_cast<const bf16x8 *>(&g8);
-#pragma unroll
-    for (int t = 0; t < 8; ++t) dst[(k + t) * ld + r] = v[t];
-}
-
-// Row and first column of granule `gi` (8 elements) of a fragment-ordered bf16
-// matrix with K columns.
-__device__ __forceinline__ void frag_granule_pos(int gi, int K, int &r, int &k) {
-    const int blk = gi >> 6, lp = gi & 63, nkb = K / 32;
-    r = (blk / nkb) * 16 + (lp & 15);
-    k = (blk % nkb) * 32 + (lp >> 4) * 8;
-}
-
 template <int DK>
-__global__ __launch_bounds__(kThreads, 1) void chunk_bwd_state_kernel(BwdArgs ba) {
+__global__ __launch_bounds__(kThreads, 2) void chunk_bwd_state_kernel(BwdArgs ba) {
     using C = StateCfg<DK>;
     using MB = Mma<bf16>;
     constexpr int DV = C::DV, SW = C::SW, NKB = C::NKB, LSW = C::LSW, LDKP = C::LDKP, L64 = C::L64;
     constexpr int NKD = DK / 32;
     const ChunkArgs &a = ba.c;
-    // persistent
-    __shared__ __attribute__((aligned(16))) bf16 sW[kChunk * DK];    // W, fragment order
-    __shared__ __attribute__((aligned(16))) bf16 sMt[kChunk * L64];  // [i][j] = M[j][i]
-    __shared__ __attribute__((aligned(16))) bf16 sKh[kChunk * LDKP]; // [i][c] = Khat[i][c]
-    __shared__ __attribute__((aligned(16))) bf16 sTt[kChunk * L64];  // [i][j] = T[j][i]
-    // per slab
+    // per slab (W, M^T, Khat and T^T are loaded as fragments from the workspace)
     __shared__ __attribute__((aligned(16))) bf16 sSt[SW * LDKP];     // [v][c] = S[c][v]
     __shared__ __attribute__((aligned(16))) bf16 sS[DK * LSW];       // [c][v]
     __shared__ __attribute__((aligned(16))) bf16 sdSt[SW * LDKP];    // [v][c] = dS'[c][v]
@@ -307,51 +267,43 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_state_kernel(BwdArgs ba
     const bf16 *Ug = reinterpret_cast<const bf16 *>(a.ws_U) + ch * kChunk * DV;
     bf16 *dv = reinterpret_cast<bf16 *>(ba.dv);
 
-    // ---- persistent operands ---------------------------------------------
-    copy16(sW, reinterpret_cast<const bf16 *>(a.ws_W) + ch * kChunk * DK, kChunk * DK * 2, tid, kThreads);
-    {
-        const granule_t *Mg = reinterpret_cast<const granule_t *>(a.ws_M) + ch * (kChunk * kChunk / 8);
-        for (int gi = tid; gi < kChunk * kChunk / 8; gi += kThreads) {
-            int r, k;
-            frag_granule_pos(gi, kChunk, r, k);   // M[r][k..k+7] -> sMt[k+t][r]
-            scatter_t8(sMt, L64, r, k, Mg[gi]);
-        }
-        const granule_t *Kg = reinterpret_cast<const granule_t *>(a.ws_KhT) + ch * (DK * kChunk / 8);
-        for (int gi = tid; gi < DK * kChunk / 8; gi += kThreads) {
-            int r, k;
-            frag_granule_pos(gi, kChunk, r, k);   // KhT[c = r][i = k..k+7] -> sKh[i][c]
-            scatter_t8(sKh, LDKP, r, k, Kg[gi]);
-        }
-        const granule_t *Tg = reinterpret_cast<const granule_t *>(a.ws_T) + ch * (kChunk * kChunk / 8);
-        for (int gi = tid; gi < kChunk * kChunk / 8; gi += kThreads)  // T row-major [j][i..i+7]
-            scatter_t8(sTt, L64, gi / 8, 8 * (gi % 8), Tg[gi]);
-    }
+    const bf16 *Wg = reinterpret_cast<const bf16 *>(a.ws_W) + ch * kChunk * DK;
+    const bf16 *Mtg = reinterpret_cast<const bf16 *>(a.ws_Mt) + ch * kChunk * kChunk;
+    const bf16 *Khg = reinterpret_cast<const bf16 *>(a.ws_Kh) + ch * kChunk * DK;
+    const bf16 *Ttg = reinterpret_cast<const bf16 *>(a.ws_Tt) + ch * kChunk * kChunk;
 
-    f32x4 dQh[NKB], dWt[NKB], dKh[NKB], dMa[4], dAp[4];
+    f32x4 dWt[NKB], dKh[NKB], dMa[4], dAp[4];
 #pragma unroll
-    for (int j = 0; j < NKB; ++j) dQh[j] = dWt[j] = dKh[j] = zero4();
+    for (int j = 0; j < NKB; ++j) dWt[j] = dKh[j] = zero4();
 #pragma unroll
     for (int j = 0; j < 4; ++j) dMa[j] = dAp[j] = zero4();
-    const float *Sc = ba.Sc + ch * DK * DV;
-    const float *dSc = ba.dSc + ch * DK * DV;
+    const bf16 *Sc = ba.Sc + ch * DK * DV;
+    const bf16 *dSc = ba.dSc + ch * DK * DV;
+    // Thread t stages row c = t / TPR of S and dS' (columns CPT (t % TPR) .. of
+    // each slab) and accumulates dgl[c] = sum_v dS'[c][v] S[c][v] over the slabs.
+    constexpr int TPR = kThreads / DK, CPT = SW / TPR;
+    static_assert(CPT % 8 == 0, "16-byte row pieces");
+    const int srow = tid / TPR, scol = CPT * (tid % TPR);
+    float dgp = 0.0f;
 
     for (int sl = 0; sl < C::NSL; ++sl) {
         const int v0 = sl * SW;
         // S and dS' columns v0..v0+SW: [c][v] and transposed [v][c].
-        for (int e = tid; e < DK * SW / 4; e += kThreads) {
-            const int c = e / (SW / 4), v4 = 4 * (e % (SW / 4));
-            const f32x4 s4 = *reinterpret_cast<const f32x4 *>(Sc + (size_t)c * DV + v0 + v4);
-            const f32x4 d4 = *reinterpret_cast<const f32x4 *>(dSc + (size_t)c * DV + v0 + v4);
-            bf16x4 sb, db;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                sb[t] = static_cast<bf16>(s4[t]);
-                db[t] = static_cast<bf16>(d4[t]);
-                sSt[(v4 + t) * LDKP + c] = sb[t];
-                sdSt[(v4 + t) * LDKP + c] = db[t];
+        for (int p8 = 0; p8 < CPT; p8 += 8) {
+            const int v = scol + p8;
+            const bf16x8 sb = *reinterpret_cast<const bf16x8 *>(Sc + (size_t)srow * DV + v0 + v);
+            const bf16x8 db = *reinterpret_cast<const bf16x8 *>(dSc + (size_t)srow * DV + v0 + v);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                sSt[(v + t) * LDKP + srow] = sb[t];
+                sdSt[(v + t) * LDKP + srow] = db[t];
+                dgp += static_cast<float>(sb[t]) * static_cast<float>(db[t]);
             }
-            *reinterpret_cast<bf16x4 *>(sS + c * LSW + v4) = sb;
-            *reinterpret_cast<bf16x4 *>(sdS + c * LSW + v4) = db;
+            *reinterpret_cast<bf16x4 *>(sS + srow * LSW + v) = bf16x4{sb[0], sb[1], sb[2], sb[3]};
+            *reinterpret_cast<bf16x4 *>(sS + srow * LSW + v + 4) = bf16x4{sb[4], sb[5], sb[6], sb[7]};
+            *reinterpret_cast<bf16x4 *>(sdS + srow * LSW + v) = bf16x4{db[0], db[1], db[2], db[3]};
+            *reinterpret_cast<bf16x4 *>(sdS + srow * LSW + v + 4) = bf16x4{db[4], db[5], db[6], db[7]};
         }
         // dO rows (zero past the chunk) and U, [i][v] and transposed.
         for (int e = tid; e < kChunk * SW / 4; e += kThreads) {
@@ -381,14 +333,14 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_state_kernel(BwdArgs ba
             f32x4 ws = zero4(), du = zero4();
 #pragma unroll
             for (int kk = 0; kk < NKD; ++kk) {
-                ws = MB::mma(load_frag_packed<bf16>(sW, DK, I, kk, lane),
+                ws = MB::mma(load_frag_packed<bf16>(Wg, DK, I, kk, lane),
                              load_frag<bf16>(sSt + 16 * cb * LDKP + 32 * kk, LDKP, lane), ws);
-                du = MB::mma(load_frag<bf16>(sKh + 16 * I * LDKP + 32 * kk, LDKP, lane),
+                du = MB::mma(load_frag_packed<bf16>(Khg, DK, I, kk, lane),
                              load_frag<bf16>(sdSt + 16 * cb * LDKP + 32 * kk, LDKP, lane), du);
             }
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
-                du = MB::mma(load_frag<bf16>(sMt + 16 * I * L64 + 32 * kk, L64, lane),
+                du = MB::mma(load_frag_packed<bf16>(Mtg, kChunk, I, kk, lane),
                              load_frag<bf16>(sdOt + 16 * cb * L64 + 32 * kk, L64, lane), du);
             // U tile in accumulator order straight from the workspace.
             const bf16x4 u4 = *reinterpret_cast<const bf16x4 *>(
@@ -408,7 +360,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_state_kernel(BwdArgs ba
             f32x4 dz = zero4();
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
-                dz = MB::mma(load_frag<bf16>(sTt + 16 * I * L64 + 32 * kk, L64, lane),
+                dz = MB::mma(load_frag_packed<bf16>(Ttg, kChunk, I, kk, lane),
                              load_frag<bf16>(sdUt + 16 * cb * L64 + 32 * kk, L64, lane), dz);
             store_tile<bf16>(sdZ + 16 * I * LSW + 16 * cb, LSW, dz, lane);
 #pragma unroll
@@ -428,9 +380,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_state_kernel(BwdArgs ba
             const MB::frag fUe = load_frag<bf16>(sUe + 16 * I * LSW, LSW, lane);
 #pragma unroll
             for (int cb = 0; cb < NKB; ++cb) {
-                const MB::frag fS = load_frag<bf16>(sS + 16 * cb * LSW, LSW, lane);
-                dQh[cb] = MB::mma(fdO, fS, dQh[cb]);
-                dWt[cb] = MB::mma(fdU, fS, dWt[cb]);
+                dWt[cb] = MB::mma(fdU, load_frag<bf16>(sS + 16 * cb * LSW, LSW, lane), dWt[cb]);
                 dKh[cb] = MB::mma(fUe, load_frag<bf16>(sdS + 16 * cb * LSW, LSW, lane), dKh[cb]);
             }
 #pragma unroll
@@ -447,68 +397,81 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_state_kernel(BwdArgs ba
         __syncthreads();  // before the next slab is staged
     }
 
-    float *oQ = ba.dQh + ch * kChunk * DK, *oW = ba.dW + ch * kChunk * DK, *oK = ba.dKh + ch * kChunk * DK;
-    float *oM = ba.dM + ch * kChunk * kChunk, *oA = ba.dAp + ch * kChunk * kChunk;
+    // dgl: the TPR threads staging a row are consecutive lanes.
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int i = 16 * I + 4 * (lane >> 4) + r;
+    for (int o = 1; o < TPR; o <<= 1) dgp += __shfl_xor(dgp, o, TPR);
+    if ((tid % TPR) == 0) ba.dG[ch * DK + srow] = dgp;
+    float *oK = ba.dKh + ch * kChunk * DK;
+    float *oA = ba.dAp + ch * kChunk * kChunk;
+    bf16 *oWt = ba.dWt + ch * DK * kChunk;      // dW^T, fragment order
+    bf16 *oM = ba.dM + ch * kChunk * kChunk;    // dM, fragment order
+    bf16 *oMt = ba.dMt + ch * kChunk * kChunk;  // dM^T, fragment order
+    const int i0 = 16 * I + 4 * (lane >> 4);
 #pragma unroll
-        for (int cb = 0; cb < NKB; ++cb) {
-            const int c = 16 * cb + (lane & 15);
-            oQ[i * DK + c] = dQh[cb][r];
-            oW[i * DK + c] = -dWt[cb][r];
-            oK[i * DK + c] = dKh[cb][r];
+    for (int cb = 0; cb < NKB; ++cb) {
+        const int c = 16 * cb + (lane & 15);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) oK[(i0 + r) * DK + c] = dKh[cb][r];
+        store4_frag<bf16>(oWt, kChunk, c, i0, -dWt[cb]);
+    }
+#pragma unroll
+    for (int J = 0; J < 4; ++J) {
+        const int j = 16 * J + (lane & 15);
+        f32x4 m;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            m[r] = j <= i0 + r ? dMa[J][r] : 0.0f;
+            oA[(i0 + r) * kChunk + j] = dAp[J][r];
+            oM[frag_index<bf16>(i0 + r, j, kChunk)] = static_cast<bf16>(m[r]);
         }
-#pragma unroll
-        for (int J = 0; J < 4; ++J) {
-            const int j = 16 * J + (lane & 15);
-            oM[i * kChunk + j] = j <= i ? dMa[J][r] : 0.0f;
-            oA[i * kChunk + j] = dAp[J][r];
-        }
+        store4_frag<bf16>(oMt, kChunk, j, i0, m);
     }
 }
 
 // ---------------------------------------------------------------------------
-// Factor side, one workgroup per (chunk, head).  Thread (qd, tg) owns key
-// channels 4qd..4qd+3 of tokens tg*TPG .. for the element-wise parts; wave w
-// owns token rows 16w .. of the 64-row products.
+// Factor side, one workgroup per (chunk, head), bf16 MFMA.  Wave w owns token
+// rows 16w .. 16w+15 of every 64-row result; the element-wise step runs in the
+// same accumulator layout (lane holds rows 16w + 4(l/16) + r, column l%16 of
+// each 16-column block), so dE, dEp, dQp and dKp never leave registers.
 // ---------------------------------------------------------------------------
 template <int DK>
 struct FacCfg {
     static constexpr int NQUAD = DK / 4, NTG = kThreads / NQUAD, TPG = kChunk / NTG;
-    static constexpr int LDT = DK + 8;    // bf16 tiles [64][LDT]
-    static constexpr int LDF = DK + 4;    // fp32 [64][LDF]
-    static constexpr int LDA = kChunk + 4;
-    static constexpr size_t SZ_RT = size_t(3) * kChunk * LDT * 2;
-    static constexpr size_t SZ_F = size_t(kChunk) * LDF * 4;
-    static constexpr size_t SZ_A = size_t(kChunk) * LDA * 4;
-    static constexpr size_t SZ_RED = size_t(2) * NTG * DK * 4;
-    static constexpr size_t OFF_RD = SZ_RT, OFF_RA = OFF_RD + SZ_F, OFF_RM = OFF_RA + SZ_A,
-                            OFF_RW = OFF_RM + SZ_A, OFF_RED = OFF_RW + SZ_F;
-    static constexpr size_t SMEM = OFF_RED + SZ_RED;
-    static_assert(SZ_F <= 2 * SZ_A && SZ_F <= SZ_RT && size_t(kChunk) * kChunk * 2 <= SZ_RT, "reuse");
-    static_assert(size_t(NTG) * DK * 4 <= SZ_F && size_t(kChunk) * DK * 2 <= SZ_F, "reuse");
+    static constexpr int L64 = kChunk + 8;   // bf16 [..][64]
+    static constexpr int LDKP = DK + 8;      // bf16 [..][DK]
+    static constexpr int LDG = DK + 4;       // fp32 [64][LDG]
+    static constexpr size_t SZ_CT = size_t(DK) * L64 * 2;       // [DK][64] bf16
+    static constexpr size_t SZ_64 = size_t(kChunk) * L64 * 2;    // [64][64] bf16
+    static constexpr size_t OFF_KP = 0;                            // Kp^T
+    static constexpr size_t OFF_E = OFF_KP + SZ_CT;                // dE (bf16 [64][LDKP]), then Ep^T
+    static constexpr size_t SZ_E = (size_t(kChunk) * LDKP * 2 > SZ_CT) ? size_t(kChunk) * LDKP * 2 : SZ_CT;
+    static constexpr size_t OFF_A = OFF_E + SZ_E;                  // dA, dA^T
+    static constexpr size_t OFF_Q = OFF_A + 2 * SZ_64;             // Qp^T
+    static constexpr size_t OFF_G = OFF_Q + SZ_CT;                 // g, then dg (fp32 [64][LDG])
+    static constexpr size_t OFF_R = OFF_G + size_t(kChunk) * LDG * 4;  // small reductions
+    static constexpr size_t SZ_R = size_t(2 * NTG + 8) * DK * 4;
+    static constexpr size_t SMEM = OFF_R + SZ_R;
     static_assert(SMEM <= 160 * 1024, "LDS");
 };
 
 template <int DK>
 __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_factor_kernel(BwdArgs ba) {
     using C = FacCfg<DK>;
-    constexpr int LDT = C::LDT, LDF = C::LDF, LDA = C::LDA, TPG = C::TPG, NKB = DK / 16;
+    using MB = Mma<bf16>;
+    constexpr int L64 = C::L64, LDKP = C::LDKP, LDG = C::LDG, TPG = C::TPG, NKB = DK / 16, NKD = DK / 32;
     const ChunkArgs &a = ba.c;
     __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
-    bf16 *sKp = reinterpret_cast<bf16 *>(smem);           // [64][LDT] k e^{g_r-g}
-    bf16 *sEp = sKp + kChunk * LDT;                        // [64][LDT] b k e^{g-g_r}
-    bf16 *sQp = sEp + kChunk * LDT;                        // [64][LDT] q e^{g-g_r}
-    bf16 *sT = reinterpret_cast<bf16 *>(smem);             // T [64][64] (before the tiles)
-    float *sdKp = reinterpret_cast<float *>(smem);         // dKp [64][LDF] (after the products)
-    float *sdE = reinterpret_cast<float *>(smem + C::OFF_RD);   // dE [64][LDF]
-    float *sA = reinterpret_cast<float *>(smem + C::OFF_RA);    // dZ U^T, then dA [64][LDA]
-    float *sMm = reinterpret_cast<float *>(smem + C::OFF_RM);   // dM [64][LDA]
-    float *sdQp = reinterpret_cast<float *>(smem + C::OFF_RA);  // dQp [64][LDF] (after the products)
-    float *sRw = reinterpret_cast<float *>(smem + C::OFF_RW);   // dW, then W, then totals, then dEp
-    bf16 *sWf = reinterpret_cast<bf16 *>(smem + C::OFF_RW);
-    float *sRed = reinterpret_cast<float *>(smem + C::OFF_RED);  // [2][NTG][DK]
+    bf16 *sKpt = reinterpret_cast<bf16 *>(smem + C::OFF_KP);   // [c][j] = Kp[j][c]
+    bf16 *sdE = reinterpret_cast<bf16 *>(smem + C::OFF_E);     // [i][c]
+    bf16 *sEpt = sdE;                                           // [c][i] = Ep[i][c]
+    bf16 *sdA = reinterpret_cast<bf16 *>(smem + C::OFF_A);     // [i][j]
+    bf16 *sdAt = sdA + kChunk * L64;                            // [j][i]
+    bf16 *sQpt = reinterpret_cast<bf16 *>(smem + C::OFF_Q);    // [c][i] = Qp[i][c]
+    float *sG = reinterpret_cast<float *>(smem + C::OFF_G);    // g, then dg [64][LDG]
+    float *sR = reinterpret_cast<float *>(smem + C::OFF_R);    // [2*NTG + 8][DK]
+    float *sGl = sR + 2 * C::NTG * DK;                          // g_last [DK]
+    float *sDG = sGl + DK;                                      // dgl [DK]
+    float *sKdk = sDG + DK;                                     // [4][DK] sum_i Khat dKhat, per wave
 
     const int H = a.H, cid = blockIdx.x / H, h = blockIdx.x % H;
     if (a.plan && cid >= a.plan[a.N]) return;
@@ -517,217 +480,216 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_factor_kernel(BwdArgs b
     const size_t ch = (size_t)cid * H + h;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, I = wave;
     const int qd = tid % C::NQUAD, tg = tid / C::NQUAD, c0 = 4 * qd;
-
-    // ---- stage dW, T, dZ U^T, dM ------------------------------------------
-    {
-        const float *dWg = ba.dW + ch * kChunk * DK;
-        for (int e = tid; e < kChunk * DK / 4; e += kThreads) {
-            const int i = e / (DK / 4), c4 = 4 * (e % (DK / 4));
-            *reinterpret_cast<f32x4 *>(sRw + i * LDF + c4) =
-                *reinterpret_cast<const f32x4 *>(dWg + (size_t)i * DK + c4);
-        }
-        copy16(sT, reinterpret_cast<const bf16 *>(a.ws_T) + ch * kChunk * kChunk, kChunk * kChunk * 2, tid,
-               kThreads);
-        const float *Ap = ba.dAp + ch * kChunk * kChunk, *Mg = ba.dM + ch * kChunk * kChunk;
-        for (int e = tid; e < kChunk * kChunk / 4; e += kThreads) {
-            const int i = e / (kChunk / 4), c4 = 4 * (e % (kChunk / 4));
-            *reinterpret_cast<f32x4 *>(sA + i * LDA + c4) =
-                *reinterpret_cast<const f32x4 *>(Ap + (size_t)i * kChunk + c4);
-            *reinterpret_cast<f32x4 *>(sMm + i * LDA + c4) =
-                *reinterpret_cast<const f32x4 *>(Mg + (size_t)i * kChunk + c4);
-        }
-    }
-    __syncthreads();
-    // dE = T^T dW (rows of block I).
-#pragma unroll
-    for (int cb = 0; cb < NKB; ++cb) {
-        const f32x4 d = mma_f32<kChunk>(
-            zero4(), lane, [&](int m, int k) { return static_cast<float>(sT[k * kChunk + 16 * I + m]); },
-            [&](int nn, int k) { return sRw[k * LDF + 16 * cb + nn]; });
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sdE[(16 * I + 4 * (lane >> 4) + r) * LDF + 16 * cb + (lane & 15)] = d[r];
-    }
-    __syncthreads();  // dW is dead: the region receives W
-    copy16(sWf, reinterpret_cast<const bf16 *>(a.ws_W) + ch * kChunk * DK, kChunk * DK * 2, tid, kThreads);
-    __syncthreads();
-    // dA = -strict_tril(dZ U^T + dE W^T), in place of dZ U^T.
-#pragma unroll
-    for (int J = 0; J < 4; ++J) {
-        const f32x4 d = mma_f32<DK>(
-            zero4(), lane, [&](int m, int k) { return sdE[(16 * I + m) * LDF + k]; },
-            [&](int nn, int k) { return fe(sWf, DK, 16 * J + nn, k); });
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int i = 16 * I + 4 * (lane >> 4) + r, j = 16 * J + (lane & 15);
-            float &x = sA[i * LDA + j];
-            x = j < i ? -(x + d[r]) : 0.0f;
-        }
-    }
-    __syncthreads();  // W is dead: the region receives the scan totals
-
-    // ---- cumulative log-decay and the scaled tiles --------------------------
-    f32x4 g[TPG];
-#pragma unroll
-    for (int j = 0; j < TPG; ++j) {
-        const int i = tg * TPG + j;
-        g[j] = i < len ? *reinterpret_cast<const f32x4 *>(a.log_alpha + ((size_t)(tok0 + i) * H + h) * DK + c0)
-                       : zero4();
-    }
-#pragma unroll
-    for (int j = 1; j < TPG; ++j) g[j] += g[j - 1];
-    *reinterpret_cast<f32x4 *>(sRw + tg * DK + c0) = g[TPG - 1];
-    __syncthreads();
-    f32x4 goff = zero4(), glast = zero4();
-#pragma unroll
-    for (int t = 0; t < C::NTG; ++t) {
-        const f32x4 tt = *reinterpret_cast<const f32x4 *>(sRw + t * DK + c0);
-        if (t < tg) goff += tt;
-        glast += tt;
-    }
-#pragma unroll
-    for (int j = 0; j < TPG; ++j) g[j] += goff;
-    const f32x4 gr = 0.5f * glast;
     const bf16 *kin = reinterpret_cast<const bf16 *>(a.k), *qin = reinterpret_cast<const bf16 *>(a.q);
+
+    for (int c = tid; c < DK; c += kThreads) sDG[c] = ba.dG[ch * DK + c];
+    const bf16 *dWtg = ba.dWt + ch * DK * kChunk;
+    const bf16 *dMg = ba.dM + ch * kChunk * kChunk, *dMtg = ba.dMt + ch * kChunk * kChunk;
+
+    // ---- dE = T^T dW (rows of block I), kept in registers and as bf16 --------
+    const bf16 *Ttg = reinterpret_cast<const bf16 *>(a.ws_Tt) + ch * kChunk * kChunk;
+    const bf16 *Wg = reinterpret_cast<const bf16 *>(a.ws_W) + ch * kChunk * DK;
+    f32x4 dE[NKB];
+    {
+        const MB::frag t0 = load_frag_packed<bf16>(Ttg, kChunk, I, 0, lane);
+        const MB::frag t1 = load_frag_packed<bf16>(Ttg, kChunk, I, 1, lane);
 #pragma unroll
-    for (int j = 0; j < TPG; ++j) {
-        const int i = tg * TPG + j;
-        f32x4 kf = zero4(), qf = zero4(), bf = zero4();
-        if (i < len) {
-            const size_t off = ((size_t)(tok0 + i) * H + h) * DK + c0;
-            const bf16x4 k4 = *reinterpret_cast<const bf16x4 *>(kin + off);
-            const bf16x4 q4 = *reinterpret_cast<const bf16x4 *>(qin + off);
-            bf = *reinterpret_cast<const f32x4 *>(a.b + off);
+        for (int cb = 0; cb < NKB; ++cb) {
+            f32x4 d = MB::mma(t0, load_frag_packed<bf16>(dWtg, kChunk, cb, 0, lane), zero4());
+            d = MB::mma(t1, load_frag_packed<bf16>(dWtg, kChunk, cb, 1, lane), d);
+            dE[cb] = d;
+            store_tile<bf16>(sdE + 16 * I * LDKP + 16 * cb, LDKP, d, lane);
+        }
+    }
+    __syncthreads();
+    // ---- dA = -strict_tril(dZ U^T + dE W^T), both orientations --------------
+    {
+        const float *Ap = ba.dAp + ch * kChunk * kChunk;
+        MB::frag fe_[NKD];
+#pragma unroll
+        for (int kk = 0; kk < NKD; ++kk) fe_[kk] = load_frag<bf16>(sdE + 16 * I * LDKP + 32 * kk, LDKP, lane);
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+            f32x4 d = zero4();
+#pragma unroll
+            for (int kk = 0; kk < NKD; ++kk) d = MB::mma(fe_[kk], load_frag_packed<bf16>(Wg, DK, J, kk, lane), d);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * I + 4 * (lane >> 4) + r, j = 16 * J + (lane & 15);
+                d[r] = j < i ? -(Ap[(size_t)i * kChunk + j] + d[r]) : 0.0f;
+            }
+            store_tile<bf16>(sdA + 16 * I * L64 + 16 * J, L64, d, lane);
+            store_tile_t<bf16>(sdAt + 16 * J * L64 + 16 * I, L64, d, lane);
+        }
+    }
+    __syncthreads();  // dE (bf16) is dead: its region receives Ep^T
+
+    // ---- cumulative log-decay (thread (qd, tg)) and the scaled tiles --------
+    f32x4 gr;
+    {
+        f32x4 g[TPG];
+#pragma unroll
+        for (int j = 0; j < TPG; ++j) {
+            const int i = tg * TPG + j;
+            g[j] = i < len ? *reinterpret_cast<const f32x4 *>(a.log_alpha + ((size_t)(tok0 + i) * H + h) * DK + c0)
+                           : zero4();
+        }
+#pragma unroll
+        for (int j = 1; j < TPG; ++j) g[j] += g[j - 1];
+        *reinterpret_cast<f32x4 *>(sR + tg * DK + c0) = g[TPG - 1];
+        __syncthreads();
+        f32x4 goff = zero4(), glast = zero4();
+#pragma unroll
+        for (int t = 0; t < C::NTG; ++t) {
+            const f32x4 tt = *reinterpret_cast<const f32x4 *>(sR + t * DK + c0);
+            if (t < tg) goff += tt;
+            glast += tt;
+        }
+        gr = 0.5f * glast;
+        if (tg == 0) *reinterpret_cast<f32x4 *>(sGl + c0) = glast;
+#pragma unroll
+        for (int j = 0; j < TPG; ++j) {
+            const int i = tg * TPG + j;
+            g[j] += goff;
+            *reinterpret_cast<f32x4 *>(sG + i * LDG + c0) = g[j];
+            f32x4 kf = zero4(), qf = zero4(), bf = zero4();
+            if (i < len) {
+                const size_t off = ((size_t)(tok0 + i) * H + h) * DK + c0;
+                const bf16x4 k4 = *reinterpret_cast<const bf16x4 *>(kin + off);
+                const bf16x4 q4 = *reinterpret_cast<const bf16x4 *>(qin + off);
+                bf = *reinterpret_cast<const f32x4 *>(a.b + off);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    kf[c] = static_cast<float>(k4[c]);
+                    qf[c] = static_cast<float>(q4[c]);
+                }
+            }
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                kf[c] = static_cast<float>(k4[c]);
-                qf[c] = static_cast<float>(q4[c]);
+                const float ex = __expf(g[j][c] - gr[c]), ei = __expf(gr[c] - g[j][c]);
+                sKpt[(c0 + c) * L64 + i] = static_cast<bf16>(kf[c] * ei);
+                sEpt[(c0 + c) * L64 + i] = static_cast<bf16>(bf[c] * kf[c] * ex);
+                sQpt[(c0 + c) * L64 + i] = static_cast<bf16>(qf[c] * ex);
             }
         }
-        bf16x4 kp, ep, qp;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const float ex = __expf(g[j][c] - gr[c]), ei = __expf(gr[c] - g[j][c]);
-            kp[c] = static_cast<bf16>(kf[c] * ei);
-            ep[c] = static_cast<bf16>(bf[c] * kf[c] * ex);
-            qp[c] = static_cast<bf16>(qf[c] * ex);
-        }
-        *reinterpret_cast<bf16x4 *>(sKp + i * LDT + c0) = kp;
-        *reinterpret_cast<bf16x4 *>(sEp + i * LDT + c0) = ep;
-        *reinterpret_cast<bf16x4 *>(sQp + i * LDT + c0) = qp;
     }
     __syncthreads();
 
-    // ---- dEp = dA Kp, dQp = dM Kp, dKp = dA^T Ep + dM^T Qp ------------------
+    // ---- dEp = dA Kp, dQp = dM Kp, dKp = dA^T Ep + dM^T Qp --------------------
     f32x4 dEp[NKB], dQp[NKB], dKp[NKB];
+    {
+        MB::frag fA[2], fM[2], fAt[2], fMt[2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            fA[kk] = load_frag<bf16>(sdA + 16 * I * L64 + 32 * kk, L64, lane);
+            fM[kk] = load_frag_packed<bf16>(dMg, kChunk, I, kk, lane);
+            fAt[kk] = load_frag<bf16>(sdAt + 16 * I * L64 + 32 * kk, L64, lane);
+            fMt[kk] = load_frag_packed<bf16>(dMtg, kChunk, I, kk, lane);
+        }
+#pragma unroll
+        for (int cb = 0; cb < NKB; ++cb) {
+            f32x4 e = zero4(), q = zero4(), k = zero4();
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const MB::frag kp = load_frag<bf16>(sKpt + 16 * cb * L64 + 32 * kk, L64, lane);
+                e = MB::mma(fA[kk], kp, e);
+                q = MB::mma(fM[kk], kp, q);
+                k = MB::mma(fAt[kk], load_frag<bf16>(sEpt + 16 * cb * L64 + 32 * kk, L64, lane), k);
+                k = MB::mma(fMt[kk], load_frag<bf16>(sQpt + 16 * cb * L64 + 32 * kk, L64, lane), k);
+            }
+            dEp[cb] = e;
+            dQp[cb] = q;
+            dKp[cb] = k;
+        }
+    }
+
+    // ---- dQhat = dO S^T (rows of block I; dO rows past the chunk are zero) ---
+    f32x4 dQh[NKB];
+    {
+        const bf16 *dout = reinterpret_cast<const bf16 *>(ba.dout);
+        const bf16 *Sc = ba.Sc + ch * DK * DK;
+        const int row = 16 * I + (lane & 15);
+        MB::frag fdO[NKD];
+#pragma unroll
+        for (int kk = 0; kk < NKD; ++kk)
+            fdO[kk] = row < len ? load_frag<bf16>(dout + ((size_t)(tok0 + 16 * I) * H + h) * DK + 32 * kk,
+                                                  H * DK, lane)
+                                : MB::zero();
+#pragma unroll
+        for (int cb = 0; cb < NKB; ++cb) {
+            f32x4 d = zero4();
+#pragma unroll
+            for (int kk = 0; kk < NKD; ++kk)
+                d = MB::mma(fdO[kk], load_frag<bf16>(Sc + 16 * cb * DK + 32 * kk, DK, lane), d);
+            dQh[cb] = d;
+        }
+    }
+
+    // ---- element-wise gradients in the accumulator layout -------------------
+    const float *dKg = ba.dKh + ch * kChunk * DK;
+    bf16 *dqo = reinterpret_cast<bf16 *>(ba.dq), *dko = reinterpret_cast<bf16 *>(ba.dk);
 #pragma unroll
     for (int cb = 0; cb < NKB; ++cb) {
-        auto kp = [&](int nn, int k) { return static_cast<float>(sKp[k * LDT + 16 * cb + nn]); };
-        dEp[cb] = mma_f32<kChunk>(zero4(), lane, [&](int m, int k) { return sA[(16 * I + m) * LDA + k]; }, kp);
-        dQp[cb] = mma_f32<kChunk>(zero4(), lane, [&](int m, int k) { return sMm[(16 * I + m) * LDA + k]; }, kp);
-        f32x4 d = mma_f32<kChunk>(zero4(), lane, [&](int m, int k) { return sA[k * LDA + 16 * I + m]; },
-                                  [&](int nn, int k) { return static_cast<float>(sEp[k * LDT + 16 * cb + nn]); });
-        dKp[cb] = mma_f32<kChunk>(d, lane, [&](int m, int k) { return sMm[k * LDA + 16 * I + m]; },
-                                  [&](int nn, int k) { return static_cast<float>(sQp[k * LDT + 16 * cb + nn]); });
-    }
-    __syncthreads();  // tiles, dA and dM are dead
-#pragma unroll
-    for (int cb = 0; cb < NKB; ++cb)
+        const int c = 16 * cb + (lane & 15);
+        const float gl_c = sGl[c], gr_c = 0.5f * gl_c, egr = __expf(gr_c);
+        float kdk = 0.0f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int o = (16 * I + 4 * (lane >> 4) + r) * LDF + 16 * cb + (lane & 15);
-            sRw[o] = dEp[cb][r];
-            sdQp[o] = dQp[cb][r];
-            sdKp[o] = dKp[cb][r];
+            const int i = 16 * I + 4 * (lane >> 4) + r;
+            float dg = 0.0f;
+            if (i < len) {
+                const size_t off = ((size_t)(tok0 + i) * H + h) * DK + c;
+                const float kf = static_cast<float>(kin[off]), qf = static_cast<float>(qin[off]);
+                const float bf = a.b[off];
+                const float dKh = dKg[(size_t)i * DK + c];
+                const float gg = sG[i * LDG + c];
+                const float ex = __expf(gg - gr_c), ei = __expf(gr_c - gg);
+                const float gam = ex * egr, eK = ei * egr;
+                const float t1 = gam * dE[cb][r] + ex * dEp[cb][r];
+                const float dq = gam * dQh[cb][r] + ex * dQp[cb][r];
+                const float kpart = ei * dKp[cb][r] + eK * dKh;
+                dqo[off] = static_cast<bf16>(dq);
+                dko[off] = static_cast<bf16>(bf * t1 + kpart);
+                ba.db[off] = kf * t1;
+                dg = bf * kf * t1 + qf * dq - kf * kpart;
+                kdk += kf * eK * dKh;
+            }
+            sG[i * LDG + c] = dg;  // each element is read, then overwritten, by this lane only
         }
+        // sum over this wave's 16 tokens: 4 per lane, then the 4 lane groups
+        kdk += __shfl_xor(kdk, 16);
+        kdk += __shfl_xor(kdk, 32);
+        if (lane < 16) sKdk[wave * DK + c] = kdk;
+    }
     __syncthreads();
 
-    // ---- element-wise gradients, thread (qd, tg) ---------------------------
-    const float *dQg = ba.dQh + ch * kChunk * DK, *dKg = ba.dKh + ch * kChunk * DK;
-    f32x4 dgv[TPG];
-    f32x4 kdk = zero4();
-    bf16 *dqo = reinterpret_cast<bf16 *>(ba.dq), *dko = reinterpret_cast<bf16 *>(ba.dk);
-    f32x4 egr;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) egr[c] = __expf(gr[c]);
-#pragma unroll
-    for (int j = 0; j < TPG; ++j) {
-        const int i = tg * TPG + j;
-        dgv[j] = zero4();
-        if (i >= len) continue;
-        const size_t off = ((size_t)(tok0 + i) * H + h) * DK + c0;
-        const bf16x4 k4 = *reinterpret_cast<const bf16x4 *>(kin + off);
-        const bf16x4 q4 = *reinterpret_cast<const bf16x4 *>(qin + off);
-        const f32x4 bf = *reinterpret_cast<const f32x4 *>(a.b + off);
-        const f32x4 dQh = *reinterpret_cast<const f32x4 *>(dQg + i * DK + c0);
-        const f32x4 dKh = *reinterpret_cast<const f32x4 *>(dKg + i * DK + c0);
-        const f32x4 dE = *reinterpret_cast<const f32x4 *>(sdE + i * LDF + c0);
-        const f32x4 dEpv = *reinterpret_cast<const f32x4 *>(sRw + i * LDF + c0);
-        const f32x4 dQpv = *reinterpret_cast<const f32x4 *>(sdQp + i * LDF + c0);
-        const f32x4 dKpv = *reinterpret_cast<const f32x4 *>(sdKp + i * LDF + c0);
-        f32x4 dq, dk, db;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const float kf = static_cast<float>(k4[c]), qf = static_cast<float>(q4[c]);
-            const float ex = __expf(g[j][c] - gr[c]), ei = __expf(gr[c] - g[j][c]);
-            const float gam = ex * egr[c], eK = ei * egr[c];
-            const float t1 = gam * dE[c] + ex * dEpv[c];
-            dq[c] = gam * dQh[c] + ex * dQpv[c];
-            db[c] = kf * t1;
-            dk[c] = bf[c] * t1 + ei * dKpv[c] + eK * dKh[c];
-            dgv[j][c] = bf[c] * kf * t1 + qf * dq[c] - kf * (ei * dKpv[c] + eK * dKh[c]);
-            kdk[c] += kf * eK * dKh[c];
-        }
-        bf16x4 dq4, dk4;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            dq4[c] = static_cast<bf16>(dq[c]);
-            dk4[c] = static_cast<bf16>(dk[c]);
-        }
-        *reinterpret_cast<bf16x4 *>(dqo + off) = dq4;
-        *reinterpret_cast<bf16x4 *>(dko + off) = dk4;
-        *reinterpret_cast<f32x4 *>(ba.db + off) = db;
-    }
-    // dlog_alpha_j = sum_{i>=j} dg_i + gl dgl + sum_i Khat_i dKhat_i.
-#pragma unroll
-    for (int j = TPG - 2; j >= 0; --j) dgv[j] += dgv[j + 1];   // suffix sums inside the group
-    *reinterpret_cast<f32x4 *>(sRed + tg * DK + c0) = dgv[0];
-    *reinterpret_cast<f32x4 *>(sRed + (C::NTG + tg) * DK + c0) = kdk;
-    __syncthreads();
-    f32x4 after = zero4(), kdk_all = zero4();
-#pragma unroll
-    for (int t = 0; t < C::NTG; ++t) {
-        if (t > tg) after += *reinterpret_cast<const f32x4 *>(sRed + t * DK + c0);
-        kdk_all += *reinterpret_cast<const f32x4 *>(sRed + (C::NTG + t) * DK + c0);
-    }
-    // dgl[c] = sum_v dS'[c][v] S[c][v]: this thread takes v in [tg*DV/NTG, ..), the
-    // group partials meet in LDS.
+    // ---- dlog_alpha_j = sum_{i>=j} dg_i + gl dgl + sum_i Khat_i dKhat_i --------
     {
-        constexpr int VPT = DK / C::NTG;
-        const float *Sc = ba.Sc + ch * DK * DK, *dSc = ba.dSc + ch * DK * DK;
-        f32x4 part = zero4();
+        f32x4 dgv[TPG];
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-            for (int v = tg * VPT; v < (tg + 1) * VPT; v += 4) {
-                const f32x4 s4 = *reinterpret_cast<const f32x4 *>(Sc + (size_t)(c0 + c) * DK + v);
-                const f32x4 d4 = *reinterpret_cast<const f32x4 *>(dSc + (size_t)(c0 + c) * DK + v);
-                part[c] += s4[0] * d4[0] + s4[1] * d4[1] + s4[2] * d4[2] + s4[3] * d4[3];
-            }
-        __syncthreads();  // the totals above have been read
-        *reinterpret_cast<f32x4 *>(sRed + tg * DK + c0) = part;
-    }
-    __syncthreads();
-    f32x4 dG = zero4();
+        for (int j = 0; j < TPG; ++j) dgv[j] = *reinterpret_cast<const f32x4 *>(sG + (tg * TPG + j) * LDG + c0);
 #pragma unroll
-    for (int t = 0; t < C::NTG; ++t) dG += *reinterpret_cast<const f32x4 *>(sRed + t * DK + c0);
-    f32x4 dglast;
+        for (int j = TPG - 2; j >= 0; --j) dgv[j] += dgv[j + 1];  // suffix sums inside the group
+        *reinterpret_cast<f32x4 *>(sR + (C::NTG + tg) * DK + c0) = dgv[0];
+        __syncthreads();
+        f32x4 after = zero4();
 #pragma unroll
-    for (int c = 0; c < 4; ++c) dglast[c] = __expf(glast[c]) * dG[c] + kdk_all[c];
+        for (int t = 0; t < C::NTG; ++t)
+            if (t > tg) after += *reinterpret_cast<const f32x4 *>(sR + (C::NTG + t) * DK + c0);
+        f32x4 dglast;
 #pragma unroll
-    for (int j = 0; j < TPG; ++j) {
-        const int i = tg * TPG + j;
-        if (i < len)
-            *reinterpret_cast<f32x4 *>(ba.dla + ((size_t)(tok0 + i) * H + h) * DK + c0) =
-                dgv[j] + after + dglast;
+        for (int c = 0; c < 4; ++c) {
+            const int cc = c0 + c;
+            dglast[c] = __expf(sGl[cc]) * sDG[cc] + sKdk[cc] + sKdk[DK + cc] + sKdk[2 * DK + cc] +
+                        sKdk[3 * DK + cc];
+        }
+#pragma unroll
+        for (int j = 0; j < TPG; ++j) {
+            const int i = tg * TPG + j;
+            if (i < len)
+                *reinterpret_cast<f32x4 *>(ba.dla + ((size_t)(tok0 + i) * H + h) * DK + c0) =
+                    dgv[j] + after + dglast;
+        }
     }
 }
 

@@ -503,6 +503,17 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(ChunkArgs a) {
                                  col0, tv);
     }
     __syncthreads();
+    if constexpr (kBwd && sizeof(E) == 2) {  // T^T in fragment order: rows i, columns j = T[j][i]
+        E *TtG = reinterpret_cast<E *>(a.ws_Tt) + ch * kChunk * kChunk;
+        for (int gi = tid; gi < kChunk * kChunk / 8; gi += kThreads) {
+            const int blk = gi >> 6, lp = gi & 63;
+            const int i = (blk >> 1) * 16 + (lp & 15), j0 = (blk & 1) * 32 + (lp >> 4) * 8;
+            bf16x8 x;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) x[t] = sTb[(j0 + t) * LDC + i];
+            *reinterpret_cast<bf16x8 *>(TtG + (size_t)gi * 8) = x;
+        }
+    }
 
     // ---- stage 3: W = T (gamma b k), formed transposed ---------------------
     // D[c][i] = sum_j Et[c][j] T[i][j]; lane holds W[i][c..c+3].

@@ -475,15 +475,15 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_prop_ws_kernel(ChunkArg
     for (int j = 0; j < 4; ++j) __syncthreads();
 
     for (int cid = cbeg; cid < cend; ++cid) {
-        if constexpr (kStates) {  // the incoming state of this chunk, fp32 [Dk][Dv]
-            float *Sc = a.ws_Sc + ((size_t)cid * H + h) * DK * DV;
+        if constexpr (kStates) {  // the incoming state of this chunk, bf16 [Dk][Dv]
+            bf16 *Sc = a.ws_Sc + ((size_t)cid * H + h) * DK * DV;
 #pragma unroll
             for (int u = 0; u < C::S_TPW; ++u) {
                 const int cblk = wave * C::KB_W + u / NCB, colb = u % NCB;
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     Sc[(size_t)(16 * cblk + 4 * (lane >> 4) + r) * DV + col0 + 16 * colb + (lane & 15)] =
-                        Sacc[u][r];
+                        static_cast<bf16>(Sacc[u][r]);
             }
         }
         load_own(nxt2, min(cid + 2, cend - 1));

@@ -8,6 +8,8 @@
 
 namespace gdn2 {
 
+typedef __bf16 bf16_t;
+
 // Per-chunk intermediates written by the chunk-factor kernel and consumed by
 // the state-propagation kernel.  All arrays are indexed [chunk id][head][...].
 struct WorkspaceLayout {
@@ -36,23 +38,25 @@ struct ChunkArgs {
     void *ws_T, *ws_W, *ws_Qh, *ws_KhT, *ws_M, *ws_U;
     float *ws_gl;
     int store_T;          // the chunk-factor kernel also stores T = (I + A)^-1
-    float *ws_Sc;         // if set, the propagation stores every chunk's incoming
-                          // state here ([chunk id][head][Dk][Dv]) and writes no o
+    bf16_t *ws_Sc;        // if set, the propagation stores every chunk's incoming
+                          // state here (bf16 [chunk id][head][Dk][Dv]) and writes no o
     // If set (backward calls), the chunk-factor kernel also writes, in fragment
-    // order: M^T [64][64], Khat [64][Dk], Qhat^T [Dk][64] and W^T [Dk][64].
-    void *ws_Mt, *ws_Kh, *ws_Qt, *ws_Wt;
+    // order: M^T [64][64], Khat [64][Dk], Qhat^T [Dk][64], W^T [Dk][64] and T^T [64][64].
+    void *ws_Mt, *ws_Kh, *ws_Qt, *ws_Wt, *ws_Tt;
 };
 
 // The backward's workspace: the forward's layout (T always stored), the
-// transposed chunk factors (io dtype, fragment order), then fp32 arrays
-// indexed [chunk id][head][...]: every chunk's incoming state Sc and the
-// gradient dSc of its outgoing state ([Dk][Dv]); the state-side partial
-// gradients dQh, dW, dKh ([64][Dk]), dM and dAp ([64][64], dAp = dZ U^T).
+// transposed chunk factors (io dtype, fragment order), then arrays indexed
+// [chunk id][head][...]: every chunk's incoming state Sc and the gradient dSc
+// of its outgoing state (bf16 [Dk][Dv]); the state-side partial gradients
+// dKh (fp32 [64][Dk]), dW^T (bf16 fragment order [Dk][64]), dM and dM^T
+// (bf16 fragment order [64][64]), dAp = dZ U^T (fp32 [64][64]) and dG =
+// rowsum(dSc * Sc) (fp32 [Dk]).
 struct BwdLayout {
     WorkspaceLayout fwd;
-    size_t off_Mt = 0, off_Kh = 0, off_Qt = 0, off_Wt = 0;
-    size_t off_Sc = 0, off_dSc = 0, off_dQh = 0, off_dW = 0, off_dKh = 0, off_dM = 0,
-           off_dAp = 0;
+    size_t off_Mt = 0, off_Kh = 0, off_Qt = 0, off_Wt = 0, off_Tt = 0;
+    size_t off_Sc = 0, off_dSc = 0, off_dKh = 0, off_dWt = 0, off_dM = 0,
+           off_dMt = 0, off_dAp = 0, off_dG = 0;
     size_t total = 0;
 };
 
@@ -65,7 +69,8 @@ struct BwdArgs {
     const float *dS_final;
     void *dq, *dk, *dv;
     float *dla, *db, *dw, *dS0;
-    float *Sc, *dSc, *dQh, *dW, *dKh, *dM, *dAp;
+    bf16_t *Sc, *dSc, *dWt, *dM, *dMt;
+    float *dKh, *dAp, *dG;
 };
 
 struct StepArgs {
