@@ -229,6 +229,48 @@ def cpu_baseline(inp, rows):
     return n_tokens / dt, dt, n_tokens
 
 
+def time_gate_logits(inp, steps, warmup):
+    """gdn2_chunk_fwd_gate_logits over the batch workload.  Returns the whole call's
+    time, the chunk-factor part (whole call minus propagation) and the propagation
+    alone, timed as the PROPAGATE stage on the workspace the call filled."""
+    import torch
+    import gated_delta_rule_47_amd as g
+    import workloads as W
+
+    def bf(x):
+        return torch.from_numpy(W.bf16_bits(x).view(np.int16)).to("cuda").view(torch.bfloat16)
+    q, k, v = bf(inp["q"]), bf(inp["k"]), bf(inp["v"])
+    la, bl, wl = bf(inp["log_alpha"]), bf(inp["b_logit"]), bf(inp["w_logit"])
+    S0 = torch.from_numpy(inp["S0"]).to("cuda")
+    B, T, H, D, N = inp["B"], inp["T"], inp["H"], inp["Dk"], inp["N"]
+    ws = torch.empty(g.gdn2_chunk_fwd_workspace_bytes(N, B, T, H, D, D, g.GDN2_BF16, 0),
+                     dtype=torch.uint8, device="cuda")
+    o = torch.empty((B, T, H, D), dtype=torch.bfloat16, device="cuda")
+    S = torch.empty((N, H, D, D), dtype=torch.float32, device="cuda")
+    for _ in range(warmup):
+        g.chunk_fwd_gate_logits(q, k, v, la, bl, wl, S0=S0, o=o, S_final=S, workspace=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        g.chunk_fwd_gate_logits(q, k, v, la, bl, wl, S0=S0, o=o, S_final=S, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    # propagation alone (it reads only the workspace the call above filled)
+    e0.record()
+    for _ in range(steps):
+        g.gdn2_chunk_fwd_stages(q.data_ptr(), k.data_ptr(), v.data_ptr(), la.data_ptr(),
+                                bl.data_ptr(), wl.data_ptr(), S0.data_ptr(), o.data_ptr(),
+                                S.data_ptr(), None, N, B, T, H, D, D, g.GDN2_BF16, ws.data_ptr(),
+                                ws.numel(), torch.cuda.current_stream().cuda_stream,
+                                g.GDN2_STAGE_PROPAGATE)
+    e1.record()
+    torch.cuda.synchronize()
+    p_ms = e0.elapsed_time(e1) / steps
+    return ms, ms - p_ms, p_ms
+
+
 def bwd_alg_bytes(n_th, chains, D, io_bytes):
     """Backward: reads q, k, v, dout (io) and log_alpha, b, w (fp32), writes dq, dk, dv (io)
     and dlog_alpha, db, dw (fp32), per token-head; S0 and dS_final in, dS0 out per chain."""
@@ -326,6 +368,24 @@ def main():
                                              "process, %.1f s" % (rows - 1, n, dt)}
             log("cpu oracle: %.1f tokens/s (%d tokens in %.1f s)" % (tps, n, dt))
         del d, inp
+
+    if a.only in ("all", "chunk"):
+        # The same batch workload with bf16 gate inputs (log alpha and the b, w logits).
+        wl = W.BATCH_4K
+        log("generating %s (bf16 gate logits)" % wl.name)
+        inp = W.make_chunk_inputs(wl, gate_logits=True)
+        ms, f_ms, p_ms = time_gate_logits(inp, max(3, a.steps // 2), 2)
+        tokens = inp["B"] * inp["T"]
+        n_th = tokens * inp["H"]
+        fbytes = n_th * inp["Dk"] * 6 * 2   # q, k, v, log_alpha, b_logit, w_logit in bf16
+        out["gate_logits"] = {"workload": wl.name, "entry": "gdn2_chunk_fwd_gate_logits",
+                              "ms": ms, "tokens_per_s": tokens / (ms * 1e-3),
+                              "kernels_ms": {"chunk_factors": f_ms, "chunk_propagate": p_ms},
+                              "chunk_factors_alg_bytes": fbytes,
+                              "chunk_factors_GBps": fbytes / (f_ms * 1e-3) / 1e9}
+        log("gate logits: %.3f ms (factors %.3f, propagate %.3f) -> %.3e tokens/s"
+            % (ms, f_ms, p_ms, tokens / (ms * 1e-3)))
+        del inp
 
     if a.only in ("all", "bwd"):
         wl = W.BATCH_4K

@@ -2,8 +2,9 @@
 
 Thin ctypes marshalling over the C ABI declared in include/libgdn2.h: the
 gdn2_* functions take raw device pointers and sizes exactly like their C
-counterparts; chunk_fwd(), chunk_bwd() and step() accept torch tensors, allocate outputs and
-the workspace with torch, and pass torch's current stream.  Every step of the
+counterparts; chunk_fwd(), chunk_fwd_gate_logits(), chunk_bwd() and step() accept
+torch tensors, allocate outputs and the workspace with torch, and pass torch's
+current stream.  Every step of the
 computation runs in the HIP library; if libgdn2.so is missing, loading fails
 with an error (there is no fallback).
 """
@@ -31,7 +32,8 @@ GDN2_STAGE_STORE_T = 8
 
 EXPORTED = ("gdn2_abi_version", "gdn2_status_string", "gdn2_chunk_fwd_workspace_bytes",
             "gdn2_chunk_fwd_workspace_layout", "gdn2_chunk_fwd", "gdn2_chunk_fwd_stages",
-            "gdn2_chunk_bwd_workspace_bytes", "gdn2_chunk_bwd", "gdn2_step")
+            "gdn2_chunk_fwd_gate_logits", "gdn2_chunk_bwd_workspace_bytes", "gdn2_chunk_bwd",
+            "gdn2_step")
 
 
 class Gdn2Error(RuntimeError):
@@ -74,6 +76,8 @@ def load_library(path=LIB_PATH):
     lib.gdn2_chunk_fwd.argtypes = [P] * 10 + [I] * 7 + [P, Z, P]
     lib.gdn2_chunk_fwd_stages.restype = I
     lib.gdn2_chunk_fwd_stages.argtypes = [P] * 10 + [I] * 7 + [P, Z, P, I]
+    lib.gdn2_chunk_fwd_gate_logits.restype = I
+    lib.gdn2_chunk_fwd_gate_logits.argtypes = [P] * 10 + [I] * 7 + [P, Z, P]
     lib.gdn2_chunk_bwd_workspace_bytes.restype = Z
     lib.gdn2_chunk_bwd_workspace_bytes.argtypes = [I] * 8
     lib.gdn2_chunk_bwd.restype = I
@@ -123,6 +127,14 @@ def gdn2_chunk_fwd_stages(q, k, v, log_alpha, b, w, S0, o, S_final, cu_seqlens, 
     return load_library().gdn2_chunk_fwd_stages(q, k, v, log_alpha, b, w, S0, o, S_final,
                                                  cu_seqlens, N, B, T, H, Dk, Dv, io, workspace,
                                                  workspace_bytes, stream, stages)
+
+
+def gdn2_chunk_fwd_gate_logits(q, k, v, log_alpha, b_logit, w_logit, S0, o, S_final, cu_seqlens,
+                               N, B, T, H, Dk, Dv, io, workspace, workspace_bytes, stream):
+    """Raw call: every pointer argument is an int (device address) or None."""
+    return load_library().gdn2_chunk_fwd_gate_logits(q, k, v, log_alpha, b_logit, w_logit, S0, o,
+                                                      S_final, cu_seqlens, N, B, T, H, Dk, Dv, io,
+                                                      workspace, workspace_bytes, stream)
 
 
 def gdn2_chunk_bwd_workspace_bytes(N, B, T, H, Dk, Dv, io, varlen):
@@ -269,3 +281,35 @@ def chunk_bwd(q, k, v, log_alpha, b, w, dout, S0=None, dS_final=None, cu_seqlens
     if st != GDN2_OK:
         raise Gdn2Error(st, "gdn2_chunk_bwd")
     return out
+
+
+def chunk_fwd_gate_logits(q, k, v, log_alpha, b_logit, w_logit, S0=None, cu_seqlens=None,
+                          o=None, S_final=None, output_final_state=True, workspace=None,
+                          stream=None):
+    """chunk_fwd with bfloat16 gate inputs: log_alpha itself and the logits of b
+    and w (sigmoid taken in the kernel).  q, k, v must be bfloat16."""
+    import torch
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    io = _io_of(q)
+    for name, t in (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha), ("b_logit", b_logit),
+                    ("w_logit", w_logit)):
+        _check(t, name, torch.bfloat16)
+    _check(S0, "S0", torch.float32)
+    _check(cu_seqlens, "cu_seqlens", torch.int32)
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    if o is None:
+        o = torch.empty((B, T, H, Dv), dtype=q.dtype, device=q.device)
+    if S_final is None and output_final_state:
+        S_final = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=q.device)
+    varlen = cu_seqlens is not None
+    nbytes = gdn2_chunk_fwd_workspace_bytes(N, B, T, H, Dk, Dv, io, varlen)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    st = gdn2_chunk_fwd_gate_logits(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b_logit),
+                                    _ptr(w_logit), _ptr(S0), _ptr(o), _ptr(S_final),
+                                    _ptr(cu_seqlens), N, B, T, H, Dk, Dv, io, _ptr(workspace),
+                                    workspace.numel(), _stream(stream))
+    if st != GDN2_OK:
+        raise Gdn2Error(st, "gdn2_chunk_fwd_gate_logits")
+    return o, S_final

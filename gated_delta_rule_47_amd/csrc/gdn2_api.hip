@@ -151,11 +151,15 @@ int gdn2_chunk_fwd_workspace_layout(int N, int B, int T, int H, int Dk, int Dv, 
     return GDN2_OK;
 }
 
-int gdn2_chunk_fwd_stages(const void *q, const void *k, const void *v, const float *log_alpha,
-                          const float *b, const float *w, const float *S0, void *o,
-                          float *S_final, const int32_t *cu_seqlens, int N, int B, int T, int H,
-                          int Dk, int Dv, int io, void *workspace, size_t workspace_bytes,
-                          void *stream_ptr, int stages) {
+}  // extern "C"
+
+// The chunk forward; gate_logits selects bf16 gate inputs (log alpha and the
+// logits of b and w) instead of fp32 gates.
+static int chunk_fwd_impl(const void *q, const void *k, const void *v, const void *log_alpha,
+                          const void *b, const void *w, const float *S0, void *o, float *S_final,
+                          const int32_t *cu_seqlens, int N, int B, int T, int H, int Dk, int Dv,
+                          int io, void *workspace, size_t workspace_bytes, void *stream_ptr,
+                          int stages, bool gate_logits) {
     if (stages & ~(GDN2_STAGE_ALL | GDN2_STAGE_STORE_T)) return GDN2_ERR_INVALID_ARGUMENT;
     if (io != GDN2_F32 && io != GDN2_BF16) return GDN2_ERR_INVALID_ARGUMENT;
     if (N < 0 || B < 0 || T < 0 || H < 0 || Dk <= 0 || Dv <= 0) return GDN2_ERR_INVALID_ARGUMENT;
@@ -191,9 +195,10 @@ int gdn2_chunk_fwd_stages(const void *q, const void *k, const void *v, const flo
     a.q = q;
     a.k = k;
     a.v = v;
-    a.log_alpha = log_alpha;
-    a.b = b;
-    a.w = w;
+    a.log_alpha = static_cast<const float *>(log_alpha);  // bf16 when gate_logits
+    a.b = static_cast<const float *>(b);
+    a.w = static_cast<const float *>(w);
+    a.gate_logits = gate_logits ? 1 : 0;
     a.S0 = S0;
     a.o = o;
     a.S_final = S_final;
@@ -224,13 +229,36 @@ int gdn2_chunk_fwd_stages(const void *q, const void *k, const void *v, const flo
     return finish(err, stream);
 }
 
+extern "C" {
+
+int gdn2_chunk_fwd_stages(const void *q, const void *k, const void *v, const float *log_alpha,
+                          const float *b, const float *w, const float *S0, void *o,
+                          float *S_final, const int32_t *cu_seqlens, int N, int B, int T, int H,
+                          int Dk, int Dv, int io, void *workspace, size_t workspace_bytes,
+                          void *stream_ptr, int stages) {
+    return chunk_fwd_impl(q, k, v, log_alpha, b, w, S0, o, S_final, cu_seqlens, N, B, T, H, Dk, Dv,
+                          io, workspace, workspace_bytes, stream_ptr, stages, false);
+}
+
 int gdn2_chunk_fwd(const void *q, const void *k, const void *v, const float *log_alpha,
                    const float *b, const float *w, const float *S0, void *o, float *S_final,
                    const int32_t *cu_seqlens, int N, int B, int T, int H, int Dk, int Dv, int io,
                    void *workspace, size_t workspace_bytes, void *stream_ptr) {
-    return gdn2_chunk_fwd_stages(q, k, v, log_alpha, b, w, S0, o, S_final, cu_seqlens, N, B, T, H,
-                                 Dk, Dv, io, workspace, workspace_bytes, stream_ptr,
-                                 GDN2_STAGE_ALL);
+    return chunk_fwd_impl(q, k, v, log_alpha, b, w, S0, o, S_final, cu_seqlens, N, B, T, H, Dk, Dv,
+                          io, workspace, workspace_bytes, stream_ptr, GDN2_STAGE_ALL, false);
+}
+
+int gdn2_chunk_fwd_gate_logits(const void *q, const void *k, const void *v,
+                               const void *log_alpha, const void *b_logit, const void *w_logit,
+                               const float *S0, void *o, float *S_final,
+                               const int32_t *cu_seqlens, int N, int B, int T, int H, int Dk,
+                               int Dv, int io, void *workspace, size_t workspace_bytes,
+                               void *stream_ptr) {
+    if (io != GDN2_F32 && io != GDN2_BF16) return GDN2_ERR_INVALID_ARGUMENT;
+    if (io != GDN2_BF16) return GDN2_ERR_UNSUPPORTED;
+    return chunk_fwd_impl(q, k, v, log_alpha, b_logit, w_logit, S0, o, S_final, cu_seqlens, N, B,
+                          T, H, Dk, Dv, io, workspace, workspace_bytes, stream_ptr, GDN2_STAGE_ALL,
+                          true);
 }
 
 size_t gdn2_chunk_bwd_workspace_bytes(int N, int B, int T, int H, int Dk, int Dv, int io,

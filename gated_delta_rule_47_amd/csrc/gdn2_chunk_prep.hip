@@ -188,9 +188,16 @@ __device__ __forceinline__ void chunk_span(const ChunkArgs &a, int cid, int &tok
     }
 }
 
+// 1 / (1 + e^-x) with the hardware reciprocal (about 1 ulp; the operands are bf16).
+__device__ __forceinline__ float sigmoid1(float x) {
+    return __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+}
+
 // kBwd: also write the transposed factors a backward call needs (a.ws_Mt,
-// ws_Kh, ws_Qt, ws_Wt).
-template <typename E, int DK, bool kBwd>
+// ws_Kh, ws_Qt, ws_Wt, ws_Tt).
+// kLogits: the gates arrive as bf16 -- log alpha itself and the logits of b
+// and w, whose sigmoid is taken here.
+template <typename E, int DK, bool kBwd, bool kLogits = false>
 __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(ChunkArgs a) {
     using C = PrepCfg<E, DK>;
     using M = Mma<E>;
@@ -229,8 +236,15 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(ChunkArgs a) {
         const int i = tg * TPG + j;
         if (i < len) {
             const size_t off = ((size_t)(tok0 + i) * H + h) * DK + c0;
-            g[j] = *reinterpret_cast<const f32x4 *>(a.log_alpha + off);
-            bk[j] = *reinterpret_cast<const f32x4 *>(a.b + off);
+            if constexpr (kLogits) {
+                g[j] = to4(*reinterpret_cast<const bf16x4 *>(reinterpret_cast<const bf16 *>(a.log_alpha) + off));
+                const f32x4 bl = to4(*reinterpret_cast<const bf16x4 *>(reinterpret_cast<const bf16 *>(a.b) + off));
+#pragma unroll
+                for (int c = 0; c < 4; ++c) bk[j][c] = sigmoid1(bl[c]);
+            } else {
+                g[j] = *reinterpret_cast<const f32x4 *>(a.log_alpha + off);
+                bk[j] = *reinterpret_cast<const f32x4 *>(a.b + off);
+            }
             kk[j] = *reinterpret_cast<const Vec4<E> *>(k + off);
             qq[j] = *reinterpret_cast<const Vec4<E> *>(q + off);
         } else {  // padding token: k = q = b = 0, log alpha = 0 (an exact no-op)
@@ -243,17 +257,26 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(ChunkArgs a) {
     *reinterpret_cast<f32x4 *>(sTot + tg * DK + c0) = g[TPG - 1];
     // w and v are multiplied only when (w v)^T is staged, after W: their loads
     // stay in flight through the following phases.
-    f32x4 zw[TPG];
+    using GW = typename std::conditional<kLogits, bf16x4, f32x4>::type;  // w, or its logit
+    GW zw[TPG];
     Vec4<E> zv[TPG];
 #pragma unroll
     for (int j = 0; j < TPG; ++j) {
         const int i = tg * TPG + j;
         if (i < len) {
             const size_t off = ((size_t)(tok0 + i) * H + h) * DK + c0;  // Dv == Dk
-            zw[j] = *reinterpret_cast<const f32x4 *>(a.w + off);
+            if constexpr (kLogits)
+                zw[j] = *reinterpret_cast<const bf16x4 *>(reinterpret_cast<const bf16 *>(a.w) + off);
+            else
+                zw[j] = *reinterpret_cast<const f32x4 *>(a.w + off);
             zv[j] = *reinterpret_cast<const Vec4<E> *>(v + off);
-        } else {
-            zw[j] = zero4();
+        } else {  // padding token: v = 0 makes w v = 0 whatever w is
+            if constexpr (kLogits) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) zw[j][c] = static_cast<bf16>(0.0f);
+            } else {
+                zw[j] = zero4();
+            }
             zv[j] = pack4<E>(zero4());
         }
     }
@@ -545,7 +568,12 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(ChunkArgs a) {
     for (int c = 0; c < 4; ++c) {
         float zt[TPG];
 #pragma unroll
-        for (int j = 0; j < TPG; ++j) zt[j] = zw[j][c] * elem<E>(zv[j], c);
+        for (int j = 0; j < TPG; ++j) {
+            float wv;
+            if constexpr (kLogits) wv = sigmoid1(static_cast<float>(zw[j][c]));
+            else wv = zw[j][c];
+            zt[j] = wv * elem<E>(zv[j], c);
+        }
         store_run<E, TPG>(sEt + (c0 + c) * LDC + tg * TPG, zt);
     }
     __syncthreads();
@@ -570,7 +598,10 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(ChunkArgs a) {
 
 hipError_t launch_chunk_prep(const ChunkArgs &a, int Dk, bool bf16_io, hipStream_t stream) {
     const dim3 grid((unsigned)((size_t)a.max_chunks * a.H)), block(kThreads);
-    if (bf16_io && a.ws_Mt) {  // backward calls (bf16 only)
+    if (bf16_io && a.gate_logits) {  // bf16 gates, sigmoid in the kernel (forward only)
+        if (Dk == 128) hipLaunchKernelGGL((chunk_prep_kernel<bf16, 128, false, true>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((chunk_prep_kernel<bf16, 64, false, true>), grid, block, 0, stream, a);
+    } else if (bf16_io && a.ws_Mt) {  // backward calls (bf16 only)
         if (Dk == 128) hipLaunchKernelGGL((chunk_prep_kernel<bf16, 128, true>), grid, block, 0, stream, a);
         else hipLaunchKernelGGL((chunk_prep_kernel<bf16, 64, true>), grid, block, 0, stream, a);
     } else if (bf16_io) {

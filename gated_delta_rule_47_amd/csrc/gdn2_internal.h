@@ -38,6 +38,7 @@ struct ChunkArgs {
     void *ws_T, *ws_W, *ws_Qh, *ws_KhT, *ws_M, *ws_U;
     float *ws_gl;
     int store_T;          // the chunk-factor kernel also stores T = (I + A)^-1
+    int gate_logits;      // log_alpha, b, w are bf16: log alpha and the logits of b and w
     bf16_t *ws_Sc;        // if set, the propagation stores every chunk's incoming
                           // state here (bf16 [chunk id][head][Dk][Dv]) and writes no o
     // If set (backward calls), the chunk-factor kernel also writes, in fragment

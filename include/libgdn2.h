@@ -140,6 +140,26 @@ int gdn2_chunk_fwd_stages(const void *q, const void *k, const void *v,
                           void *workspace, size_t workspace_bytes, void *stream, int stages);
 
 /*
+ * gdn2_chunk_fwd with bf16 gate inputs.  The gates are the sigmoids of learned
+ * projections (iplexlaw digest, section "Decisiones independientes en dos
+ * ejes": b and w in (0, 1) per channel), so a layer can hand over the logits
+ * and let the chunk kernel take the sigmoid, halving the gate bytes:
+ *   log_alpha  [B, T, H, Dk] bf16, log alpha itself (<= 0)
+ *   b_logit    [B, T, H, Dk] bf16, b = 1 / (1 + exp(-b_logit))
+ *   w_logit    [B, T, H, Dv] bf16, w = 1 / (1 + exp(-w_logit))
+ * The sigmoids are taken in fp32.  Everything else (shapes, S0, o, S_final,
+ * cu_seqlens, workspace and its size, the decay precondition) is as for
+ * gdn2_chunk_fwd.  Only io = GDN2_BF16 is implemented (GDN2_F32 returns
+ * GDN2_ERR_UNSUPPORTED).
+ */
+int gdn2_chunk_fwd_gate_logits(const void *q, const void *k, const void *v,
+                               const void *log_alpha, const void *b_logit, const void *w_logit,
+                               const float *S0, void *o, float *S_final,
+                               const int32_t *cu_seqlens, int N,
+                               int B, int T, int H, int Dk, int Dv, int io,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Where gdn2_chunk_fwd keeps its per-chunk intermediates inside the
  * workspace, for inspection by tests.  Offsets are in bytes from the
  * workspace start; every array is indexed by (chunk id c, head h) as

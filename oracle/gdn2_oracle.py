@@ -213,6 +213,19 @@ def chunked(q, k, v, log_alpha, b, w, S0=None, cu_seqlens=None, chunk=CHUNK):
 
 
 # ---------------------------------------------------------------------------
+# Gate-logit inputs
+# ---------------------------------------------------------------------------
+
+def gates_from_logits(b_logit, w_logit):
+    """The erase and write gates from their pre-activations: each gate is the
+    sigmoid of its own linear projection of the token [iplexlaw, "Decisiones
+    independientes en dos ejes"], so b = 1 / (1 + exp(-b_logit)) and likewise
+    w.  Returns (b, w) in float64."""
+    b_logit, w_logit = _f64(b_logit), _f64(w_logit)
+    return 1.0 / (1.0 + np.exp(-b_logit)), 1.0 / (1.0 + np.exp(-w_logit))
+
+
+# ---------------------------------------------------------------------------
 # Backward: gradients of the recurrence
 # ---------------------------------------------------------------------------
 #

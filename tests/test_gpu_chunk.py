@@ -231,3 +231,32 @@ def test_varlen_workload_sampled_sequences():
     lens = W.varlen_lengths(W.VARLEN)
     longest = int(np.argmax(lens))
     _check_sampled(W.VARLEN, [(0, 0), (longest, 6), (31, 15)])
+
+
+def _check_gate_logits(inp, label):
+    import torch
+    io = inp["io"]
+    q, k, v = dev(inp["q"], io), dev(inp["k"], io), dev(inp["v"], io)
+    la, bl, wl_ = (dev(inp[x], W.BF16) for x in ("log_alpha", "b_logit", "w_logit"))
+    o, S = g.chunk_fwd_gate_logits(q, k, v, la, bl, wl_, S0=dev(inp["S0"]),
+                                   cu_seqlens=dev(inp["cu_seqlens"]))
+    torch.cuda.synchronize()
+    b, w = O.gates_from_logits(inp["b_logit"], inp["w_logit"])
+    o_ref, S_ref = O.recurrence(inp["q"], inp["k"], inp["v"], inp["log_alpha"], b, w,
+                                S0=inp["S0"], cu_seqlens=inp["cu_seqlens"])
+    eo, es = O.rel_max_err(host(o), o_ref), O.rel_max_err(host(S), S_ref)
+    log("%s: err_o %.3e err_S %.3e" % (label, eo, es))
+    assert eo <= tol(io) and es <= tol(io)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_gate_logits_dense(D):
+    """bf16 log alpha and gate logits, sigmoid in the kernel; ragged tail, S0."""
+    wl = W.ChunkWorkload("logits_dense", 2, 200, 3, D, D, W.BF16, 666 + D, with_S0=True)
+    _check_gate_logits(W.make_chunk_inputs(wl, gate_logits=True), "gate logits D=%d" % D)
+
+
+def test_gate_logits_varlen():
+    wl = W.ChunkWorkload("logits_varlen", 1, 0, 2, 128, 128, W.BF16, 668, with_S0=True, n_seqs=7)
+    _check_gate_logits(W.make_chunk_inputs(wl, lengths=[1, 63, 64, 65, 130, 0, 7], gate_logits=True),
+                       "gate logits varlen")

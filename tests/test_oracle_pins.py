@@ -354,3 +354,17 @@ def test_rel_max_err():
     assert O.rel_max_err([1.0, -2.0], [1.0, -2.0]) == 0.0
     assert abs(O.rel_max_err([1.0, -2.1], [1.0, -2.0]) - 0.05) < 1e-12
     assert O.rel_max_err([0.0], [0.0]) == 0.0
+
+
+def test_gates_from_logits_closed_forms():
+    """Gates are sigmoids of their projections [iplexlaw, "Decisiones
+    independientes en dos ejes"]: sigma(0) = 1/2, sigma(ln 3) = 3/4,
+    sigma(-x) = 1 - sigma(x), values in (0, 1), and the erase and write
+    logits map independently."""
+    b, w = O.gates_from_logits(np.array([0.0, np.log(3.0), -np.log(3.0)]), np.array([40.0, -40.0]))
+    np.testing.assert_allclose(b, [0.5, 0.75, 0.25], rtol=1e-15)
+    assert 1.0 - w[0] < 1e-17 and 0.0 < w[1] < 1e-17
+    x = np.linspace(-8, 8, 33)
+    bx, wx = O.gates_from_logits(x, -x)
+    np.testing.assert_allclose(bx + wx, 1.0, rtol=1e-15)
+    assert np.all(np.diff(bx) > 0)

@@ -139,7 +139,7 @@ def varlen_lengths(wl: ChunkWorkload):
 def make_chunk_inputs(wl: ChunkWorkload, lengths=None, T: Optional[int] = None,
                       B: Optional[int] = None, H: Optional[int] = None,
                       seed: Optional[int] = None, log_alpha_range=(-0.2, -0.001),
-                      b_scale: float = 1.0):
+                      b_scale: float = 1.0, gate_logits: bool = False):
     """Draw the inputs of one chunk-forward call.
 
     Optional overrides (T, B, H, lengths, seed) shrink a workload for
@@ -148,6 +148,10 @@ def make_chunk_inputs(wl: ChunkWorkload, lengths=None, T: Optional[int] = None,
 
     Returns a dict with float32 arrays q, k, v, log_alpha, b, w, S0 (or None),
     cu_seqlens (int32 [N+1] or None) and meta fields B, T, H, Dk, Dv, N, io.
+    With gate_logits, the gates are handed over as bfloat16 values instead:
+    log_alpha rounded to bfloat16 and the N(0, 1) logits b_logit, w_logit
+    (rounded to bfloat16); b and w are then None (the sigmoid belongs to the
+    computation under test).
     """
     seed = wl.seed if seed is None else seed
     rng = np.random.Generator(np.random.PCG64(seed))
@@ -172,15 +176,23 @@ def make_chunk_inputs(wl: ChunkWorkload, lengths=None, T: Optional[int] = None,
     v = _io_cast(_normal(rng, (B_, T_, H, Dv)), wl.io)
     lo, hi = log_alpha_range
     log_alpha = (lo + (hi - lo) * rng.random((B_, T_, H, Dk), dtype=np.float32)).astype(np.float32)
-    b = _sigmoid(_normal(rng, (B_, T_, H, Dk)))
-    if b_scale != 1.0:
-        b = (b * np.float32(b_scale)).astype(np.float32)
-    w = _sigmoid(_normal(rng, (B_, T_, H, Dv)))
+    b_logit = _normal(rng, (B_, T_, H, Dk))
+    w_logit = _normal(rng, (B_, T_, H, Dv))
+    extra = {}
+    if gate_logits:
+        log_alpha = bf16_round(log_alpha)
+        extra = dict(b_logit=bf16_round(b_logit), w_logit=bf16_round(w_logit))
+        b = w = None
+    else:
+        b = _sigmoid(b_logit)
+        if b_scale != 1.0:
+            b = (b * np.float32(b_scale)).astype(np.float32)
+        w = _sigmoid(w_logit)
     S0 = None
     if wl.with_S0:
         S0 = (0.02 * _normal(rng, (N, H, Dk, Dv))).astype(np.float32)
     return dict(q=q, k=k, v=v, log_alpha=log_alpha, b=b, w=w, S0=S0, cu_seqlens=cu,
-                B=B_, T=T_, H=H, Dk=Dk, Dv=Dv, N=N, io=wl.io)
+                B=B_, T=T_, H=H, Dk=Dk, Dv=Dv, N=N, io=wl.io, **extra)
 
 
 def make_chunk_grads(inp, seed: int, with_dS_final: bool = True):
