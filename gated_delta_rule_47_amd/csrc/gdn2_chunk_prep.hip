@@ -465,6 +465,17 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(ChunkArgs a) {
             store_tile_t<float>(sA + 16 * I * LDA + 16 * J, LDA, accA[u], lane);
         }
     }
+    // T as E (sTb, row-major) is written block by block by the solve below;
+    // its strictly upper blocks are zero.
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int t = wave + 4 * u;
+        if (t < 6) {
+            int I, J;
+            upper_tile(t, I, J);
+            store_tile<E>(sTb + 16 * I * LDC + 16 * J, LDC, zero4(), lane);
+        }
+    }
     __syncthreads();
 
     // ---- stage 2b: T = (I + A)^-1 in fp32, in place ------------------------
@@ -482,7 +493,10 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(ChunkArgs a) {
             x[i] = s;
         }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) Ab[i * LDA + c] = x[i];
+        for (int i = 0; i < 16; ++i) {
+            Ab[i * LDA + c] = x[i];
+            sTb[(16 * I + i) * LDC + 16 * I + c] = from_f32<E>(x[i]);
+        }
     }
     __syncthreads();
     // Off-diagonal blocks, level s = I - J:  T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ.
@@ -505,27 +519,19 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(ChunkArgs a) {
             const f32x4 t = mma16_f32(zero4(), sA + 16 * I * LDA + 16 * I, LDA, X, LDX, 1, lane);
             // store -t transposed into block (J, I): element (m, n) of T_IJ at [16J+n][16I+m]
             store_tile_t<float>(sA + 16 * J * LDA + 16 * I, LDA, -t, lane);
+            store_tile<E>(sTb + 16 * I * LDC + 16 * J, LDC, -t, lane);
         }
         __syncthreads();
     }
 
-    // ---- T as E (row-major) for W and U; optionally T itself -------------
-    {
+    // ---- optionally T itself (row-major, from its E copy) ---------------
+    if (a.store_T) {
         const int row = tid >> 2, col0 = 16 * (tid & 3);
-        float tv[16];
+        E *Tg = reinterpret_cast<E *>(a.ws_T) + ch * kChunk * kChunk + row * kChunk + col0;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int col = col0 + j;
-            const bool same = (row >> 4) == (col >> 4);
-            const float vv = same ? sA[row * LDA + col] : (row > col ? sA[col * LDA + row] : 0.0f);
-            tv[j] = vv;
-        }
-        store_run<E, 16>(sTb + row * LDC + col0, tv);
-        if (a.store_T)
-            store_run<E, 16>(reinterpret_cast<E *>(a.ws_T) + ch * kChunk * kChunk + row * kChunk +
-                                 col0, tv);
+        for (int j = 0; j < 16; j += 4)
+            *reinterpret_cast<Vec4<E> *>(Tg + j) = *reinterpret_cast<const Vec4<E> *>(sTb + row * LDC + col0 + j);
     }
-    __syncthreads();
     if constexpr (kBwd && sizeof(E) == 2) {  // T^T in fragment order: rows i, columns j = T[j][i]
         E *TtG = reinterpret_cast<E *>(a.ws_Tt) + ch * kChunk * kChunk;
         for (int gi = tid; gi < kChunk * kChunk / 8; gi += kThreads) {
