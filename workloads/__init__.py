@@ -236,3 +236,82 @@ def make_decode_step(wl: DecodeWorkload, step: int, B: Optional[int] = None,
     b = _sigmoid(_normal(rng, (B, H, wl.Dk)))
     w = _sigmoid(_normal(rng, (B, H, wl.Dv)))
     return dict(q=q, k=k, v=v, log_alpha=log_alpha, b=b, w=w)
+
+
+# ---------------------------------------------------------------------------
+# Token-mixer layer inputs
+# ---------------------------------------------------------------------------
+#
+# The layer's width D = H * Dv (16 heads of 128 make the 2048-wide hidden
+# state of a 1.3B-parameter model).  Distributions (all weights drawn here are
+# random initialisations, not trained values):
+#   x ~ N(0, 1) [B, T, D], bf16;
+#   W_in ~ N(0, 1/D) [7 blocks, D], bf16 (projections come out ~ N(0, 1));
+#   conv_w ~ U(-1, 1) / sqrt(L) [2*H*Dk + H*Dv, L], fp32;
+#   alpha_bias ~ U(3, 6) [H*Dk], fp32 (alpha = sigmoid(~N(4.5, 1)) ~ 0.95..0.999);
+#   norm_w = 1 + 0.1 N(0, 1) [Dv], fp32;
+#   W_o ~ N(0, 1/(H*Dv)) [D, H*Dv], bf16;
+#   S0 ~ N(0, 0.02^2) where present.
+# Draw order: (lengths) -> x -> W_in -> conv_w -> alpha_bias -> norm_w -> W_o
+# -> (state).  Generator: numpy PCG64.
+
+@dataclass(frozen=True)
+class LayerWorkload:
+    name: str
+    B: int
+    T: int            # tokens per batch row (dense) or total packed tokens (varlen)
+    H: int
+    Dk: int
+    Dv: int
+    D: int            # model width
+    conv_len: int
+    seed: int
+    with_S0: bool = False
+    n_seqs: int = 0
+    len_lo: int = 0
+    len_hi: int = 0
+
+
+LAYER_4K = LayerWorkload("layer_batch_B8_H16_T4096_d128_D2048", 8, 4096, 16, 128, 128, 2048, 4,
+                         47005)
+
+
+def layer_in_rows(H, Dk, Dv):
+    """Rows of the stacked input weight: q, k, v, alpha, output gate, b, w."""
+    return 4 * H * Dk + 3 * H * Dv
+
+
+def make_layer_inputs(wl: LayerWorkload, lengths=None, T: Optional[int] = None,
+                      B: Optional[int] = None, seed: Optional[int] = None):
+    """Draw the inputs and weights of one layer-forward call.  bf16 values are
+    float32 arrays holding bf16-representable numbers.  Returns a dict with
+    x, W_in, conv_w, alpha_bias, norm_w, W_o, S0 (or None), cu_seqlens (or
+    None) and meta fields B, T, H, Dk, Dv, D, L, N."""
+    seed = wl.seed if seed is None else seed
+    rng = np.random.Generator(np.random.PCG64(seed))
+    cu = None
+    if wl.n_seqs or lengths is not None:
+        if lengths is None:
+            lengths = rng.integers(wl.len_lo, wl.len_hi, size=wl.n_seqs, endpoint=True)
+        lengths = np.asarray(lengths, dtype=np.int64)
+        cu = np.zeros(len(lengths) + 1, dtype=np.int32)
+        cu[1:] = np.cumsum(lengths)
+        B_, T_, N = 1, int(cu[-1]), len(lengths)
+    else:
+        B_ = wl.B if B is None else B
+        T_ = wl.T if T is None else T
+        N = B_
+    H, Dk, Dv, D, L = wl.H, wl.Dk, wl.Dv, wl.D, wl.conv_len
+    rows = layer_in_rows(H, Dk, Dv)
+    x = bf16_round(_normal(rng, (B_, T_, D)))
+    W_in = bf16_round(_normal(rng, (rows, D)) * np.float32(1.0 / np.sqrt(D)))
+    conv_w = ((2.0 * rng.random((2 * H * Dk + H * Dv, L), dtype=np.float32) - 1.0)
+              / np.float32(np.sqrt(L))).astype(np.float32)
+    alpha_bias = (3.0 + 3.0 * rng.random(H * Dk, dtype=np.float32)).astype(np.float32)
+    norm_w = (1.0 + 0.1 * _normal(rng, (Dv,))).astype(np.float32)
+    W_o = bf16_round(_normal(rng, (D, H * Dv)) * np.float32(1.0 / np.sqrt(H * Dv)))
+    S0 = None
+    if wl.with_S0:
+        S0 = (0.02 * _normal(rng, (N, H, Dk, Dv))).astype(np.float32)
+    return dict(x=x, W_in=W_in, conv_w=conv_w, alpha_bias=alpha_bias, norm_w=norm_w, W_o=W_o,
+                S0=S0, cu_seqlens=cu, B=B_, T=T_, H=H, Dk=Dk, Dv=Dv, D=D, L=L, N=N)
