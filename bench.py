@@ -45,7 +45,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-steps", type=int, default=1024)
-    ap.add_argument("--only", choices=["all", "chunk", "decode", "varlen", "bwd"], default="all")
+    ap.add_argument("--only", choices=["all", "chunk", "decode", "varlen", "bwd", "layer"],
+                    default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=8,
                     help="batch rows (4096 tokens x 16 heads each) the oracle runs on")
@@ -304,6 +305,38 @@ def time_bwd(d, inp, steps, warmup):
     return e0.elapsed_time(e1) / steps, ws.numel()
 
 
+def time_layer(inp, steps, warmup):
+    """Time `steps` gdn2_layer_fwd calls on the token-mixer layer workload
+    (events on the launch stream).  Returns (ms, workspace bytes)."""
+    import torch
+    import gated_delta_rule_47_amd as g
+    import workloads as W
+
+    def bf(x):
+        return torch.from_numpy(W.bf16_bits(x).view(np.int16)).to("cuda").view(torch.bfloat16)
+
+    def f32(x):
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to("cuda")
+    x, W_in, W_o = bf(inp["x"]), bf(inp["W_in"]), bf(inp["W_o"])
+    cw, ab, nw = f32(inp["conv_w"]), f32(inp["alpha_bias"]), f32(inp["norm_w"])
+    B, T, H, D, Dm, N = inp["B"], inp["T"], inp["H"], inp["Dk"], inp["D"], inp["N"]
+    ws = torch.empty(g.gdn2_layer_fwd_workspace_bytes(N, B, T, H, D, D, Dm, 0), dtype=torch.uint8,
+                     device="cuda")
+    y = torch.empty((B, T, Dm), dtype=torch.bfloat16, device="cuda")
+    S = torch.empty((N, H, D, D), dtype=torch.float32, device="cuda")
+    call = lambda: g.layer_fwd(x, W_in, cw, ab, nw, W_o, H, D, D, y=y, S_final=S, workspace=ws)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps, ws.numel()
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -406,6 +439,26 @@ def main():
             out.update({"value": tokens / (ms * 1e-3), "ms_per_step": ms,
                         "config": {"workload": wl.name, "pass": "backward"}})
         del d, inp
+
+    if a.only in ("all", "layer"):
+        wl = W.LAYER_4K
+        log("generating %s" % wl.name)
+        inp = W.make_layer_inputs(wl)
+        ms, ws_bytes = time_layer(inp, max(3, a.steps // 2), 2)
+        M, H, D, Dm = inp["B"] * inp["T"], inp["H"], inp["Dk"], inp["D"]
+        gemm_flops = 2 * M * Dm * 7 * H * D + 2 * M * H * D * Dm
+        core_flops = chunk_flops_dense(inp["B"] * (inp["T"] // 64) * H, D)
+        out["layer"] = {"workload": wl.name, "entry": "gdn2_layer_fwd", "ms": ms,
+                        "tokens_per_s": M / (ms * 1e-3), "D_model": Dm, "conv_len": inp["L"],
+                        "gemm_flops": gemm_flops, "core_mfma_flops": core_flops,
+                        "mfma_TFLOPs_over_whole_layer": (gemm_flops + core_flops) / (ms * 1e-3) / 1e12,
+                        "workspace_bytes": ws_bytes}
+        log("layer: %.3f ms -> %.3e tokens/s (%.0f TFLOP/s of MFMA work over the whole call)"
+            % (ms, M / (ms * 1e-3), out["layer"]["mfma_TFLOPs_over_whole_layer"]))
+        if "value" not in out:
+            out.update({"value": M / (ms * 1e-3), "ms_per_step": ms,
+                        "config": {"workload": wl.name, "pass": "layer forward"}})
+        del inp
 
     if a.only in ("all", "decode"):
         wl = W.DECODE

@@ -33,13 +33,20 @@ GDN2_STAGE_STORE_T = 8
 EXPORTED = ("gdn2_abi_version", "gdn2_status_string", "gdn2_chunk_fwd_workspace_bytes",
             "gdn2_chunk_fwd_workspace_layout", "gdn2_chunk_fwd", "gdn2_chunk_fwd_stages",
             "gdn2_chunk_fwd_gate_logits", "gdn2_chunk_bwd_workspace_bytes", "gdn2_chunk_bwd",
-            "gdn2_step")
+            "gdn2_step", "gdn2_layer_fwd_workspace_bytes", "gdn2_layer_fwd")
 
 
 class Gdn2Error(RuntimeError):
     def __init__(self, status, where):
         self.status = status
         super().__init__("%s failed: %s" % (where, gdn2_status_string(status)))
+
+
+class LayerWeights(ctypes.Structure):
+    """gdn2_layer_weights: device addresses of the layer's weights."""
+    _fields_ = [("W_in", ctypes.c_void_p), ("conv_w", ctypes.c_void_p),
+                ("alpha_bias", ctypes.c_void_p), ("norm_w", ctypes.c_void_p),
+                ("W_o", ctypes.c_void_p)]
 
 
 class WorkspaceLayout(ctypes.Structure):
@@ -84,6 +91,11 @@ def load_library(path=LIB_PATH):
     lib.gdn2_chunk_bwd.argtypes = [P] * 17 + [I] * 7 + [P, Z, P]
     lib.gdn2_step.restype = I
     lib.gdn2_step.argtypes = [P] * 8 + [I] * 5 + [P]
+    lib.gdn2_layer_fwd_workspace_bytes.restype = Z
+    lib.gdn2_layer_fwd_workspace_bytes.argtypes = [I] * 8
+    lib.gdn2_layer_fwd.restype = I
+    lib.gdn2_layer_fwd.argtypes = ([P, ctypes.POINTER(LayerWeights), I, ctypes.c_float] + [P] * 4
+                                   + [I] * 7 + [P, Z, P])
     _lib = lib
     return lib
 
@@ -119,6 +131,18 @@ def gdn2_chunk_fwd(q, k, v, log_alpha, b, w, S0, o, S_final, cu_seqlens, N, B, T
     return load_library().gdn2_chunk_fwd(q, k, v, log_alpha, b, w, S0, o, S_final, cu_seqlens,
                                           N, B, T, H, Dk, Dv, io, workspace, workspace_bytes,
                                           stream)
+
+
+def gdn2_layer_fwd_workspace_bytes(N, B, T, H, Dk, Dv, D, varlen):
+    return load_library().gdn2_layer_fwd_workspace_bytes(N, B, T, H, Dk, Dv, D, int(varlen))
+
+
+def gdn2_layer_fwd(x, weights, conv_len, norm_eps, S0, y, S_final, cu_seqlens, N, B, T, H, Dk,
+                   Dv, D, workspace, workspace_bytes, stream):
+    """Raw call: weights is a LayerWeights; other pointers are ints or None."""
+    return load_library().gdn2_layer_fwd(x, ctypes.byref(weights), conv_len, norm_eps, S0, y,
+                                          S_final, cu_seqlens, N, B, T, H, Dk, Dv, D, workspace,
+                                          workspace_bytes, stream)
 
 
 def gdn2_chunk_fwd_stages(q, k, v, log_alpha, b, w, S0, o, S_final, cu_seqlens, N, B, T, H, Dk,
@@ -313,3 +337,39 @@ def chunk_fwd_gate_logits(q, k, v, log_alpha, b_logit, w_logit, S0=None, cu_seql
     if st != GDN2_OK:
         raise Gdn2Error(st, "gdn2_chunk_fwd_gate_logits")
     return o, S_final
+
+
+def layer_fwd(x, W_in, conv_w, alpha_bias, norm_w, W_o, H, Dk, Dv, norm_eps=1e-6, S0=None,
+              cu_seqlens=None, y=None, S_final=None, output_final_state=True, workspace=None,
+              stream=None):
+    """Token-mixer layer forward (gdn2_layer_fwd).  x [B, T, D], W_in
+    [7*H*Dk, D] and W_o [D, H*Dv] are bfloat16; conv_w [3*H*Dk, L],
+    alpha_bias [H*Dk] and norm_w [Dv] float32.  Returns (y, S_final)."""
+    import torch
+    B, T, D = x.shape
+    for name, t in (("x", x), ("W_in", W_in), ("W_o", W_o)):
+        _check(t, name, torch.bfloat16)
+    for name, t in (("conv_w", conv_w), ("alpha_bias", alpha_bias), ("norm_w", norm_w)):
+        _check(t, name, torch.float32)
+    _check(S0, "S0", torch.float32)
+    _check(cu_seqlens, "cu_seqlens", torch.int32)
+    if W_in.shape != (7 * H * Dk, D) or W_o.shape != (D, H * Dv) or conv_w.dim() != 2 \
+            or conv_w.shape[0] != 3 * H * Dk or alpha_bias.numel() != H * Dk \
+            or norm_w.numel() != Dv:
+        raise ValueError("layer weight shapes do not match H=%d, Dk=%d, Dv=%d, D=%d"
+                         % (H, Dk, Dv, D))
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    if y is None:
+        y = torch.empty((B, T, D), dtype=torch.bfloat16, device=x.device)
+    if S_final is None and output_final_state:
+        S_final = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=x.device)
+    nbytes = gdn2_layer_fwd_workspace_bytes(N, B, T, H, Dk, Dv, D, cu_seqlens is not None)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    wts = LayerWeights(_ptr(W_in), _ptr(conv_w), _ptr(alpha_bias), _ptr(norm_w), _ptr(W_o))
+    st = gdn2_layer_fwd(_ptr(x), wts, conv_w.shape[1], float(norm_eps), _ptr(S0), _ptr(y),
+                        _ptr(S_final), _ptr(cu_seqlens), N, B, T, H, Dk, Dv, D, _ptr(workspace),
+                        workspace.numel(), _stream(stream))
+    if st != GDN2_OK:
+        raise Gdn2Error(st, "gdn2_layer_fwd")
+    return y, S_final

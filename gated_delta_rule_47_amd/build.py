@@ -20,6 +20,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgdn2.so")
 
 ARCH = "gfx950"
+ROCM_LIB = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "lib")
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 
 # Packed-fp32 VALU instructions are disabled for all device code.
@@ -56,7 +57,8 @@ def build(verbose=False, jobs=None):
             for ln in warns:
                 print(ln, file=sys.stderr)
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
+    cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs + [
+        "-L" + ROCM_LIB, "-lhipblaslt", "-Wl,-rpath," + ROCM_LIB]
     proc = subprocess.run(cmd, capture_output=True, text=True)
     if proc.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), proc.stderr))

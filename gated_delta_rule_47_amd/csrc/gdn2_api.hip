@@ -159,7 +159,7 @@ static int chunk_fwd_impl(const void *q, const void *k, const void *v, const voi
                           const void *b, const void *w, const float *S0, void *o, float *S_final,
                           const int32_t *cu_seqlens, int N, int B, int T, int H, int Dk, int Dv,
                           int io, void *workspace, size_t workspace_bytes, void *stream_ptr,
-                          int stages, bool gate_logits) {
+                          int stages, bool gate_logits, const float *alpha_bias = nullptr) {
     if (stages & ~(GDN2_STAGE_ALL | GDN2_STAGE_STORE_T)) return GDN2_ERR_INVALID_ARGUMENT;
     if (io != GDN2_F32 && io != GDN2_BF16) return GDN2_ERR_INVALID_ARGUMENT;
     if (N < 0 || B < 0 || T < 0 || H < 0 || Dk <= 0 || Dv <= 0) return GDN2_ERR_INVALID_ARGUMENT;
@@ -199,6 +199,7 @@ static int chunk_fwd_impl(const void *q, const void *k, const void *v, const voi
     a.b = static_cast<const float *>(b);
     a.w = static_cast<const float *>(w);
     a.gate_logits = gate_logits ? 1 : 0;
+    a.alpha_bias = gate_logits ? alpha_bias : nullptr;
     a.S0 = S0;
     a.o = o;
     a.S_final = S_final;
@@ -390,6 +391,149 @@ int gdn2_step(const void *q, const void *k, const void *v, const float *log_alph
     hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
     (void)hipGetLastError();  // a stale error left by other code is not ours to report
     return finish(launch_step(a, Dk, io == GDN2_BF16, stream), stream);
+}
+
+}  // extern "C"
+
+// ---- token-mixer layer -----------------------------------------------------
+
+namespace {
+
+constexpr size_t kLayerGemmWs = 32u << 20;  // hipBLASLt workspace cap
+
+struct LayerLayout {
+    size_t off_P = 0, off_al = 0, off_gt = 0, off_bl = 0, off_wl = 0, off_q = 0, off_k = 0,
+           off_v = 0, off_o = 0, off_gemm = 0, off_core = 0, core_bytes = 0, total = 0;
+};
+
+bool layer_layout(int N, int B, int T, int H, int Dk, int Dv, int D, bool varlen, LayerLayout *out) {
+    if (N < 0 || B < 0 || T < 0 || H < 0 || D <= 0 || (D & 7) || !supported_dims(Dk, Dv))
+        return false;
+    if (varlen ? B != 1 : N != B) return false;
+    const long long M = (long long)B * T;
+    if (M > INT_MAX / 2) return false;
+    const size_t hd = (size_t)H * Dk, row = hd * sizeof(bf16_t);
+    LayerLayout L;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off = align_up(off + bytes);
+        return at;
+    };
+    L.off_P = take((size_t)M * 3 * row);  // q | k | v projections
+    L.off_al = take((size_t)M * row);     // gate logits: alpha, output gate, b, w
+    L.off_gt = take((size_t)M * row);
+    L.off_bl = take((size_t)M * row);
+    L.off_wl = take((size_t)M * row);
+    L.off_q = take((size_t)M * row);
+    L.off_k = take((size_t)M * row);
+    L.off_v = take((size_t)M * row);
+    L.off_o = take((size_t)M * row);
+    L.off_gemm = take(kLayerGemmWs);
+    WorkspaceLayout C;
+    if (!workspace_layout(N, B, T, H, Dk, Dv, 2, varlen, &C)) return false;
+    L.core_bytes = C.total;
+    L.off_core = take(C.total);
+    L.total = off;
+    *out = L;
+    return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t gdn2_layer_fwd_workspace_bytes(int N, int B, int T, int H, int Dk, int Dv, int D,
+                                      int varlen) {
+    LayerLayout L;
+    return layer_layout(N, B, T, H, Dk, Dv, D, varlen != 0, &L) ? L.total : 0;
+}
+
+int gdn2_layer_fwd(const void *x, const gdn2_layer_weights *wt, int conv_len, float norm_eps,
+                   const float *S0, void *y, float *S_final, const int32_t *cu_seqlens, int N,
+                   int B, int T, int H, int Dk, int Dv, int D, void *workspace,
+                   size_t workspace_bytes, void *stream_ptr) {
+    if (N < 0 || B < 0 || T < 0 || H < 0 || Dk <= 0 || Dv <= 0 || D <= 0)
+        return GDN2_ERR_INVALID_ARGUMENT;
+    if (!supported_dims(Dk, Dv) || (D & 7)) return GDN2_ERR_UNSUPPORTED;
+    if (conv_len < 1 || conv_len > 8 || !(norm_eps >= 0.0f) || norm_eps > 3.0e38f || !wt)
+        return GDN2_ERR_INVALID_ARGUMENT;
+    const bool varlen = cu_seqlens != nullptr;
+    if (varlen ? B != 1 : N != B) return GDN2_ERR_INVALID_ARGUMENT;
+    if (N == 0 || H == 0) return GDN2_OK;
+    const long long M = (long long)B * T;
+    if (M > INT_MAX / 2) return GDN2_ERR_UNSUPPORTED;
+    const void *ptrs[] = {wt->W_in, wt->conv_w, wt->alpha_bias, wt->norm_w, wt->W_o};
+    for (const void *p : ptrs)
+        if (!p || !aligned16(p)) return GDN2_ERR_INVALID_ARGUMENT;
+    if (M > 0 && (!x || !y)) return GDN2_ERR_INVALID_ARGUMENT;
+    if ((x && !aligned16(x)) || (y && !aligned16(y)) || (S0 && !aligned16(S0)) ||
+        (S_final && !aligned16(S_final)) ||
+        (cu_seqlens && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3)))
+        return GDN2_ERR_INVALID_ARGUMENT;
+    if (y && (y == x || y == wt->W_in || y == wt->W_o || y == (const void *)S0 ||
+              y == (void *)S_final))
+        return GDN2_ERR_INVALID_ARGUMENT;
+
+    LayerLayout L;
+    if (!layer_layout(N, B, T, H, Dk, Dv, D, varlen, &L)) return GDN2_ERR_INVALID_ARGUMENT;
+    if (!workspace || workspace_bytes < L.total) return GDN2_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) return GDN2_ERR_WORKSPACE;
+
+    hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+    (void)hipGetLastError();
+    char *ws = static_cast<char *>(workspace);
+    const int HD = H * Dk, m = (int)M;
+    const bf16_t *X = static_cast<const bf16_t *>(x);
+    const bf16_t *Win = static_cast<const bf16_t *>(wt->W_in);
+    bf16_t *P = reinterpret_cast<bf16_t *>(ws + L.off_P);
+    bf16_t *al = reinterpret_cast<bf16_t *>(ws + L.off_al);
+    bf16_t *gt = reinterpret_cast<bf16_t *>(ws + L.off_gt);
+    bf16_t *bl = reinterpret_cast<bf16_t *>(ws + L.off_bl);
+    bf16_t *wl = reinterpret_cast<bf16_t *>(ws + L.off_wl);
+    void *gws = ws + L.off_gemm;
+
+    LayerArgs a{};
+    a.P = P;
+    a.ldP = 3LL * HD;
+    a.conv_w = wt->conv_w;
+    a.norm_w = wt->norm_w;
+    a.q = reinterpret_cast<bf16_t *>(ws + L.off_q);
+    a.k = reinterpret_cast<bf16_t *>(ws + L.off_k);
+    a.v = reinterpret_cast<bf16_t *>(ws + L.off_v);
+    a.o = reinterpret_cast<bf16_t *>(ws + L.off_o);
+    a.gate = gt;
+    a.z = a.q;  // q is dead once the core has run
+    a.cu_seqlens = cu_seqlens;
+    a.M = m;
+    a.H = H;
+    a.T = T;
+    a.N = N;
+    a.L = conv_len;
+    a.norm_eps = norm_eps;
+
+    if (m > 0) {
+        // q | k | v for the convolution kernel; each gate block into a
+        // contiguous [M, H*Dk] array (alpha, b and w go to the core as logits)
+        bool ok = gemm_bf16_nt(X, D, Win, D, P, a.ldP, m, 3 * HD, D, gws, kLayerGemmWs, stream);
+        bf16_t *gate_out[4] = {al, gt, bl, wl};
+        for (int blk = 0; ok && blk < 4; ++blk)
+            ok = gemm_bf16_nt(X, D, Win + (size_t)(3 + blk) * HD * D, D, gate_out[blk], HD, m, HD, D,
+                              gws, kLayerGemmWs, stream);
+        if (!ok) return GDN2_ERR_HIP;
+        if (launch_layer_mix_in(a, Dk, stream) != hipSuccess) return GDN2_ERR_HIP;
+    }
+    const int st = chunk_fwd_impl(a.q, a.k, a.v, al, bl, wl, S0, ws + L.off_o, S_final, cu_seqlens,
+                                  N, B, T, H, Dk, Dv, GDN2_BF16, ws + L.off_core, L.core_bytes,
+                                  stream_ptr, GDN2_STAGE_ALL, true, wt->alpha_bias);
+    if (st != GDN2_OK) return st;
+    if (m > 0) {
+        if (launch_layer_mix_out(a, Dk, stream) != hipSuccess) return GDN2_ERR_HIP;
+        if (!gemm_bf16_nt(a.z, HD, static_cast<const bf16_t *>(wt->W_o), HD,
+                          static_cast<bf16_t *>(y), D, m, D, HD, gws, kLayerGemmWs, stream))
+            return GDN2_ERR_HIP;
+    }
+    return finish(hipSuccess, stream);
 }
 
 }  // extern "C"

@@ -196,8 +196,9 @@ __device__ __forceinline__ float sigmoid1(float x) {
 // kBwd: also write the transposed factors a backward call needs (a.ws_Mt,
 // ws_Kh, ws_Qt, ws_Wt, ws_Tt).
 // kLogits: the gates arrive as bf16 -- log alpha itself and the logits of b
-// and w, whose sigmoid is taken here.
-template <typename E, int DK, bool kBwd, bool kLogits = false>
+// and w, whose sigmoid is taken here.  kAlphaLogit (with kLogits): log_alpha
+// holds logits too, and log alpha = logsigmoid(logit + a.alpha_bias).
+template <typename E, int DK, bool kBwd, bool kLogits = false, bool kAlphaLogit = false>
 __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(ChunkArgs a) {
     using C = PrepCfg<E, DK>;
     using M = Mma<E>;
@@ -231,6 +232,8 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(ChunkArgs a) {
     // q and k stay in their input type (exact) until used.
     f32x4 g[TPG], bk[TPG];
     Vec4<E> kk[TPG], qq[TPG];
+    f32x4 abias = zero4();
+    if constexpr (kAlphaLogit) abias = *reinterpret_cast<const f32x4 *>(a.alpha_bias + h * DK + c0);
 #pragma unroll
     for (int j = 0; j < TPG; ++j) {
         const int i = tg * TPG + j;
@@ -238,6 +241,10 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(ChunkArgs a) {
             const size_t off = ((size_t)(tok0 + i) * H + h) * DK + c0;
             if constexpr (kLogits) {
                 g[j] = to4(*reinterpret_cast<const bf16x4 *>(reinterpret_cast<const bf16 *>(a.log_alpha) + off));
+                if constexpr (kAlphaLogit) {
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) g[j][c] = logsigmoid_fast(g[j][c] + abias[c]);
+                }
                 const f32x4 bl = to4(*reinterpret_cast<const bf16x4 *>(reinterpret_cast<const bf16 *>(a.b) + off));
 #pragma unroll
                 for (int c = 0; c < 4; ++c) bk[j][c] = sigmoid1(bl[c]);
@@ -604,7 +611,10 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(ChunkArgs a) {
 
 hipError_t launch_chunk_prep(const ChunkArgs &a, int Dk, bool bf16_io, hipStream_t stream) {
     const dim3 grid((unsigned)((size_t)a.max_chunks * a.H)), block(kThreads);
-    if (bf16_io && a.gate_logits) {  // bf16 gates, sigmoid in the kernel (forward only)
+    if (bf16_io && a.gate_logits && a.alpha_bias) {  // all three gates as logits
+        if (Dk == 128) hipLaunchKernelGGL((chunk_prep_kernel<bf16, 128, false, true, true>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((chunk_prep_kernel<bf16, 64, false, true, true>), grid, block, 0, stream, a);
+    } else if (bf16_io && a.gate_logits) {  // bf16 gates, sigmoid in the kernel (forward only)
         if (Dk == 128) hipLaunchKernelGGL((chunk_prep_kernel<bf16, 128, false, true>), grid, block, 0, stream, a);
         else hipLaunchKernelGGL((chunk_prep_kernel<bf16, 64, false, true>), grid, block, 0, stream, a);
     } else if (bf16_io && a.ws_Mt) {  // backward calls (bf16 only)

@@ -24,6 +24,24 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
+// 2^x on the hardware exp2 (results outside the fp32 range saturate to 0 or
+// inf, which every caller absorbs).
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// log(1 + u) for u in [0, 1] from the hardware logarithm, with Goldberg's
+// correction log(w) * u / (w - 1), w = fl(1 + u) (D. Goldberg, "What every
+// computer scientist should know about floating-point arithmetic", 1991,
+// theorem 4), which keeps the relative accuracy for small u.
+__device__ __forceinline__ float log1p_unit(float u) {
+    const float w = 1.0f + u;
+    return w == 1.0f ? u : __logf(w) * u * __builtin_amdgcn_rcpf(w - 1.0f);
+}
+
+// log(1 / (1 + e^-z)) = min(z, 0) - log1p(e^-|z|), finite for every finite z.
+__device__ __forceinline__ float logsigmoid_fast(float z) {
+    return fminf(z, 0.0f) - log1p_unit(exp2_hw(-1.4426950408889634f * fabsf(z)));
+}
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 

@@ -39,6 +39,8 @@ struct ChunkArgs {
     float *ws_gl;
     int store_T;          // the chunk-factor kernel also stores T = (I + A)^-1
     int gate_logits;      // log_alpha, b, w are bf16: log alpha and the logits of b and w
+    const float *alpha_bias;  // with gate_logits: if set, log_alpha holds logits and
+                              // log alpha = logsigmoid(log_alpha + alpha_bias[h][c])
     bf16_t *ws_Sc;        // if set, the propagation stores every chunk's incoming
                           // state here (bf16 [chunk id][head][Dk][Dv]) and writes no o
     // If set (backward calls), the chunk-factor kernel also writes, in fragment
@@ -74,6 +76,20 @@ struct BwdArgs {
     float *dKh, *dAp, *dG;
 };
 
+// Token-mixer layer: the element-wise kernels around the core.
+struct LayerArgs {
+    const bf16_t *P;      // q | k | v projections [M][ldP], blocks of H*D columns
+    long long ldP;
+    const float *conv_w, *norm_w;
+    bf16_t *q, *k, *v;    // mix_in outputs [M][H*D]
+    const bf16_t *o;      // core output [M][H*D]
+    const bf16_t *gate;   // output-gate logits [M][H*D]
+    bf16_t *z;            // mix_out output [M][H*D]
+    const int32_t *cu_seqlens;
+    int M, H, T, N, L;
+    float norm_eps;
+};
+
 struct StepArgs {
     const void *q, *k, *v;
     const float *log_alpha, *b, *w;
@@ -89,5 +105,11 @@ hipError_t launch_chunk_prop(const ChunkArgs &a, int Dk, bool bf16_io, hipStream
 hipError_t launch_step(const StepArgs &a, int Dk, bool bf16_io, hipStream_t stream);
 // Backward (bf16 only): reverse state-gradient pass, then the two per-chunk kernels.
 hipError_t launch_chunk_bwd(const BwdArgs &a, int Dk, hipStream_t stream);
+hipError_t launch_layer_mix_in(const LayerArgs &a, int D, hipStream_t stream);
+hipError_t launch_layer_mix_out(const LayerArgs &a, int D, hipStream_t stream);
+// Row-major C[M][N] = A[M][K] B[N][K]^T in bf16 (fp32 accumulation) by
+// hipBLASLt; false if no algorithm fits ws_bytes or the library call fails.
+bool gemm_bf16_nt(const bf16_t *A, long long lda, const bf16_t *B, long long ldb, bf16_t *C,
+                  long long ldc, int M, int N, int K, void *ws, size_t ws_bytes, hipStream_t stream);
 
 }  // namespace gdn2

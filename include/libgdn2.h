@@ -253,6 +253,56 @@ int gdn2_step(const void *q, const void *k, const void *v,
               float *S, void *o, int B, int H, int Dk, int Dv, int io,
               void *stream);
 
+/*
+ * Token-mixer layer forward around the core (the iplexlaw digest, section
+ * "Procesamiento del token y entrenamiento paralelo"; gates as in section
+ * "Decisiones independientes en dos ejes"), for x [B, T, D] bf16:
+ *   P = x W_in^T split into the blocks q | k | v | alpha | gate | b | w
+ *   q, k, v = SiLU(causal depthwise conv_L(P_q, P_k, P_v))
+ *   q, k   /= sqrt(|.|^2 + 1e-6) per head (L2 normalisation over Dk)
+ *   log alpha = logsigmoid(P_alpha + alpha_bias), b = sigmoid(P_b), w = sigmoid(P_w)
+ *   o, S_final = the core recurrence (gdn2_chunk_fwd_gate_logits)
+ *   z = o / sqrt(mean_c(o^2) + norm_eps) * norm_w * sigmoid(P_gate)   per head over Dv
+ *   y = z W_o^T
+ * The convolution reads conv_w[c][j] * x_{t-L+1+j} for taps j < L, with
+ * zeros before the first token of each sequence.  Readings where the page is
+ * silent: no projection biases; the decay is a logsigmoid gate with a
+ * per-channel bias; one RMS weight vector [Dv] shared by the heads; the
+ * output gate is a sigmoid.
+ *
+ * Weights (device pointers, row-major, caller-owned, 16-byte aligned):
+ *   W_in        bf16 [7 * H * Dk, D]  (blocks of H*Dk rows in the order above)
+ *   conv_w      f32  [3 * H * Dk, conv_len]  (q, k, v channels; tap j = 0 oldest)
+ *   alpha_bias  f32  [H * Dk]
+ *   norm_w      f32  [Dv]
+ *   W_o         bf16 [D, H * Dv]
+ * Activations: x, y bf16 [B, T, D] (y must not alias x or any weight); S0,
+ * S_final, cu_seqlens, N, B, T as for gdn2_chunk_fwd.  Requirements: Dk == Dv
+ * in {64, 128}; D > 0 and a multiple of 8; 1 <= conv_len <= 8; norm_eps >= 0.
+ *
+ * The projections are bf16 GEMMs with fp32 accumulation run by hipBLASLt; the
+ * first call on a device creates that device's hipBLASLt handle and caches
+ * the chosen GEMM algorithm per shape (both kept until the process ends).
+ * All intermediates live in the caller's workspace (at least
+ * gdn2_layer_fwd_workspace_bytes, 0 on invalid sizes; varlen != 0 for packed
+ * calls).  Only bf16 is implemented.
+ */
+typedef struct gdn2_layer_weights {
+    const void *W_in;
+    const float *conv_w;
+    const float *alpha_bias;
+    const float *norm_w;
+    const void *W_o;
+} gdn2_layer_weights;
+
+size_t gdn2_layer_fwd_workspace_bytes(int N, int B, int T, int H, int Dk, int Dv, int D,
+                                      int varlen);
+
+int gdn2_layer_fwd(const void *x, const gdn2_layer_weights *weights, int conv_len,
+                   float norm_eps, const float *S0, void *y, float *S_final,
+                   const int32_t *cu_seqlens, int N, int B, int T, int H, int Dk, int Dv,
+                   int D, void *workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -111,3 +111,35 @@ def test_binding_fails_loudly_without_library(tmp_path):
             mod.load_library(str(tmp_path / "missing.so"))
         finally:
             mod._lib = mod._lib_backup
+
+
+def _layer(weights=None, **kw):
+    w = weights or g.LayerWeights(P16, P16 + 1024, P16 + 2048, P16 + 3072, P16 + 4096)
+    args = dict(x=P16 + 8192, weights=w, conv_len=4, norm_eps=1e-6, S0=None, y=P16 + 16384,
+                S_final=None, cu_seqlens=None, N=1, B=1, T=64, H=1, Dk=128, Dv=128, D=256,
+                workspace=None, workspace_bytes=0, stream=None)
+    args.update(kw)
+    return g.gdn2_layer_fwd(**args)
+
+
+def test_layer_fwd_validation():
+    assert _layer(x=None) == g.GDN2_ERR_INVALID_ARGUMENT
+    assert _layer(y=P16 + 8) == g.GDN2_ERR_INVALID_ARGUMENT               # misaligned
+    assert _layer(y=P16 + 8192) == g.GDN2_ERR_INVALID_ARGUMENT            # y aliases x
+    assert _layer(y=P16) == g.GDN2_ERR_INVALID_ARGUMENT                   # y aliases W_in
+    bad_w = g.LayerWeights(P16, None, P16 + 2048, P16 + 3072, P16 + 4096)
+    assert _layer(weights=bad_w) == g.GDN2_ERR_INVALID_ARGUMENT           # conv_w missing
+    assert _layer(conv_len=0) == g.GDN2_ERR_INVALID_ARGUMENT
+    assert _layer(conv_len=9) == g.GDN2_ERR_INVALID_ARGUMENT
+    assert _layer(norm_eps=-1.0) == g.GDN2_ERR_INVALID_ARGUMENT
+    assert _layer(norm_eps=float("nan")) == g.GDN2_ERR_INVALID_ARGUMENT
+    assert _layer(D=100) == g.GDN2_ERR_UNSUPPORTED                        # D % 8 != 0
+    assert _layer(Dk=96, Dv=96) == g.GDN2_ERR_UNSUPPORTED
+    assert _layer(N=2, B=1) == g.GDN2_ERR_INVALID_ARGUMENT
+    assert _layer() == g.GDN2_ERR_WORKSPACE
+    need = g.gdn2_layer_fwd_workspace_bytes(1, 1, 64, 1, 128, 128, 256, 0)
+    assert need > g.gdn2_chunk_fwd_workspace_bytes(1, 1, 64, 1, 128, 128, g.GDN2_BF16, 0)
+    assert _layer(workspace=P16, workspace_bytes=need - 1) == g.GDN2_ERR_WORKSPACE
+    assert g.gdn2_layer_fwd_workspace_bytes(1, 1, 64, 1, 128, 128, 100, 0) == 0
+    assert _layer(N=0, B=0) == g.GDN2_OK
+    assert _layer(H=0) == g.GDN2_OK
