@@ -9,9 +9,9 @@ gdn2_oracle.py for the citation keys.
 from .gdn2_oracle import (CHUNK, step, recurrence, chunk_factors, chunk_apply,
                           chunk_affine_map, chunked, gates_from_logits, recurrence_bwd, chunk_bwd,
                           chunked_bwd, rel_max_err)
-from . import layer_oracle
+from . import layer_oracle, swa_oracle
 
 __all__ = ["CHUNK", "step", "recurrence", "chunk_factors", "chunk_apply",
            "chunk_affine_map", "chunked", "gates_from_logits", "recurrence_bwd", "chunk_bwd",
            "chunked_bwd",
-           "rel_max_err", "layer_oracle"]
+           "rel_max_err", "layer_oracle", "swa_oracle"]

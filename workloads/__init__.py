@@ -315,3 +315,53 @@ def make_layer_inputs(wl: LayerWorkload, lengths=None, T: Optional[int] = None,
         S0 = (0.02 * _normal(rng, (N, H, Dk, Dv))).astype(np.float32)
     return dict(x=x, W_in=W_in, conv_w=conv_w, alpha_bias=alpha_bias, norm_w=norm_w, W_o=W_o,
                 S0=S0, cu_seqlens=cu, B=B_, T=T_, H=H, Dk=Dk, Dv=Dv, D=D, L=L, N=N)
+
+
+# ---------------------------------------------------------------------------
+# Sliding-window attention inputs
+# ---------------------------------------------------------------------------
+#
+# The hybrid model's attention layer over the same 16 heads of 128 and a
+# 2048-token window.  q, k, v ~ N(0, 1) in bf16 (the scale 1/sqrt(d) keeps the
+# logits ~ N(0, 1)).  Draw order: (lengths) -> q -> k -> v.  PCG64.
+
+@dataclass(frozen=True)
+class SwaWorkload:
+    name: str
+    B: int
+    T: int
+    H: int
+    D: int
+    window: int
+    seed: int
+    n_seqs: int = 0
+    len_lo: int = 0
+    len_hi: int = 0
+
+
+SWA_4K = SwaWorkload("swa_batch_B8_H16_T4096_d128_W2048", 8, 4096, 16, 128, 2048, 47006)
+
+
+def make_swa_inputs(wl: SwaWorkload, lengths=None, T: Optional[int] = None,
+                    B: Optional[int] = None, seed: Optional[int] = None):
+    """q, k, v (float32 arrays of bf16 values, [B, T, H, D]), cu_seqlens (or
+    None) and meta fields B, T, H, D, N, window."""
+    seed = wl.seed if seed is None else seed
+    rng = np.random.Generator(np.random.PCG64(seed))
+    cu = None
+    if wl.n_seqs or lengths is not None:
+        if lengths is None:
+            lengths = rng.integers(wl.len_lo, wl.len_hi, size=wl.n_seqs, endpoint=True)
+        lengths = np.asarray(lengths, dtype=np.int64)
+        cu = np.zeros(len(lengths) + 1, dtype=np.int32)
+        cu[1:] = np.cumsum(lengths)
+        B_, T_, N = 1, int(cu[-1]), len(lengths)
+    else:
+        B_ = wl.B if B is None else B
+        T_ = wl.T if T is None else T
+        N = B_
+    shape = (B_, T_, wl.H, wl.D)
+    q = bf16_round(_normal(rng, shape))
+    k = bf16_round(_normal(rng, shape))
+    v = bf16_round(_normal(rng, shape))
+    return dict(q=q, k=k, v=v, cu_seqlens=cu, B=B_, T=T_, H=wl.H, D=wl.D, N=N, window=wl.window)
