@@ -33,7 +33,8 @@ GDN2_STAGE_STORE_T = 8
 EXPORTED = ("gdn2_abi_version", "gdn2_status_string", "gdn2_chunk_fwd_workspace_bytes",
             "gdn2_chunk_fwd_workspace_layout", "gdn2_chunk_fwd", "gdn2_chunk_fwd_stages",
             "gdn2_chunk_fwd_gate_logits", "gdn2_chunk_bwd_workspace_bytes", "gdn2_chunk_bwd",
-            "gdn2_step", "gdn2_layer_fwd_workspace_bytes", "gdn2_layer_fwd")
+            "gdn2_step", "gdn2_layer_fwd_workspace_bytes", "gdn2_layer_fwd",
+            "gdn2_swa_fwd_workspace_bytes", "gdn2_swa_fwd")
 
 
 class Gdn2Error(RuntimeError):
@@ -96,6 +97,10 @@ def load_library(path=LIB_PATH):
     lib.gdn2_layer_fwd.restype = I
     lib.gdn2_layer_fwd.argtypes = ([P, ctypes.POINTER(LayerWeights), I, ctypes.c_float] + [P] * 4
                                    + [I] * 7 + [P, Z, P])
+    lib.gdn2_swa_fwd_workspace_bytes.restype = Z
+    lib.gdn2_swa_fwd_workspace_bytes.argtypes = [I, I]
+    lib.gdn2_swa_fwd.restype = I
+    lib.gdn2_swa_fwd.argtypes = [P] * 6 + [I] * 6 + [ctypes.c_float, P, Z, P]
     _lib = lib
     return lib
 
@@ -143,6 +148,17 @@ def gdn2_layer_fwd(x, weights, conv_len, norm_eps, S0, y, S_final, cu_seqlens, N
     return load_library().gdn2_layer_fwd(x, ctypes.byref(weights), conv_len, norm_eps, S0, y,
                                           S_final, cu_seqlens, N, B, T, H, Dk, Dv, D, workspace,
                                           workspace_bytes, stream)
+
+
+def gdn2_swa_fwd_workspace_bytes(N, varlen):
+    return load_library().gdn2_swa_fwd_workspace_bytes(N, int(varlen))
+
+
+def gdn2_swa_fwd(q, k, v, o, lse, cu_seqlens, N, B, T, H, D, window, scale, workspace,
+                 workspace_bytes, stream):
+    """Raw call: pointers are ints or None."""
+    return load_library().gdn2_swa_fwd(q, k, v, o, lse, cu_seqlens, N, B, T, H, D, window,
+                                        scale, workspace, workspace_bytes, stream)
 
 
 def gdn2_chunk_fwd_stages(q, k, v, log_alpha, b, w, S0, o, S_final, cu_seqlens, N, B, T, H, Dk,
@@ -373,3 +389,33 @@ def layer_fwd(x, W_in, conv_w, alpha_bias, norm_w, W_o, H, Dk, Dv, norm_eps=1e-6
     if st != GDN2_OK:
         raise Gdn2Error(st, "gdn2_layer_fwd")
     return y, S_final
+
+
+def swa_fwd(q, k, v, window, scale=None, cu_seqlens=None, o=None, lse=None, return_lse=True,
+            workspace=None, stream=None):
+    """Sliding-window attention forward (gdn2_swa_fwd).  q, k, v bfloat16
+    [B, T, H, D]; returns (o, lse) with lse float32 [B, H, T] (None if
+    return_lse is False)."""
+    import torch
+    B, T, H, D = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check(t, name, torch.bfloat16)
+    _check(cu_seqlens, "cu_seqlens", torch.int32)
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must have the same shape")
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    if scale is None:
+        scale = D ** -0.5
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
+    nbytes = gdn2_swa_fwd_workspace_bytes(N, cu_seqlens is not None)
+    if workspace is None and nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    st = gdn2_swa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens), N, B, T,
+                      H, D, int(window), float(scale), _ptr(workspace),
+                      0 if workspace is None else workspace.numel(), _stream(stream))
+    if st != GDN2_OK:
+        raise Gdn2Error(st, "gdn2_swa_fwd")
+    return o, lse

@@ -537,3 +537,63 @@ int gdn2_layer_fwd(const void *x, const gdn2_layer_weights *wt, int conv_len, fl
 }
 
 }  // extern "C"
+
+// ---- sliding-window attention ------------------------------------------------
+
+extern "C" {
+
+size_t gdn2_swa_fwd_workspace_bytes(int N, int varlen) {
+    if (N < 0) return 0;
+    return varlen ? align_up((size_t)(N + 1) * sizeof(int32_t)) : 0;
+}
+
+int gdn2_swa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+                 const int32_t *cu_seqlens, int N, int B, int T, int H, int D, int window,
+                 float scale, void *workspace, size_t workspace_bytes, void *stream_ptr) {
+    if (N < 0 || B < 0 || T < 0 || H < 0 || D <= 0) return GDN2_ERR_INVALID_ARGUMENT;
+    if (D != 64 && D != 128) return GDN2_ERR_UNSUPPORTED;
+    if (window < 1 || !(scale > 0.0f) || scale > 3.0e38f) return GDN2_ERR_INVALID_ARGUMENT;
+    const bool varlen = cu_seqlens != nullptr;
+    if (varlen ? B != 1 : N != B) return GDN2_ERR_INVALID_ARGUMENT;
+    if (N == 0 || H == 0 || T == 0) return GDN2_OK;
+    if ((long long)B * T > INT_MAX / 2) return GDN2_ERR_UNSUPPORTED;
+    const void *ptrs[] = {q, k, v, o};
+    for (const void *p : ptrs)
+        if (!p || !aligned16(p)) return GDN2_ERR_INVALID_ARGUMENT;
+    if ((lse && (reinterpret_cast<uintptr_t>(lse) & 3)) ||
+        (cu_seqlens && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3)))
+        return GDN2_ERR_INVALID_ARGUMENT;
+    if (o == q || o == k || o == v || (const void *)o == (const void *)lse)
+        return GDN2_ERR_INVALID_ARGUMENT;
+    const size_t need = gdn2_swa_fwd_workspace_bytes(N, varlen);
+    if (need && (!workspace || workspace_bytes < need)) return GDN2_ERR_WORKSPACE;
+    if (need && (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1))) return GDN2_ERR_WORKSPACE;
+
+    const long long nb = (T + kSwaBlockQueries - 1) / kSwaBlockQueries;
+    const long long items = varlen ? (long long)H * (nb + N) : (long long)B * H * nb;
+    if (items > INT_MAX / 2) return GDN2_ERR_UNSUPPORTED;
+
+    hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+    (void)hipGetLastError();
+    SwaArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.lse = lse;
+    a.cu_seqlens = cu_seqlens;
+    a.blk_start = varlen ? static_cast<const int32_t *>(workspace) : nullptr;
+    a.N = N;
+    a.B = B;
+    a.T = T;
+    a.H = H;
+    a.window = window;
+    a.scale = scale;
+    a.n_items = (int)items;
+    hipError_t err = hipSuccess;
+    if (varlen) err = launch_swa_plan(cu_seqlens, N, T, H, static_cast<int32_t *>(workspace), stream);
+    if (err == hipSuccess) err = launch_swa_fwd(a, D, stream);
+    return finish(err, stream);
+}
+
+}  // extern "C"

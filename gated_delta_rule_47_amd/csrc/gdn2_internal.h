@@ -90,6 +90,18 @@ struct LayerArgs {
     float norm_eps;
 };
 
+// Sliding-window attention forward.
+struct SwaArgs {
+    const void *q, *k, *v;   // bf16 [tokens][H][D]
+    void *o;                 // bf16 [tokens][H][D]
+    float *lse;              // [B][H][T] or nullptr
+    const int32_t *cu_seqlens;
+    const int32_t *blk_start;  // packed calls: [N+1] prefix of H * query blocks per sequence
+    int N, B, T, H, window;
+    float scale;
+    int n_items;             // grid work items (packed calls: an upper bound)
+};
+
 struct StepArgs {
     const void *q, *k, *v;
     const float *log_alpha, *b, *w;
@@ -105,6 +117,10 @@ hipError_t launch_chunk_prop(const ChunkArgs &a, int Dk, bool bf16_io, hipStream
 hipError_t launch_step(const StepArgs &a, int Dk, bool bf16_io, hipStream_t stream);
 // Backward (bf16 only): reverse state-gradient pass, then the two per-chunk kernels.
 hipError_t launch_chunk_bwd(const BwdArgs &a, int Dk, hipStream_t stream);
+hipError_t launch_swa_fwd(const SwaArgs &a, int D, hipStream_t stream);
+hipError_t launch_swa_plan(const int32_t *cu, int N, int T, int H, int32_t *blk_start,
+                           hipStream_t stream);
+constexpr int kSwaBlockQueries = 128;  // queries per workgroup of the attention kernel
 hipError_t launch_layer_mix_in(const LayerArgs &a, int D, hipStream_t stream);
 hipError_t launch_layer_mix_out(const LayerArgs &a, int D, hipStream_t stream);
 // Row-major C[M][N] = A[M][K] B[N][K]^T in bf16 (fp32 accumulation) by

@@ -303,6 +303,31 @@ int gdn2_layer_fwd(const void *x, const gdn2_layer_weights *weights, int conv_le
                    const int32_t *cu_seqlens, int N, int B, int T, int H, int Dk, int Dv,
                    int D, void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Sliding-window softmax attention, forward: the hybrid model's local
+ * attention layer core (iplexlaw digest, section "Condiciones de
+ * comparación": a 2K sliding window; gist.science summary, part
+ * "4. Architecture": SWA interleaved with the mixer).  Per sequence and head,
+ * query i attends to the keys j of the same sequence with i - window < j <= i:
+ *   o_i = sum_j softmax_j(scale * q_i . k_j) v_j,
+ *   lse_i = log sum_j exp(scale * q_i . k_j)      (natural log)
+ * One key/value head per query head; no positional encoding is applied here.
+ *   q, k, v, o  [B, T, H, D] bf16 (o must not alias an input)
+ *   lse         [B, H, T] f32, or NULL (not written)
+ *   cu_seqlens / N / B / T as for gdn2_chunk_fwd (packed: B == 1, T = total tokens)
+ *   window >= 1 (the 1.3B hybrid uses 2048), scale > 0 (1/sqrt(D) is usual)
+ *   D = 64 or 128.  Packed calls need a workspace of
+ *   gdn2_swa_fwd_workspace_bytes(N, 1) bytes (256-byte aligned); dense calls
+ *   need none (workspace may be NULL).
+ * bf16 inputs, fp32 scores, softmax statistics and accumulation (the
+ * probabilities enter the second product as bf16).
+ */
+size_t gdn2_swa_fwd_workspace_bytes(int N, int varlen);
+
+int gdn2_swa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+                 const int32_t *cu_seqlens, int N, int B, int T, int H, int D, int window,
+                 float scale, void *workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

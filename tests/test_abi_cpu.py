@@ -143,3 +143,28 @@ def test_layer_fwd_validation():
     assert g.gdn2_layer_fwd_workspace_bytes(1, 1, 64, 1, 128, 128, 100, 0) == 0
     assert _layer(N=0, B=0) == g.GDN2_OK
     assert _layer(H=0) == g.GDN2_OK
+
+
+def _swa(**kw):
+    args = dict(q=P16, k=P16 + 4096, v=P16 + 8192, o=P16 + 12288, lse=None, cu_seqlens=None, N=1,
+                B=1, T=64, H=1, D=128, window=16, scale=0.088, workspace=None, workspace_bytes=0,
+                stream=None)
+    args.update(kw)
+    return g.gdn2_swa_fwd(**args)
+
+
+def test_swa_fwd_validation():
+    assert _swa(q=None) == g.GDN2_ERR_INVALID_ARGUMENT
+    assert _swa(o=P16 + 12296) == g.GDN2_ERR_INVALID_ARGUMENT       # misaligned
+    assert _swa(o=P16) == g.GDN2_ERR_INVALID_ARGUMENT               # o aliases q
+    assert _swa(window=0) == g.GDN2_ERR_INVALID_ARGUMENT
+    assert _swa(scale=0.0) == g.GDN2_ERR_INVALID_ARGUMENT
+    assert _swa(scale=float("nan")) == g.GDN2_ERR_INVALID_ARGUMENT
+    assert _swa(D=96) == g.GDN2_ERR_UNSUPPORTED
+    assert _swa(N=2) == g.GDN2_ERR_INVALID_ARGUMENT                 # dense needs N == B
+    assert _swa(cu_seqlens=P16, N=2, B=2) == g.GDN2_ERR_INVALID_ARGUMENT
+    need = g.gdn2_swa_fwd_workspace_bytes(3, 1)
+    assert need >= 16 and g.gdn2_swa_fwd_workspace_bytes(3, 0) == 0
+    assert _swa(cu_seqlens=P16, N=3) == g.GDN2_ERR_WORKSPACE        # packed needs a workspace
+    assert _swa(cu_seqlens=P16, N=3, workspace=P16 + 16, workspace_bytes=need) == g.GDN2_ERR_WORKSPACE
+    assert _swa(T=0) == g.GDN2_OK and _swa(H=0) == g.GDN2_OK and _swa(N=0, B=0) == g.GDN2_OK
