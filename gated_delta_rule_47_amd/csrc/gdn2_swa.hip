@@ -14,8 +14,8 @@
 //   O^T += V^T P^T   (A = V^T rows from LDS, B = P straight from the S^T
 //                     accumulator registers, with the keys of each 32-wide
 //                     contraction taken in the order the accumulator holds them)
-// so the running max, the rescaling of O and the row sums need no
-// cross-lane traffic except one 4-way reduction per tile for the max.
+// so the rescaling of O and the row sums need no cross-lane traffic; the row
+// max is reduced across lanes only when it grows (lazy rescaling).
 // Workgroups are mapped XCD-contiguously: consecutive query blocks of one
 // head share most of their key window and run on the same XCD's L2.
 
@@ -28,12 +28,16 @@ namespace {
 
 constexpr float kLog2eF = 1.4426950408889634f;
 constexpr float kLn2F = 0.6931471805599453f;
+constexpr float kLazy = 8.0f;  // base-2 headroom before the running max is raised
 
 template <int D>
 struct SwaCfg {
     static constexpr int BM = kSwaBlockQueries, BN = 64, NC = D / 32, NDT = D / 16, NKT = BN / 16;
     static constexpr int LDK = D + 8;   // K tile [BN][LDK] bf16
-    static constexpr int LDV = BN + 8;  // V^T tile [D][LDV] bf16
+    // V^T tile [D][LDV] bf16.  LDV = BN + 4 (34 dwords per row) puts the 16 rows
+    // a fragment read touches on distinct bank pairs, and the transposing
+    // stores (key group fastest across lanes) on distinct banks too.
+    static constexpr int LDV = BN + 4;
     static constexpr int SZ_K = BN * LDK, SZ_V = D * LDV;  // elements
     static constexpr int KG = BN * D / 8;                  // 16-byte granules of a K tile
     static constexpr int VG = (D / 8) * (BN / 4);          // (8 dims x 4 keys) groups of a V tile
@@ -62,7 +66,8 @@ __device__ __forceinline__ void swa_load(const SwaArgs &a, int h, int s0, int s1
         const int t = min(max(k0 + key, s0), s1 - 1);
         st.kx[i] = *reinterpret_cast<const bf16x8 *>(K + (size_t)t * ld + h * D + 8 * dc);
     }
-    const int g = min(tid, C::VG - 1), dc = g % (D / 8), kg = g / (D / 8);
+    // V: thread -> (key group kg, fastest across lanes; 8-dim chunk dc)
+    const int g = min(tid, C::VG - 1), kg = g % (C::BN / 4), dc = g / (C::BN / 4);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         const int t = min(max(k0 + 4 * kg + u, s0), s1 - 1);
@@ -82,7 +87,7 @@ __device__ __forceinline__ void swa_store(bf16 *sK, bf16 *sV, int tid, const Swa
         }
     }
     if (tid < C::VG) {  // 4 keys x 8 dims -> 8 rows of V^T, 4 keys each
-        const int dc = tid % (D / 8), kg = tid / (D / 8);
+        const int kg = tid % (C::BN / 4), dc = tid / (C::BN / 4);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             bf16x4 w;
@@ -174,19 +179,45 @@ __global__ __launch_bounds__(kThreads, 2) void swa_fwd_kernel(SwaArgs a) {
         const bf16 *cK = smem + (j & 1) * BUF, *cV = cK + C::SZ_K;
 
         // ---- S^T = K Q^T: s[rt][kt] = [key 16 kt + 4 grp + r][query col] ----
+        // The K fragments of key tile kt+1 are read while the MFMAs of tile kt
+        // run (the scheduling fences keep that order).
         f32x4 s[2][C::NKT];
+        MB::frag kf[2][C::NC];
+#pragma unroll
+        for (int c = 0; c < C::NC; ++c) kf[0][c] = load_frag<bf16>(cK + 32 * c, C::LDK, lane);
 #pragma unroll
         for (int kt = 0; kt < C::NKT; ++kt) {
+            if (kt + 1 < C::NKT) {
+#pragma unroll
+                for (int c = 0; c < C::NC; ++c)
+                    kf[(kt + 1) & 1][c] = load_frag<bf16>(cK + 16 * (kt + 1) * C::LDK + 32 * c, C::LDK, lane);
+            }
+            __builtin_amdgcn_sched_barrier(0);
             f32x4 d0 = zero4(), d1 = zero4();
 #pragma unroll
             for (int c = 0; c < C::NC; ++c) {
-                const MB::frag kf = load_frag<bf16>(cK + 16 * kt * C::LDK + 32 * c, C::LDK, lane);
-                d0 = MB::mma(kf, qf[0][c], d0);
-                d1 = MB::mma(kf, qf[1][c], d1);
+                d0 = MB::mma(kf[kt & 1][c], qf[0][c], d0);
+                d1 = MB::mma(kf[kt & 1][c], qf[1][c], d1);
             }
-            s[0][kt] = d0 * cs;
-            s[1][kt] = d1 * cs;
+            __builtin_amdgcn_sched_barrier(0);
+            s[0][kt] = d0;  // raw q.k; the scale enters the exponent below
+            s[1][kt] = d1;
         }
+        // V^T fragments of the first two dim tiles, in flight through the softmax
+        // (keys in the order the S^T accumulator holds them: 4 grp .. +3 of each
+        // 16-key half of a 32-key contraction)
+        MB::frag vf[3][C::BN / 32];
+        auto load_v = [&](int dt, MB::frag (&dst)[C::BN / 32]) {
+#pragma unroll
+            for (int jj = 0; jj < C::BN / 32; ++jj) {
+                const bf16 *vr = cV + (16 * dt + col) * C::LDV + 32 * jj + 4 * grp;
+                const bf16x4 lo4 = *reinterpret_cast<const bf16x4 *>(vr);
+                const bf16x4 hi4 = *reinterpret_cast<const bf16x4 *>(vr + 16);
+                dst[jj] = MB::frag{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+            }
+        };
+        load_v(0, vf[0]);
+        load_v(1, vf[1]);
         // mask the tile unless every key is inside every query's window
         const bool full = (k0 + C::BN - 1 <= wq0) && (k0 > wq_hi - W);
         if (!full) {
@@ -203,31 +234,41 @@ __global__ __launch_bounds__(kThreads, 2) void swa_fwd_kernel(SwaArgs a) {
             }
         }
         // ---- online softmax; P packed as the B operand of O^T += V^T P^T ----
+        // The running max m (base-2 units) is raised only when a row's tile max
+        // exceeds it by more than kLazy; otherwise p = 2^(cs s - m) <= 2^kLazy,
+        // which fp32 sums and bf16 probabilities carry without loss, and the
+        // O rescaling is skipped for the whole wave.
         MB::frag pf[2][C::BN / 32];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
+            // this lane's max over its 16 keys; the row max across the four
+            // lane groups is only needed when some lane would exceed the headroom
             float mx = s[rt][0][0];
 #pragma unroll
             for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[rt][kt][r]);
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_new = fmaxf(m_run[rt], mx);
-            const float alpha = exp2_hw(m_run[rt] - m_new);
-            m_run[rt] = m_new;
+            if (__any(mx * cs > m_run[rt] + kLazy)) {
+                mx = fmaxf(mx, __shfl_xor(mx, 16));
+                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                const float m_new = fmaxf(m_run[rt], mx * cs);
+                const float alpha = exp2_hw(m_run[rt] - m_new);
+                m_run[rt] = m_new;
+                l_run[rt] *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < C::NDT; ++dt) acc[rt][dt] *= alpha;
+            }
+            const float nm = -m_run[rt];
             float ls = 0.0f;
 #pragma unroll
             for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float p = exp2_hw(s[rt][kt][r] - m_new);
+                    const float p = exp2_hw(fmaf(s[rt][kt][r], cs, nm));
                     s[rt][kt][r] = p;
                     ls += p;
                 }
-            l_run[rt] = l_run[rt] * alpha + ls;
-#pragma unroll
-            for (int dt = 0; dt < C::NDT; ++dt) acc[rt][dt] *= alpha;
+            l_run[rt] += ls;
 #pragma unroll
             for (int jj = 0; jj < C::BN / 32; ++jj) {
                 bf16x8 p8;
@@ -239,18 +280,17 @@ __global__ __launch_bounds__(kThreads, 2) void swa_fwd_kernel(SwaArgs a) {
                 pf[rt][jj] = p8;
             }
         }
-        // ---- O^T += V^T P^T: A = V^T rows (dims), keys in the same order as P ----
+        // ---- O^T += V^T P^T, the V^T fragments two dim tiles ahead ----
 #pragma unroll
         for (int dt = 0; dt < C::NDT; ++dt) {
+            if (dt + 2 < C::NDT) load_v(dt + 2, vf[(dt + 2) % 3]);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int jj = 0; jj < C::BN / 32; ++jj) {
-                const bf16 *vr = cV + (16 * dt + col) * C::LDV + 32 * jj + 4 * grp;
-                const bf16x4 lo4 = *reinterpret_cast<const bf16x4 *>(vr);
-                const bf16x4 hi4 = *reinterpret_cast<const bf16x4 *>(vr + 16);
-                const MB::frag vf = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-                acc[0][dt] = MB::mma(vf, pf[0][jj], acc[0][dt]);
-                acc[1][dt] = MB::mma(vf, pf[1][jj], acc[1][dt]);
+                acc[0][dt] = MB::mma(vf[dt % 3][jj], pf[0][jj], acc[0][dt]);
+                acc[1][dt] = MB::mma(vf[dt % 3][jj], pf[1][jj], acc[1][dt]);
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
         if (j + 1 < ntiles) {
             bf16 *nK = smem + ((j + 1) & 1) * BUF;
