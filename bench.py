@@ -45,7 +45,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-steps", type=int, default=1024)
-    ap.add_argument("--only", choices=["all", "chunk", "decode", "varlen", "bwd", "layer"],
+    ap.add_argument("--only", choices=["all", "chunk", "decode", "varlen", "bwd", "layer", "swa"],
                     default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=8,
@@ -337,6 +337,40 @@ def time_layer(inp, steps, warmup):
     return e0.elapsed_time(e1) / steps, ws.numel()
 
 
+def swa_useful_flops(lengths, H, D, window):
+    """Flops of the unmasked score pairs: 2 D for q.k and 2 D for p v per pair."""
+    pairs = 0
+    for L in lengths:
+        L = int(L)
+        full = max(0, L - window)
+        tri = min(L, window)
+        pairs += tri * (tri + 1) // 2 + full * window
+    return pairs * H * 4 * D
+
+
+def time_swa(inp, steps, warmup):
+    """Time `steps` gdn2_swa_fwd calls (events on the launch stream)."""
+    import torch
+    import gated_delta_rule_47_amd as g
+    import workloads as W
+
+    def bf(x):
+        return torch.from_numpy(W.bf16_bits(x).view(np.int16)).to("cuda").view(torch.bfloat16)
+    q, k, v = bf(inp["q"]), bf(inp["k"]), bf(inp["v"])
+    o = torch.empty_like(q)
+    lse = torch.empty((inp["B"], inp["H"], inp["T"]), dtype=torch.float32, device="cuda")
+    for _ in range(warmup):
+        g.swa_fwd(q, k, v, inp["window"], o=o, lse=lse)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        g.swa_fwd(q, k, v, inp["window"], o=o, lse=lse)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -458,6 +492,26 @@ def main():
         if "value" not in out:
             out.update({"value": M / (ms * 1e-3), "ms_per_step": ms,
                         "config": {"workload": wl.name, "pass": "layer forward"}})
+        del inp
+
+    if a.only in ("all", "swa"):
+        wl = W.SWA_4K
+        log("generating %s" % wl.name)
+        inp = W.make_swa_inputs(wl)
+        ms = time_swa(inp, max(3, a.steps // 2), 2)
+        fl = swa_useful_flops([inp["T"]] * inp["B"], inp["H"], inp["D"], inp["window"])
+        tf = fl / (ms * 1e-3) / 1e12
+        out["swa"] = {"workload": wl.name, "entry": "gdn2_swa_fwd", "ms": ms,
+                      "tokens_per_s": inp["B"] * inp["T"] / (ms * 1e-3),
+                      "roofline": {"bound": "mfma", "kernel": "swa_fwd", "achieved": tf,
+                                   "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                   "frac": tf / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                                   "alg_flops_per_launch": fl, "avg_launch_ms": ms}}
+        log("swa: %.3f ms -> %.1f TFLOP/s of unmasked attention (%.1f%% of bf16 MFMA peak)"
+            % (ms, tf, 100 * tf / MFMA_BF16_PEAK_TFLOPS))
+        if "value" not in out:
+            out.update({"value": inp["B"] * inp["T"] / (ms * 1e-3), "ms_per_step": ms,
+                        "config": {"workload": wl.name, "pass": "swa forward"}})
         del inp
 
     if a.only in ("all", "decode"):
