@@ -7,11 +7,12 @@
 //
 // One workgroup (4 waves) takes 128 consecutive queries of one (sequence,
 // head); wave w owns queries 32w .. 32w+31 as two 16-query tiles.  The keys
-// of the window are walked in tiles of 64, double-buffered in LDS (K
-// row-major, V transposed), with an online softmax in base 2.  Everything is
+// of the window are walked in tiles of 64, double-buffered in LDS (both
+// row-major, filled by direct global->LDS loads), with an online softmax in
+// base 2.  Everything is
 // computed transposed so that each lane owns one query column:
 //   S^T = K Q^T      (16x16x32 bf16 MFMA; A = K rows from LDS, B = Q in registers)
-//   O^T += V^T P^T   (A = V^T rows from LDS, B = P straight from the S^T
+//   O^T += V^T P^T   (A = V^T fragments by LDS transposing reads, B = P straight from the S^T
 //                     accumulator registers, with the keys of each 32-wide
 //                     contraction taken in the order the accumulator holds them)
 // so the rescaling of O and the row sums need no cross-lane traffic; the row
@@ -33,68 +34,47 @@ constexpr float kLazy = 8.0f;  // base-2 headroom before the running max is rais
 template <int D>
 struct SwaCfg {
     static constexpr int BM = kSwaBlockQueries, BN = 64, NC = D / 32, NDT = D / 16, NKT = BN / 16;
-    static constexpr int LDK = D + 8;   // K tile [BN][LDK] bf16
-    // V^T tile [D][LDV] bf16.  LDV = BN + 4 (34 dwords per row) puts the 16 rows
-    // a fragment read touches on distinct bank pairs, and the transposing
-    // stores (key group fastest across lanes) on distinct banks too.
-    static constexpr int LDV = BN + 4;
-    static constexpr int SZ_K = BN * LDK, SZ_V = D * LDV;  // elements
-    static constexpr int KG = BN * D / 8;                  // 16-byte granules of a K tile
-    static constexpr int VG = (D / 8) * (BN / 4);          // (8 dims x 4 keys) groups of a V tile
-    static constexpr int KPT = (KG + kThreads - 1) / kThreads;
-    static constexpr size_t SMEM = 2 * size_t(SZ_K + SZ_V) * 2;
-    static_assert(VG <= kThreads, "one V group per thread");
+    // K and V tiles are row-major [BN][D] bf16 without padding (the direct
+    // global->LDS loads fill 1 KB contiguously per wave instruction); bank
+    // conflicts are avoided by XOR-swizzling the 16-byte chunks of each row.
+    static constexpr int CPR = D / 8;                  // 16-byte chunks per row
+    static constexpr int SZ = BN * D;                  // elements per tile
+    static constexpr int LOADS = BN * CPR / 64 / 4;    // wave instructions per tile, per wave
+    static_assert(BN * CPR % 256 == 0, "tile splits evenly over 4 waves");
 };
 
+// Physical chunk of logical chunk c in row r.  K rows are read as 16-byte
+// fragments of 16 consecutive rows (c ^ (r mod CPR) keeps each phase of 8 or
+// 16 lanes on distinct banks); V rows are read by the transposing 8-byte loads,
+// 4 rows x 2 chunks per 16 lanes (c ^ 2(r mod 8) spreads them).
 template <int D>
-struct SwaStage {
-    bf16x8 kx[SwaCfg<D>::KPT];
-    bf16x8 vx[4];
-};
+__device__ __forceinline__ int k_chunk(int r, int c) { return c ^ (r & (SwaCfg<D>::CPR - 1)); }
+template <int D>
+__device__ __forceinline__ int v_chunk(int r, int c) { return c ^ ((2 * r) & (SwaCfg<D>::CPR - 2)); }
 
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// Issue the direct global->LDS loads of key tile [k0, k0+BN) (rows clamped
+// to the sequence; rows past it are masked by the caller).  Wave w fills
+// chunks [(w*LOADS + i)*64, +64) of each tile, lane t chunk +t.
 template <int D>
-__device__ __forceinline__ void swa_load(const SwaArgs &a, int h, int s0, int s1, int k0, int tid,
-                                         SwaStage<D> &st) {
+__device__ __forceinline__ void swa_issue(const SwaArgs &a, int h, int s0, int s1, int k0,
+                                          bf16 *tK, bf16 *tV, int wave, int lane) {
     using C = SwaCfg<D>;
     const bf16 *K = reinterpret_cast<const bf16 *>(a.k);
     const bf16 *V = reinterpret_cast<const bf16 *>(a.v);
     const size_t ld = (size_t)a.H * D;
 #pragma unroll
-    for (int i = 0; i < C::KPT; ++i) {
-        const int id = tid + i * kThreads;
-        const int key = min(id / (D / 8), C::BN - 1), dc = id % (D / 8);
-        const int t = min(max(k0 + key, s0), s1 - 1);
-        st.kx[i] = *reinterpret_cast<const bf16x8 *>(K + (size_t)t * ld + h * D + 8 * dc);
-    }
-    // V: thread -> (key group kg, fastest across lanes; 8-dim chunk dc)
-    const int g = min(tid, C::VG - 1), kg = g % (C::BN / 4), dc = g / (C::BN / 4);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int t = min(max(k0 + 4 * kg + u, s0), s1 - 1);
-        st.vx[u] = *reinterpret_cast<const bf16x8 *>(V + (size_t)t * ld + h * D + 8 * dc);
-    }
-}
-
-template <int D>
-__device__ __forceinline__ void swa_store(bf16 *sK, bf16 *sV, int tid, const SwaStage<D> &st) {
-    using C = SwaCfg<D>;
-#pragma unroll
-    for (int i = 0; i < C::KPT; ++i) {
-        const int id = tid + i * kThreads;
-        if (id < C::KG) {
-            const int key = id / (D / 8), dc = id % (D / 8);
-            *reinterpret_cast<bf16x8 *>(sK + key * C::LDK + 8 * dc) = st.kx[i];
-        }
-    }
-    if (tid < C::VG) {  // 4 keys x 8 dims -> 8 rows of V^T, 4 keys each
-        const int kg = tid % (C::BN / 4), dc = tid / (C::BN / 4);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            bf16x4 w;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) w[u] = st.vx[u][e];
-            *reinterpret_cast<bf16x4 *>(sV + (8 * dc + e) * C::LDV + 4 * kg) = w;
-        }
+    for (int i = 0; i < C::LOADS; ++i) {
+        const int base = (wave * C::LOADS + i) * 64, p = base + lane;
+        const int row = p / C::CPR, pc = p % C::CPR;
+        const int t = min(max(k0 + row, s0), s1 - 1);
+        const size_t g = (size_t)t * ld + h * D;
+        __builtin_amdgcn_global_load_lds(K + g + 8 * k_chunk<D>(row, pc),
+                                         (lds_void *)(tK + 8 * base), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(V + g + 8 * v_chunk<D>(row, pc),
+                                         (lds_void *)(tV + 8 * base), 16, 0, 0);
     }
 }
 
@@ -102,7 +82,7 @@ template <int D>
 __global__ __launch_bounds__(kThreads, 2) void swa_fwd_kernel(SwaArgs a) {
     using C = SwaCfg<D>;
     using MB = Mma<bf16>;
-    __shared__ __attribute__((aligned(16))) bf16 smem[2 * (C::SZ_K + C::SZ_V)];
+    __shared__ __attribute__((aligned(16))) bf16 smem[4 * C::SZ];  // 2 x (K tile, V tile)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int col = lane & 15, grp = lane >> 4;
 
@@ -142,8 +122,8 @@ __global__ __launch_bounds__(kThreads, 2) void swa_fwd_kernel(SwaArgs a) {
     const int kstart = max(s0, q0 - W + 1), kend = qlast;
     const int ntiles = (kend - kstart) / C::BN + 1;
 
-    // buffer b: K tile at smem + b * (SZ_K + SZ_V), V^T tile right after it
-    constexpr int BUF = C::SZ_K + C::SZ_V;
+    // buffer b: K tile at smem + 2 b SZ, V tile right after it
+    constexpr int BUF = 2 * C::SZ;
 
     // Q fragments (B operand of S^T = K Q^T): lane holds query col of tile rt,
     // dims 32c + 8 grp .. + 8
@@ -167,57 +147,79 @@ __global__ __launch_bounds__(kThreads, 2) void swa_fwd_kernel(SwaArgs a) {
     float m_run[2] = {-1e30f, -1e30f}, l_run[2] = {0.0f, 0.0f};
     const float cs = a.scale * kLog2eF;  // scores in base-2 units
 
-    SwaStage<D> st;
-    swa_load<D>(a, h, s0, s1, kstart, tid, st);
-    swa_store<D>(smem, smem + C::SZ_K, tid, st);
+    swa_issue<D>(a, h, s0, s1, kstart, smem, smem + C::SZ, wave, lane);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     const int wq_hi = min(wq0 + 31, s1 - 1);
     for (int j = 0; j < ntiles; ++j) {
         const int k0 = kstart + j * C::BN;
-        if (j + 1 < ntiles) swa_load<D>(a, h, s0, s1, k0 + C::BN, tid, st);
-        const bf16 *cK = smem + (j & 1) * BUF, *cV = cK + C::SZ_K;
+        const bf16 *cK = smem + (j & 1) * BUF, *cV = cK + C::SZ;
 
         // ---- S^T = K Q^T: s[rt][kt] = [key 16 kt + 4 grp + r][query col] ----
-        // The K fragments of key tile kt+1 are read while the MFMAs of tile kt
-        // run (the scheduling fences keep that order).
+        // Contraction chunk c outermost: the 8 accumulators advance together,
+        // so consecutive MFMAs are independent.  The K fragments of chunk c+1
+        // are read while the MFMAs of chunk c run (the fences keep the order).
         f32x4 s[2][C::NKT];
-        MB::frag kf[2][C::NC];
 #pragma unroll
-        for (int c = 0; c < C::NC; ++c) kf[0][c] = load_frag<bf16>(cK + 32 * c, C::LDK, lane);
-#pragma unroll
-        for (int kt = 0; kt < C::NKT; ++kt) {
-            if (kt + 1 < C::NKT) {
-#pragma unroll
-                for (int c = 0; c < C::NC; ++c)
-                    kf[(kt + 1) & 1][c] = load_frag<bf16>(cK + 16 * (kt + 1) * C::LDK + 32 * c, C::LDK, lane);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            f32x4 d0 = zero4(), d1 = zero4();
-#pragma unroll
-            for (int c = 0; c < C::NC; ++c) {
-                d0 = MB::mma(kf[kt & 1][c], qf[0][c], d0);
-                d1 = MB::mma(kf[kt & 1][c], qf[1][c], d1);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            s[0][kt] = d0;  // raw q.k; the scale enters the exponent below
-            s[1][kt] = d1;
-        }
-        // V^T fragments of the first two dim tiles, in flight through the softmax
-        // (keys in the order the S^T accumulator holds them: 4 grp .. +3 of each
-        // 16-key half of a 32-key contraction)
-        MB::frag vf[3][C::BN / 32];
-        auto load_v = [&](int dt, MB::frag (&dst)[C::BN / 32]) {
-#pragma unroll
-            for (int jj = 0; jj < C::BN / 32; ++jj) {
-                const bf16 *vr = cV + (16 * dt + col) * C::LDV + 32 * jj + 4 * grp;
-                const bf16x4 lo4 = *reinterpret_cast<const bf16x4 *>(vr);
-                const bf16x4 hi4 = *reinterpret_cast<const bf16x4 *>(vr + 16);
-                dst[jj] = MB::frag{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-            }
+        for (int kt = 0; kt < C::NKT; ++kt) s[0][kt] = s[1][kt] = zero4();
+        // K fragment (rows 16 kt .. +15, dims 32 cc .. +31): lane reads row
+        // 16 kt + col, logical chunk 4 cc + grp
+        auto load_k = [&](int kt, int cc) {
+            const int row = 16 * kt + col;
+            return *reinterpret_cast<const MB::frag *>(cK + row * D + 8 * k_chunk<D>(row, 4 * cc + grp));
         };
-        load_v(0, vf[0]);
-        load_v(1, vf[1]);
+        MB::frag kf[2][C::NKT];
+#pragma unroll
+        for (int kt = 0; kt < C::NKT; ++kt) kf[0][kt] = load_k(kt, 0);
+#pragma unroll
+        for (int c = 0; c < C::NC; ++c) {
+            if (c + 1 < C::NC) {
+#pragma unroll
+                for (int kt = 0; kt < C::NKT; ++kt)
+                    kf[(c + 1) & 1][kt] = load_k(kt, c + 1);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int kt = 0; kt < C::NKT; ++kt) {
+                s[0][kt] = MB::mma(kf[c & 1][kt], qf[0][c], s[0][kt]);
+                s[1][kt] = MB::mma(kf[c & 1][kt], qf[1][c], s[1][kt]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // (s holds raw q.k; the scale enters the exponent below)
+        // V^T fragments (keys in the order the S^T accumulator holds them: 4 grp
+        // .. +3 of each 16-key half of a 32-key contraction); the first group
+        // is read before the softmax so it is in flight meanwhile
+        // V^T fragment (dims 16 dt .. +15, keys of contraction jj): two
+        // transposing 8-byte reads of the row-major V tile.  In each group of 16
+        // lanes, lane j points at row (key) 32 jj + 4 grp + j/4 (+16), dims
+        // 16 dt + 4 (j%4) .. +3; lane i then receives dim 16 dt + i of those 4 rows.
+        auto load_v = [&](int dt, int jj) {
+            const int row = 32 * jj + 4 * grp + ((lane & 15) >> 2);
+            const int c = 2 * dt + ((lane & 3) >> 1), half = lane & 1;
+            const bf16 *p0 = cV + row * D + 8 * v_chunk<D>(row, c) + 4 * half;
+            const bf16 *p1 = cV + (row + 16) * D + 8 * v_chunk<D>(row + 16, c) + 4 * half;
+            const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4i16 *)(p0));
+            const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4i16 *)(p1));
+            typedef short v8i16 __attribute__((ext_vector_type(8)));
+            const v8i16 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            return __builtin_bit_cast(MB::frag, both);
+        };
+        constexpr int VGRP = 4;  // dim tiles per read group
+        MB::frag vf[2][VGRP];
+#pragma unroll
+        for (int u = 0; u < VGRP; ++u) vf[0][u] = load_v(u, 0);
+        // The next tile's direct loads go out only now: the compiler makes every
+        // transposing LDS read wait for all outstanding direct loads, so they
+        // are issued after the first group of V^T reads and land during the
+        // softmax and the first group of MFMAs.
+        if (j + 1 < ntiles) {
+            bf16 *nK = smem + ((j + 1) & 1) * BUF;
+            swa_issue<D>(a, h, s0, s1, k0 + C::BN, nK, nK + C::SZ, wave, lane);
+        }
         // mask the tile unless every key is inside every query's window
         const bool full = (k0 + C::BN - 1 <= wq0) && (k0 > wq_hi - W);
         if (!full) {
@@ -280,22 +282,26 @@ __global__ __launch_bounds__(kThreads, 2) void swa_fwd_kernel(SwaArgs a) {
                 pf[rt][jj] = p8;
             }
         }
-        // ---- O^T += V^T P^T, the V^T fragments two dim tiles ahead ----
+        // ---- O^T += V^T P^T: 32-key half jj outermost, 16 independent
+        // accumulators; V^T fragments read one group of 4 dim tiles ahead ----
+        constexpr int NG = (C::BN / 32) * (C::NDT / VGRP);
 #pragma unroll
-        for (int dt = 0; dt < C::NDT; ++dt) {
-            if (dt + 2 < C::NDT) load_v(dt + 2, vf[(dt + 2) % 3]);
+        for (int gi = 0; gi < NG; ++gi) {
+            const int jj = gi / (C::NDT / VGRP), d0 = (gi % (C::NDT / VGRP)) * VGRP;
+            if (gi + 1 < NG) {
+                const int jn = (gi + 1) / (C::NDT / VGRP), dn = ((gi + 1) % (C::NDT / VGRP)) * VGRP;
+#pragma unroll
+                for (int u = 0; u < VGRP; ++u) vf[(gi + 1) & 1][u] = load_v(dn + u, jn);
+            }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int jj = 0; jj < C::BN / 32; ++jj) {
-                acc[0][dt] = MB::mma(vf[dt % 3][jj], pf[0][jj], acc[0][dt]);
-                acc[1][dt] = MB::mma(vf[dt % 3][jj], pf[1][jj], acc[1][dt]);
+            for (int u = 0; u < VGRP; ++u) {
+                acc[0][d0 + u] = MB::mma(vf[gi & 1][u], pf[0][jj], acc[0][d0 + u]);
+                acc[1][d0 + u] = MB::mma(vf[gi & 1][u], pf[1][jj], acc[1][d0 + u]);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        if (j + 1 < ntiles) {
-            bf16 *nK = smem + ((j + 1) & 1) * BUF;
-            swa_store<D>(nK, nK + C::SZ_K, tid, st);
-        }
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's part of the next tile has landed
         __syncthreads();
     }
 
