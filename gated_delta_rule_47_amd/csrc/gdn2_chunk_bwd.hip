@@ -433,45 +433,52 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_state_kernel(BwdArgs ba
 // rows 16w .. 16w+15 of every 64-row result; the element-wise step runs in the
 // same accumulator layout (lane holds rows 16w + 4(l/16) + r, column l%16 of
 // each 16-column block), so dE, dEp, dQp and dKp never leave registers.
+// After dE and dA (which contract over all channels), the key channels are
+// processed in two halves of DK/2: the decay scan, the scaled tiles, dEp, dQp,
+// dKp, dQhat, the element-wise gradients and d log alpha of one half share
+// LDS with the other's, which keeps the workgroup under 80 KB of LDS (two per
+// CU).
 // ---------------------------------------------------------------------------
 template <int DK>
 struct FacCfg {
-    static constexpr int NQUAD = DK / 4, NTG = kThreads / NQUAD, TPG = kChunk / NTG;
-    static constexpr int L64 = kChunk + 8;   // bf16 [..][64]
-    static constexpr int LDKP = DK + 8;      // bf16 [..][DK]
-    static constexpr int LDG = DK + 4;       // fp32 [64][LDG]
-    static constexpr size_t SZ_CT = size_t(DK) * L64 * 2;       // [DK][64] bf16
+    static constexpr int DH = DK / 2;                 // channels per half
+    static constexpr int NQUAD = DH / 4, NTG = kThreads / NQUAD, TPG = kChunk / NTG;
+    static constexpr int L64 = kChunk + 8;            // bf16 [..][64]
+    static constexpr int LDKP = DK + 8;               // bf16 [..][DK]
+    static constexpr int LDG = DH + 4;                // fp32 [64][LDG]
+    static constexpr size_t SZ_CT = size_t(DH) * L64 * 2;       // [DH][64] bf16
     static constexpr size_t SZ_64 = size_t(kChunk) * L64 * 2;    // [64][64] bf16
-    static constexpr size_t OFF_KP = 0;                            // Kp^T
-    static constexpr size_t OFF_E = OFF_KP + SZ_CT;                // dE (bf16 [64][LDKP]), then Ep^T
-    static constexpr size_t SZ_E = (size_t(kChunk) * LDKP * 2 > SZ_CT) ? size_t(kChunk) * LDKP * 2 : SZ_CT;
-    static constexpr size_t OFF_A = OFF_E + SZ_E;                  // dA, dA^T
-    static constexpr size_t OFF_Q = OFF_A + 2 * SZ_64;             // Qp^T
-    static constexpr size_t OFF_G = OFF_Q + SZ_CT;                 // g, then dg (fp32 [64][LDG])
-    static constexpr size_t OFF_R = OFF_G + size_t(kChunk) * LDG * 4;  // small reductions
-    static constexpr size_t SZ_R = size_t(2 * NTG + 8) * DK * 4;
+    static constexpr size_t SZ_DE = size_t(kChunk) * LDKP * 2;   // dE bf16 [64][LDKP]
+    static constexpr size_t SZ_T3 = 3 * SZ_CT;                   // Kp^T, Ep^T, Qp^T of a half
+    static constexpr size_t OFF_T = 0;                           // dE, then the half's tiles
+    static constexpr size_t OFF_A = OFF_T + (SZ_DE > SZ_T3 ? SZ_DE : SZ_T3);  // dA, dA^T
+    static constexpr size_t OFF_G = OFF_A + 2 * SZ_64;           // g, then dg of a half (fp32)
+    static constexpr size_t OFF_R = OFF_G + size_t(kChunk) * LDG * 4;
+    static constexpr size_t SZ_R = size_t(2 * NTG + 4) * DH * 4 + size_t(2) * DK * 4;
     static constexpr size_t SMEM = OFF_R + SZ_R;
-    static_assert(SMEM <= 160 * 1024, "LDS");
+    static_assert(SMEM <= 80 * 1024, "two workgroups per CU");
 };
 
 template <int DK>
-__global__ __launch_bounds__(kThreads, 1) void chunk_bwd_factor_kernel(BwdArgs ba) {
+__global__ __launch_bounds__(kThreads, 2) void chunk_bwd_factor_kernel(BwdArgs ba) {
     using C = FacCfg<DK>;
     using MB = Mma<bf16>;
-    constexpr int L64 = C::L64, LDKP = C::LDKP, LDG = C::LDG, TPG = C::TPG, NKB = DK / 16, NKD = DK / 32;
+    constexpr int DH = C::DH, L64 = C::L64, LDKP = C::LDKP, LDG = C::LDG, TPG = C::TPG;
+    constexpr int NKB = DK / 16, NKD = DK / 32, NHB = DH / 16;
     const ChunkArgs &a = ba.c;
     __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
-    bf16 *sKpt = reinterpret_cast<bf16 *>(smem + C::OFF_KP);   // [c][j] = Kp[j][c]
-    bf16 *sdE = reinterpret_cast<bf16 *>(smem + C::OFF_E);     // [i][c]
-    bf16 *sEpt = sdE;                                           // [c][i] = Ep[i][c]
+    bf16 *sdE = reinterpret_cast<bf16 *>(smem + C::OFF_T);     // [i][c] (until dA is formed)
+    bf16 *sKpt = reinterpret_cast<bf16 *>(smem + C::OFF_T);    // [c][j] = Kp[j][c], half
+    bf16 *sEpt = sKpt + DH * L64;                               // [c][i] = Ep[i][c]
+    bf16 *sQpt = sEpt + DH * L64;                               // [c][i] = Qp[i][c]
     bf16 *sdA = reinterpret_cast<bf16 *>(smem + C::OFF_A);     // [i][j]
     bf16 *sdAt = sdA + kChunk * L64;                            // [j][i]
-    bf16 *sQpt = reinterpret_cast<bf16 *>(smem + C::OFF_Q);    // [c][i] = Qp[i][c]
-    float *sG = reinterpret_cast<float *>(smem + C::OFF_G);    // g, then dg [64][LDG]
-    float *sR = reinterpret_cast<float *>(smem + C::OFF_R);    // [2*NTG + 8][DK]
-    float *sGl = sR + 2 * C::NTG * DK;                          // g_last [DK]
-    float *sDG = sGl + DK;                                      // dgl [DK]
-    float *sKdk = sDG + DK;                                     // [4][DK] sum_i Khat dKhat, per wave
+    float *sG = reinterpret_cast<float *>(smem + C::OFF_G);    // g, then dg [64][LDG], half
+    float *sR = reinterpret_cast<float *>(smem + C::OFF_R);    // [2*NTG][DH] scan partials
+    float *sGl = sR + 2 * C::NTG * DH;                          // g_last [DH]
+    float *sKdk = sGl + DH;                                     // [3][DH] per-wave sums (waves 1..3)
+    float *sDG = sKdk + 3 * DH;                                 // dgl [DK]
+    float *sKdk0 = sDG + DK;                                    // wave 0's sums [DK]
 
     const int H = a.H, cid = blockIdx.x / H, h = blockIdx.x % H;
     if (a.plan && cid >= a.plan[a.N]) return;
@@ -479,7 +486,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_factor_kernel(BwdArgs b
     dense_span(a, cid, tok0, len);
     const size_t ch = (size_t)cid * H + h;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, I = wave;
-    const int qd = tid % C::NQUAD, tg = tid / C::NQUAD, c0 = 4 * qd;
+    const int qd = tid % C::NQUAD, tg = tid / C::NQUAD, cq = 4 * qd;  // channel quad within a half
     const bf16 *kin = reinterpret_cast<const bf16 *>(a.k), *qin = reinterpret_cast<const bf16 *>(a.q);
 
     for (int c = tid; c < DK; c += kThreads) sDG[c] = ba.dG[ch * DK + c];
@@ -501,6 +508,8 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_factor_kernel(BwdArgs b
             store_tile<bf16>(sdE + 16 * I * LDKP + 16 * cb, LDKP, d, lane);
         }
     }
+    // (each wave reads back only its own rows of dE: a wave-level fence suffices,
+    // but the block barrier below also orders sDG)
     __syncthreads();
     // ---- dA = -strict_tril(dZ U^T + dE W^T), both orientations --------------
     {
@@ -519,177 +528,169 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_factor_kernel(BwdArgs b
                 d[r] = j < i ? -(Ap[(size_t)i * kChunk + j] + d[r]) : 0.0f;
             }
             store_tile<bf16>(sdA + 16 * I * L64 + 16 * J, L64, d, lane);
-            store_tile_t<bf16>(sdAt + 16 * J * L64 + 16 * I, L64, d, lane);
+            store_tile_t<bf16>(sdAt + 16 * I + 16 * J * L64, L64, d, lane);
         }
     }
-    __syncthreads();  // dE (bf16) is dead: its region receives Ep^T
+    __syncthreads();  // dE (bf16) is dead: its region receives the half's tiles
 
-    // ---- cumulative log-decay (thread (qd, tg)) and the scaled tiles --------
-    f32x4 gr;
-    {
-        f32x4 g[TPG];
+    // operands of the whole chunk, loaded once
+    MB::frag fA[2], fM[2], fAt[2], fMt[2];
 #pragma unroll
-        for (int j = 0; j < TPG; ++j) {
-            const int i = tg * TPG + j;
-            g[j] = i < len ? *reinterpret_cast<const f32x4 *>(a.log_alpha + ((size_t)(tok0 + i) * H + h) * DK + c0)
-                           : zero4();
-        }
-#pragma unroll
-        for (int j = 1; j < TPG; ++j) g[j] += g[j - 1];
-        *reinterpret_cast<f32x4 *>(sR + tg * DK + c0) = g[TPG - 1];
-        __syncthreads();
-        f32x4 goff = zero4(), glast = zero4();
-#pragma unroll
-        for (int t = 0; t < C::NTG; ++t) {
-            const f32x4 tt = *reinterpret_cast<const f32x4 *>(sR + t * DK + c0);
-            if (t < tg) goff += tt;
-            glast += tt;
-        }
-        gr = 0.5f * glast;
-        if (tg == 0) *reinterpret_cast<f32x4 *>(sGl + c0) = glast;
-#pragma unroll
-        for (int j = 0; j < TPG; ++j) {
-            const int i = tg * TPG + j;
-            g[j] += goff;
-            *reinterpret_cast<f32x4 *>(sG + i * LDG + c0) = g[j];
-            f32x4 kf = zero4(), qf = zero4(), bf = zero4();
-            if (i < len) {
-                const size_t off = ((size_t)(tok0 + i) * H + h) * DK + c0;
-                const bf16x4 k4 = *reinterpret_cast<const bf16x4 *>(kin + off);
-                const bf16x4 q4 = *reinterpret_cast<const bf16x4 *>(qin + off);
-                bf = *reinterpret_cast<const f32x4 *>(a.b + off);
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    kf[c] = static_cast<float>(k4[c]);
-                    qf[c] = static_cast<float>(q4[c]);
-                }
-            }
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const float ex = __expf(g[j][c] - gr[c]), ei = __expf(gr[c] - g[j][c]);
-                sKpt[(c0 + c) * L64 + i] = static_cast<bf16>(kf[c] * ei);
-                sEpt[(c0 + c) * L64 + i] = static_cast<bf16>(bf[c] * kf[c] * ex);
-                sQpt[(c0 + c) * L64 + i] = static_cast<bf16>(qf[c] * ex);
-            }
-        }
+    for (int kk = 0; kk < 2; ++kk) {
+        fA[kk] = load_frag<bf16>(sdA + 16 * I * L64 + 32 * kk, L64, lane);
+        fM[kk] = load_frag_packed<bf16>(dMg, kChunk, I, kk, lane);
+        fAt[kk] = load_frag<bf16>(sdAt + 16 * I * L64 + 32 * kk, L64, lane);
+        fMt[kk] = load_frag_packed<bf16>(dMtg, kChunk, I, kk, lane);
     }
-    __syncthreads();
-
-    // ---- dEp = dA Kp, dQp = dM Kp, dKp = dA^T Ep + dM^T Qp --------------------
-    f32x4 dEp[NKB], dQp[NKB], dKp[NKB];
-    {
-        MB::frag fA[2], fM[2], fAt[2], fMt[2];
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            fA[kk] = load_frag<bf16>(sdA + 16 * I * L64 + 32 * kk, L64, lane);
-            fM[kk] = load_frag_packed<bf16>(dMg, kChunk, I, kk, lane);
-            fAt[kk] = load_frag<bf16>(sdAt + 16 * I * L64 + 32 * kk, L64, lane);
-            fMt[kk] = load_frag_packed<bf16>(dMtg, kChunk, I, kk, lane);
-        }
-#pragma unroll
-        for (int cb = 0; cb < NKB; ++cb) {
-            f32x4 e = zero4(), q = zero4(), k = zero4();
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const MB::frag kp = load_frag<bf16>(sKpt + 16 * cb * L64 + 32 * kk, L64, lane);
-                e = MB::mma(fA[kk], kp, e);
-                q = MB::mma(fM[kk], kp, q);
-                k = MB::mma(fAt[kk], load_frag<bf16>(sEpt + 16 * cb * L64 + 32 * kk, L64, lane), k);
-                k = MB::mma(fMt[kk], load_frag<bf16>(sQpt + 16 * cb * L64 + 32 * kk, L64, lane), k);
-            }
-            dEp[cb] = e;
-            dQp[cb] = q;
-            dKp[cb] = k;
-        }
-    }
-
-    // ---- dQhat = dO S^T (rows of block I; dO rows past the chunk are zero) ---
-    f32x4 dQh[NKB];
+    MB::frag fdO[NKD];
     {
         const bf16 *dout = reinterpret_cast<const bf16 *>(ba.dout);
-        const bf16 *Sc = ba.Sc + ch * DK * DK;
         const int row = 16 * I + (lane & 15);
-        MB::frag fdO[NKD];
 #pragma unroll
         for (int kk = 0; kk < NKD; ++kk)
             fdO[kk] = row < len ? load_frag<bf16>(dout + ((size_t)(tok0 + 16 * I) * H + h) * DK + 32 * kk,
                                                   H * DK, lane)
                                 : MB::zero();
-#pragma unroll
-        for (int cb = 0; cb < NKB; ++cb) {
-            f32x4 d = zero4();
-#pragma unroll
-            for (int kk = 0; kk < NKD; ++kk)
-                d = MB::mma(fdO[kk], load_frag<bf16>(Sc + 16 * cb * DK + 32 * kk, DK, lane), d);
-            dQh[cb] = d;
-        }
     }
-
-    // ---- element-wise gradients in the accumulator layout -------------------
+    const bf16 *Sc = ba.Sc + ch * DK * DK;
     const float *dKg = ba.dKh + ch * kChunk * DK;
     bf16 *dqo = reinterpret_cast<bf16 *>(ba.dq), *dko = reinterpret_cast<bf16 *>(ba.dk);
-#pragma unroll
-    for (int cb = 0; cb < NKB; ++cb) {
-        const int c = 16 * cb + (lane & 15);
-        const float gl_c = sGl[c], gr_c = 0.5f * gl_c, egr = __expf(gr_c);
-        float kdk = 0.0f;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int i = 16 * I + 4 * (lane >> 4) + r;
-            float dg = 0.0f;
-            if (i < len) {
-                const size_t off = ((size_t)(tok0 + i) * H + h) * DK + c;
-                const float kf = static_cast<float>(kin[off]), qf = static_cast<float>(qin[off]);
-                const float bf = a.b[off];
-                const float dKh = dKg[(size_t)i * DK + c];
-                const float gg = sG[i * LDG + c];
-                const float ex = __expf(gg - gr_c), ei = __expf(gr_c - gg);
-                const float gam = ex * egr, eK = ei * egr;
-                const float t1 = gam * dE[cb][r] + ex * dEp[cb][r];
-                const float dq = gam * dQh[cb][r] + ex * dQp[cb][r];
-                const float kpart = ei * dKp[cb][r] + eK * dKh;
-                dqo[off] = static_cast<bf16>(dq);
-                dko[off] = static_cast<bf16>(bf * t1 + kpart);
-                ba.db[off] = kf * t1;
-                dg = bf * kf * t1 + qf * dq - kf * kpart;
-                kdk += kf * eK * dKh;
-            }
-            sG[i * LDG + c] = dg;  // each element is read, then overwritten, by this lane only
-        }
-        // sum over this wave's 16 tokens: 4 per lane, then the 4 lane groups
-        kdk += __shfl_xor(kdk, 16);
-        kdk += __shfl_xor(kdk, 32);
-        if (lane < 16) sKdk[wave * DK + c] = kdk;
-    }
-    __syncthreads();
 
-    // ---- dlog_alpha_j = sum_{i>=j} dg_i + gl dgl + sum_i Khat_i dKhat_i --------
-    {
-        f32x4 dgv[TPG];
 #pragma unroll
-        for (int j = 0; j < TPG; ++j) dgv[j] = *reinterpret_cast<const f32x4 *>(sG + (tg * TPG + j) * LDG + c0);
+    for (int half = 0; half < 2; ++half) {  // unrolled: dE is indexed by half
+        const int cbase = half * DH;
+        // ---- cumulative log-decay of the half's channels, the scaled tiles ----
+        {
+            f32x4 g[TPG];
 #pragma unroll
-        for (int j = TPG - 2; j >= 0; --j) dgv[j] += dgv[j + 1];  // suffix sums inside the group
-        *reinterpret_cast<f32x4 *>(sR + (C::NTG + tg) * DK + c0) = dgv[0];
+            for (int j = 0; j < TPG; ++j) {
+                const int i = tg * TPG + j;
+                g[j] = i < len ? *reinterpret_cast<const f32x4 *>(a.log_alpha + ((size_t)(tok0 + i) * H + h) * DK + cbase + cq)
+                               : zero4();
+            }
+#pragma unroll
+            for (int j = 1; j < TPG; ++j) g[j] += g[j - 1];
+            *reinterpret_cast<f32x4 *>(sR + tg * DH + cq) = g[TPG - 1];
+            __syncthreads();
+            f32x4 goff = zero4(), glast = zero4();
+#pragma unroll
+            for (int t = 0; t < C::NTG; ++t) {
+                const f32x4 tt = *reinterpret_cast<const f32x4 *>(sR + t * DH + cq);
+                if (t < tg) goff += tt;
+                glast += tt;
+            }
+            const f32x4 gr = 0.5f * glast;
+            if (tg == 0) *reinterpret_cast<f32x4 *>(sGl + cq) = glast;
+#pragma unroll
+            for (int j = 0; j < TPG; ++j) {
+                const int i = tg * TPG + j;
+                g[j] += goff;
+                *reinterpret_cast<f32x4 *>(sG + i * LDG + cq) = g[j];
+                f32x4 kf = zero4(), qf = zero4(), bf = zero4();
+                if (i < len) {
+                    const size_t off = ((size_t)(tok0 + i) * H + h) * DK + cbase + cq;
+                    const bf16x4 k4 = *reinterpret_cast<const bf16x4 *>(kin + off);
+                    const bf16x4 q4 = *reinterpret_cast<const bf16x4 *>(qin + off);
+                    bf = *reinterpret_cast<const f32x4 *>(a.b + off);
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        kf[c] = static_cast<float>(k4[c]);
+                        qf[c] = static_cast<float>(q4[c]);
+                    }
+                }
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const float ex = __expf(g[j][c] - gr[c]), ei = __expf(gr[c] - g[j][c]);
+                    sKpt[(cq + c) * L64 + i] = static_cast<bf16>(kf[c] * ei);
+                    sEpt[(cq + c) * L64 + i] = static_cast<bf16>(bf[c] * kf[c] * ex);
+                    sQpt[(cq + c) * L64 + i] = static_cast<bf16>(qf[c] * ex);
+                }
+            }
+        }
         __syncthreads();
-        f32x4 after = zero4();
+
+        // Per 16-channel block hb: dEp = dA Kp, dQp = dM Kp, dKp = dA^T Ep +
+        // dM^T Qp and dQhat = dO S^T, then the element-wise gradients in the
+        // accumulator layout (one block's results live at a time).
 #pragma unroll
-        for (int t = 0; t < C::NTG; ++t)
-            if (t > tg) after += *reinterpret_cast<const f32x4 *>(sR + (C::NTG + t) * DK + c0);
-        f32x4 dglast;
+        for (int hb = 0; hb < NHB; ++hb) {
+            f32x4 dEp = zero4(), dQp = zero4(), dKp = zero4(), dQh = zero4();
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int cc = c0 + c;
-            dglast[c] = __expf(sGl[cc]) * sDG[cc] + sKdk[cc] + sKdk[DK + cc] + sKdk[2 * DK + cc] +
-                        sKdk[3 * DK + cc];
+            for (int kk = 0; kk < 2; ++kk) {
+                const MB::frag kp = load_frag<bf16>(sKpt + 16 * hb * L64 + 32 * kk, L64, lane);
+                dEp = MB::mma(fA[kk], kp, dEp);
+                dQp = MB::mma(fM[kk], kp, dQp);
+                dKp = MB::mma(fAt[kk], load_frag<bf16>(sEpt + 16 * hb * L64 + 32 * kk, L64, lane), dKp);
+                dKp = MB::mma(fMt[kk], load_frag<bf16>(sQpt + 16 * hb * L64 + 32 * kk, L64, lane), dKp);
+            }
+#pragma unroll
+            for (int kk = 0; kk < NKD; ++kk)
+                dQh = MB::mma(fdO[kk], load_frag<bf16>(Sc + (cbase + 16 * hb) * DK + 32 * kk, DK, lane), dQh);
+            const int cl = 16 * hb + (lane & 15), c = cbase + cl;
+            const float gl_c = sGl[cl], gr_c = 0.5f * gl_c, egr = __expf(gr_c);
+            const f32x4 dEc = dE[half * NHB + hb];
+            float kdk = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * I + 4 * (lane >> 4) + r;
+                float dg = 0.0f;
+                if (i < len) {
+                    const size_t off = ((size_t)(tok0 + i) * H + h) * DK + c;
+                    const float kf = static_cast<float>(kin[off]), qf = static_cast<float>(qin[off]);
+                    const float bf = a.b[off];
+                    const float dKh = dKg[(size_t)i * DK + c];
+                    const float gg = sG[i * LDG + cl];
+                    const float ex = __expf(gg - gr_c), ei = __expf(gr_c - gg);
+                    const float gam = ex * egr, eK = ei * egr;
+                    const float t1 = gam * dEc[r] + ex * dEp[r];
+                    const float dq = gam * dQh[r] + ex * dQp[r];
+                    const float kpart = ei * dKp[r] + eK * dKh;
+                    dqo[off] = static_cast<bf16>(dq);
+                    dko[off] = static_cast<bf16>(bf * t1 + kpart);
+                    ba.db[off] = kf * t1;
+                    dg = bf * kf * t1 + qf * dq - kf * kpart;
+                    kdk += kf * eK * dKh;
+                }
+                sG[i * LDG + cl] = dg;  // each element is read, then overwritten, by this lane only
+            }
+            // sum over this wave's 16 tokens: 4 per lane, then the 4 lane groups
+            kdk += __shfl_xor(kdk, 16);
+            kdk += __shfl_xor(kdk, 32);
+            if (lane < 16) {
+                if (wave == 0) sKdk0[c] = kdk;
+                else sKdk[(wave - 1) * DH + cl] = kdk;
+            }
         }
+        __syncthreads();
+
+        // ---- dlog_alpha_j = sum_{i>=j} dg_i + gl dgl + sum_i Khat_i dKhat_i -------
+        {
+            f32x4 dgv[TPG];
 #pragma unroll
-        for (int j = 0; j < TPG; ++j) {
-            const int i = tg * TPG + j;
-            if (i < len)
-                *reinterpret_cast<f32x4 *>(ba.dla + ((size_t)(tok0 + i) * H + h) * DK + c0) =
-                    dgv[j] + after + dglast;
+            for (int j = 0; j < TPG; ++j) dgv[j] = *reinterpret_cast<const f32x4 *>(sG + (tg * TPG + j) * LDG + cq);
+#pragma unroll
+            for (int j = TPG - 2; j >= 0; --j) dgv[j] += dgv[j + 1];  // suffix sums inside the group
+            *reinterpret_cast<f32x4 *>(sR + (C::NTG + tg) * DH + cq) = dgv[0];
+            __syncthreads();
+            f32x4 after = zero4();
+#pragma unroll
+            for (int t = 0; t < C::NTG; ++t)
+                if (t > tg) after += *reinterpret_cast<const f32x4 *>(sR + (C::NTG + t) * DH + cq);
+            f32x4 dglast;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int cl = cq + c, cc = cbase + cl;
+                dglast[c] = __expf(sGl[cl]) * sDG[cc] + sKdk0[cc] + sKdk[cl] + sKdk[DH + cl] + sKdk[2 * DH + cl];
+            }
+#pragma unroll
+            for (int j = 0; j < TPG; ++j) {
+                const int i = tg * TPG + j;
+                if (i < len)
+                    *reinterpret_cast<f32x4 *>(ba.dla + ((size_t)(tok0 + i) * H + h) * DK + cbase + cq) =
+                        dgv[j] + after + dglast;
+            }
         }
+        __syncthreads();  // the next half reuses the tiles, g and the partials
     }
 }
 
