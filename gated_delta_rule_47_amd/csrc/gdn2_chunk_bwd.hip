@@ -279,6 +279,20 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_state_kernel(BwdArgs ba
     for (int j = 0; j < 4; ++j) dMa[j] = dAp[j] = zero4();
     const bf16 *Sc = ba.Sc + ch * DK * DV;
     const bf16 *dSc = ba.dSc + ch * DK * DV;
+    // The wave's rows of W, Khat, M^T and T^T, held in registers across the
+    // slabs (reloading them per slab re-reads them from HBM once the working
+    // set of the resident workgroups has left L2).
+    MB::frag fW[NKD], fKh[NKD], fMt[2], fTt[2];
+#pragma unroll
+    for (int kk = 0; kk < NKD; ++kk) {
+        fW[kk] = load_frag_packed<bf16>(Wg, DK, I, kk, lane);
+        fKh[kk] = load_frag_packed<bf16>(Khg, DK, I, kk, lane);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        fMt[kk] = load_frag_packed<bf16>(Mtg, kChunk, I, kk, lane);
+        fTt[kk] = load_frag_packed<bf16>(Ttg, kChunk, I, kk, lane);
+    }
     // Thread t stages row c = t / TPR of S and dS' (columns CPT (t % TPR) .. of
     // each slab) and accumulates dgl[c] = sum_v dS'[c][v] S[c][v] over the slabs.
     constexpr int TPR = kThreads / DK, CPT = SW / TPR;
@@ -333,14 +347,14 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_state_kernel(BwdArgs ba
             f32x4 ws = zero4(), du = zero4();
 #pragma unroll
             for (int kk = 0; kk < NKD; ++kk) {
-                ws = MB::mma(load_frag_packed<bf16>(Wg, DK, I, kk, lane),
+                ws = MB::mma(fW[kk],
                              load_frag<bf16>(sSt + 16 * cb * LDKP + 32 * kk, LDKP, lane), ws);
-                du = MB::mma(load_frag_packed<bf16>(Khg, DK, I, kk, lane),
+                du = MB::mma(fKh[kk],
                              load_frag<bf16>(sdSt + 16 * cb * LDKP + 32 * kk, LDKP, lane), du);
             }
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
-                du = MB::mma(load_frag_packed<bf16>(Mtg, kChunk, I, kk, lane),
+                du = MB::mma(fMt[kk],
                              load_frag<bf16>(sdOt + 16 * cb * L64 + 32 * kk, L64, lane), du);
             // U tile in accumulator order straight from the workspace.
             const bf16x4 u4 = *reinterpret_cast<const bf16x4 *>(
@@ -360,7 +374,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_state_kernel(BwdArgs ba
             f32x4 dz = zero4();
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
-                dz = MB::mma(load_frag_packed<bf16>(Ttg, kChunk, I, kk, lane),
+                dz = MB::mma(fTt[kk],
                              load_frag<bf16>(sdUt + 16 * cb * L64 + 32 * kk, L64, lane), dz);
             store_tile<bf16>(sdZ + 16 * I * LSW + 16 * cb, LSW, dz, lane);
 #pragma unroll
