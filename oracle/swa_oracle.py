@@ -72,3 +72,21 @@ def swa_fwd(q, k, v, window, scale=None, cu_seqlens=None, heads=None):
             o[row, t0:t1, h] = (p / den) @ v[row, t0:t1, h]
             lse[row, h, t0:t1] = (m + np.log(den))[:, 0]
     return o, lse
+
+
+def swa_layer_fwd(x, W_qkv, W_o, H, D, window, scale=None, cu_seqlens=None):
+    """The attention layer of the hybrid model around swa_fwd: q, k, v are
+    the three row blocks of one projection x W_qkv^T (W_qkv [3 H D, Dm], rows
+    q | k | v, no biases), attention over the window, then y = o W_o^T
+    (W_o [Dm, H D]).  Reading: the pages name only the window, so the layer
+    is the plain projection-attention-projection form with no positional
+    encoding, normalisation or gate.  Returns (y [B, T, Dm], lse [B, H, T])."""
+    x, W_qkv, W_o = _f64(x), _f64(W_qkv), _f64(W_o)
+    B, T, Dm = x.shape
+    HD = H * D
+    P = x @ W_qkv.T
+    q = P[..., :HD].reshape(B, T, H, D)
+    k = P[..., HD:2 * HD].reshape(B, T, H, D)
+    v = P[..., 2 * HD:].reshape(B, T, H, D)
+    o, lse = swa_fwd(q, k, v, window, scale=scale, cu_seqlens=cu_seqlens)
+    return o.reshape(B, T, HD) @ W_o.T, lse

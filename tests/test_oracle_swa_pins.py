@@ -81,3 +81,19 @@ def test_packed_equals_separate():
         o1, l1 = SO.swa_fwd(inp["q"][:, sl], inp["k"][:, sl], inp["v"][:, sl], 5)
         np.testing.assert_allclose(o[:, sl], o1, rtol=1e-14, atol=1e-15)
         np.testing.assert_allclose(lse[:, :, sl], l1, rtol=1e-14, atol=1e-15)
+
+
+def test_swa_layer_matches_torch_composition():
+    """The layer around the attention: torch float64 linear + windowed
+    scaled_dot_product_attention + linear."""
+    wl = W.SwaLayerWorkload("tiny_layer", 2, 19, 2, 4, 6, 5, 77)
+    inp = W.make_swa_layer_inputs(wl)
+    y, _ = SO.swa_layer_fwd(inp["x"], inp["W_qkv"], inp["W_o"], 2, 4, 5)
+    t = {k_: torch.from_numpy(np.asarray(inp[k_], dtype=np.float64)) for k_ in ("x", "W_qkv", "W_o")}
+    P = F.linear(t["x"], t["W_qkv"])
+    q, k, v = (z.reshape(2, 19, 2, 4).transpose(1, 2) for z in torch.split(P, 8, dim=-1))
+    i = torch.arange(19)[:, None]
+    j = torch.arange(19)[None, :]
+    o = F.scaled_dot_product_attention(q, k, v, attn_mask=(j <= i) & (j > i - 5))
+    y_ref = F.linear(o.transpose(1, 2).reshape(2, 19, 8), t["W_o"]).numpy()
+    np.testing.assert_allclose(y, y_ref, rtol=1e-12, atol=1e-13)

@@ -365,3 +365,44 @@ def make_swa_inputs(wl: SwaWorkload, lengths=None, T: Optional[int] = None,
     k = bf16_round(_normal(rng, shape))
     v = bf16_round(_normal(rng, shape))
     return dict(q=q, k=k, v=v, cu_seqlens=cu, B=B_, T=T_, H=wl.H, D=wl.D, N=N, window=wl.window)
+
+
+# Sliding-window attention layer: x ~ N(0, 1) [B, T, Dm] bf16; W_qkv ~
+# N(0, 1/Dm) [3 H D, Dm] bf16; W_o ~ N(0, 1/(H D)) [Dm, H D] bf16.  Draw order:
+# (lengths) -> x -> W_qkv -> W_o.  PCG64.
+
+@dataclass(frozen=True)
+class SwaLayerWorkload:
+    name: str
+    B: int
+    T: int
+    H: int
+    D: int
+    Dm: int
+    window: int
+    seed: int
+
+
+SWA_LAYER_4K = SwaLayerWorkload("swa_layer_B8_H16_T4096_d128_D2048_W2048", 8, 4096, 16, 128, 2048,
+                                2048, 47007)
+
+
+def make_swa_layer_inputs(wl: SwaLayerWorkload, lengths=None, T: Optional[int] = None,
+                          B: Optional[int] = None):
+    rng = np.random.Generator(np.random.PCG64(wl.seed))
+    cu = None
+    if lengths is not None:
+        lengths = np.asarray(lengths, dtype=np.int64)
+        cu = np.zeros(len(lengths) + 1, dtype=np.int32)
+        cu[1:] = np.cumsum(lengths)
+        B_, T_, N = 1, int(cu[-1]), len(lengths)
+    else:
+        B_ = wl.B if B is None else B
+        T_ = wl.T if T is None else T
+        N = B_
+    HD = wl.H * wl.D
+    x = bf16_round(_normal(rng, (B_, T_, wl.Dm)))
+    W_qkv = bf16_round(_normal(rng, (3 * HD, wl.Dm)) * np.float32(1.0 / np.sqrt(wl.Dm)))
+    W_o = bf16_round(_normal(rng, (wl.Dm, HD)) * np.float32(1.0 / np.sqrt(HD)))
+    return dict(x=x, W_qkv=W_qkv, W_o=W_o, cu_seqlens=cu, B=B_, T=T_, H=wl.H, D=wl.D, Dm=wl.Dm,
+                N=N, window=wl.window)
