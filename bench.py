@@ -371,6 +371,33 @@ def time_swa(inp, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
+def time_swa_layer(inp, steps, warmup):
+    """Time `steps` gdn2_swa_layer_fwd calls (events on the launch stream)."""
+    import torch
+    import gated_delta_rule_47_amd as g
+    import workloads as W
+
+    def bf(x):
+        return torch.from_numpy(W.bf16_bits(x).view(np.int16)).to("cuda").view(torch.bfloat16)
+    x, Wq, Wo = bf(inp["x"]), bf(inp["W_qkv"]), bf(inp["W_o"])
+    B, T, H, D, Dm = inp["B"], inp["T"], inp["H"], inp["D"], inp["Dm"]
+    ws = torch.empty(g.gdn2_swa_layer_fwd_workspace_bytes(B, B, T, H, D, Dm, 0), dtype=torch.uint8,
+                     device="cuda")
+    y = torch.empty((B, T, Dm), dtype=torch.bfloat16, device="cuda")
+    call = lambda: g.swa_layer_fwd(x, Wq, Wo, H, D, inp["window"], y=y, return_lse=False,
+                                   workspace=ws)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -509,6 +536,18 @@ def main():
                                    "alg_flops_per_launch": fl, "avg_launch_ms": ms}}
         log("swa: %.3f ms -> %.1f TFLOP/s of unmasked attention (%.1f%% of bf16 MFMA peak)"
             % (ms, tf, 100 * tf / MFMA_BF16_PEAK_TFLOPS))
+        del inp
+        # the attention layer around it (projections on hipBLASLt)
+        lw = W.SWA_LAYER_4K
+        li = W.make_swa_layer_inputs(lw)
+        lms = time_swa_layer(li, max(3, a.steps // 2), 2)
+        M = li["B"] * li["T"]
+        gemm = 2 * M * li["Dm"] * 3 * li["H"] * li["D"] + 2 * M * li["H"] * li["D"] * li["Dm"]
+        out["swa"]["layer"] = {"workload": lw.name, "entry": "gdn2_swa_layer_fwd", "ms": lms,
+                               "tokens_per_s": M / (lms * 1e-3), "gemm_flops": gemm,
+                               "mfma_TFLOPs_over_whole_layer": (gemm + fl) / (lms * 1e-3) / 1e12}
+        log("swa layer: %.3f ms -> %.3e tokens/s" % (lms, M / (lms * 1e-3)))
+        inp = None
         if "value" not in out:
             out.update({"value": inp["B"] * inp["T"] / (ms * 1e-3), "ms_per_step": ms,
                         "config": {"workload": wl.name, "pass": "swa forward"}})

@@ -34,7 +34,8 @@ EXPORTED = ("gdn2_abi_version", "gdn2_status_string", "gdn2_chunk_fwd_workspace_
             "gdn2_chunk_fwd_workspace_layout", "gdn2_chunk_fwd", "gdn2_chunk_fwd_stages",
             "gdn2_chunk_fwd_gate_logits", "gdn2_chunk_bwd_workspace_bytes", "gdn2_chunk_bwd",
             "gdn2_step", "gdn2_layer_fwd_workspace_bytes", "gdn2_layer_fwd",
-            "gdn2_swa_fwd_workspace_bytes", "gdn2_swa_fwd")
+            "gdn2_swa_fwd_workspace_bytes", "gdn2_swa_fwd", "gdn2_swa_layer_fwd_workspace_bytes",
+            "gdn2_swa_layer_fwd")
 
 
 class Gdn2Error(RuntimeError):
@@ -101,6 +102,10 @@ def load_library(path=LIB_PATH):
     lib.gdn2_swa_fwd_workspace_bytes.argtypes = [I, I]
     lib.gdn2_swa_fwd.restype = I
     lib.gdn2_swa_fwd.argtypes = [P] * 6 + [I] * 6 + [ctypes.c_float, P, Z, P]
+    lib.gdn2_swa_layer_fwd_workspace_bytes.restype = Z
+    lib.gdn2_swa_layer_fwd_workspace_bytes.argtypes = [I] * 7
+    lib.gdn2_swa_layer_fwd.restype = I
+    lib.gdn2_swa_layer_fwd.argtypes = [P] * 6 + [I] * 7 + [ctypes.c_float, P, Z, P]
     _lib = lib
     return lib
 
@@ -159,6 +164,17 @@ def gdn2_swa_fwd(q, k, v, o, lse, cu_seqlens, N, B, T, H, D, window, scale, work
     """Raw call: pointers are ints or None."""
     return load_library().gdn2_swa_fwd(q, k, v, o, lse, cu_seqlens, N, B, T, H, D, window,
                                         scale, workspace, workspace_bytes, stream)
+
+
+def gdn2_swa_layer_fwd_workspace_bytes(N, B, T, H, D, Dm, varlen):
+    return load_library().gdn2_swa_layer_fwd_workspace_bytes(N, B, T, H, D, Dm, int(varlen))
+
+
+def gdn2_swa_layer_fwd(x, W_qkv, W_o, y, lse, cu_seqlens, N, B, T, H, D, Dm, window, scale,
+                       workspace, workspace_bytes, stream):
+    """Raw call: pointers are ints or None."""
+    return load_library().gdn2_swa_layer_fwd(x, W_qkv, W_o, y, lse, cu_seqlens, N, B, T, H, D, Dm,
+                                              window, scale, workspace, workspace_bytes, stream)
 
 
 def gdn2_chunk_fwd_stages(q, k, v, log_alpha, b, w, S0, o, S_final, cu_seqlens, N, B, T, H, Dk,
@@ -419,3 +435,32 @@ def swa_fwd(q, k, v, window, scale=None, cu_seqlens=None, o=None, lse=None, retu
     if st != GDN2_OK:
         raise Gdn2Error(st, "gdn2_swa_fwd")
     return o, lse
+
+
+def swa_layer_fwd(x, W_qkv, W_o, H, D, window, scale=None, cu_seqlens=None, y=None, lse=None,
+                  return_lse=True, workspace=None, stream=None):
+    """Sliding-window attention layer (gdn2_swa_layer_fwd).  x [B, T, Dm],
+    W_qkv [3 H D, Dm], W_o [Dm, H D], all bfloat16.  Returns (y, lse)."""
+    import torch
+    B, T, Dm = x.shape
+    for name, t in (("x", x), ("W_qkv", W_qkv), ("W_o", W_o)):
+        _check(t, name, torch.bfloat16)
+    _check(cu_seqlens, "cu_seqlens", torch.int32)
+    if W_qkv.shape != (3 * H * D, Dm) or W_o.shape != (Dm, H * D):
+        raise ValueError("weight shapes do not match H=%d, D=%d, Dm=%d" % (H, D, Dm))
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    if scale is None:
+        scale = D ** -0.5
+    if y is None:
+        y = torch.empty((B, T, Dm), dtype=torch.bfloat16, device=x.device)
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, T), dtype=torch.float32, device=x.device)
+    nbytes = gdn2_swa_layer_fwd_workspace_bytes(N, B, T, H, D, Dm, cu_seqlens is not None)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    st = gdn2_swa_layer_fwd(_ptr(x), _ptr(W_qkv), _ptr(W_o), _ptr(y), _ptr(lse), _ptr(cu_seqlens),
+                            N, B, T, H, D, Dm, int(window), float(scale), _ptr(workspace),
+                            workspace.numel(), _stream(stream))
+    if st != GDN2_OK:
+        raise Gdn2Error(st, "gdn2_swa_layer_fwd")
+    return y, lse

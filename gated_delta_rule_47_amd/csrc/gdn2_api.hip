@@ -540,40 +540,20 @@ int gdn2_layer_fwd(const void *x, const gdn2_layer_weights *wt, int conv_len, fl
 
 // ---- sliding-window attention ------------------------------------------------
 
-extern "C" {
+namespace {
 
-size_t gdn2_swa_fwd_workspace_bytes(int N, int varlen) {
-    if (N < 0) return 0;
-    return varlen ? align_up((size_t)(N + 1) * sizeof(int32_t)) : 0;
-}
-
-int gdn2_swa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+// q rows are ldq elements apart, k and v rows ldkv apart (H*D when contiguous).
+int swa_fwd_impl(const void *q, const void *k, const void *v, void *o, float *lse,
                  const int32_t *cu_seqlens, int N, int B, int T, int H, int D, int window,
-                 float scale, void *workspace, size_t workspace_bytes, void *stream_ptr) {
-    if (N < 0 || B < 0 || T < 0 || H < 0 || D <= 0) return GDN2_ERR_INVALID_ARGUMENT;
-    if (D != 64 && D != 128) return GDN2_ERR_UNSUPPORTED;
-    if (window < 1 || !(scale > 0.0f) || scale > 3.0e38f) return GDN2_ERR_INVALID_ARGUMENT;
+                 float scale, long long ldq, long long ldkv, void *workspace,
+                 size_t workspace_bytes, hipStream_t stream) {
     const bool varlen = cu_seqlens != nullptr;
-    if (varlen ? B != 1 : N != B) return GDN2_ERR_INVALID_ARGUMENT;
-    if (N == 0 || H == 0 || T == 0) return GDN2_OK;
-    if ((long long)B * T > INT_MAX / 2) return GDN2_ERR_UNSUPPORTED;
-    const void *ptrs[] = {q, k, v, o};
-    for (const void *p : ptrs)
-        if (!p || !aligned16(p)) return GDN2_ERR_INVALID_ARGUMENT;
-    if ((lse && (reinterpret_cast<uintptr_t>(lse) & 3)) ||
-        (cu_seqlens && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3)))
-        return GDN2_ERR_INVALID_ARGUMENT;
-    if (o == q || o == k || o == v || (const void *)o == (const void *)lse)
-        return GDN2_ERR_INVALID_ARGUMENT;
-    const size_t need = gdn2_swa_fwd_workspace_bytes(N, varlen);
+    const size_t need = varlen ? align_up((size_t)(N + 1) * sizeof(int32_t)) : 0;
     if (need && (!workspace || workspace_bytes < need)) return GDN2_ERR_WORKSPACE;
     if (need && (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1))) return GDN2_ERR_WORKSPACE;
-
     const long long nb = (T + kSwaBlockQueries - 1) / kSwaBlockQueries;
     const long long items = varlen ? (long long)H * (nb + N) : (long long)B * H * nb;
     if (items > INT_MAX / 2) return GDN2_ERR_UNSUPPORTED;
-
-    hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
     (void)hipGetLastError();
     SwaArgs a{};
     a.q = q;
@@ -590,10 +570,134 @@ int gdn2_swa_fwd(const void *q, const void *k, const void *v, void *o, float *ls
     a.window = window;
     a.scale = scale;
     a.n_items = (int)items;
+    a.ldq = ldq;
+    a.ldkv = ldkv;
     hipError_t err = hipSuccess;
     if (varlen) err = launch_swa_plan(cu_seqlens, N, T, H, static_cast<int32_t *>(workspace), stream);
     if (err == hipSuccess) err = launch_swa_fwd(a, D, stream);
     return finish(err, stream);
+}
+
+bool swa_common_args_ok(int N, int B, int T, int H, int D, int window, float scale,
+                        const int32_t *cu_seqlens, int *status) {
+    *status = GDN2_OK;
+    if (N < 0 || B < 0 || T < 0 || H < 0 || D <= 0) *status = GDN2_ERR_INVALID_ARGUMENT;
+    else if (D != 64 && D != 128) *status = GDN2_ERR_UNSUPPORTED;
+    else if (window < 1 || !(scale > 0.0f) || scale > 3.0e38f) *status = GDN2_ERR_INVALID_ARGUMENT;
+    else if (cu_seqlens ? B != 1 : N != B) *status = GDN2_ERR_INVALID_ARGUMENT;
+    else if ((long long)B * T > INT_MAX / 2) *status = GDN2_ERR_UNSUPPORTED;
+    else if (cu_seqlens && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3)) *status = GDN2_ERR_INVALID_ARGUMENT;
+    return *status == GDN2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t gdn2_swa_fwd_workspace_bytes(int N, int varlen) {
+    if (N < 0) return 0;
+    return varlen ? align_up((size_t)(N + 1) * sizeof(int32_t)) : 0;
+}
+
+int gdn2_swa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+                 const int32_t *cu_seqlens, int N, int B, int T, int H, int D, int window,
+                 float scale, void *workspace, size_t workspace_bytes, void *stream_ptr) {
+    int st;
+    if (!swa_common_args_ok(N, B, T, H, D, window, scale, cu_seqlens, &st)) return st;
+    if (N == 0 || H == 0 || T == 0) return GDN2_OK;
+    const void *ptrs[] = {q, k, v, o};
+    for (const void *p : ptrs)
+        if (!p || !aligned16(p)) return GDN2_ERR_INVALID_ARGUMENT;
+    if (lse && (reinterpret_cast<uintptr_t>(lse) & 3)) return GDN2_ERR_INVALID_ARGUMENT;
+    if (o == q || o == k || o == v || (const void *)o == (const void *)lse)
+        return GDN2_ERR_INVALID_ARGUMENT;
+    return swa_fwd_impl(q, k, v, o, lse, cu_seqlens, N, B, T, H, D, window, scale,
+                        (long long)H * D, (long long)H * D, workspace, workspace_bytes,
+                        static_cast<hipStream_t>(stream_ptr));
+}
+
+}  // extern "C"
+
+// ---- sliding-window attention layer --------------------------------------------
+
+namespace {
+
+struct SwaLayerLayout {
+    size_t off_P = 0, off_O = 0, off_gemm = 0, off_plan = 0, plan_bytes = 0, total = 0;
+};
+
+bool swa_layer_layout(int N, int B, int T, int H, int D, int Dm, bool varlen, SwaLayerLayout *out) {
+    if (N < 0 || B < 0 || T < 0 || H < 0 || Dm <= 0 || (Dm & 7) || (D != 64 && D != 128))
+        return false;
+    if (varlen ? B != 1 : N != B) return false;
+    const long long M = (long long)B * T;
+    if (M > INT_MAX / 2) return false;
+    const size_t row = (size_t)H * D * sizeof(bf16_t);
+    SwaLayerLayout L;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off = align_up(off + bytes);
+        return at;
+    };
+    L.off_P = take((size_t)M * 3 * row);
+    L.off_O = take((size_t)M * row);
+    L.off_gemm = take(kLayerGemmWs);
+    L.plan_bytes = varlen ? align_up((size_t)(N + 1) * sizeof(int32_t)) : 0;
+    L.off_plan = take(L.plan_bytes);
+    L.total = off;
+    *out = L;
+    return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t gdn2_swa_layer_fwd_workspace_bytes(int N, int B, int T, int H, int D, int Dm, int varlen) {
+    SwaLayerLayout L;
+    return swa_layer_layout(N, B, T, H, D, Dm, varlen != 0, &L) ? L.total : 0;
+}
+
+int gdn2_swa_layer_fwd(const void *x, const void *W_qkv, const void *W_o, void *y, float *lse,
+                       const int32_t *cu_seqlens, int N, int B, int T, int H, int D, int Dm,
+                       int window, float scale, void *workspace, size_t workspace_bytes,
+                       void *stream_ptr) {
+    int st;
+    if (!swa_common_args_ok(N, B, T, H, D, window, scale, cu_seqlens, &st)) return st;
+    if (Dm <= 0) return GDN2_ERR_INVALID_ARGUMENT;
+    if (Dm & 7) return GDN2_ERR_UNSUPPORTED;
+    if (N == 0 || H == 0 || T == 0) return GDN2_OK;
+    const void *ptrs[] = {x, W_qkv, W_o, y};
+    for (const void *p : ptrs)
+        if (!p || !aligned16(p)) return GDN2_ERR_INVALID_ARGUMENT;
+    if (lse && (reinterpret_cast<uintptr_t>(lse) & 3)) return GDN2_ERR_INVALID_ARGUMENT;
+    if (y == x || y == W_qkv || y == W_o || (const void *)y == (const void *)lse)
+        return GDN2_ERR_INVALID_ARGUMENT;
+    SwaLayerLayout L;
+    if (!swa_layer_layout(N, B, T, H, D, Dm, cu_seqlens != nullptr, &L))
+        return GDN2_ERR_INVALID_ARGUMENT;
+    if (!workspace || workspace_bytes < L.total) return GDN2_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) return GDN2_ERR_WORKSPACE;
+
+    hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+    (void)hipGetLastError();
+    char *ws = static_cast<char *>(workspace);
+    const int HD = H * D, m = B * T;
+    bf16_t *P = reinterpret_cast<bf16_t *>(ws + L.off_P);
+    bf16_t *O = reinterpret_cast<bf16_t *>(ws + L.off_O);
+    void *gws = ws + L.off_gemm;
+    // q | k | v in one GEMM; the attention reads them as strided rows
+    if (!gemm_bf16_nt(static_cast<const bf16_t *>(x), Dm, static_cast<const bf16_t *>(W_qkv), Dm, P,
+                      3LL * HD, m, 3 * HD, Dm, gws, kLayerGemmWs, stream))
+        return GDN2_ERR_HIP;
+    st = swa_fwd_impl(P, P + HD, P + 2 * HD, O, lse, cu_seqlens, N, B, T, H, D, window, scale,
+                      3LL * HD, 3LL * HD, ws + L.off_plan, L.plan_bytes, stream);
+    if (st != GDN2_OK) return st;
+    if (!gemm_bf16_nt(O, HD, static_cast<const bf16_t *>(W_o), HD, static_cast<bf16_t *>(y), Dm, m,
+                      Dm, HD, gws, kLayerGemmWs, stream))
+        return GDN2_ERR_HIP;
+    return finish(hipSuccess, stream);
 }
 
 }  // extern "C"

@@ -100,6 +100,8 @@ struct SwaArgs {
     int N, B, T, H, window;
     float scale;
     int n_items;             // grid work items (packed calls: an upper bound)
+    long long ldq, ldkv;     // elements between consecutive tokens of q, and of k and v
+                             // (H*D when contiguous; the layer reads its projections)
 };
 
 struct StepArgs {

@@ -64,7 +64,7 @@ __device__ __forceinline__ void swa_issue(const SwaArgs &a, int h, int s0, int s
     using C = SwaCfg<D>;
     const bf16 *K = reinterpret_cast<const bf16 *>(a.k);
     const bf16 *V = reinterpret_cast<const bf16 *>(a.v);
-    const size_t ld = (size_t)a.H * D;
+    const size_t ld = (size_t)a.ldkv;
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
         const int base = (wave * C::LOADS + i) * 64, p = base + lane;
@@ -128,7 +128,7 @@ __global__ __launch_bounds__(kThreads, 2) void swa_fwd_kernel(SwaArgs a) {
     // Q fragments (B operand of S^T = K Q^T): lane holds query col of tile rt,
     // dims 32c + 8 grp .. + 8
     const bf16 *Q = reinterpret_cast<const bf16 *>(a.q);
-    const size_t ld = (size_t)a.H * D;
+    const size_t ldq = (size_t)a.ldq, ld = (size_t)a.H * D;  // ld: o
     const int wq0 = q0 + 32 * wave;  // this wave's first query
     MB::frag qf[2][C::NC];
 #pragma unroll
@@ -136,7 +136,7 @@ __global__ __launch_bounds__(kThreads, 2) void swa_fwd_kernel(SwaArgs a) {
         const int t = min(wq0 + 16 * rt + col, s1 - 1);
 #pragma unroll
         for (int c = 0; c < C::NC; ++c)
-            qf[rt][c] = *reinterpret_cast<const bf16x8 *>(Q + (size_t)t * ld + h * D + 32 * c + 8 * grp);
+            qf[rt][c] = *reinterpret_cast<const bf16x8 *>(Q + (size_t)t * ldq + h * D + 32 * c + 8 * grp);
     }
 
     f32x4 acc[2][C::NDT];  // O^T: [dim 16 dt + 4 grp + r][query col]

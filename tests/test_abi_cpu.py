@@ -168,3 +168,24 @@ def test_swa_fwd_validation():
     assert _swa(cu_seqlens=P16, N=3) == g.GDN2_ERR_WORKSPACE        # packed needs a workspace
     assert _swa(cu_seqlens=P16, N=3, workspace=P16 + 16, workspace_bytes=need) == g.GDN2_ERR_WORKSPACE
     assert _swa(T=0) == g.GDN2_OK and _swa(H=0) == g.GDN2_OK and _swa(N=0, B=0) == g.GDN2_OK
+
+
+def _swa_layer(**kw):
+    args = dict(x=P16, W_qkv=P16 + 4096, W_o=P16 + 8192, y=P16 + 12288, lse=None, cu_seqlens=None,
+                N=1, B=1, T=64, H=1, D=128, Dm=256, window=16, scale=0.088, workspace=None,
+                workspace_bytes=0, stream=None)
+    args.update(kw)
+    return g.gdn2_swa_layer_fwd(**args)
+
+
+def test_swa_layer_fwd_validation():
+    assert _swa_layer(x=None) == g.GDN2_ERR_INVALID_ARGUMENT
+    assert _swa_layer(y=P16) == g.GDN2_ERR_INVALID_ARGUMENT          # y aliases x
+    assert _swa_layer(Dm=100) == g.GDN2_ERR_UNSUPPORTED
+    assert _swa_layer(D=96) == g.GDN2_ERR_UNSUPPORTED
+    assert _swa_layer(window=0) == g.GDN2_ERR_INVALID_ARGUMENT
+    assert _swa_layer() == g.GDN2_ERR_WORKSPACE
+    need = g.gdn2_swa_layer_fwd_workspace_bytes(1, 1, 64, 1, 128, 256, 0)
+    assert need > 0 and g.gdn2_swa_layer_fwd_workspace_bytes(1, 1, 64, 1, 128, 100, 0) == 0
+    assert _swa_layer(workspace=P16, workspace_bytes=need - 1) == g.GDN2_ERR_WORKSPACE
+    assert _swa_layer(T=0) == g.GDN2_OK and _swa_layer(H=0) == g.GDN2_OK

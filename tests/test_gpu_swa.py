@@ -76,3 +76,38 @@ def test_swa_full_size_sampled():
         el = float(np.abs(lse[b, h] - lse_ref[0, h]).max())
         log("%s (%d, %d): err_o %.3e err_lse %.3e" % (wl.name, b, h, eo, el))
         assert eo <= TOL_O and el <= TOL_LSE
+
+
+def _run_layer(inp):
+    import torch
+    y, lse = g.swa_layer_fwd(dev(inp["x"], W.BF16), dev(inp["W_qkv"], W.BF16),
+                             dev(inp["W_o"], W.BF16), inp["H"], inp["D"], inp["window"],
+                             cu_seqlens=dev(inp["cu_seqlens"]))
+    torch.cuda.synchronize()
+    return host(y), host(lse)
+
+
+@pytest.mark.parametrize("lengths", [None, [1, 130, 0, 300, 7]])
+def test_swa_layer(lengths):
+    """The projection-attention-projection layer; the projections are bf16
+    GEMMs (rounded to bf16 before the attention), so the bound is the layer's
+    2e-2 on y; lse within 2e-2 (its logits come from bf16-rounded q, k)."""
+    wl = W.SwaLayerWorkload("swa_layer_small", 2, 200, 2, 128, 256, 64, 9900)
+    inp = W.make_swa_layer_inputs(wl, lengths=lengths)
+    y, lse = _run_layer(inp)
+    y_ref, lse_ref = SO.swa_layer_fwd(inp["x"], inp["W_qkv"], inp["W_o"], inp["H"], inp["D"],
+                                      inp["window"], cu_seqlens=inp["cu_seqlens"])
+    ey, el = O.rel_max_err(y, y_ref), float(np.abs(lse - lse_ref).max())
+    log("swa layer lengths=%s: err_y %.3e err_lse %.3e" % (lengths, ey, el))
+    assert ey <= 2e-2 and el <= 2e-2
+
+
+def test_swa_layer_full_size_row():
+    inp = W.make_swa_layer_inputs(W.SWA_LAYER_4K)
+    y, _ = _run_layer(inp)
+    r = 6
+    y_ref, _ = SO.swa_layer_fwd(inp["x"][r:r + 1], inp["W_qkv"], inp["W_o"], inp["H"], inp["D"],
+                                inp["window"])
+    ey = O.rel_max_err(y[r:r + 1], y_ref)
+    log("%s row %d: err_y %.3e" % (W.SWA_LAYER_4K.name, r, ey))
+    assert ey <= 2e-2
