@@ -527,6 +527,7 @@ def main():
         inp = W.make_swa_inputs(wl)
         ms = time_swa(inp, max(3, a.steps // 2), 2)
         fl = swa_useful_flops([inp["T"]] * inp["B"], inp["H"], inp["D"], inp["window"])
+        swa_tokens = inp["B"] * inp["T"]
         tf = fl / (ms * 1e-3) / 1e12
         out["swa"] = {"workload": wl.name, "entry": "gdn2_swa_fwd", "ms": ms,
                       "tokens_per_s": inp["B"] * inp["T"] / (ms * 1e-3),
@@ -547,11 +548,10 @@ def main():
                                "tokens_per_s": M / (lms * 1e-3), "gemm_flops": gemm,
                                "mfma_TFLOPs_over_whole_layer": (gemm + fl) / (lms * 1e-3) / 1e12}
         log("swa layer: %.3f ms -> %.3e tokens/s" % (lms, M / (lms * 1e-3)))
-        inp = None
+        del li
         if "value" not in out:
-            out.update({"value": inp["B"] * inp["T"] / (ms * 1e-3), "ms_per_step": ms,
+            out.update({"value": swa_tokens / (ms * 1e-3), "ms_per_step": ms,
                         "config": {"workload": wl.name, "pass": "swa forward"}})
-        del inp
 
     if a.only in ("all", "decode"):
         wl = W.DECODE
