@@ -711,7 +711,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_factor_kernel(BwdArgs b
 template <int D>
 static void launch_bwd_d(const BwdArgs &a, hipStream_t stream) {
     const int chains = a.c.N * a.c.H, groups = (chains + 7) / 8;
-    const int dvs = (D >= 64 && chains >= 128) ? 64 : (chains >= 64 ? 32 : 16);
+    const int dvs = (D >= 64 && chains >= 256) ? 64 : (chains >= 64 ? 32 : 16);
     const dim3 block(kThreads);
     if (dvs == 64)
         hipLaunchKernelGGL((chunk_bwd_rev_kernel<D, 64>), dim3(groups * 8 * (D / 64)), block, 0, stream, a);
