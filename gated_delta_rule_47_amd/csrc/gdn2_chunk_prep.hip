@@ -94,14 +94,43 @@ __device__ __forceinline__ void stage_copy_out(E *dst, const E *img, int tid) {
             *reinterpret_cast<const u32x4 *>(src + (size_t)stage_slot(t) * 16);
 }
 
-// acc += X[16x16] * Y[16x16], fp32, X row-major; Y[k][n] read at Y[k*ysk + n*ysn].
-__device__ __forceinline__ f32x4 mma16_f32(f32x4 acc, const float *X, int ldx, const float *Y,
-                                           int ysk, int ysn, int lane) {
+// acc += X[16x16] * Y[16x16] in fp32, with X[m][k] read at X[m*xsm + k*xsk] and
+// Y[k][n] at Y[k*ysk + n*ysn] (either operand may be stored transposed).
+__device__ __forceinline__ f32x4 mma16_f32(f32x4 acc, const float *X, int xsm, int xsk,
+                                           const float *Y, int ysk, int ysn, int lane) {
 #pragma unroll
     for (int kk = 0; kk < 16; kk += 4) {
-        const float a = X[(lane & 15) * ldx + kk + (lane >> 4)];
+        const float a = X[(lane & 15) * xsm + (kk + (lane >> 4)) * xsk];
         const float b = Y[(kk + (lane >> 4)) * ysk + (lane & 15) * ysn];
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+    }
+    return acc;
+}
+
+// The channel-major tile (rows = channels, columns = the chunk's tokens) keeps
+// the 16-byte token granule g of channel row c at granule g ^ ((c / 16) mod 8).
+// The XOR is uniform over each 16-row MFMA tile, so operand reads see the plain
+// padded layout, and it spreads the transposing stores of the thread map
+// (32 lanes on 32 different channels, one granule each) over all banks.
+template <typename E>
+__device__ __forceinline__ int et_col(int c, int t) {
+    constexpr int G = 16 / sizeof(E);
+    return (((t / G) ^ ((c >> 4) & 7)) * G) + t % G;
+}
+
+// acc += A[16 x K] * B[16 x K]^T from row-major tiles with k contiguous, where
+// an operand with swizzle s != 0 is a channel-major tile row block whose
+// granules are permuted by XOR with s (see et_col).
+template <typename E>
+__device__ __forceinline__ f32x4 mma_tile_swz(f32x4 acc, const E *A, int lda, int swa, const E *B,
+                                              int ldb, int swb, int K, int lane) {
+    using M = Mma<E>;
+    constexpr int G = 16 / sizeof(E);
+    for (int kk = 0; kk < K; kk += M::KS) {
+        const int k = kk + M::KPL * (lane >> 4);
+        const int ka = (((k / G) ^ swa) * G) + k % G, kb = (((k / G) ^ swb) * G) + k % G;
+        acc = M::mma(*reinterpret_cast<const typename M::frag *>(A + (lane & 15) * lda + ka),
+                     *reinterpret_cast<const typename M::frag *>(B + (lane & 15) * ldb + kb), acc);
     }
     return acc;
 }
@@ -154,11 +183,23 @@ __device__ __forceinline__ f32x4 to4(bf16x4 x) {
                  static_cast<float>(x[3])};
 }
 
-// Store n (a multiple of 4) consecutive values as E.
+// Store the n (a multiple of 4) tokens t0.. of channel c into the channel-major
+// tile (row pointer `row`), in the granule order of et_col.
 template <typename E, int n>
-__device__ __forceinline__ void store_run(E *p, const float *x) {
+__device__ __forceinline__ void store_run_et(E *row, int c, int t0, const float *x) {
+    if constexpr (sizeof(E) == 2 && n % 8 == 0) {  // whole granules: one 16-byte store each
 #pragma unroll
-    for (int i = 0; i < n; i += 4) store4<E>(p + i, f32x4{x[i], x[i + 1], x[i + 2], x[i + 3]});
+        for (int i = 0; i < n; i += 8) {
+            bf16x8 v;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = static_cast<bf16>(x[i + u]);
+            *reinterpret_cast<bf16x8 *>(row + et_col<E>(c, t0 + i)) = v;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < n; i += 4)
+            store4<E>(row + et_col<E>(c, t0 + i), f32x4{x[i], x[i + 1], x[i + 2], x[i + 3]});
+    }
 }
 
 // Lower-triangle 16x16 tiles (I >= J) in a fixed order, dealt to the 4 waves
@@ -332,7 +373,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(ChunkArgs a) {
         float et[TPG];
 #pragma unroll
         for (int j = 0; j < TPG; ++j) et[j] = bk[j][c];
-        store_run<E, TPG>(sEt + (c0 + c) * LDC + tg * TPG, et);
+        store_run_et<E, TPG>(sEt + (c0 + c) * LDC, c0 + c, tg * TPG, et);
     }
     if constexpr (kBwd) {  // backward calls: Khat token-major and Qhat^T, fragment order
         E *KhG = reinterpret_cast<E *>(a.ws_Kh) + ch * kChunk * DK;
@@ -469,7 +510,10 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(ChunkArgs a) {
         if (t < 10) {
             int I, J;
             lower_tile(t, I, J);
-            store_tile_t<float>(sA + 16 * I * LDA + 16 * J, LDA, accA[u], lane);
+            // A_IJ row-major below the diagonal; the diagonal blocks transposed
+            // (A_II^T), so that the substitution below reads columns as rows.
+            if (I == J) store_tile<float>(sA + 16 * I * LDA + 16 * I, LDA, accA[u], lane);
+            else store_tile_t<float>(sA + 16 * I * LDA + 16 * J, LDA, accA[u], lane);
         }
     }
     // T as E (sTb, row-major) is written block by block by the solve below;
@@ -486,18 +530,21 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(ChunkArgs a) {
     __syncthreads();
 
     // ---- stage 2b: T = (I + A)^-1 in fp32, in place ------------------------
-    // T_II overwrites A_II; T_IJ (I > J) is stored transposed in the unused
-    // upper block (J, I), so every A_IK stays readable.
+    // Diagonal blocks: forward substitution, one column c of T_II per lane,
+    // eliminating one unknown at a time (so the updates of the later rows are
+    // independent of each other); column j of A_II is row j of the stored
+    // A_II^T.  T_II then overwrites the block, row-major.
     if (wave == 0) {
         const int I = lane >> 4, c = lane & 15;
         float *Ab = sA + 16 * I * LDA + 16 * I;
         float x[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            float s = (i == c) ? 1.0f : 0.0f;
+        for (int i = 0; i < 16; ++i) x[i] = (i == c) ? 1.0f : 0.0f;
 #pragma unroll
-            for (int j = 0; j < i; ++j) s -= Ab[i * LDA + j] * x[j];
-            x[i] = s;
+        for (int j = 0; j < 15; ++j) {
+            const float *colj = Ab + j * LDA;  // A_II[i][j] at colj[i]
+#pragma unroll
+            for (int i = j + 1; i < 16; ++i) x[i] -= colj[i] * x[j];
         }
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -506,27 +553,51 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(ChunkArgs a) {
         }
     }
     __syncthreads();
-    // Off-diagonal blocks, level s = I - J:  T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ.
-#pragma unroll
-    for (int s = 1; s < 4; ++s) {
-        const int J = wave, I = wave + s;
-        if (I < 4) {
-            f32x4 acc = zero4();
-            for (int K = J; K < I; ++K) {
-                // T_KJ: diagonal block in place, else stored transposed at (J, K).
-                const float *Y = (K == J) ? sA + 16 * J * LDA + 16 * J : sA + 16 * J * LDA + 16 * K;
-                const int ysk = (K == J) ? LDA : 1, ysn = (K == J) ? 1 : LDA;
-                acc = mma16_f32(acc, sA + 16 * I * LDA + 16 * K, LDA, Y, ysk, ysn, lane);
-            }
-            float *X = sS + wave * 16 * LDX;
-            store_tile<float>(X, LDX, acc, lane);
+    // Off-diagonal blocks, T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ, grouped as
+    // 2x2 super-blocks T = [[Ta, 0], [Tc, Tb]] with Tc = -Tb (Ac Ta): three
+    // dependent phases of at most two 16x16 products per wave.  T_IJ (I > J)
+    // is stored transposed in the free upper block (J, I); sS slot w holds
+    // wave w's intermediate X blocks.
+    {
+        auto blk = [&](int I, int J) { return sA + 16 * I * LDA + 16 * J; };
+        const float *T10 = blk(0, 1), *T32 = blk(2, 3);  // transposed: X[m][k] at X[k*LDA + m]
+        auto slot = [&](int w) { return sS + w * 16 * LDX; };
+        auto put_T = [&](int I, int J, f32x4 t) {
+            store_tile_t<float>(sA + 16 * J * LDA + 16 * I, LDA, t, lane);
+            store_tile<E>(sTb + 16 * I * LDC + 16 * J, LDC, t, lane);
+        };
+        if (wave < 2) {  // T_10 (wave 0), T_32 (wave 1) = -T_II (A_IJ T_JJ)
+            const int J = 2 * wave, I = J + 1;
+            store_tile<float>(slot(wave), LDX, mma16_f32(zero4(), blk(I, J), LDA, 1, blk(J, J), LDA, 1, lane),
+                              lane);
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            const f32x4 t = mma16_f32(zero4(), sA + 16 * I * LDA + 16 * I, LDA, X, LDX, 1, lane);
-            // store -t transposed into block (J, I): element (m, n) of T_IJ at [16J+n][16I+m]
-            store_tile_t<float>(sA + 16 * J * LDA + 16 * I, LDA, -t, lane);
-            store_tile<E>(sTb + 16 * I * LDC + 16 * J, LDC, -t, lane);
+            put_T(I, J, -mma16_f32(zero4(), blk(I, I), LDA, 1, slot(wave), LDX, 1, lane));
+        } else {  // X_21 (wave 2), X_31 (wave 3) = A_I1 T_11
+            store_tile<float>(slot(wave), LDX, mma16_f32(zero4(), blk(wave, 1), LDA, 1, blk(1, 1), LDA, 1, lane),
+                              lane);
+        }
+        __syncthreads();
+        if (wave < 2) {  // X_20 (wave 0), X_30 (wave 1) = A_I0 T_00 + A_I1 T_10
+            const int I = 2 + wave;
+            f32x4 x = mma16_f32(zero4(), blk(I, 0), LDA, 1, blk(0, 0), LDA, 1, lane);
+            x = mma16_f32(x, blk(I, 1), LDA, 1, T10, 1, LDA, lane);
+            store_tile<float>(slot(wave), LDX, x, lane);
+        } else if (wave == 2) {  // T_21 = -T_22 X_21
+            put_T(2, 1, -mma16_f32(zero4(), blk(2, 2), LDA, 1, slot(2), LDX, 1, lane));
+        } else {  // T_31 = -(T_32 X_21 + T_33 X_31)
+            f32x4 t = mma16_f32(zero4(), T32, 1, LDA, slot(2), LDX, 1, lane);
+            t = mma16_f32(t, blk(3, 3), LDA, 1, slot(3), LDX, 1, lane);
+            put_T(3, 1, -t);
+        }
+        __syncthreads();
+        if (wave == 0) {  // T_20 = -T_22 X_20
+            put_T(2, 0, -mma16_f32(zero4(), blk(2, 2), LDA, 1, slot(0), LDX, 1, lane));
+        } else if (wave == 1) {  // T_30 = -(T_32 X_20 + T_33 X_30)
+            f32x4 t = mma16_f32(zero4(), T32, 1, LDA, slot(0), LDX, 1, lane);
+            t = mma16_f32(t, blk(3, 3), LDA, 1, slot(1), LDX, 1, lane);
+            put_T(3, 0, -t);
         }
         __syncthreads();
     }
@@ -563,12 +634,12 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(ChunkArgs a) {
             for (int I = 0; I < 4; ++I) {
                 constexpr int KS = M::KS;
                 const int K = ((16 * (I + 1) + KS - 1) / KS) * KS;
-                f32x4 acc = mma_tile_k<E>(zero4(), sEt + 16 * cblk * LDC, LDC, sTb + 16 * I * LDC,
-                                          LDC, K, lane);
+                f32x4 acc = mma_tile_swz<E>(zero4(), sEt + 16 * cblk * LDC, LDC, cblk & 7,
+                                            sTb + 16 * I * LDC, LDC, 0, K, lane);
                 store4_frag<E>(Wg, DK, 16 * I + (lane & 15), 16 * cblk + 4 * (lane >> 4), acc);
                 if constexpr (kBwd) {  // W^T: the same tile with the operands swapped
-                    const f32x4 t = mma_tile_k<E>(zero4(), sTb + 16 * I * LDC, LDC, sEt + 16 * cblk * LDC,
-                                                  LDC, K, lane);
+                    const f32x4 t = mma_tile_swz<E>(zero4(), sTb + 16 * I * LDC, LDC, 0,
+                                                    sEt + 16 * cblk * LDC, LDC, cblk & 7, K, lane);
                     store4_frag<E>(reinterpret_cast<E *>(a.ws_Wt) + ch * DK * kChunk, kChunk,
                                    16 * cblk + (lane & 15), 16 * I + 4 * (lane >> 4), t);
                 }
@@ -587,7 +658,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(ChunkArgs a) {
             else wv = zw[j][c];
             zt[j] = wv * elem<E>(zv[j], c);
         }
-        store_run<E, TPG>(sEt + (c0 + c) * LDC + tg * TPG, zt);
+        store_run_et<E, TPG>(sEt + (c0 + c) * LDC, c0 + c, tg * TPG, zt);
     }
     __syncthreads();
 
@@ -602,8 +673,8 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(ChunkArgs a) {
         const int K = ((16 * (I + 1) + KS - 1) / KS) * KS;
 #pragma unroll
         for (int cb = 0; cb < NCBU; ++cb) {
-            f32x4 acc = mma_tile_k<E>(zero4(), sTb + 16 * I * LDC, LDC, sEt + 16 * cb * LDC, LDC, K,
-                                      lane);
+            f32x4 acc = mma_tile_swz<E>(zero4(), sTb + 16 * I * LDC, LDC, 0, sEt + 16 * cb * LDC, LDC,
+                                        cb & 7, K, lane);
             store4<E>(Ug + ((I * NCBU + cb) * 64 + lane) * 4, acc);
         }
     }
