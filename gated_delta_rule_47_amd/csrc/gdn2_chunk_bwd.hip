@@ -453,6 +453,19 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_state_kernel(BwdArgs ba
 // LDS with the other's, which keeps the workgroup under 80 KB of LDS (two per
 // CU).
 // ---------------------------------------------------------------------------
+// The half's channel-major tiles (rows = channels, columns = the chunk's
+// tokens) keep the 16-byte token granule g of row c at granule
+// g ^ ((c / 16) mod 8): uniform over each 16-row MFMA tile, so operand reads
+// keep the padded layout's bank spread, while the stores of a thread's token
+// run for 16 different channels land on different banks.
+__device__ __forceinline__ int fac_col(int c, int t) { return (((t >> 3) ^ ((c >> 4) & 7)) << 3) + (t & 7); }
+
+// Operand fragment kk (tokens 32kk ..) of the 16-row block starting at `tile`
+// (row block rb of a swizzled half tile).
+__device__ __forceinline__ bf16x8 load_frag_fac(const bf16 *tile, int ld, int rb, int kk, int lane) {
+    return *reinterpret_cast<const bf16x8 *>(tile + (lane & 15) * ld + (((4 * kk + (lane >> 4)) ^ (rb & 7)) << 3));
+}
+
 template <int DK>
 struct FacCfg {
     static constexpr int DH = DK / 2;                 // channels per half
@@ -498,6 +511,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_factor_kernel(BwdArgs b
     if (a.plan && cid >= a.plan[a.N]) return;
     int tok0, len;
     dense_span(a, cid, tok0, len);
+    if (len <= 0) return;  // (a malformed table only) no token: nothing to write
     const size_t ch = (size_t)cid * H + h;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, I = wave;
     const int qd = tid % C::NQUAD, tg = tid / C::NQUAD, cq = 4 * qd;  // channel quad within a half
@@ -507,9 +521,36 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_factor_kernel(BwdArgs b
     const bf16 *dWtg = ba.dWt + ch * DK * kChunk;
     const bf16 *dMg = ba.dM + ch * kChunk * kChunk, *dMtg = ba.dMt + ch * kChunk * kChunk;
 
-    // ---- dE = T^T dW (rows of block I), kept in registers and as bf16 --------
     const bf16 *Ttg = reinterpret_cast<const bf16 *>(a.ws_Tt) + ch * kChunk * kChunk;
     const bf16 *Wg = reinterpret_cast<const bf16 *>(a.ws_W) + ch * kChunk * DK;
+    // Global operands of dA and of the per-half products, issued before dE so
+    // that their loads are in flight together.  Token rows past the chunk's end
+    // read row 0 (always valid) and are zeroed or skipped where used.
+    MB::frag fWd[4][NKD], fM[2], fMt[2], fdO[NKD];
+    float apv[4][4];
+    {
+        const float *Ap = ba.dAp + ch * kChunk * kChunk;
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+#pragma unroll
+            for (int kk = 0; kk < NKD; ++kk) fWd[J][kk] = load_frag_packed<bf16>(Wg, DK, J, kk, lane);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                apv[J][r] = Ap[(size_t)(16 * I + 4 * (lane >> 4) + r) * kChunk + 16 * J + (lane & 15)];
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            fM[kk] = load_frag_packed<bf16>(dMg, kChunk, I, kk, lane);
+            fMt[kk] = load_frag_packed<bf16>(dMtg, kChunk, I, kk, lane);
+        }
+        const bf16 *dout = reinterpret_cast<const bf16 *>(ba.dout);
+        const int row = 16 * I + (lane & 15);
+        const bf16 *src = dout + ((size_t)(tok0 + (row < len ? row : 0)) * H + h) * DK + 8 * (lane >> 4);
+#pragma unroll
+        for (int kk = 0; kk < NKD; ++kk) fdO[kk] = *reinterpret_cast<const MB::frag *>(src + 32 * kk);
+    }
+
+    // ---- dE = T^T dW (rows of block I), kept in registers and as bf16 --------
     f32x4 dE[NKB];
     {
         const MB::frag t0 = load_frag_packed<bf16>(Ttg, kChunk, I, 0, lane);
@@ -527,7 +568,6 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_factor_kernel(BwdArgs b
     __syncthreads();
     // ---- dA = -strict_tril(dZ U^T + dE W^T), both orientations --------------
     {
-        const float *Ap = ba.dAp + ch * kChunk * kChunk;
         MB::frag fe_[NKD];
 #pragma unroll
         for (int kk = 0; kk < NKD; ++kk) fe_[kk] = load_frag<bf16>(sdE + 16 * I * LDKP + 32 * kk, LDKP, lane);
@@ -535,11 +575,11 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_factor_kernel(BwdArgs b
         for (int J = 0; J < 4; ++J) {
             f32x4 d = zero4();
 #pragma unroll
-            for (int kk = 0; kk < NKD; ++kk) d = MB::mma(fe_[kk], load_frag_packed<bf16>(Wg, DK, J, kk, lane), d);
+            for (int kk = 0; kk < NKD; ++kk) d = MB::mma(fe_[kk], fWd[J][kk], d);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = 16 * I + 4 * (lane >> 4) + r, j = 16 * J + (lane & 15);
-                d[r] = j < i ? -(Ap[(size_t)i * kChunk + j] + d[r]) : 0.0f;
+                d[r] = j < i ? -(apv[J][r] + d[r]) : 0.0f;
             }
             store_tile<bf16>(sdA + 16 * I * L64 + 16 * J, L64, d, lane);
             store_tile_t<bf16>(sdAt + 16 * I + 16 * J * L64, L64, d, lane);
@@ -548,23 +588,15 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_factor_kernel(BwdArgs b
     __syncthreads();  // dE (bf16) is dead: its region receives the half's tiles
 
     // operands of the whole chunk, loaded once
-    MB::frag fA[2], fM[2], fAt[2], fMt[2];
+    MB::frag fA[2], fAt[2];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
         fA[kk] = load_frag<bf16>(sdA + 16 * I * L64 + 32 * kk, L64, lane);
-        fM[kk] = load_frag_packed<bf16>(dMg, kChunk, I, kk, lane);
         fAt[kk] = load_frag<bf16>(sdAt + 16 * I * L64 + 32 * kk, L64, lane);
-        fMt[kk] = load_frag_packed<bf16>(dMtg, kChunk, I, kk, lane);
     }
-    MB::frag fdO[NKD];
-    {
-        const bf16 *dout = reinterpret_cast<const bf16 *>(ba.dout);
-        const int row = 16 * I + (lane & 15);
+    if (16 * I + (lane & 15) >= len) {  // dO rows past the chunk's end are zero
 #pragma unroll
-        for (int kk = 0; kk < NKD; ++kk)
-            fdO[kk] = row < len ? load_frag<bf16>(dout + ((size_t)(tok0 + 16 * I) * H + h) * DK + 32 * kk,
-                                                  H * DK, lane)
-                                : MB::zero();
+        for (int kk = 0; kk < NKD; ++kk) fdO[kk] = MB::zero();
     }
     const bf16 *Sc = ba.Sc + ch * DK * DK;
     const float *dKg = ba.dKh + ch * kChunk * DK;
@@ -575,13 +607,20 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_factor_kernel(BwdArgs b
         const int cbase = half * DH;
         // ---- cumulative log-decay of the half's channels, the scaled tiles ----
         {
-            f32x4 g[TPG];
+            f32x4 g[TPG], bf[TPG];
+            bf16x4 k4[TPG], q4[TPG];
 #pragma unroll
-            for (int j = 0; j < TPG; ++j) {
+            for (int j = 0; j < TPG; ++j) {  // every load first (rows past the end read row 0)
                 const int i = tg * TPG + j;
-                g[j] = i < len ? *reinterpret_cast<const f32x4 *>(a.log_alpha + ((size_t)(tok0 + i) * H + h) * DK + cbase + cq)
-                               : zero4();
+                const size_t off = ((size_t)(tok0 + (i < len ? i : 0)) * H + h) * DK + cbase + cq;
+                g[j] = *reinterpret_cast<const f32x4 *>(a.log_alpha + off);
+                k4[j] = *reinterpret_cast<const bf16x4 *>(kin + off);
+                q4[j] = *reinterpret_cast<const bf16x4 *>(qin + off);
+                bf[j] = *reinterpret_cast<const f32x4 *>(a.b + off);
             }
+#pragma unroll
+            for (int j = 0; j < TPG; ++j)  // padding tokens: k = q = b = 0, log alpha = 0
+                if (tg * TPG + j >= len) g[j] = bf[j] = zero4();
 #pragma unroll
             for (int j = 1; j < TPG; ++j) g[j] += g[j - 1];
             *reinterpret_cast<f32x4 *>(sR + tg * DH + cq) = g[TPG - 1];
@@ -595,29 +634,39 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_factor_kernel(BwdArgs b
             }
             const f32x4 gr = 0.5f * glast;
             if (tg == 0) *reinterpret_cast<f32x4 *>(sGl + cq) = glast;
+            float kp[4][TPG], ep[4][TPG], qp[4][TPG];
 #pragma unroll
             for (int j = 0; j < TPG; ++j) {
                 const int i = tg * TPG + j;
                 g[j] += goff;
                 *reinterpret_cast<f32x4 *>(sG + i * LDG + cq) = g[j];
-                f32x4 kf = zero4(), qf = zero4(), bf = zero4();
-                if (i < len) {
-                    const size_t off = ((size_t)(tok0 + i) * H + h) * DK + cbase + cq;
-                    const bf16x4 k4 = *reinterpret_cast<const bf16x4 *>(kin + off);
-                    const bf16x4 q4 = *reinterpret_cast<const bf16x4 *>(qin + off);
-                    bf = *reinterpret_cast<const f32x4 *>(a.b + off);
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        kf[c] = static_cast<float>(k4[c]);
-                        qf[c] = static_cast<float>(q4[c]);
-                    }
-                }
+                const bool ok = i < len;
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
+                    const float kf = ok ? static_cast<float>(k4[j][c]) : 0.0f;
+                    const float qf = ok ? static_cast<float>(q4[j][c]) : 0.0f;
                     const float ex = __expf(g[j][c] - gr[c]), ei = __expf(gr[c] - g[j][c]);
-                    sKpt[(cq + c) * L64 + i] = static_cast<bf16>(kf[c] * ei);
-                    sEpt[(cq + c) * L64 + i] = static_cast<bf16>(bf[c] * kf[c] * ex);
-                    sQpt[(cq + c) * L64 + i] = static_cast<bf16>(qf[c] * ex);
+                    kp[c][j] = kf * ei;
+                    ep[c][j] = bf[j][c] * kf * ex;
+                    qp[c][j] = qf * ex;
+                }
+            }
+            // each channel's TPG tokens as one store per tile
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int at = (cq + c) * L64 + fac_col(cq + c, tg * TPG);
+                if constexpr (TPG == 4) {
+                    *reinterpret_cast<bf16x4 *>(sKpt + at) = bf16x4{static_cast<bf16>(kp[c][0]), static_cast<bf16>(kp[c][1]),
+                                                                    static_cast<bf16>(kp[c][2]), static_cast<bf16>(kp[c][3])};
+                    *reinterpret_cast<bf16x4 *>(sEpt + at) = bf16x4{static_cast<bf16>(ep[c][0]), static_cast<bf16>(ep[c][1]),
+                                                                    static_cast<bf16>(ep[c][2]), static_cast<bf16>(ep[c][3])};
+                    *reinterpret_cast<bf16x4 *>(sQpt + at) = bf16x4{static_cast<bf16>(qp[c][0]), static_cast<bf16>(qp[c][1]),
+                                                                    static_cast<bf16>(qp[c][2]), static_cast<bf16>(qp[c][3])};
+                } else {
+                    static_assert(TPG == 2, "token runs of 2 or 4");
+                    *reinterpret_cast<bf16x2 *>(sKpt + at) = bf16x2{static_cast<bf16>(kp[c][0]), static_cast<bf16>(kp[c][1])};
+                    *reinterpret_cast<bf16x2 *>(sEpt + at) = bf16x2{static_cast<bf16>(ep[c][0]), static_cast<bf16>(ep[c][1])};
+                    *reinterpret_cast<bf16x2 *>(sQpt + at) = bf16x2{static_cast<bf16>(qp[c][0]), static_cast<bf16>(qp[c][1])};
                 }
             }
         }
@@ -626,20 +675,44 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_factor_kernel(BwdArgs b
         // Per 16-channel block hb: dEp = dA Kp, dQp = dM Kp, dKp = dA^T Ep +
         // dM^T Qp and dQhat = dO S^T, then the element-wise gradients in the
         // accumulator layout (one block's results live at a time).
+        // The global operands of block hb (S^T fragments and the element-wise
+        // inputs, raw as loaded) are issued one block ahead.
+        struct HbIn {
+            MB::frag s[NKD];
+            bf16 k[4], q[4];
+            float b[4], dk[4];
+        };
+        auto load_hb = [&](HbIn &x, int hb) {
+#pragma unroll
+            for (int kk = 0; kk < NKD; ++kk) x.s[kk] = load_frag<bf16>(Sc + (cbase + 16 * hb) * DK + 32 * kk, DK, lane);
+            const int c = cbase + 16 * hb + (lane & 15);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * I + 4 * (lane >> 4) + r, ic = i < len ? i : 0;
+                const size_t off = ((size_t)(tok0 + ic) * H + h) * DK + c;
+                x.k[r] = kin[off];
+                x.q[r] = qin[off];
+                x.b[r] = a.b[off];
+                x.dk[r] = dKg[(size_t)ic * DK + c];
+            }
+        };
+        HbIn hin[2];
+        load_hb(hin[0], 0);
 #pragma unroll
         for (int hb = 0; hb < NHB; ++hb) {
+            if (hb + 1 < NHB) load_hb(hin[(hb + 1) & 1], hb + 1);
+            const HbIn &x = hin[hb & 1];
             f32x4 dEp = zero4(), dQp = zero4(), dKp = zero4(), dQh = zero4();
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                const MB::frag kp = load_frag<bf16>(sKpt + 16 * hb * L64 + 32 * kk, L64, lane);
+                const MB::frag kp = load_frag_fac(sKpt + 16 * hb * L64, L64, hb, kk, lane);
                 dEp = MB::mma(fA[kk], kp, dEp);
                 dQp = MB::mma(fM[kk], kp, dQp);
-                dKp = MB::mma(fAt[kk], load_frag<bf16>(sEpt + 16 * hb * L64 + 32 * kk, L64, lane), dKp);
-                dKp = MB::mma(fMt[kk], load_frag<bf16>(sQpt + 16 * hb * L64 + 32 * kk, L64, lane), dKp);
+                dKp = MB::mma(fAt[kk], load_frag_fac(sEpt + 16 * hb * L64, L64, hb, kk, lane), dKp);
+                dKp = MB::mma(fMt[kk], load_frag_fac(sQpt + 16 * hb * L64, L64, hb, kk, lane), dKp);
             }
 #pragma unroll
-            for (int kk = 0; kk < NKD; ++kk)
-                dQh = MB::mma(fdO[kk], load_frag<bf16>(Sc + (cbase + 16 * hb) * DK + 32 * kk, DK, lane), dQh);
+            for (int kk = 0; kk < NKD; ++kk) dQh = MB::mma(fdO[kk], x.s[kk], dQh);
             const int cl = 16 * hb + (lane & 15), c = cbase + cl;
             const float gl_c = sGl[cl], gr_c = 0.5f * gl_c, egr = __expf(gr_c);
             const f32x4 dEc = dE[half * NHB + hb];
@@ -650,9 +723,9 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_factor_kernel(BwdArgs b
                 float dg = 0.0f;
                 if (i < len) {
                     const size_t off = ((size_t)(tok0 + i) * H + h) * DK + c;
-                    const float kf = static_cast<float>(kin[off]), qf = static_cast<float>(qin[off]);
-                    const float bf = a.b[off];
-                    const float dKh = dKg[(size_t)i * DK + c];
+                    const float kf = static_cast<float>(x.k[r]), qf = static_cast<float>(x.q[r]);
+                    const float bf = x.b[r];
+                    const float dKh = x.dk[r];
                     const float gg = sG[i * LDG + cl];
                     const float ex = __expf(gg - gr_c), ei = __expf(gr_c - gg);
                     const float gam = ex * egr, eK = ei * egr;
