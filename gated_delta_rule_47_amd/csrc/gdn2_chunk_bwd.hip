@@ -260,6 +260,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_state_kernel(BwdArgs ba
     if (a.plan && cid >= a.plan[a.N]) return;
     int tok0, len;
     dense_span(a, cid, tok0, len);
+    if (len <= 0) return;  // (a malformed table only) no token; the factor side skips it too
     const size_t ch = (size_t)cid * H + h;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, I = wave;
     const bf16 *dout = reinterpret_cast<const bf16 *>(ba.dout);
@@ -368,22 +369,37 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_state_kernel(BwdArgs ba
         }
         __syncthreads();
 
-        // dZ = T^T dU_eff; dv = w dZ, dw = v dZ.
+        // dZ = T^T dU_eff; dv = w dZ, dw = v dZ (w and v of both column blocks
+        // loaded first; rows past the chunk read row 0 and are not stored).
+        {
+            constexpr int NCS = SW / 16;
+            float wv[NCS][4];
+            bf16 vv_[NCS][4];
 #pragma unroll
-        for (int cb = 0; cb < SW / 16; ++cb) {
-            f32x4 dz = zero4();
+            for (int cb = 0; cb < NCS; ++cb)
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-                dz = MB::mma(fTt[kk],
-                             load_frag<bf16>(sdUt + 16 * cb * L64 + 32 * kk, L64, lane), dz);
-            store_tile<bf16>(sdZ + 16 * I * LSW + 16 * cb, LSW, dz, lane);
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 16 * I + 4 * (lane >> 4) + r;
+                    const size_t o = ((size_t)(tok0 + (i < len ? i : 0)) * H + h) * DV + v0 + 16 * cb + (lane & 15);
+                    wv[cb][r] = a.w[o];
+                    vv_[cb][r] = vin[o];
+                }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 16 * I + 4 * (lane >> 4) + r, vv = 16 * cb + (lane & 15);
-                if (i < len) {
-                    const size_t o = ((size_t)(tok0 + i) * H + h) * DV + v0 + vv;
-                    dv[o] = static_cast<bf16>(a.w[o] * dz[r]);
-                    ba.dw[o] = static_cast<float>(vin[o]) * dz[r];
+            for (int cb = 0; cb < NCS; ++cb) {
+                f32x4 dz = zero4();
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk)
+                    dz = MB::mma(fTt[kk],
+                                 load_frag<bf16>(sdUt + 16 * cb * L64 + 32 * kk, L64, lane), dz);
+                store_tile<bf16>(sdZ + 16 * I * LSW + 16 * cb, LSW, dz, lane);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 16 * I + 4 * (lane >> 4) + r, vv = 16 * cb + (lane & 15);
+                    if (i < len) {
+                        const size_t o = ((size_t)(tok0 + i) * H + h) * DV + v0 + vv;
+                        dv[o] = static_cast<bf16>(wv[cb][r] * dz[r]);
+                        ba.dw[o] = static_cast<float>(vv_[cb][r]) * dz[r];
+                    }
                 }
             }
         }
