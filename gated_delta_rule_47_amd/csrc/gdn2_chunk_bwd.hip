@@ -126,32 +126,58 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_rev_kernel(BwdArgs ba) 
         }
     }
     const bf16 *dout = reinterpret_cast<const bf16 *>(ba.dout);
-    for (int cid = cend - 1; cid >= cbeg; --cid) {
+    // Everything a chunk reads from global memory, loaded one chunk ahead (the
+    // chunks run last to first): M^T and Khat rows of block `wave`, Qhat^T and
+    // W^T rows of this wave's state row blocks, gamma_last, and this thread's
+    // dO pieces (raw; rows past the chunk's end read row 0, zeroed at use).
+    constexpr int NE = kChunk * DVS / 4 / kThreads;
+    static_assert(NE * kThreads * 4 == kChunk * DVS, "dO split");
+    struct RevIn {
+        MB::frag fM[2], fK[NKD], fQ[C::KB_W][2], fW[C::KB_W][2];
+        f32x4 gl[C::KB_W];
+        bf16x4 o[NE];
+        int len;
+    };
+    auto load_in = [&](RevIn &x, int cid) {
         const size_t ch = (size_t)cid * H + h;
         int tok0, len;
         chunk_span_of(a, cid, cbeg, n, tok0, len);
-        // Fragments of this chunk: M^T and Khat rows of block `wave`, Qhat^T
-        // and W^T rows of this wave's state row blocks; gamma_last.
+        x.len = len;
         const bf16 *Mt = reinterpret_cast<const bf16 *>(a.ws_Mt) + ch * kChunk * kChunk;
         const bf16 *Kh = reinterpret_cast<const bf16 *>(a.ws_Kh) + ch * kChunk * DK;
         const bf16 *Qt = reinterpret_cast<const bf16 *>(a.ws_Qt) + ch * DK * kChunk;
         const bf16 *Wt = reinterpret_cast<const bf16 *>(a.ws_Wt) + ch * DK * kChunk;
-        MB::frag fM[2], fK[NKD], fQ[C::KB_W][2], fW[C::KB_W][2];
-        f32x4 gl[C::KB_W];
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) fM[kk] = load_frag_packed<bf16>(Mt, kChunk, wave, kk, lane);
+        for (int kk = 0; kk < 2; ++kk) x.fM[kk] = load_frag_packed<bf16>(Mt, kChunk, wave, kk, lane);
 #pragma unroll
-        for (int kk = 0; kk < NKD; ++kk) fK[kk] = load_frag_packed<bf16>(Kh, DK, wave, kk, lane);
+        for (int kk = 0; kk < NKD; ++kk) x.fK[kk] = load_frag_packed<bf16>(Kh, DK, wave, kk, lane);
 #pragma unroll
         for (int b = 0; b < C::KB_W; ++b) {
             const int cblk = wave * C::KB_W + b;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                fQ[b][kk] = load_frag_packed<bf16>(Qt, kChunk, cblk, kk, lane);
-                fW[b][kk] = load_frag_packed<bf16>(Wt, kChunk, cblk, kk, lane);
+                x.fQ[b][kk] = load_frag_packed<bf16>(Qt, kChunk, cblk, kk, lane);
+                x.fW[b][kk] = load_frag_packed<bf16>(Wt, kChunk, cblk, kk, lane);
             }
-            gl[b] = *reinterpret_cast<const f32x4 *>(a.ws_gl + ch * DK + 16 * cblk + 4 * (lane >> 4));
+            x.gl[b] = *reinterpret_cast<const f32x4 *>(a.ws_gl + ch * DK + 16 * cblk + 4 * (lane >> 4));
         }
+#pragma unroll
+        for (int q = 0; q < NE; ++q) {
+            const int e = tid + q * kThreads, i = e / (DVS / 4), c4 = 4 * (e % (DVS / 4));
+            const size_t off = len > 0 ? ((size_t)(tok0 + (i < len ? i : 0)) * H + h) * DV + col0 + c4 : 0;
+            x.o[q] = *reinterpret_cast<const bf16x4 *>(dout + off);
+        }
+    };
+    // (With 64-column slabs a second register set would drop 128-wide heads to
+    // one wave per SIMD: those load each chunk's operands at its start.)
+    constexpr bool kAhead = DVS <= 32;
+    RevIn cur, nxt;
+    if (kAhead && cend > cbeg) load_in(cur, cend - 1);
+    for (int cid = cend - 1; cid >= cbeg; --cid) {
+        const size_t ch = (size_t)cid * H + h;
+        if constexpr (kAhead) load_in(nxt, max(cid - 1, cbeg));
+        else load_in(cur, cid);
+        const int len = cur.len;
         // dS' of this chunk: to the workspace (bf16, for the per-chunk kernels)
         // and, transposed, to LDS.
         bf16 *dSc = ba.dSc + ch * DK * DV;
@@ -165,12 +191,11 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_rev_kernel(BwdArgs ba) 
             store_tile_t<bf16>(sdSt + 16 * colb * LDKP + 16 * cblk, LDKP, dS[u], lane);
         }
         // dO rows of the chunk (zero past its end), transposed.
-        for (int e = tid; e < kChunk * DVS / 4; e += kThreads) {
-            const int i = e / (DVS / 4), c4 = 4 * (e % (DVS / 4));
-            bf16x4 v4;
-            if (i < len) {
-                v4 = *reinterpret_cast<const bf16x4 *>(dout + ((size_t)(tok0 + i) * H + h) * DV + col0 + c4);
-            } else {
+#pragma unroll
+        for (int q = 0; q < NE; ++q) {
+            const int e = tid + q * kThreads, i = e / (DVS / 4), c4 = 4 * (e % (DVS / 4));
+            bf16x4 v4 = cur.o[q];
+            if (i >= len) {
 #pragma unroll
                 for (int t = 0; t < 4; ++t) v4[t] = static_cast<bf16>(0.0f);
             }
@@ -185,10 +210,10 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_rev_kernel(BwdArgs ba) 
             f32x4 acc = zero4();
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
-                acc = MB::mma(fM[kk], load_frag<bf16>(sdOt + 16 * cb * L64 + 32 * kk, L64, lane), acc);
+                acc = MB::mma(cur.fM[kk], load_frag<bf16>(sdOt + 16 * cb * L64 + 32 * kk, L64, lane), acc);
 #pragma unroll
             for (int kk = 0; kk < NKD; ++kk)
-                acc = MB::mma(fK[kk], load_frag<bf16>(sdSt + 16 * cb * LDKP + 32 * kk, LDKP, lane), acc);
+                acc = MB::mma(cur.fK[kk], load_frag<bf16>(sdSt + 16 * cb * LDKP + 32 * kk, LDKP, lane), acc);
             store_tile_t<bf16>(sdUt + 16 * cb * L64 + 16 * wave, L64, acc, lane);
         }
         __syncthreads();
@@ -200,12 +225,13 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_rev_kernel(BwdArgs ba) 
             f32x4 q = zero4(), wu = zero4();
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                q = MB::mma(fQ[b][kk], load_frag<bf16>(sdOt + 16 * colb * L64 + 32 * kk, L64, lane), q);
-                wu = MB::mma(fW[b][kk], load_frag<bf16>(sdUt + 16 * colb * L64 + 32 * kk, L64, lane), wu);
+                q = MB::mma(cur.fQ[b][kk], load_frag<bf16>(sdOt + 16 * colb * L64 + 32 * kk, L64, lane), q);
+                wu = MB::mma(cur.fW[b][kk], load_frag<bf16>(sdUt + 16 * colb * L64 + 32 * kk, L64, lane), wu);
             }
-            dS[u] = gl[b] * dS[u] + q - wu;
+            dS[u] = cur.gl[b] * dS[u] + q - wu;
         }
         __syncthreads();
+        if constexpr (kAhead) cur = nxt;
     }
     if (ba.dS0) {
 #pragma unroll

@@ -235,7 +235,7 @@ __device__ __forceinline__ float sigmoid1(float x) {
 }
 
 // kBwd: also write the transposed factors a backward call needs (a.ws_Mt,
-// ws_Kh, ws_Qt, ws_Wt, ws_Tt).
+// ws_Kh, ws_Qt, ws_Wt, ws_Tt), and not Qhat or M, which only o needs.
 // kLogits: the gates arrive as bf16 -- log alpha itself and the logits of b
 // and w, whose sigmoid is taken here.  kAlphaLogit (with kLogits): log_alpha
 // holds logits too, and log alpha = logsigmoid(logit + a.alpha_bias).
@@ -451,7 +451,9 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(ChunkArgs a) {
     __syncthreads();  // Ep and the Khat^T image are dead: X receives q e^{g-g_r}, the image Qhat
 #pragma unroll
     for (int j = 0; j < TPG; ++j) *reinterpret_cast<Vec4<E> *>(sX + (tg * TPG + j) * LDT + c0) = qp[j];
-    if constexpr (sizeof(E) == 2) {  // a granule is 8 channels of one token
+    // (A backward call needs neither Qhat nor M: its propagation forms no o.)
+    if constexpr (kBwd) {
+    } else if constexpr (sizeof(E) == 2) {  // a granule is 8 channels of one token
 #pragma unroll
         for (int j = 0; j < TPG; ++j)
             *reinterpret_cast<Vec4<E> *>(stage_ptr(sStg, frag_index<E>(tg * TPG + j, c0, DK))) = qh[j];
@@ -464,7 +466,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(ChunkArgs a) {
                     f32x4{qh[m][c], qh[m + 1][c], qh[m + 2][c], qh[m + 3][c]};
     }
     __syncthreads();
-    stage_copy_out<E, C::NG>(Qh, sStg, tid);
+    if constexpr (!kBwd) stage_copy_out<E, C::NG>(Qh, sStg, tid);
     E *Mg = reinterpret_cast<E *>(a.ws_M) + ch * kChunk * kChunk;
 #pragma unroll
     for (int u = 0; u < 3; ++u) {
@@ -472,16 +474,17 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(ChunkArgs a) {
         if (t < 10) {
             int I, J;
             lower_tile(t, I, J);
-            f32x4 acc = mma_tile<E, DK>(zero4(), sKp + 16 * J * LDT, LDT, sX + 16 * I * LDT, LDT,
-                                        lane);
-            const int i = 16 * I + (lane & 15);
+            if constexpr (!kBwd) {
+                f32x4 acc = mma_tile<E, DK>(zero4(), sKp + 16 * J * LDT, LDT, sX + 16 * I * LDT, LDT,
+                                            lane);
+                const int i = 16 * I + (lane & 15);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int j = 16 * J + 4 * (lane >> 4) + r;
-                acc[r] = j <= i ? acc[r] : 0.0f;
-            }
-            store4_frag<E>(Mg, kChunk, i, 16 * J + 4 * (lane >> 4), acc);
-            if constexpr (kBwd) {  // M^T[j][i] = M[i][j]: the same tile with the operands swapped
+                for (int r = 0; r < 4; ++r) {
+                    const int j = 16 * J + 4 * (lane >> 4) + r;
+                    acc[r] = j <= i ? acc[r] : 0.0f;
+                }
+                store4_frag<E>(Mg, kChunk, i, 16 * J + 4 * (lane >> 4), acc);
+            } else {  // M^T[j][i] = M[i][j]: the same tile with the operands swapped
                 f32x4 t = mma_tile<E, DK>(zero4(), sX + 16 * I * LDT, LDT, sKp + 16 * J * LDT, LDT, lane);
                 const int jj = 16 * J + (lane & 15);
 #pragma unroll
@@ -497,8 +500,9 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(ChunkArgs a) {
         if (t < 6) {
             int I, J;
             upper_tile(t, I, J);
-            store4_frag<E>(Mg, kChunk, 16 * I + (lane & 15), 16 * J + 4 * (lane >> 4), zero4());
-            if constexpr (kBwd)  // the zero lower blocks of M^T
+            if constexpr (!kBwd)
+                store4_frag<E>(Mg, kChunk, 16 * I + (lane & 15), 16 * J + 4 * (lane >> 4), zero4());
+            else  // the zero lower blocks of M^T
                 store4_frag<E>(reinterpret_cast<E *>(a.ws_Mt) + ch * kChunk * kChunk, kChunk,
                                16 * J + (lane & 15), 16 * I + 4 * (lane >> 4), zero4());
         }

@@ -310,14 +310,20 @@ __device__ __forceinline__ granule_t ws_load(const ChunkArgs &a, size_t ch, int 
 // Loads J .. J1-1: store each register of the chunk already loaded into
 // `stage`, then reuse it for the same load of chunk-head `ch_next`, so that the
 // loads stay in flight one after another.  The sequence has no branches, which
-// lets every store wait for its own load only.
-template <int DK, int DVS, int J, int J1>
+// lets every store wait for its own load only.  kStates (no output) moves
+// only W and Khat^T: Qhat and M serve o alone.
+template <int DK, int DVS, int J, int J1, bool kStates = false>
 __device__ __forceinline__ void ws_pipe(StageRegs<WsCfg<DK, DVS>::NJ> &buf, char *stage,
                                         const ChunkArgs &a, size_t ch_next, int t) {
     if constexpr (J < J1) {
-        *reinterpret_cast<granule_t *>(stage + ((size_t)J * kThreads + t) * 16) = buf.v[J];
-        buf.v[J] = ws_load<DK, DVS, J>(a, ch_next, t);
-        ws_pipe<DK, DVS, J + 1, J1>(buf, stage, a, ch_next, t);
+        using C = WsCfg<DK, DVS>;
+        constexpr int g = J * kThreads;
+        constexpr bool skip = kStates && g >= C::NG_W && g < 2 * C::NG_W + C::NG_M;
+        if constexpr (!skip) {
+            *reinterpret_cast<granule_t *>(stage + ((size_t)J * kThreads + t) * 16) = buf.v[J];
+            buf.v[J] = ws_load<DK, DVS, J>(a, ch_next, t);
+        }
+        ws_pipe<DK, DVS, J + 1, J1, kStates>(buf, stage, a, ch_next, t);
     }
 }
 
@@ -417,18 +423,18 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_prop_ws_kernel(ChunkArg
         // chunk 0 into buf1 (stored at step 1); buf0 receives chunk 1 at step 0
 #pragma unroll
         for (int j = 0; j < NJ; ++j) buf1.v[j] = granule_t{0u, 0u, 0u, 0u};
-        ws_pipe<DK, DVS, 0, NJ>(buf1, smem + C::SZ_STAGE, a, chunk_head(0), t);
+        ws_pipe<DK, DVS, 0, NJ, kStates>(buf1, smem + C::SZ_STAGE, a, chunk_head(0), t);
         const int nsteps = (nch + 3) & ~1;  // nch + 2, rounded up to even
         for (int it = 0; it < nsteps; it += 2) {
             if (it >= 3 && it - 3 < nch) store_o(it - 3);
-            ws_pipe<DK, DVS, 0, NJ2>(buf0, smem + C::SZ_STAGE, a, chunk_head(it + 1), t);
+            ws_pipe<DK, DVS, 0, NJ2, kStates>(buf0, smem + C::SZ_STAGE, a, chunk_head(it + 1), t);
             __syncthreads();
-            ws_pipe<DK, DVS, NJ2, NJ>(buf0, smem + C::SZ_STAGE, a, chunk_head(it + 1), t);
+            ws_pipe<DK, DVS, NJ2, NJ, kStates>(buf0, smem + C::SZ_STAGE, a, chunk_head(it + 1), t);
             __syncthreads();
             if (it + 1 >= 3 && it - 2 < nch) store_o(it - 2);
-            ws_pipe<DK, DVS, 0, NJ2>(buf1, smem, a, chunk_head(it + 2), t);
+            ws_pipe<DK, DVS, 0, NJ2, kStates>(buf1, smem, a, chunk_head(it + 2), t);
             __syncthreads();
-            ws_pipe<DK, DVS, NJ2, NJ>(buf1, smem, a, chunk_head(it + 2), t);
+            ws_pipe<DK, DVS, NJ2, NJ, kStates>(buf1, smem, a, chunk_head(it + 2), t);
             __syncthreads();
         }
         if (nsteps - 3 < nch) store_o(nch - 1);  // the last chunk when no step after it remained
@@ -502,7 +508,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_prop_ws_kernel(ChunkArg
 #pragma unroll
             for (int kk = 0; kk < NKD; ++kk) {
                 wf[kk] = load_frag_packed<bf16>(Wf, DK, wave, kk, lane);
-                qf[kk] = load_frag_packed<bf16>(Qf, DK, wave, kk, lane);
+                if constexpr (!kStates) qf[kk] = load_frag_packed<bf16>(Qf, DK, wave, kk, lane);
             }
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb)
@@ -517,7 +523,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_prop_ws_kernel(ChunkArg
 #pragma unroll
                 for (int cb = 0; cb < NCB; ++cb) {
                     ws[cb] = M::mma(wf[kk], sf[cb][kk], ws[cb]);
-                    oacc[cb] = M::mma(sf[cb][kk], qf[kk], oacc[cb]);
+                    if constexpr (!kStates) oacc[cb] = M::mma(sf[cb][kk], qf[kk], oacc[cb]);
                 }
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb)
@@ -531,7 +537,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_prop_ws_kernel(ChunkArg
             M::frag uf[NCB][NK64], mf[NK64], kf[C::KB_W][NK64];
 #pragma unroll
             for (int kk = 0; kk < NK64; ++kk) {
-                mf[kk] = load_frag_packed<bf16>(Mf, kChunk, wave, kk, lane);
+                if constexpr (!kStates) mf[kk] = load_frag_packed<bf16>(Mf, kChunk, wave, kk, lane);
 #pragma unroll
                 for (int b = 0; b < C::KB_W; ++b)
                     kf[b][kk] = load_frag_packed<bf16>(Kf, kChunk, wave * C::KB_W + b, kk, lane);
@@ -544,15 +550,17 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_prop_ws_kernel(ChunkArg
             for (int u = 0; u < C::S_TPW; ++u) d[u] = zero4();
 #pragma unroll
             for (int kk = 0; kk < NK64; ++kk) {
+                if constexpr (!kStates) {
 #pragma unroll
-                for (int cb = 0; cb < NCB; ++cb) oacc[cb] = M::mma(uf[cb][kk], mf[kk], oacc[cb]);
+                    for (int cb = 0; cb < NCB; ++cb) oacc[cb] = M::mma(uf[cb][kk], mf[kk], oacc[cb]);
+                }
 #pragma unroll
                 for (int u = 0; u < C::S_TPW; ++u)
                     d[u] = M::mma(kf[u / NCB][kk], uf[u % NCB][kk], d[u]);
             }
             // O rows to the staging buffer; the loader waves write them out.
 #pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) {
+            for (int cb = 0; cb < (kStates ? 0 : NCB); ++cb) {
                 bf16x4 ov;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) ov[r] = static_cast<bf16>(oacc[cb][r]);
