@@ -342,7 +342,7 @@ int gdn2_chunk_bwd(const void *q, const void *k, const void *v, const float *log
     a.ws_M = ws + F.off_M;
     a.ws_U = ws + F.off_U;
     a.ws_gl = reinterpret_cast<float *>(ws + F.off_gl);
-    a.store_T = 1;
+    a.store_T = 0;  // the backward kernels read T^T (ws_Tt) only
     a.ws_Sc = reinterpret_cast<bf16_t *>(ws + L.off_Sc);
     a.ws_Mt = ws + L.off_Mt;
     a.ws_Kh = ws + L.off_Kh;

@@ -186,7 +186,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_rev_kernel(BwdArgs ba) 
             const int cblk = wave * C::KB_W + u / NCB, colb = u % NCB;
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                dSc[(size_t)(16 * cblk + 4 * (lane >> 4) + r) * DV + col0 + 16 * colb + (lane & 15)] =
+                dSc[sc_index(16 * cblk + 4 * (lane >> 4) + r, col0 + 16 * colb + (lane & 15), DK)] =
                     static_cast<bf16>(dS[u][r]);
             store_tile_t<bf16>(sdSt + 16 * colb * LDKP + 16 * cblk, LDKP, dS[u], lane);
         }
@@ -333,8 +333,8 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_state_kernel(BwdArgs ba
 #pragma unroll
         for (int p8 = 0; p8 < CPT; p8 += 8) {
             const int v = scol + p8;
-            const bf16x8 sb = *reinterpret_cast<const bf16x8 *>(Sc + (size_t)srow * DV + v0 + v);
-            const bf16x8 db = *reinterpret_cast<const bf16x8 *>(dSc + (size_t)srow * DV + v0 + v);
+            const bf16x8 sb = *reinterpret_cast<const bf16x8 *>(Sc + sc_index(srow, v0 + v, DK));
+            const bf16x8 db = *reinterpret_cast<const bf16x8 *>(dSc + sc_index(srow, v0 + v, DK));
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
                 sSt[(v + t) * LDKP + srow] = sb[t];
@@ -726,7 +726,8 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_factor_kernel(BwdArgs b
         };
         auto load_hb = [&](HbIn &x, int hb) {
 #pragma unroll
-            for (int kk = 0; kk < NKD; ++kk) x.s[kk] = load_frag<bf16>(Sc + (cbase + 16 * hb) * DK + 32 * kk, DK, lane);
+            for (int kk = 0; kk < NKD; ++kk)  // rows cbase+16hb.., columns 32kk..: one 32-column slab
+                x.s[kk] = load_frag<bf16>(Sc + sc_index(cbase + 16 * hb, 32 * kk, DK), 32, lane);
             const int c = cbase + 16 * hb + (lane & 15);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {

@@ -488,7 +488,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_prop_ws_kernel(ChunkArg
                 const int cblk = wave * C::KB_W + u / NCB, colb = u % NCB;
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    Sc[(size_t)(16 * cblk + 4 * (lane >> 4) + r) * DV + col0 + 16 * colb + (lane & 15)] =
+                    Sc[sc_index(16 * cblk + 4 * (lane >> 4) + r, col0 + 16 * colb + (lane & 15), DK)] =
                         static_cast<bf16>(Sacc[u][r]);
             }
         }

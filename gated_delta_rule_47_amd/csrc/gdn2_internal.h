@@ -42,7 +42,8 @@ struct ChunkArgs {
     const float *alpha_bias;  // with gate_logits: if set, log_alpha holds logits and
                               // log alpha = logsigmoid(log_alpha + alpha_bias[h][c])
     bf16_t *ws_Sc;        // if set, the propagation stores every chunk's incoming
-                          // state here (bf16 [chunk id][head][Dk][Dv]) and writes no o
+                          // state here (bf16 [chunk id][head], layout of sc_index)
+                          // and writes no o
     // If set (backward calls), the chunk-factor kernel also writes, in fragment
     // order: M^T [64][64], Khat [64][Dk], Qhat^T [Dk][64], W^T [Dk][64] and T^T [64][64].
     void *ws_Mt, *ws_Kh, *ws_Qt, *ws_Wt, *ws_Tt;
@@ -51,10 +52,18 @@ struct ChunkArgs {
 // The backward's workspace: the forward's layout (T always stored), the
 // transposed chunk factors (io dtype, fragment order), then arrays indexed
 // [chunk id][head][...]: every chunk's incoming state Sc and the gradient dSc
-// of its outgoing state (bf16 [Dk][Dv]); the state-side partial gradients
+// of its outgoing state (bf16 Dk x Dv, laid out by sc_index); the state-side
+// partial gradients
 // dKh (fp32 [64][Dk]), dW^T (bf16 fragment order [Dk][64]), dM and dM^T
 // (bf16 fragment order [64][64]), dAp = dZ U^T (fp32 [64][64]) and dG =
 // rowsum(dSc * Sc) (fp32 [Dk]).
+// Element (c, v) of a per-chunk bf16 state (Sc, dSc) of Dk rows: 32-column
+// slabs [v / 32][c][v % 32], so that a slab is one contiguous block and a
+// row's part of it is 64 contiguous bytes.
+__host__ __device__ inline size_t sc_index(int c, int v, int Dk) {
+    return ((size_t)(v >> 5) * Dk + c) * 32 + (v & 31);
+}
+
 struct BwdLayout {
     WorkspaceLayout fwd;
     size_t off_Mt = 0, off_Kh = 0, off_Qt = 0, off_Wt = 0, off_Tt = 0;
