@@ -159,7 +159,8 @@ static int chunk_fwd_impl(const void *q, const void *k, const void *v, const voi
                           const void *b, const void *w, const float *S0, void *o, float *S_final,
                           const int32_t *cu_seqlens, int N, int B, int T, int H, int Dk, int Dv,
                           int io, void *workspace, size_t workspace_bytes, void *stream_ptr,
-                          int stages, bool gate_logits, const float *alpha_bias = nullptr) {
+                          int stages, bool gate_logits, const float *alpha_bias = nullptr,
+                          long long ld_gate = 0) {
     if (stages & ~(GDN2_STAGE_ALL | GDN2_STAGE_STORE_T)) return GDN2_ERR_INVALID_ARGUMENT;
     if (io != GDN2_F32 && io != GDN2_BF16) return GDN2_ERR_INVALID_ARGUMENT;
     if (N < 0 || B < 0 || T < 0 || H < 0 || Dk <= 0 || Dv <= 0) return GDN2_ERR_INVALID_ARGUMENT;
@@ -199,6 +200,7 @@ static int chunk_fwd_impl(const void *q, const void *k, const void *v, const voi
     a.b = static_cast<const float *>(b);
     a.w = static_cast<const float *>(w);
     a.gate_logits = gate_logits ? 1 : 0;
+    a.ld_gate = ld_gate > 0 ? ld_gate : (long long)H * Dk;
     a.alpha_bias = gate_logits ? alpha_bias : nullptr;
     a.S0 = S0;
     a.o = o;
@@ -402,8 +404,8 @@ namespace {
 constexpr size_t kLayerGemmWs = 32u << 20;  // hipBLASLt workspace cap
 
 struct LayerLayout {
-    size_t off_P = 0, off_al = 0, off_gt = 0, off_bl = 0, off_wl = 0, off_q = 0, off_k = 0,
-           off_v = 0, off_o = 0, off_gemm = 0, off_core = 0, core_bytes = 0, total = 0;
+    size_t off_P = 0, off_q = 0, off_k = 0, off_v = 0, off_o = 0, off_gemm = 0, off_core = 0,
+           core_bytes = 0, total = 0;
 };
 
 bool layer_layout(int N, int B, int T, int H, int Dk, int Dv, int D, bool varlen, LayerLayout *out) {
@@ -420,11 +422,9 @@ bool layer_layout(int N, int B, int T, int H, int Dk, int Dv, int D, bool varlen
         off = align_up(off + bytes);
         return at;
     };
-    L.off_P = take((size_t)M * 3 * row);  // q | k | v projections
-    L.off_al = take((size_t)M * row);     // gate logits: alpha, output gate, b, w
-    L.off_gt = take((size_t)M * row);
-    L.off_bl = take((size_t)M * row);
-    L.off_wl = take((size_t)M * row);
+    // all seven projections x W_in^T as one [M][7 H Dk] array, row blocks
+    // q | k | v | alpha | output gate | b | w
+    L.off_P = take((size_t)M * 7 * row);
     L.off_q = take((size_t)M * row);
     L.off_k = take((size_t)M * row);
     L.off_v = take((size_t)M * row);
@@ -487,15 +487,13 @@ int gdn2_layer_fwd(const void *x, const gdn2_layer_weights *wt, int conv_len, fl
     const bf16_t *X = static_cast<const bf16_t *>(x);
     const bf16_t *Win = static_cast<const bf16_t *>(wt->W_in);
     bf16_t *P = reinterpret_cast<bf16_t *>(ws + L.off_P);
-    bf16_t *al = reinterpret_cast<bf16_t *>(ws + L.off_al);
-    bf16_t *gt = reinterpret_cast<bf16_t *>(ws + L.off_gt);
-    bf16_t *bl = reinterpret_cast<bf16_t *>(ws + L.off_bl);
-    bf16_t *wl = reinterpret_cast<bf16_t *>(ws + L.off_wl);
+    const long long ld7 = 7LL * HD;  // the gate logits are column blocks 3..6 of P
+    const bf16_t *al = P + 3LL * HD, *gt = P + 4LL * HD, *bl = P + 5LL * HD, *wl = P + 6LL * HD;
     void *gws = ws + L.off_gemm;
 
     LayerArgs a{};
     a.P = P;
-    a.ldP = 3LL * HD;
+    a.ldP = ld7;
     a.conv_w = wt->conv_w;
     a.norm_w = wt->norm_w;
     a.q = reinterpret_cast<bf16_t *>(ws + L.off_q);
@@ -503,6 +501,7 @@ int gdn2_layer_fwd(const void *x, const gdn2_layer_weights *wt, int conv_len, fl
     a.v = reinterpret_cast<bf16_t *>(ws + L.off_v);
     a.o = reinterpret_cast<bf16_t *>(ws + L.off_o);
     a.gate = gt;
+    a.ldg = ld7;
     a.z = a.q;  // q is dead once the core has run
     a.cu_seqlens = cu_seqlens;
     a.M = m;
@@ -513,19 +512,15 @@ int gdn2_layer_fwd(const void *x, const gdn2_layer_weights *wt, int conv_len, fl
     a.norm_eps = norm_eps;
 
     if (m > 0) {
-        // q | k | v for the convolution kernel; each gate block into a
-        // contiguous [M, H*Dk] array (alpha, b and w go to the core as logits)
-        bool ok = gemm_bf16_nt(X, D, Win, D, P, a.ldP, m, 3 * HD, D, gws, kLayerGemmWs, stream);
-        bf16_t *gate_out[4] = {al, gt, bl, wl};
-        for (int blk = 0; ok && blk < 4; ++blk)
-            ok = gemm_bf16_nt(X, D, Win + (size_t)(3 + blk) * HD * D, D, gate_out[blk], HD, m, HD, D,
-                              gws, kLayerGemmWs, stream);
-        if (!ok) return GDN2_ERR_HIP;
+        // one GEMM for all seven projections: q | k | v feed the convolution
+        // kernel, alpha, b and w go to the core as logits, the gate to the output
+        if (!gemm_bf16_nt(X, D, Win, D, P, ld7, m, 7 * HD, D, gws, kLayerGemmWs, stream))
+            return GDN2_ERR_HIP;
         if (launch_layer_mix_in(a, Dk, stream) != hipSuccess) return GDN2_ERR_HIP;
     }
     const int st = chunk_fwd_impl(a.q, a.k, a.v, al, bl, wl, S0, ws + L.off_o, S_final, cu_seqlens,
                                   N, B, T, H, Dk, Dv, GDN2_BF16, ws + L.off_core, L.core_bytes,
-                                  stream_ptr, GDN2_STAGE_ALL, true, wt->alpha_bias);
+                                  stream_ptr, GDN2_STAGE_ALL, true, wt->alpha_bias, ld7);
     if (st != GDN2_OK) return st;
     if (m > 0) {
         if (launch_layer_mix_out(a, Dk, stream) != hipSuccess) return GDN2_ERR_HIP;

@@ -281,12 +281,13 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(ChunkArgs a) {
         if (i < len) {
             const size_t off = ((size_t)(tok0 + i) * H + h) * DK + c0;
             if constexpr (kLogits) {
-                g[j] = to4(*reinterpret_cast<const bf16x4 *>(reinterpret_cast<const bf16 *>(a.log_alpha) + off));
+                const size_t offg = (size_t)(tok0 + i) * a.ld_gate + (size_t)h * DK + c0;
+                g[j] = to4(*reinterpret_cast<const bf16x4 *>(reinterpret_cast<const bf16 *>(a.log_alpha) + offg));
                 if constexpr (kAlphaLogit) {
 #pragma unroll
                     for (int c = 0; c < 4; ++c) g[j][c] = logsigmoid_fast(g[j][c] + abias[c]);
                 }
-                const f32x4 bl = to4(*reinterpret_cast<const bf16x4 *>(reinterpret_cast<const bf16 *>(a.b) + off));
+                const f32x4 bl = to4(*reinterpret_cast<const bf16x4 *>(reinterpret_cast<const bf16 *>(a.b) + offg));
 #pragma unroll
                 for (int c = 0; c < 4; ++c) bk[j][c] = sigmoid1(bl[c]);
             } else {
@@ -314,7 +315,8 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(ChunkArgs a) {
         if (i < len) {
             const size_t off = ((size_t)(tok0 + i) * H + h) * DK + c0;  // Dv == Dk
             if constexpr (kLogits)
-                zw[j] = *reinterpret_cast<const bf16x4 *>(reinterpret_cast<const bf16 *>(a.w) + off);
+                zw[j] = *reinterpret_cast<const bf16x4 *>(reinterpret_cast<const bf16 *>(a.w) +
+                                                          (size_t)(tok0 + i) * a.ld_gate + (size_t)h * DK + c0);
             else
                 zw[j] = *reinterpret_cast<const f32x4 *>(a.w + off);
             zv[j] = *reinterpret_cast<const Vec4<E> *>(v + off);

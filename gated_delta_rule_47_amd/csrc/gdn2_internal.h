@@ -39,6 +39,8 @@ struct ChunkArgs {
     float *ws_gl;
     int store_T;          // the chunk-factor kernel also stores T = (I + A)^-1
     int gate_logits;      // log_alpha, b, w are bf16: log alpha and the logits of b and w
+    long long ld_gate;    // with gate_logits: elements between consecutive tokens of
+                          // log_alpha, b and w (H * Dk when they are separate arrays)
     const float *alpha_bias;  // with gate_logits: if set, log_alpha holds logits and
                               // log alpha = logsigmoid(log_alpha + alpha_bias[h][c])
     bf16_t *ws_Sc;        // if set, the propagation stores every chunk's incoming
@@ -92,7 +94,8 @@ struct LayerArgs {
     const float *conv_w, *norm_w;
     bf16_t *q, *k, *v;    // mix_in outputs [M][H*D]
     const bf16_t *o;      // core output [M][H*D]
-    const bf16_t *gate;   // output-gate logits [M][H*D]
+    const bf16_t *gate;   // output-gate logits [M][ldg] (the first H*D columns used)
+    long long ldg;
     bf16_t *z;            // mix_out output [M][H*D]
     const int32_t *cu_seqlens;
     int M, H, T, N, L;

@@ -14,8 +14,8 @@
 // one weight vector shared by the heads; the output gate is a sigmoid.
 //
 // Data flow for M tokens (all bf16 in HBM, fp32 arithmetic in registers):
-//   P   = x W_in[q|k|v]^T              [M, 3 HD]   (GEMM)
-//   al, gt, bl, wl = x W_{alpha,gate,b,w}^T   [M, HD] each (GEMMs; logits)
+//   P   = x W_in^T                     [M, 7 HD]   (one GEMM), column blocks
+//         q | k | v | al | gt | bl | wl (the last four are logits)
 //   mix_in:  q, k, v                   [M, HD] each, from P
 //   core:    o = the chunk forward with all three gates as logits: log alpha =
 //            logsigmoid(al + alpha_bias), b = sigmoid(bl), w = sigmoid(wl),
@@ -209,7 +209,7 @@ __global__ __launch_bounds__(256) void layer_mix_out_kernel(LayerArgs a) {
     const size_t off = (size_t)m * HD + h * D + c0;
     float o[8], g[8];
     load8(a.o + off, o);
-    load8(a.gate + off, g);
+    load8(a.gate + (size_t)m * a.ldg + h * D + c0, g);
     float ss = 0.0f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) ss += o[e] * o[e];
