@@ -62,6 +62,15 @@ def test_bwd_varlen_edge_lengths():
     _check(inp, W.make_chunk_grads(inp, 13), "bwd varlen")
 
 
+@pytest.mark.parametrize("B", [4, 16])
+def test_bwd_many_chains(B):
+    """H = 16 with B = 4 and 16 (64 and 256 chains): the reverse pass's 32- and
+    64-column value slabs (the small cases above take 16-column slabs)."""
+    wl = W.ChunkWorkload("bwd_many", B, 70, 16, 128, 128, W.BF16, 4646 + B, with_S0=True)
+    inp = W.make_chunk_inputs(wl)
+    _check(inp, W.make_chunk_grads(inp, 15 + B), "bwd %d chains" % (B * 16))
+
+
 def test_bwd_erase_gate_to_two():
     wl = W.ChunkWorkload("bwd_b2", 1, 128, 2, 128, 128, W.BF16, 4545, with_S0=True)
     inp = W.make_chunk_inputs(wl, b_scale=2.0)

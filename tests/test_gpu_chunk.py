@@ -51,6 +51,15 @@ def test_varlen_edge_lengths(io):
     _check_all(W.make_chunk_inputs(wl, lengths=[1, 63, 64, 65, 130, 0, 7]), "varlen io=%s" % io)
 
 
+@pytest.mark.parametrize("io,B", [(W.BF16, 4), (W.BF16, 8), (W.F32, 4)])
+def test_slab_widths(io, B):
+    """H = 16 with B = 4 and 8 (64 and 128 chains): the propagation's 32- and
+    64-column value slabs at a size the oracle checks whole (the cases above
+    take 16-column slabs)."""
+    wl = W.ChunkWorkload("slab_test", B, 70, 16, 128, 128, io, 999 + B, with_S0=True)
+    _check_all(W.make_chunk_inputs(wl), "slabs io=%s chains=%d" % (io, 16 * B))
+
+
 def test_erase_gate_range_zero_to_two():
     """The kernels do not assume b <= 1 (widened [0, 2] erase range)."""
     wl = W.ChunkWorkload("b2_test", 1, 192, 2, 128, 128, W.BF16, 888, with_S0=True)
