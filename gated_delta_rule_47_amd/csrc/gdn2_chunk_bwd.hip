@@ -24,9 +24,9 @@
 //   dg = E dE + Ep dEp + Qhat dQhat + Qp dQp - Kp dKp - Khat dKhat,
 //   dlog_alpha_j = sum_{i>=j} dg_i + gl dgl + sum_i Khat_i dKhat_i.
 //
-// Three kernels after the forward (chunk factors with T and, for backward
-// calls, their transposes M^T, Khat, Qhat^T, W^T, T^T; the propagation storing
-// every chunk's incoming state):
+// Three kernels after the forward (the chunk factors a backward call needs:
+// W, Khat^T, U, gamma_last and the transposes M^T, Khat, Qhat^T, W^T, T^T; the
+// propagation storing every chunk's incoming state and forming no o):
 //   chunk_bwd_rev_kernel     sequential over the chunks of a sequence, in
 //                            reverse: dU_eff and dS, storing each chunk's dS'
 //   chunk_bwd_state_kernel   per chunk: the state-side products, dv and dw

@@ -51,7 +51,8 @@ struct ChunkArgs {
     void *ws_Mt, *ws_Kh, *ws_Qt, *ws_Wt, *ws_Tt;
 };
 
-// The backward's workspace: the forward's layout (T always stored), the
+// The backward's workspace: the forward's layout (its T, Qhat and M regions
+// unused), the
 // transposed chunk factors (io dtype, fragment order), then arrays indexed
 // [chunk id][head][...]: every chunk's incoming state Sc and the gradient dSc
 // of its outgoing state (bf16 Dk x Dv, laid out by sc_index); the state-side
