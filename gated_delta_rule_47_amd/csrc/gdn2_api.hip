@@ -92,11 +92,11 @@ bool bwd_layout(int N, int B, int T, int H, int Dk, int Dv, size_t io_bytes, boo
     L.off_Tt = take(chd * kChunk * kChunk * io_bytes);
     L.off_Sc = take(chd * Dk * Dv * 2);
     L.off_dSc = take(chd * Dk * Dv * 2);
-    L.off_dKh = take(chd * kChunk * Dk * sizeof(float));
+    L.off_dKh = take(chd * kChunk * Dk * 2);
     L.off_dWt = take(chd * Dk * kChunk * 2);
     L.off_dM = take(chd * kChunk * kChunk * 2);
     L.off_dMt = take(chd * kChunk * kChunk * 2);
-    L.off_dAp = take(chd * kChunk * kChunk * sizeof(float));
+    L.off_dAp = take(chd * kChunk * kChunk * 2);
     L.off_dG = take(chd * Dk * sizeof(float));
     L.total = off;
     *out = L;
@@ -362,11 +362,11 @@ int gdn2_chunk_bwd(const void *q, const void *k, const void *v, const float *log
     ba.dS0 = dS0;
     ba.Sc = a.ws_Sc;
     ba.dSc = reinterpret_cast<bf16_t *>(ws + L.off_dSc);
-    ba.dKh = reinterpret_cast<float *>(ws + L.off_dKh);
+    ba.dKh = reinterpret_cast<bf16_t *>(ws + L.off_dKh);
     ba.dWt = reinterpret_cast<bf16_t *>(ws + L.off_dWt);
     ba.dM = reinterpret_cast<bf16_t *>(ws + L.off_dM);
     ba.dMt = reinterpret_cast<bf16_t *>(ws + L.off_dMt);
-    ba.dAp = reinterpret_cast<float *>(ws + L.off_dAp);
+    ba.dAp = reinterpret_cast<bf16_t *>(ws + L.off_dAp);
     ba.dG = reinterpret_cast<float *>(ws + L.off_dG);
 
     hipError_t err = hipSuccess;

@@ -457,8 +457,8 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_state_kernel(BwdArgs ba
 #pragma unroll
     for (int o = 1; o < TPR; o <<= 1) dgp += __shfl_xor(dgp, o, TPR);
     if ((tid % TPR) == 0) ba.dG[ch * DK + srow] = dgp;
-    float *oK = ba.dKh + ch * kChunk * DK;
-    float *oA = ba.dAp + ch * kChunk * kChunk;
+    bf16 *oK = ba.dKh + ch * kChunk * DK;
+    bf16 *oA = ba.dAp + ch * kChunk * kChunk;
     bf16 *oWt = ba.dWt + ch * DK * kChunk;      // dW^T, fragment order
     bf16 *oM = ba.dM + ch * kChunk * kChunk;    // dM, fragment order
     bf16 *oMt = ba.dMt + ch * kChunk * kChunk;  // dM^T, fragment order
@@ -467,7 +467,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_state_kernel(BwdArgs ba
     for (int cb = 0; cb < NKB; ++cb) {
         const int c = 16 * cb + (lane & 15);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) oK[(i0 + r) * DK + c] = dKh[cb][r];
+        for (int r = 0; r < 4; ++r) oK[(i0 + r) * DK + c] = static_cast<bf16>(dKh[cb][r]);
         store4_frag<bf16>(oWt, kChunk, c, i0, -dWt[cb]);
     }
 #pragma unroll
@@ -477,7 +477,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_state_kernel(BwdArgs ba
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             m[r] = j <= i0 + r ? dMa[J][r] : 0.0f;
-            oA[(i0 + r) * kChunk + j] = dAp[J][r];
+            oA[(i0 + r) * kChunk + j] = static_cast<bf16>(dAp[J][r]);
             oM[frag_index<bf16>(i0 + r, j, kChunk)] = static_cast<bf16>(m[r]);
         }
         store4_frag<bf16>(oMt, kChunk, j, i0, m);
@@ -569,9 +569,9 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_factor_kernel(BwdArgs b
     // that their loads are in flight together.  Token rows past the chunk's end
     // read row 0 (always valid) and are zeroed or skipped where used.
     MB::frag fWd[4][NKD], fM[2], fMt[2], fdO[NKD];
-    float apv[4][4];
+    bf16 apv[4][4];  // raw, converted where used
     {
-        const float *Ap = ba.dAp + ch * kChunk * kChunk;
+        const bf16 *Ap = ba.dAp + ch * kChunk * kChunk;
 #pragma unroll
         for (int J = 0; J < 4; ++J) {
 #pragma unroll
@@ -621,7 +621,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_factor_kernel(BwdArgs b
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = 16 * I + 4 * (lane >> 4) + r, j = 16 * J + (lane & 15);
-                d[r] = j < i ? -(apv[J][r] + d[r]) : 0.0f;
+                d[r] = j < i ? -(static_cast<float>(apv[J][r]) + d[r]) : 0.0f;
             }
             store_tile<bf16>(sdA + 16 * I * L64 + 16 * J, L64, d, lane);
             store_tile_t<bf16>(sdAt + 16 * I + 16 * J * L64, L64, d, lane);
@@ -641,7 +641,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_factor_kernel(BwdArgs b
         for (int kk = 0; kk < NKD; ++kk) fdO[kk] = MB::zero();
     }
     const bf16 *Sc = ba.Sc + ch * DK * DK;
-    const float *dKg = ba.dKh + ch * kChunk * DK;
+    const bf16 *dKg = ba.dKh + ch * kChunk * DK;
     bf16 *dqo = reinterpret_cast<bf16 *>(ba.dq), *dko = reinterpret_cast<bf16 *>(ba.dk);
 
 #pragma unroll
@@ -721,8 +721,8 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_factor_kernel(BwdArgs b
         // inputs, raw as loaded) are issued one block ahead.
         struct HbIn {
             MB::frag s[NKD];
-            bf16 k[4], q[4];
-            float b[4], dk[4];
+            bf16 k[4], q[4], dk[4];
+            float b[4];
         };
         auto load_hb = [&](HbIn &x, int hb) {
 #pragma unroll
@@ -768,7 +768,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_factor_kernel(BwdArgs b
                     const size_t off = ((size_t)(tok0 + i) * H + h) * DK + c;
                     const float kf = static_cast<float>(x.k[r]), qf = static_cast<float>(x.q[r]);
                     const float bf = x.b[r];
-                    const float dKh = x.dk[r];
+                    const float dKh = static_cast<float>(x.dk[r]);
                     const float gg = sG[i * LDG + cl];
                     const float ex = __expf(gg - gr_c), ei = __expf(gr_c - gg);
                     const float gam = ex * egr, eK = ei * egr;

@@ -57,8 +57,8 @@ struct ChunkArgs {
 // [chunk id][head][...]: every chunk's incoming state Sc and the gradient dSc
 // of its outgoing state (bf16 Dk x Dv, laid out by sc_index); the state-side
 // partial gradients
-// dKh (fp32 [64][Dk]), dW^T (bf16 fragment order [Dk][64]), dM and dM^T
-// (bf16 fragment order [64][64]), dAp = dZ U^T (fp32 [64][64]) and dG =
+// dKh (bf16 [64][Dk]), dW^T (bf16 fragment order [Dk][64]), dM and dM^T
+// (bf16 fragment order [64][64]), dAp = dZ U^T (bf16 [64][64]) and dG =
 // rowsum(dSc * Sc) (fp32 [Dk]).
 // Element (c, v) of a per-chunk bf16 state (Sc, dSc) of Dk rows: 32-column
 // slabs [v / 32][c][v % 32], so that a slab is one contiguous block and a
@@ -85,7 +85,8 @@ struct BwdArgs {
     void *dq, *dk, *dv;
     float *dla, *db, *dw, *dS0;
     bf16_t *Sc, *dSc, *dWt, *dM, *dMt;
-    float *dKh, *dAp, *dG;
+    bf16_t *dKh, *dAp;
+    float *dG;
 };
 
 // Token-mixer layer: the element-wise kernels around the core.
