@@ -108,11 +108,14 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
         for (int j = 0; j < 4; ++j) oo[j] = from_f32<IO>(p[j] + qk * u[j]);
     }
 
+    // The new state is stored non-temporally: it is read again only by the
+    // next step's launch, and keeping it out of the caches measured 6.5% more
+    // bandwidth at B = 256, H = 16 (non-temporal loads measured slower).
 #pragma unroll
     for (int m = 0; m < RPT; ++m) {
         const f32x4 cf = coef[rg + NRG * m];
         const f32x4 snew = cf[0] * s[m] + cf[3] * u;
-        *reinterpret_cast<f32x4 *>(S + (size_t)(rg + NRG * m) * DV + 4 * cq) = snew;
+        __builtin_nontemporal_store(snew, reinterpret_cast<f32x4 *>(S + (size_t)(rg + NRG * m) * DV + 4 * cq));
     }
 }
 
