@@ -329,7 +329,7 @@ __device__ __forceinline__ void ws_pipe(StageRegs<WsCfg<DK, DVS>::NJ> &buf, char
 
 // Loader side: the O rows of one chunk (staged in LDS by the compute waves)
 // to global memory, 16 bytes per lane, the slab's part of each token row
-// contiguous.
+// contiguous, stored non-temporally (o is not read again by this call).
 template <int DK, int DV, int DVS>
 __device__ __forceinline__ void ws_store_o(const ChunkArgs &a, const bf16 *sO, int h, int tok0, int len,
                                            int col0, int t) {
@@ -339,8 +339,8 @@ __device__ __forceinline__ void ws_store_o(const ChunkArgs &a, const bf16 *sO, i
     for (int g = t; g < kChunk * C::GPR_O; g += kThreads) {
         const int row = g / C::GPR_O, piece = g % C::GPR_O;
         if (row < len)
-            *reinterpret_cast<granule_t *>(out + ((size_t)(tok0 + row) * a.H + h) * DV + col0 + 8 * piece) =
-                *reinterpret_cast<const granule_t *>(sO + row * C::LDO + 8 * piece);
+            __builtin_nontemporal_store(*reinterpret_cast<const granule_t *>(sO + row * C::LDO + 8 * piece),
+                                        reinterpret_cast<granule_t *>(out + ((size_t)(tok0 + row) * a.H + h) * DV + col0 + 8 * piece));
     }
 }
 
