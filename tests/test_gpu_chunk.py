@@ -66,6 +66,27 @@ def test_erase_gate_range_zero_to_two():
     _check_all(W.make_chunk_inputs(wl, b_scale=2.0), "b in [0,2]")
 
 
+def test_long_sequence():
+    """One 32768-token sequence (512 chunks in one chain), H = 2, nonzero S0:
+    the state carried through a long propagation, whole output checked."""
+    wl = W.ChunkWorkload("long_test", 1, 32768, 2, 128, 128, W.BF16, 5151, with_S0=True)
+    _check_all(W.make_chunk_inputs(wl), "long sequence T=32768")
+
+
+@pytest.mark.parametrize("case", ["no_decay_no_erase", "strong_decay"])
+def test_degenerate_gates(case):
+    """Gate settings at the ends of their ranges: log alpha = 0 with b = 0 (the
+    state only accumulates, linear attention), and per-token decay of 2 to
+    2.5 nats (up to 160 nats per chunk, near the decay precondition), where the
+    midpoint-scaled factors span e^{+-80}."""
+    wl = W.ChunkWorkload("degen_test", 2, 200, 2, 128, 128, W.BF16, 6161, with_S0=True)
+    if case == "no_decay_no_erase":
+        inp = W.make_chunk_inputs(wl, log_alpha_range=(0.0, 0.0), b_scale=0.0)
+    else:
+        inp = W.make_chunk_inputs(wl, log_alpha_range=(-2.5, -2.0))
+    _check_all(inp, "degenerate gates: %s" % case)
+
+
 def test_empty_sequence_returns_initial_state():
     import torch
     wl = W.ChunkWorkload("empty_test", 2, 64, 2, 128, 128, W.BF16, 999, with_S0=True)
