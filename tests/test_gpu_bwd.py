@@ -71,6 +71,18 @@ def test_bwd_many_chains(B):
     _check(inp, W.make_chunk_grads(inp, 15 + B), "bwd %d chains" % (B * 16))
 
 
+@pytest.mark.parametrize("case", ["no_decay_no_erase", "strong_decay"])
+def test_bwd_degenerate_gates(case):
+    """log alpha = 0 with b = 0, and 2 to 2.5 nats of decay per token (up to
+    160 per chunk, near the decay precondition)."""
+    wl = W.ChunkWorkload("bwd_degen", 2, 150, 2, 128, 128, W.BF16, 4747, with_S0=True)
+    if case == "no_decay_no_erase":
+        inp = W.make_chunk_inputs(wl, log_alpha_range=(0.0, 0.0), b_scale=0.0)
+    else:
+        inp = W.make_chunk_inputs(wl, log_alpha_range=(-2.5, -2.0))
+    _check(inp, W.make_chunk_grads(inp, 16), "bwd %s" % case)
+
+
 def test_bwd_erase_gate_to_two():
     wl = W.ChunkWorkload("bwd_b2", 1, 128, 2, 128, 128, W.BF16, 4545, with_S0=True)
     inp = W.make_chunk_inputs(wl, b_scale=2.0)
