@@ -512,6 +512,10 @@ template <int DK>
 struct FacCfg {
     static constexpr int DH = DK / 2;                 // channels per half
     static constexpr int NQUAD = DH / 4, NTG = kThreads / NQUAD, TPG = kChunk / NTG;
+    // the loops over the NTG token groups' partial sums: fully unrolled for
+    // 128-wide heads; by 4 for 64-wide ones, whose 32 groups would otherwise
+    // hold 32 LDS reads in flight and spill
+    static constexpr int NTG_UNROLL = NTG > 16 ? 4 : NTG;
     static constexpr int L64 = kChunk + 8;            // bf16 [..][64]
     static constexpr int LDKP = DK + 8;               // bf16 [..][DK]
     static constexpr int LDG = DH + 4;                // fp32 [64][LDG]
@@ -668,7 +672,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_factor_kernel(BwdArgs b
             *reinterpret_cast<f32x4 *>(sR + tg * DH + cq) = g[TPG - 1];
             __syncthreads();
             f32x4 goff = zero4(), glast = zero4();
-#pragma unroll
+#pragma unroll C::NTG_UNROLL
             for (int t = 0; t < C::NTG; ++t) {
                 const f32x4 tt = *reinterpret_cast<const f32x4 *>(sR + t * DH + cq);
                 if (t < tg) goff += tt;
@@ -803,7 +807,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_factor_kernel(BwdArgs b
             *reinterpret_cast<f32x4 *>(sR + (C::NTG + tg) * DH + cq) = dgv[0];
             __syncthreads();
             f32x4 after = zero4();
-#pragma unroll
+#pragma unroll C::NTG_UNROLL
             for (int t = 0; t < C::NTG; ++t)
                 if (t > tg) after += *reinterpret_cast<const f32x4 *>(sR + (C::NTG + t) * DH + cq);
             f32x4 dglast;
