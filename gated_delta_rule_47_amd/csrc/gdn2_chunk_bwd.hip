@@ -93,7 +93,9 @@ template <int DK, int DVS>
 struct RevCfg {
     static constexpr int DV = DK, NS = DV / DVS, NCB = DVS / 16, NKB = DK / 16;
     static constexpr int KB_W = NKB / 4, S_TPW = KB_W * NCB;
-    static constexpr int LDKP = DK + 8, L64 = kChunk + 8;
+    static constexpr int LDKP = DK + 8, L64 = kChunk + 8, LDV = DVS + 8;
+    static constexpr int NP = DK * DVS / 8;                   // 16-byte pieces of dS'
+    static constexpr int NPC = (NP + kThreads - 1) / kThreads;  // per thread
 };
 
 template <int DK, int DVS>
@@ -105,6 +107,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_rev_kernel(BwdArgs ba) 
     __shared__ __attribute__((aligned(16))) bf16 sdSt[DVS * LDKP];  // [v][c] = dS'[c][v]
     __shared__ __attribute__((aligned(16))) bf16 sdOt[DVS * L64];   // [v][i] = dO[i][v]
     __shared__ __attribute__((aligned(16))) bf16 sdUt[DVS * L64];   // [v][i] = dU_eff[i][v]
+    __shared__ __attribute__((aligned(16))) bf16 sdS[DK * C::LDV];  // [c][v] = dS'[c][v]
 
     const int H = a.H;
     const int x = blockIdx.x, xcd = x & 7, rest = x >> 3;
@@ -175,19 +178,16 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_rev_kernel(BwdArgs ba) 
     if (kAhead && cend > cbeg) load_in(cur, cend - 1);
     for (int cid = cend - 1; cid >= cbeg; --cid) {
         const size_t ch = (size_t)cid * H + h;
-        if constexpr (kAhead) load_in(nxt, max(cid - 1, cbeg));
-        else load_in(cur, cid);
+        if constexpr (!kAhead) load_in(cur, cid);
         const int len = cur.len;
-        // dS' of this chunk: to the workspace (bf16, for the per-chunk kernels)
-        // and, transposed, to LDS.
-        bf16 *dSc = ba.dSc + ch * DK * DV;
+        // dS' of this chunk to LDS (bf16), as it is and transposed; the plain
+        // copy goes on to the workspace for the per-chunk kernels in 16-byte
+        // row pieces (2-byte stores straight from the accumulators cost more
+        // than the rest of the chunk's work).
 #pragma unroll
         for (int u = 0; u < C::S_TPW; ++u) {
             const int cblk = wave * C::KB_W + u / NCB, colb = u % NCB;
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                dSc[sc_index(16 * cblk + 4 * (lane >> 4) + r, col0 + 16 * colb + (lane & 15), DK)] =
-                    static_cast<bf16>(dS[u][r]);
+            store_tile<bf16>(sdS + 16 * cblk * C::LDV + 16 * colb, C::LDV, dS[u], lane);
             store_tile_t<bf16>(sdSt + 16 * colb * LDKP + 16 * cblk, LDKP, dS[u], lane);
         }
         // dO rows of the chunk (zero past its end), transposed.
@@ -203,6 +203,17 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_rev_kernel(BwdArgs ba) 
             for (int t = 0; t < 4; ++t) sdOt[(c4 + t) * L64 + i] = v4[t];
         }
         __syncthreads();
+        // (The next chunk's operands are requested only now: issued before the
+        // LDS stores above, they hold those stores back.)
+        if constexpr (kAhead) load_in(nxt, max(cid - 1, cbeg));
+        bf16 *dSc = ba.dSc + ch * DK * DV;
+#pragma unroll
+        for (int p = 0; p < C::NPC; ++p) {
+            const int e = tid + p * kThreads, c = e / (DVS / 8), v8 = 8 * (e % (DVS / 8));
+            if (C::NP % kThreads == 0 || e < C::NP)
+                *reinterpret_cast<bf16x8 *>(dSc + sc_index(c, col0 + v8, DK)) =
+                    *reinterpret_cast<const bf16x8 *>(sdS + c * C::LDV + v8);
+        }
 
         // dU_eff rows of block `wave`:  M^T dO + Khat dS'.
 #pragma unroll

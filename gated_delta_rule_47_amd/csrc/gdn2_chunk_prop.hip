@@ -286,6 +286,28 @@ struct WsCfg {
 
 typedef unsigned int granule_t __attribute__((ext_vector_type(4)));
 
+// A states-only call stages each chunk's incoming state, bf16 [Dk][DVS], in
+// the Qhat part of stage 0 (unused by such a call) so that it leaves in
+// 16-byte pieces.  Unpadded rows; the 16-byte granules of row c are permuted
+// by an even XOR key taken from c / 4, which puts the four row groups of an
+// accumulator tile store on different banks.
+template <int DVS>
+__device__ __forceinline__ int sr_index(int c, int v) {
+    constexpr int NGR = DVS / 8;
+    const int key = 2 * ((c >> 2) & (NGR / 2 - 1));
+    return c * DVS + (((v >> 3) ^ key) << 3) + (v & 7);
+}
+
+// Accumulator tile (state rows 16 cblk.., columns 16 colb.. of the slab) into
+// that order.
+template <int DVS>
+__device__ __forceinline__ void store_state_rows(bf16 *sSr, int cblk, int colb, f32x4 acc, int lane) {
+    const int v = 16 * colb + (lane & 15);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+        sSr[sr_index<DVS>(16 * cblk + 4 * (lane >> 4) + r, v)] = static_cast<bf16>(acc[r]);
+}
+
 template <int NJ>
 struct StageRegs {
     granule_t v[NJ];
@@ -358,6 +380,8 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_prop_ws_kernel(ChunkArg
     bf16 *sS = reinterpret_cast<bf16 *>(smem + 2 * C::SZ_STAGE);
     bf16 *sU = reinterpret_cast<bf16 *>(smem + 2 * C::SZ_STAGE + C::SZ_S);  // U_eff^T
     bf16 *sO = reinterpret_cast<bf16 *>(smem + 2 * C::SZ_STAGE + C::SZ_S + C::SZ_U);  // O, row-major
+    bf16 *sSr = reinterpret_cast<bf16 *>(smem + (size_t)C::NG_W * 16);  // kStates: S, sr_index order
+    static_assert(!kStates || DK * DVS * 2 <= C::NG_W * 16, "state rows fit the Qhat stage part");
 
     const int H = a.H;
     const int x = blockIdx.x, xcd = x & 7, rest = x >> 3;
@@ -475,6 +499,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_prop_ws_kernel(ChunkArg
             Sacc[u][r] = a.S0 ? a.S0[((size_t)chain * DK + c) * DV + col] : 0.0f;
         }
         store_tile_t<bf16>(sS + 16 * colb * LDS_ + 16 * cblk, LDS_, Sacc[u], lane);
+        if constexpr (kStates) store_state_rows<DVS>(sSr, cblk, colb, Sacc[u], lane);
     }
     // The loader's steps 0 and 1 (the first chunk reaches stage 0).
 #pragma unroll
@@ -483,13 +508,13 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_prop_ws_kernel(ChunkArg
     for (int cid = cbeg; cid < cend; ++cid) {
         if constexpr (kStates) {  // the incoming state of this chunk, bf16 [Dk][Dv]
             bf16 *Sc = a.ws_Sc + ((size_t)cid * H + h) * DK * DV;
+            constexpr int NP = DK * DVS / 8, NPC = (NP + kThreads - 1) / kThreads;
 #pragma unroll
-            for (int u = 0; u < C::S_TPW; ++u) {
-                const int cblk = wave * C::KB_W + u / NCB, colb = u % NCB;
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    Sc[sc_index(16 * cblk + 4 * (lane >> 4) + r, col0 + 16 * colb + (lane & 15), DK)] =
-                        static_cast<bf16>(Sacc[u][r]);
+            for (int p = 0; p < NPC; ++p) {
+                const int e = tid + p * kThreads, c = e / (DVS / 8), v8 = 8 * (e % (DVS / 8));
+                if (NP % kThreads == 0 || e < NP)
+                    *reinterpret_cast<granule_t *>(Sc + sc_index(c, col0 + v8, DK)) =
+                        *reinterpret_cast<const granule_t *>(sSr + sr_index<DVS>(c, v8));
             }
         }
         load_own(nxt2, min(cid + 2, cend - 1));
@@ -573,6 +598,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_prop_ws_kernel(ChunkArg
                 Sacc[u] = cur.gl[b] * Sacc[u] + d[u];
                 store_tile_t<bf16>(sS + 16 * colb * LDS_ + 16 * (wave * C::KB_W + b), LDS_, Sacc[u],
                                    lane);
+                if constexpr (kStates) store_state_rows<DVS>(sSr, wave * C::KB_W + b, colb, Sacc[u], lane);
             }
         }
         __syncthreads();
