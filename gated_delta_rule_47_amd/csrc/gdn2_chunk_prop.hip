@@ -440,6 +440,22 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_prop_ws_kernel(ChunkArg
                 ws_store_o<DK, DV, DVS>(a, sO, h, tok0, min(kChunk, seq_end - tok0), col0_, t);
             }
         };
+        // kStates: the incoming state of chunk k, staged by the compute waves
+        // before the barrier that ends chunk k-1 and rewritten only after the
+        // mid-chunk barrier of chunk k, to the workspace.
+        auto store_sc = [&](int k) {
+            if constexpr (kStates) {
+                bf16 *Sc = a.ws_Sc + ((size_t)(cbeg + k) * H + h) * DK * DV;
+                constexpr int NP = DK * DVS / 8, NPC = (NP + kThreads - 1) / kThreads;
+#pragma unroll
+                for (int p = 0; p < NPC; ++p) {
+                    const int e = t + p * kThreads, c = e / (DVS / 8), v8 = 8 * (e % (DVS / 8));
+                    if (NP % kThreads == 0 || e < NP)
+                        *reinterpret_cast<granule_t *>(Sc + sc_index(c, col0_ + v8, DK)) =
+                            *reinterpret_cast<const granule_t *>(sSr + sr_index<DVS>(c, v8));
+                }
+            }
+        };
         auto chunk_head = [&](int k) { return (size_t)(cbeg + min(k, nch - 1)) * H + h; };
         StageRegs<NJ> buf0, buf1;
 #pragma unroll
@@ -451,11 +467,13 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_prop_ws_kernel(ChunkArg
         const int nsteps = (nch + 3) & ~1;  // nch + 2, rounded up to even
         for (int it = 0; it < nsteps; it += 2) {
             if (it >= 3 && it - 3 < nch) store_o(it - 3);
+            if (kStates && it >= 2 && it - 2 < nch) store_sc(it - 2);
             ws_pipe<DK, DVS, 0, NJ2, kStates>(buf0, smem + C::SZ_STAGE, a, chunk_head(it + 1), t);
             __syncthreads();
             ws_pipe<DK, DVS, NJ2, NJ, kStates>(buf0, smem + C::SZ_STAGE, a, chunk_head(it + 1), t);
             __syncthreads();
             if (it + 1 >= 3 && it - 2 < nch) store_o(it - 2);
+            if (kStates && it + 1 >= 2 && it - 1 < nch) store_sc(it - 1);
             ws_pipe<DK, DVS, 0, NJ2, kStates>(buf1, smem, a, chunk_head(it + 2), t);
             __syncthreads();
             ws_pipe<DK, DVS, NJ2, NJ, kStates>(buf1, smem, a, chunk_head(it + 2), t);
@@ -506,17 +524,6 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_prop_ws_kernel(ChunkArg
     for (int j = 0; j < 4; ++j) __syncthreads();
 
     for (int cid = cbeg; cid < cend; ++cid) {
-        if constexpr (kStates) {  // the incoming state of this chunk, bf16 [Dk][Dv]
-            bf16 *Sc = a.ws_Sc + ((size_t)cid * H + h) * DK * DV;
-            constexpr int NP = DK * DVS / 8, NPC = (NP + kThreads - 1) / kThreads;
-#pragma unroll
-            for (int p = 0; p < NPC; ++p) {
-                const int e = tid + p * kThreads, c = e / (DVS / 8), v8 = 8 * (e % (DVS / 8));
-                if (NP % kThreads == 0 || e < NP)
-                    *reinterpret_cast<granule_t *>(Sc + sc_index(c, col0 + v8, DK)) =
-                        *reinterpret_cast<const granule_t *>(sSr + sr_index<DVS>(c, v8));
-            }
-        }
         load_own(nxt2, min(cid + 2, cend - 1));
         const bf16 *stage = reinterpret_cast<const bf16 *>(smem + ((cid - cbeg) & 1) * C::SZ_STAGE);
         const bf16 *Wf = stage;
