@@ -429,15 +429,23 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_state_kernel(BwdArgs ba
                     dz = MB::mma(fTt[kk],
                                  load_frag<bf16>(sdUt + 16 * cb * L64 + 32 * kk, L64, lane), dz);
                 store_tile<bf16>(sdZ + 16 * I * LSW + 16 * cb, LSW, dz, lane);
+                // dv and dw as row pieces (quad transpose: 4 columns of one token per lane)
+                f32x4 dvv, dwv;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int i = 16 * I + 4 * (lane >> 4) + r, vv = 16 * cb + (lane & 15);
-                    if (i < len) {
-                        const size_t o = ((size_t)(tok0 + i) * H + h) * DV + v0 + vv;
-                        dv[o] = static_cast<bf16>(wv[cb][r] * dz[r]);
-                        ba.dw[o] = static_cast<float>(vv_[cb][r]) * dz[r];
-                    }
+                    dvv[r] = wv[cb][r] * dz[r];
+                    dwv[r] = static_cast<float>(vv_[cb][r]) * dz[r];
                 }
+                const int i = 16 * I + 4 * (lane >> 4) + (lane & 3);
+                const size_t o = ((size_t)(tok0 + (i < len ? i : 0)) * H + h) * DV + v0 + 16 * cb +
+                                 4 * ((lane >> 2) & 3);
+                dvv = quad_transpose(dvv, lane);
+                if (i < len)
+                    *reinterpret_cast<bf16x4 *>(dv + o) =
+                        bf16x4{static_cast<bf16>(dvv[0]), static_cast<bf16>(dvv[1]), static_cast<bf16>(dvv[2]),
+                               static_cast<bf16>(dvv[3])};
+                dwv = quad_transpose(dwv, lane);
+                if (i < len) *reinterpret_cast<f32x4 *>(ba.dw + o) = dwv;
             }
         }
         // Products accumulated over the slabs (k = the slab's 32 columns).
@@ -473,12 +481,17 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_state_kernel(BwdArgs ba
     bf16 *oWt = ba.dWt + ch * DK * kChunk;      // dW^T, fragment order
     bf16 *oM = ba.dM + ch * kChunk * kChunk;    // dM, fragment order
     bf16 *oMt = ba.dMt + ch * kChunk * kChunk;  // dM^T, fragment order
-    const int i0 = 16 * I + 4 * (lane >> 4);
+    // Row-major and row-fragment results leave as row pieces after a quad
+    // transpose (row it, columns 4 lq ..); the transposed ones as they are.
+    const int i0 = 16 * I + 4 * (lane >> 4), it = 16 * I + 4 * (lane >> 4) + (lane & 3);
+    const int lq = (lane >> 2) & 3;
 #pragma unroll
     for (int cb = 0; cb < NKB; ++cb) {
         const int c = 16 * cb + (lane & 15);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) oK[(i0 + r) * DK + c] = static_cast<bf16>(dKh[cb][r]);
+        const f32x4 kt = quad_transpose(dKh[cb], lane);
+        *reinterpret_cast<bf16x4 *>(oK + it * DK + 16 * cb + 4 * lq) =
+            bf16x4{static_cast<bf16>(kt[0]), static_cast<bf16>(kt[1]), static_cast<bf16>(kt[2]),
+                   static_cast<bf16>(kt[3])};
         store4_frag<bf16>(oWt, kChunk, c, i0, -dWt[cb]);
     }
 #pragma unroll
@@ -486,12 +499,13 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_state_kernel(BwdArgs ba
         const int j = 16 * J + (lane & 15);
         f32x4 m;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            m[r] = j <= i0 + r ? dMa[J][r] : 0.0f;
-            oA[(i0 + r) * kChunk + j] = static_cast<bf16>(dAp[J][r]);
-            oM[frag_index<bf16>(i0 + r, j, kChunk)] = static_cast<bf16>(m[r]);
-        }
+        for (int r = 0; r < 4; ++r) m[r] = j <= i0 + r ? dMa[J][r] : 0.0f;
         store4_frag<bf16>(oMt, kChunk, j, i0, m);
+        const f32x4 at = quad_transpose(dAp[J], lane);
+        *reinterpret_cast<bf16x4 *>(oA + it * kChunk + 16 * J + 4 * lq) =
+            bf16x4{static_cast<bf16>(at[0]), static_cast<bf16>(at[1]), static_cast<bf16>(at[2]),
+                   static_cast<bf16>(at[3])};
+        store4_frag<bf16>(oM, kChunk, it, 16 * J + 4 * lq, quad_transpose(m, lane));
     }
 }
 
@@ -775,12 +789,13 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_factor_kernel(BwdArgs b
             const float gl_c = sGl[cl], gr_c = 0.5f * gl_c, egr = __expf(gr_c);
             const f32x4 dEc = dE[half * NHB + hb];
             float kdk = 0.0f;
+            f32x4 dqv, dkv, dbv;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = 16 * I + 4 * (lane >> 4) + r;
                 float dg = 0.0f;
+                dqv[r] = dkv[r] = dbv[r] = 0.0f;
                 if (i < len) {
-                    const size_t off = ((size_t)(tok0 + i) * H + h) * DK + c;
                     const float kf = static_cast<float>(x.k[r]), qf = static_cast<float>(x.q[r]);
                     const float bf = x.b[r];
                     const float dKh = static_cast<float>(x.dk[r]);
@@ -790,13 +805,32 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_factor_kernel(BwdArgs b
                     const float t1 = gam * dEc[r] + ex * dEp[r];
                     const float dq = gam * dQh[r] + ex * dQp[r];
                     const float kpart = ei * dKp[r] + eK * dKh;
-                    dqo[off] = static_cast<bf16>(dq);
-                    dko[off] = static_cast<bf16>(bf * t1 + kpart);
-                    ba.db[off] = kf * t1;
+                    dqv[r] = dq;
+                    dkv[r] = bf * t1 + kpart;
+                    dbv[r] = kf * t1;
                     dg = bf * kf * t1 + qf * dq - kf * kpart;
                     kdk += kf * eK * dKh;
                 }
                 sG[i * LDG + cl] = dg;  // each element is read, then overwritten, by this lane only
+            }
+            // dq, dk, db leave as row pieces (4 channels of one token per lane)
+            // after a transpose inside each lane quad: one 8- or 16-byte store
+            // per lane instead of four 2- or 4-byte ones.
+            dqv = quad_transpose(dqv, lane);
+            dkv = quad_transpose(dkv, lane);
+            dbv = quad_transpose(dbv, lane);
+            {
+                const int i = 16 * I + 4 * (lane >> 4) + (lane & 3);
+                if (i < len) {
+                    const size_t off = ((size_t)(tok0 + i) * H + h) * DK + cbase + 16 * hb + 4 * ((lane >> 2) & 3);
+                    *reinterpret_cast<bf16x4 *>(dqo + off) =
+                        bf16x4{static_cast<bf16>(dqv[0]), static_cast<bf16>(dqv[1]), static_cast<bf16>(dqv[2]),
+                               static_cast<bf16>(dqv[3])};
+                    *reinterpret_cast<bf16x4 *>(dko + off) =
+                        bf16x4{static_cast<bf16>(dkv[0]), static_cast<bf16>(dkv[1]), static_cast<bf16>(dkv[2]),
+                               static_cast<bf16>(dkv[3])};
+                    *reinterpret_cast<f32x4 *>(ba.db + off) = dbv;
+                }
             }
             // sum over this wave's 16 tokens: 4 per lane, then the 4 lane groups
             kdk += __shfl_xor(kdk, 16);

@@ -42,6 +42,30 @@ __device__ __forceinline__ float logsigmoid_fast(float z) {
     return fminf(z, 0.0f) - log1p_unit(exp2_hw(-1.4426950408889634f * fabsf(z)));
 }
 
+// Value of lane l ^ kXor (kXor = 1 or 2) inside each group of four lanes
+// (DPP quad permutation [1,0,3,2] or [2,3,0,1]).
+template <int kXor>
+__device__ __forceinline__ float quad_xor(float x) {
+    static_assert(kXor == 1 || kXor == 2, "quad partner");
+    constexpr int ctrl = kXor == 1 ? 0xB1 : 0x4E;
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), ctrl, 0xF, 0xF, false));
+}
+
+// 4x4 transpose inside each group of four lanes: lane 4m + j enters with
+// x[r] = X[r][j] of its group's block and leaves with x[c] = X[j][c].  On an
+// MFMA accumulator tile (lane l: D[4(l/16) + r][l%16]) this leaves lane l
+// with row 4(l/16) + l%4, columns 4((l/4)%4) .. +3.
+__device__ __forceinline__ f32x4 quad_transpose(f32x4 x, int lane) {
+    const bool odd = lane & 1, hi = lane & 2;
+    // the off-diagonal elements of each 2x2 block, with lane j ^ 1
+    float r0 = quad_xor<1>(odd ? x[0] : x[1]), r1 = quad_xor<1>(odd ? x[2] : x[3]);
+    const f32x4 y = odd ? f32x4{r0, x[1], r1, x[3]} : f32x4{x[0], r0, x[2], r1};
+    // the off-diagonal 2x2 blocks, with lane j ^ 2
+    r0 = quad_xor<2>(hi ? y[0] : y[2]);
+    r1 = quad_xor<2>(hi ? y[1] : y[3]);
+    return hi ? f32x4{r0, r1, y[2], y[3]} : f32x4{y[0], y[1], r0, r1};
+}
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 
