@@ -27,8 +27,9 @@
 // Three kernels after the forward (the chunk factors a backward call needs:
 // W, Khat^T, U, gamma_last and the transposes M^T, Khat, Qhat^T, W^T, T^T; the
 // propagation storing every chunk's incoming state and forming no o):
-//   chunk_bwd_rev_kernel     sequential over the chunks of a sequence, in
-//                            reverse: dU_eff and dS, storing each chunk's dS'
+//   chunk_bwd_rev2_kernel    sequential over the chunks of a sequence, in
+//   (chunk_bwd_rev_kernel    reverse: dU_eff and dS, storing each chunk's dS'
+//    with 256+ chains)
 //   chunk_bwd_state_kernel   per chunk: the state-side products, dv and dw
 //   chunk_bwd_factor_kernel  per chunk: the factor side, dq, dk, db, dlog_alpha
 // All products are bf16 MFMA (16x16x32) with fp32 accumulation; each operand is
@@ -129,10 +130,10 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_rev_kernel(BwdArgs ba) 
         }
     }
     const bf16 *dout = reinterpret_cast<const bf16 *>(ba.dout);
-    // Everything a chunk reads from global memory, loaded one chunk ahead (the
-    // chunks run last to first): M^T and Khat rows of block `wave`, Qhat^T and
-    // W^T rows of this wave's state row blocks, gamma_last, and this thread's
-    // dO pieces (raw; rows past the chunk's end read row 0, zeroed at use).
+    // Everything a chunk reads from global memory: M^T and Khat rows of block
+    // `wave`, Qhat^T and W^T rows of this wave's state row blocks, gamma_last,
+    // and this thread's dO pieces (raw; rows past the chunk's end read row 0,
+    // zeroed at use).
     constexpr int NE = kChunk * DVS / 4 / kThreads;
     static_assert(NE * kThreads * 4 == kChunk * DVS, "dO split");
     struct RevIn {
@@ -171,14 +172,12 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_rev_kernel(BwdArgs ba) 
             x.o[q] = *reinterpret_cast<const bf16x4 *>(dout + off);
         }
     };
-    // (With 64-column slabs a second register set would drop 128-wide heads to
-    // one wave per SIMD: those load each chunk's operands at its start.)
-    constexpr bool kAhead = DVS <= 32;
-    RevIn cur, nxt;
-    if (kAhead && cend > cbeg) load_in(cur, cend - 1);
+    // (A second register set, to load a chunk ahead, would drop 128-wide heads
+    // to one wave per SIMD: each chunk's operands are loaded at its start.)
+    RevIn cur;
     for (int cid = cend - 1; cid >= cbeg; --cid) {
         const size_t ch = (size_t)cid * H + h;
-        if constexpr (!kAhead) load_in(cur, cid);
+        load_in(cur, cid);
         const int len = cur.len;
         // dS' of this chunk to LDS (bf16), as it is and transposed; the plain
         // copy goes on to the workspace for the per-chunk kernels in 16-byte
@@ -203,9 +202,6 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_rev_kernel(BwdArgs ba) 
             for (int t = 0; t < 4; ++t) sdOt[(c4 + t) * L64 + i] = v4[t];
         }
         __syncthreads();
-        // (The next chunk's operands are requested only now: issued before the
-        // LDS stores above, they hold those stores back.)
-        if constexpr (kAhead) load_in(nxt, max(cid - 1, cbeg));
         bf16 *dSc = ba.dSc + ch * DK * DV;
 #pragma unroll
         for (int p = 0; p < C::NPC; ++p) {
@@ -242,7 +238,6 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_rev_kernel(BwdArgs ba) 
             dS[u] = cur.gl[b] * dS[u] + q - wu;
         }
         __syncthreads();
-        if constexpr (kAhead) cur = nxt;
     }
     if (ba.dS0) {
 #pragma unroll
@@ -251,6 +246,225 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_rev_kernel(BwdArgs ba) 
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = 16 * cblk + 4 * (lane >> 4) + r, col = col0 + 16 * colb + (lane & 15);
+                ba.dS0[((size_t)chain * DK + row) * DV + col] = dS[u][r];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Reverse pass with shared factor reads: one workgroup of 8 waves per
+// (sequence, head, 2*SUB-column slab).  Waves 0-3 and 4-7 each run the form
+// above on SUB columns.  The chunk's factors (M^T, Khat, Qhat^T, W^T in
+// fragment order) are read from the workspace once per workgroup, by all
+// 512 threads, into registers one chunk ahead, and staged in LDS at the
+// chunk's start; the four waves of a half read their fragments from there.
+// The per-CU vector-memory path bounds this pass, and the two halves now
+// share one read of the factors.
+// ---------------------------------------------------------------------------
+template <int DK, int SUB>
+struct Rev2Cfg {
+    static constexpr int DV = DK, WC = 2 * SUB, NS = DV / WC, NCB = SUB / 16, NKB = DK / 16;
+    static constexpr int KB_W = NKB / 4, S_TPW = KB_W * NCB;
+    static constexpr int LDKP = DK + 8, L64 = kChunk + 8, LDV = WC + 8;
+    static constexpr int NT = 2 * kThreads;
+    // 16-byte granules of M^T, and of each of Khat, Qhat^T, W^T
+    static constexpr int GM = kChunk * kChunk / 8, GK = kChunk * DK / 8;
+    static constexpr int NG = GM + 3 * GK, NJ = NG / NT;
+    static constexpr int NGO = kChunk * WC / 8, NJO = (NGO + NT - 1) / NT;  // dO granules
+    static constexpr int NP = DK * WC / 8, NPC = (NP + NT - 1) / NT;       // dS' pieces
+    static_assert(GM % NT == 0 && GK % NT == 0, "factor granules split");
+};
+
+template <int DK, int SUB>
+__global__ __launch_bounds__(2 * kThreads, 1) void chunk_bwd_rev2_kernel(BwdArgs ba) {
+    using C = Rev2Cfg<DK, SUB>;
+    using MB = Mma<bf16>;
+    constexpr int DV = C::DV, WC = C::WC, NCB = C::NCB, LDKP = C::LDKP, L64 = C::L64, LDV = C::LDV;
+    constexpr int NKD = DK / 32, NT = C::NT;
+    const ChunkArgs &a = ba.c;
+    __shared__ __attribute__((aligned(16))) bf16 sF[C::NG * 8];     // M^T | Khat | Qhat^T | W^T
+    __shared__ __attribute__((aligned(16))) bf16 sdSt[WC * LDKP];   // [v][c] = dS'[c][v]
+    __shared__ __attribute__((aligned(16))) bf16 sdOt[WC * L64];    // [v][i] = dO[i][v]
+    __shared__ __attribute__((aligned(16))) bf16 sdUt[WC * L64];    // [v][i] = dU_eff[i][v]
+    __shared__ __attribute__((aligned(16))) bf16 sdS[DK * LDV];     // [c][v] = dS'[c][v]
+    const bf16 *sMt = sF, *sKh = sF + C::GM * 8, *sQt = sKh + C::GK * 8, *sWt = sQt + C::GK * 8;
+
+    const int H = a.H;
+    const int x = blockIdx.x, xcd = x & 7, rest = x >> 3;
+    const int slab = rest % C::NS, chain = (rest / C::NS) * 8 + xcd;
+    if (chain >= a.N * H) return;
+    const int n = chain / H, h = chain % H, col0 = slab * WC;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wl = wave & 3;
+    const int hc = (wave >> 2) * SUB;  // the half's first column within the slab
+    int cbeg, cend;
+    seq_chunks(a, n, cbeg, cend);
+
+    f32x4 dS[C::S_TPW];
+#pragma unroll
+    for (int u = 0; u < C::S_TPW; ++u) {
+        const int cblk = wl * C::KB_W + u / NCB, colb = u % NCB;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = 16 * cblk + 4 * (lane >> 4) + r, col = col0 + hc + 16 * colb + (lane & 15);
+            dS[u][r] = ba.dS_final ? ba.dS_final[((size_t)chain * DK + row) * DV + col] : 0.0f;
+        }
+    }
+    const bf16 *dout = reinterpret_cast<const bf16 *>(ba.dout);
+    // One chunk's global operands: its factor granules (thread t holds
+    // granules t, t + 512, ...), dO granules (8 columns of one token row; rows
+    // past the chunk's end read row 0, zeroed at use) and gamma_last of the
+    // wave's state rows.  Two sets alternate, so each is requested two chunks
+    // before its use: one chunk ahead left the pass waiting on those loads.
+    struct In {
+        granule_t f[C::NJ], o[C::NJO];
+        f32x4 gl[C::KB_W];
+    };
+    auto load_f = [&](In &x, int cid) {
+        const size_t ch = (size_t)cid * H + h;
+        const granule_t *Mt = reinterpret_cast<const granule_t *>(a.ws_Mt) + ch * C::GM;
+        const granule_t *Kh = reinterpret_cast<const granule_t *>(a.ws_Kh) + ch * C::GK;
+        const granule_t *Qt = reinterpret_cast<const granule_t *>(a.ws_Qt) + ch * C::GK;
+        const granule_t *Wt = reinterpret_cast<const granule_t *>(a.ws_Wt) + ch * C::GK;
+#pragma unroll
+        for (int j = 0; j < C::NJ; ++j) {
+            const int g = j * NT + tid;
+            if (j * NT < C::GM) x.f[j] = Mt[g];
+            else if (j * NT < C::GM + C::GK) x.f[j] = Kh[g - C::GM];
+            else if (j * NT < C::GM + 2 * C::GK) x.f[j] = Qt[g - C::GM - C::GK];
+            else x.f[j] = Wt[g - C::GM - 2 * C::GK];
+        }
+    };
+    auto load_o = [&](In &x, int cid) {
+        int tok0, len;
+        chunk_span_of(a, cid, cbeg, n, tok0, len);
+#pragma unroll
+        for (int q = 0; q < C::NJO; ++q) {
+            const int e = tid + q * NT, i = e / (WC / 8), c8 = 8 * (e % (WC / 8));
+            if (C::NGO % NT == 0 || e < C::NGO) {
+                const size_t off = len > 0 ? ((size_t)(tok0 + (i < len ? i : 0)) * H + h) * DV + col0 + c8 : 0;
+                x.o[q] = *reinterpret_cast<const granule_t *>(dout + off);
+            }
+        }
+    };
+    auto load_gl = [&](In &x, int cid) {
+        const size_t ch = (size_t)cid * H + h;
+#pragma unroll
+        for (int b = 0; b < C::KB_W; ++b)
+            x.gl[b] = *reinterpret_cast<const f32x4 *>(a.ws_gl + ch * DK + 16 * (wl * C::KB_W + b) +
+                                                       4 * (lane >> 4));
+    };
+    // Chunk cid with its operands in x; x is refilled with chunk cid - 2 as
+    // each part of it is consumed.
+    auto step = [&](int cid, In &x) {
+        const size_t ch = (size_t)cid * H + h;
+        const int nxt2 = max(cid - 2, cbeg);
+        int tok0, len;
+        chunk_span_of(a, cid, cbeg, n, tok0, len);
+        // This chunk's factors, dS' (as it is and transposed) and dO
+        // (transposed, zero past the chunk's end) into LDS.
+#pragma unroll
+        for (int j = 0; j < C::NJ; ++j) *reinterpret_cast<granule_t *>(sF + (j * NT + tid) * 8) = x.f[j];
+        load_f(x, nxt2);
+#pragma unroll
+        for (int u = 0; u < C::S_TPW; ++u) {
+            const int cblk = wl * C::KB_W + u / NCB, colb = u % NCB;
+            store_tile<bf16>(sdS + 16 * cblk * LDV + hc + 16 * colb, LDV, dS[u], lane);
+            store_tile_t<bf16>(sdSt + (hc + 16 * colb) * LDKP + 16 * cblk, LDKP, dS[u], lane);
+        }
+#pragma unroll
+        for (int q = 0; q < C::NJO; ++q) {
+            const int e = tid + q * NT, i = e / (WC / 8), c8 = 8 * (e % (WC / 8));
+            if (C::NGO % NT == 0 || e < C::NGO) {
+                bf16x8 v8 = __builtin_bit_cast(bf16x8, x.o[q]);
+                if (i >= len) {
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) v8[t] = static_cast<bf16>(0.0f);
+                }
+#pragma unroll
+                for (int t = 0; t < 8; ++t) sdOt[(c8 + t) * L64 + i] = v8[t];
+            }
+        }
+        load_o(x, nxt2);
+        __syncthreads();
+        // dS' to the workspace.
+        bf16 *dSc = ba.dSc + ch * DK * DV;
+#pragma unroll
+        for (int p = 0; p < C::NPC; ++p) {
+            const int e = tid + p * NT, c = e / (WC / 8), v8 = 8 * (e % (WC / 8));
+            if (C::NP % NT == 0 || e < C::NP)
+                *reinterpret_cast<granule_t *>(dSc + sc_index(c, col0 + v8, DK)) =
+                    *reinterpret_cast<const granule_t *>(sdS + c * LDV + v8);
+        }
+
+        // dU_eff rows of block wl, the half's columns:  M^T dO + Khat dS'.
+        {
+            MB::frag fM[2], fK[NKD];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) fM[kk] = load_frag_packed<bf16>(sMt, kChunk, wl, kk, lane);
+#pragma unroll
+            for (int kk = 0; kk < NKD; ++kk) fK[kk] = load_frag_packed<bf16>(sKh, DK, wl, kk, lane);
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+                const int v = hc + 16 * cb;
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk)
+                    acc = MB::mma(fM[kk], load_frag<bf16>(sdOt + v * L64 + 32 * kk, L64, lane), acc);
+#pragma unroll
+                for (int kk = 0; kk < NKD; ++kk)
+                    acc = MB::mma(fK[kk], load_frag<bf16>(sdSt + v * LDKP + 32 * kk, LDKP, lane), acc);
+                store_tile_t<bf16>(sdUt + v * L64 + 16 * wl, L64, acc, lane);
+            }
+        }
+        __syncthreads();
+
+        // dS <- Diag(gl) dS' + Qhat^T dO - W^T dU_eff.
+#pragma unroll
+        for (int b = 0; b < C::KB_W; ++b) {
+            const int cblk = wl * C::KB_W + b;
+            MB::frag fQ[2], fW[2];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                fQ[kk] = load_frag_packed<bf16>(sQt, kChunk, cblk, kk, lane);
+                fW[kk] = load_frag_packed<bf16>(sWt, kChunk, cblk, kk, lane);
+            }
+#pragma unroll
+            for (int colb = 0; colb < NCB; ++colb) {
+                const int v = hc + 16 * colb;
+                f32x4 q = zero4(), wu = zero4();
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    q = MB::mma(fQ[kk], load_frag<bf16>(sdOt + v * L64 + 32 * kk, L64, lane), q);
+                    wu = MB::mma(fW[kk], load_frag<bf16>(sdUt + v * L64 + 32 * kk, L64, lane), wu);
+                }
+                const int u = b * NCB + colb;
+                dS[u] = x.gl[b] * dS[u] + q - wu;
+            }
+        }
+        load_gl(x, nxt2);
+        __syncthreads();
+    };
+    In inA, inB;
+    if (cend > cbeg) {
+        load_f(inA, cend - 1);
+        load_o(inA, cend - 1);
+        load_gl(inA, cend - 1);
+        load_f(inB, max(cend - 2, cbeg));
+        load_o(inB, max(cend - 2, cbeg));
+        load_gl(inB, max(cend - 2, cbeg));
+    }
+    for (int cid = cend - 1; cid >= cbeg; cid -= 2) {
+        step(cid, inA);
+        if (cid - 1 >= cbeg) step(cid - 1, inB);
+    }
+    if (ba.dS0) {
+#pragma unroll
+        for (int u = 0; u < C::S_TPW; ++u) {
+            const int cblk = wl * C::KB_W + u / NCB, colb = u % NCB;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * cblk + 4 * (lane >> 4) + r, col = col0 + hc + 16 * colb + (lane & 15);
                 ba.dS0[((size_t)chain * DK + row) * DV + col] = dS[u][r];
             }
         }
@@ -876,14 +1090,15 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_factor_kernel(BwdArgs b
 template <int D>
 static void launch_bwd_d(const BwdArgs &a, hipStream_t stream) {
     const int chains = a.c.N * a.c.H, groups = (chains + 7) / 8;
-    const int dvs = (D >= 64 && chains >= 256) ? 64 : (chains >= 64 ? 32 : 16);
     const dim3 block(kThreads);
-    if (dvs == 64)
+    if (chains >= 256)  // 64-column slabs, 4 waves: two workgroups per CU
         hipLaunchKernelGGL((chunk_bwd_rev_kernel<D, 64>), dim3(groups * 8 * (D / 64)), block, 0, stream, a);
-    else if (dvs == 32)
-        hipLaunchKernelGGL((chunk_bwd_rev_kernel<D, 32>), dim3(groups * 8 * (D / 32)), block, 0, stream, a);
-    else
-        hipLaunchKernelGGL((chunk_bwd_rev_kernel<D, 16>), dim3(groups * 8 * (D / 16)), block, 0, stream, a);
+    else if (chains >= 64)  // 64-column slabs, two 32-column halves
+        hipLaunchKernelGGL((chunk_bwd_rev2_kernel<D, 32>), dim3(groups * 8 * (D / 64)), dim3(2 * kThreads),
+                           0, stream, a);
+    else  // 32-column slabs, two 16-column halves
+        hipLaunchKernelGGL((chunk_bwd_rev2_kernel<D, 16>), dim3(groups * 8 * (D / 32)), dim3(2 * kThreads),
+                           0, stream, a);
     if (a.c.max_chunks == 0) return;
     const dim3 grid((unsigned)((size_t)a.c.max_chunks * a.c.H));
     hipLaunchKernelGGL((chunk_bwd_state_kernel<D>), grid, block, 0, stream, a);

@@ -62,13 +62,15 @@ def test_bwd_varlen_edge_lengths():
     _check(inp, W.make_chunk_grads(inp, 13), "bwd varlen")
 
 
-@pytest.mark.parametrize("B", [4, 16])
-def test_bwd_many_chains(B):
-    """H = 16 with B = 4 and 16 (64 and 256 chains): the reverse pass's 32- and
-    64-column value slabs (the small cases above take 16-column slabs)."""
-    wl = W.ChunkWorkload("bwd_many", B, 70, 16, 128, 128, W.BF16, 4646 + B, with_S0=True)
+@pytest.mark.parametrize("B,D", [(4, 128), (16, 128), (4, 64), (16, 64)])
+def test_bwd_many_chains(B, D):
+    """H = 16 with B = 4 and 16 (64 and 256 chains), d = 64 and 128: the
+    reverse pass's 8-wave workgroups on 64-column slabs (two 32-column halves)
+    and its 4-wave workgroups on 64-column slabs (the small cases above take
+    32-column slabs in two 16-column halves)."""
+    wl = W.ChunkWorkload("bwd_many", B, 70, 16, D, D, W.BF16, 4646 + B + D, with_S0=True)
     inp = W.make_chunk_inputs(wl)
-    _check(inp, W.make_chunk_grads(inp, 15 + B), "bwd %d chains" % (B * 16))
+    _check(inp, W.make_chunk_grads(inp, 15 + B + D), "bwd %d chains d=%d" % (B * 16, D))
 
 
 @pytest.mark.parametrize("case", ["no_decay_no_erase", "strong_decay"])
