@@ -144,11 +144,14 @@ __global__ __launch_bounds__(256) void layer_mix_in_kernel(LayerArgs a) {
         for (int e = 0; e < 8; ++e) hist[j][e] = in ? x[e] : 0.0f;
     }
 
-    for (int mb = m0; mb < m1; mb += 4) {
-        // four rows in flight at once; rows past the strip repeat its last row
-        float xr[4][8];
+    // four rows per block, the next block's rows in flight during this one's
+    // math; rows past the strip repeat its last row
+    float xr[4][8], xn[4][8];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) load8(src + (size_t)min(mb + u, m1 - 1) * a.ldP, xr[u]);
+    for (int u = 0; u < 4; ++u) load8(src + (size_t)min(m0 + u, m1 - 1) * a.ldP, xr[u]);
+    for (int mb = m0; mb < m1; mb += 4) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) load8(src + (size_t)min(mb + 4 + u, m1 - 1) * a.ldP, xn[u]);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int m = mb + u;
@@ -192,6 +195,10 @@ __global__ __launch_bounds__(256) void layer_mix_in_kernel(LayerArgs a) {
         for (int j = (MAXL - 2 < 3 ? MAXL - 2 : 3); j >= 0; --j)
 #pragma unroll
             for (int e = 0; e < 8; ++e) hist[j][e] = xr[3 - j][e];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) xr[u][e] = xn[u][e];
     }
 }
 
