@@ -62,6 +62,16 @@ def test_bwd_varlen_edge_lengths():
     _check(inp, W.make_chunk_grads(inp, 13), "bwd varlen")
 
 
+def test_bwd_varlen_many_chains():
+    """Packed sequences of lengths 0-200 on H = 8 heads (9 sequences, 72
+    chains): the reverse pass's 8-wave workgroups driven by the chunk table."""
+    lengths = [200, 0, 65, 1, 128, 63, 130, 7, 64]
+    wl = W.ChunkWorkload("bwd_varlen_many", 1, 0, 8, 128, 128, W.BF16, 4545, with_S0=True,
+                         n_seqs=len(lengths))
+    inp = W.make_chunk_inputs(wl, lengths=lengths)
+    _check(inp, W.make_chunk_grads(inp, 14), "bwd varlen 72 chains")
+
+
 @pytest.mark.parametrize("B,D", [(4, 128), (16, 128), (4, 64), (16, 64)])
 def test_bwd_many_chains(B, D):
     """H = 16 with B = 4 and 16 (64 and 256 chains), d = 64 and 128: the
