@@ -401,7 +401,7 @@ def time_swa_layer(inp, steps, warmup):
 def main():
     a = parse()
     if a.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: libgdn2 has no multi-GPU path "
               "(--gpus %d requested)" % a.gpus, file=sys.stderr)
         sys.exit(2)
     import torch

@@ -49,7 +49,7 @@ extern "C" {
 typedef enum gdn2_status {
     GDN2_OK = 0,
     GDN2_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, bad size or dtype */
-    GDN2_ERR_UNSUPPORTED = 2,      /* valid request this build does not implement */
+    GDN2_ERR_UNSUPPORTED = 2,      /* valid request the library does not implement */
     GDN2_ERR_WORKSPACE = 3,        /* workspace missing or smaller than required */
     GDN2_ERR_HIP = 4               /* a HIP launch or runtime call failed */
 } gdn2_status;
