@@ -16,8 +16,9 @@
  *
  * Conventions shared by every call
  *   - All tensor pointers are DEVICE pointers, allocated and owned by the
- *     caller.  Compute calls allocate nothing; intermediates of the chunk
- *     forward live in a caller-supplied device workspace.
+ *     caller.  Intermediates live in a caller-supplied device workspace;
+ *     the only allocation the library makes is the hipBLASLt handle the
+ *     layer calls create on their first call on a device (see below).
  *   - Layouts are dense, row-major, last dimension fastest.  Every tensor
  *     pointer must be 16-byte aligned.
  *   - `io` selects the element type of q, k, v and o (GDN2_BF16 or GDN2_F32).
