@@ -80,6 +80,25 @@ __device__ __forceinline__ void dense_span(const ChunkArgs &a, int cid, int &tok
     }
 }
 
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+
+// Operand fragment of the transpose of a row-major bf16 tile X in LDS (pitch
+// ld, 8-byte aligned rows): lane l receives X[r0 + 8 (l/16) + t][c0 + l%16],
+// t = 0..7, i.e. the fragment of X^T at rows c0.., contraction index r0...
+// Two transposing 8-byte reads: in each group of 16 lanes, lane j points at
+// row r0 + 8 (l/16) + j/4 (+4), columns c0 + 4 (j%4) .. +3, and lane i then
+// receives column c0 + i of those 4 rows.
+__device__ __forceinline__ Mma<bf16>::frag load_frag_tr(const bf16 *X, int ld, int r0, int c0, int lane) {
+    const int j = lane & 15, row = r0 + 8 * (lane >> 4) + (j >> 2), col = c0 + 4 * (j & 3);
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16 *)(X + row * ld + col));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16 *)(X + (row + 4) * ld + col));
+    const v8i16 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(Mma<bf16>::frag, both);
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -476,14 +495,15 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_bwd_rev2_kernel(BwdArgs
 // (except dQhat = dO S^T, which the factor side forms),
 // taken over 32-column slabs of the value axis with bf16 MFMA (16x16x32).
 // Every operand is staged in LDS in the orientation its fragment load wants
-// (k contiguous), transposing on the way in where needed.  Wave w owns token
-// rows 16w .. 16w+15 of every 64-row result.
+// (k contiguous), transposing on the way in where needed; S and dS' are
+// staged once, [c][v], and read through transposing LDS reads where the
+// contraction runs over c.  Wave w owns token rows 16w .. 16w+15 of every
+// 64-row result.
 // ---------------------------------------------------------------------------
 template <int DK>
 struct StateCfg {
     static constexpr int DV = DK, SW = 32, NSL = DV / SW, NKB = DK / 16;
     static constexpr int LSW = SW + 8;     // [..][SW] bf16 rows
-    static constexpr int LDKP = DK + 8;    // [..][DK] bf16 rows
     static constexpr int L64 = kChunk + 8; // [..][64] bf16 rows
 };
 
@@ -491,13 +511,11 @@ template <int DK>
 __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_state_kernel(BwdArgs ba) {
     using C = StateCfg<DK>;
     using MB = Mma<bf16>;
-    constexpr int DV = C::DV, SW = C::SW, NKB = C::NKB, LSW = C::LSW, LDKP = C::LDKP, L64 = C::L64;
+    constexpr int DV = C::DV, SW = C::SW, NKB = C::NKB, LSW = C::LSW, L64 = C::L64;
     constexpr int NKD = DK / 32;
     const ChunkArgs &a = ba.c;
     // per slab (W, M^T, Khat and T^T are loaded as fragments from the workspace)
-    __shared__ __attribute__((aligned(16))) bf16 sSt[SW * LDKP];     // [v][c] = S[c][v]
     __shared__ __attribute__((aligned(16))) bf16 sS[DK * LSW];       // [c][v]
-    __shared__ __attribute__((aligned(16))) bf16 sdSt[SW * LDKP];    // [v][c] = dS'[c][v]
     __shared__ __attribute__((aligned(16))) bf16 sdS[DK * LSW];      // [c][v]
     __shared__ __attribute__((aligned(16))) bf16 sdOt[SW * L64];     // [v][j] = dO[j][v]
     __shared__ __attribute__((aligned(16))) bf16 sdO[kChunk * LSW];  // [i][v]
@@ -554,18 +572,15 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_state_kernel(BwdArgs ba
 
     for (int sl = 0; sl < C::NSL; ++sl) {
         const int v0 = sl * SW;
-        // S and dS' columns v0..v0+SW: [c][v] and transposed [v][c].
+        // S and dS' columns v0..v0+SW, [c][v] (products contracting over c
+        // read them with transposing LDS reads).
 #pragma unroll
         for (int p8 = 0; p8 < CPT; p8 += 8) {
             const int v = scol + p8;
             const bf16x8 sb = *reinterpret_cast<const bf16x8 *>(Sc + sc_index(srow, v0 + v, DK));
             const bf16x8 db = *reinterpret_cast<const bf16x8 *>(dSc + sc_index(srow, v0 + v, DK));
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                sSt[(v + t) * LDKP + srow] = sb[t];
-                sdSt[(v + t) * LDKP + srow] = db[t];
-                dgp += static_cast<float>(sb[t]) * static_cast<float>(db[t]);
-            }
+            for (int t = 0; t < 8; ++t) dgp += static_cast<float>(sb[t]) * static_cast<float>(db[t]);
             *reinterpret_cast<bf16x4 *>(sS + srow * LSW + v) = bf16x4{sb[0], sb[1], sb[2], sb[3]};
             *reinterpret_cast<bf16x4 *>(sS + srow * LSW + v + 4) = bf16x4{sb[4], sb[5], sb[6], sb[7]};
             *reinterpret_cast<bf16x4 *>(sdS + srow * LSW + v) = bf16x4{db[0], db[1], db[2], db[3]};
@@ -599,10 +614,8 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_state_kernel(BwdArgs ba
             f32x4 ws = zero4(), du = zero4();
 #pragma unroll
             for (int kk = 0; kk < NKD; ++kk) {
-                ws = MB::mma(fW[kk],
-                             load_frag<bf16>(sSt + 16 * cb * LDKP + 32 * kk, LDKP, lane), ws);
-                du = MB::mma(fKh[kk],
-                             load_frag<bf16>(sdSt + 16 * cb * LDKP + 32 * kk, LDKP, lane), du);
+                ws = MB::mma(fW[kk], load_frag_tr(sS, LSW, 32 * kk, 16 * cb, lane), ws);
+                du = MB::mma(fKh[kk], load_frag_tr(sdS, LSW, 32 * kk, 16 * cb, lane), du);
             }
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
