@@ -304,7 +304,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_bwd_rev2_kernel(BwdArgs
     const ChunkArgs &a = ba.c;
     __shared__ __attribute__((aligned(16))) bf16 sF[C::NG * 8];     // M^T | Khat | Qhat^T | W^T
     __shared__ __attribute__((aligned(16))) bf16 sdSt[WC * LDKP];   // [v][c] = dS'[c][v]
-    __shared__ __attribute__((aligned(16))) bf16 sdOt[WC * L64];    // [v][i] = dO[i][v]
+    __shared__ __attribute__((aligned(16))) bf16 sdO[kChunk * LDV];  // [i][v] = dO[i][v]
     __shared__ __attribute__((aligned(16))) bf16 sdUt[WC * L64];    // [v][i] = dU_eff[i][v]
     __shared__ __attribute__((aligned(16))) bf16 sdS[DK * LDV];     // [c][v] = dS'[c][v]
     const bf16 *sMt = sF, *sKh = sF + C::GM * 8, *sQt = sKh + C::GK * 8, *sWt = sQt + C::GK * 8;
@@ -380,8 +380,9 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_bwd_rev2_kernel(BwdArgs
         const int nxt2 = max(cid - 2, cbeg);
         int tok0, len;
         chunk_span_of(a, cid, cbeg, n, tok0, len);
-        // This chunk's factors, dS' (as it is and transposed) and dO
-        // (transposed, zero past the chunk's end) into LDS.
+        // This chunk's factors, dS' (as it is and transposed) and dO (rows,
+        // zero past the chunk's end; read through transposing LDS reads)
+        // into LDS.
 #pragma unroll
         for (int j = 0; j < C::NJ; ++j) *reinterpret_cast<granule_t *>(sF + (j * NT + tid) * 8) = x.f[j];
         load_f(x, nxt2);
@@ -400,8 +401,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_bwd_rev2_kernel(BwdArgs
 #pragma unroll
                     for (int t = 0; t < 8; ++t) v8[t] = static_cast<bf16>(0.0f);
                 }
-#pragma unroll
-                for (int t = 0; t < 8; ++t) sdOt[(c8 + t) * L64 + i] = v8[t];
+                *reinterpret_cast<bf16x8 *>(sdO + i * LDV + c8) = v8;
             }
         }
         load_o(x, nxt2);
@@ -429,7 +429,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_bwd_rev2_kernel(BwdArgs
                 f32x4 acc = zero4();
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk)
-                    acc = MB::mma(fM[kk], load_frag<bf16>(sdOt + v * L64 + 32 * kk, L64, lane), acc);
+                    acc = MB::mma(fM[kk], load_frag_tr(sdO, LDV, 32 * kk, v, lane), acc);
 #pragma unroll
                 for (int kk = 0; kk < NKD; ++kk)
                     acc = MB::mma(fK[kk], load_frag<bf16>(sdSt + v * LDKP + 32 * kk, LDKP, lane), acc);
@@ -454,7 +454,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_bwd_rev2_kernel(BwdArgs
                 f32x4 q = zero4(), wu = zero4();
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
-                    q = MB::mma(fQ[kk], load_frag<bf16>(sdOt + v * L64 + 32 * kk, L64, lane), q);
+                    q = MB::mma(fQ[kk], load_frag_tr(sdO, LDV, 32 * kk, v, lane), q);
                     wu = MB::mma(fW[kk], load_frag<bf16>(sdUt + v * L64 + 32 * kk, L64, lane), wu);
                 }
                 const int u = b * NCB + colb;
@@ -517,7 +517,6 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_state_kernel(BwdArgs ba
     // per slab (W, M^T, Khat and T^T are loaded as fragments from the workspace)
     __shared__ __attribute__((aligned(16))) bf16 sS[DK * LSW];       // [c][v]
     __shared__ __attribute__((aligned(16))) bf16 sdS[DK * LSW];      // [c][v]
-    __shared__ __attribute__((aligned(16))) bf16 sdOt[SW * L64];     // [v][j] = dO[j][v]
     __shared__ __attribute__((aligned(16))) bf16 sdO[kChunk * LSW];  // [i][v]
     __shared__ __attribute__((aligned(16))) bf16 sU[kChunk * LSW];   // [j][v] = U[j][v]
     __shared__ __attribute__((aligned(16))) bf16 sUe[kChunk * LSW];  // [i][v] = U_eff
@@ -586,7 +585,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_state_kernel(BwdArgs ba
             *reinterpret_cast<bf16x4 *>(sdS + srow * LSW + v) = bf16x4{db[0], db[1], db[2], db[3]};
             *reinterpret_cast<bf16x4 *>(sdS + srow * LSW + v + 4) = bf16x4{db[4], db[5], db[6], db[7]};
         }
-        // dO rows (zero past the chunk) and U, [i][v] and transposed.
+        // dO rows (zero past the chunk), [i][v]; U, [j][v].
         for (int e = tid; e < kChunk * SW / 4; e += kThreads) {
             const int i = e / (SW / 4), v4 = 4 * (e % (SW / 4));
             bf16x4 o4;
@@ -597,8 +596,6 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_state_kernel(BwdArgs ba
                 for (int t = 0; t < 4; ++t) o4[t] = static_cast<bf16>(0.0f);
             }
             *reinterpret_cast<bf16x4 *>(sdO + i * LSW + v4) = o4;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) sdOt[(v4 + t) * L64 + i] = o4[t];
             // U in accumulator order: [I][cb][lane][r] = U[16I + 4(lane/16) + r][16cb + lane%16]
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
@@ -619,8 +616,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_state_kernel(BwdArgs ba
             }
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
-                du = MB::mma(fMt[kk],
-                             load_frag<bf16>(sdOt + 16 * cb * L64 + 32 * kk, L64, lane), du);
+                du = MB::mma(fMt[kk], load_frag_tr(sdO, LSW, 32 * kk, 16 * cb, lane), du);
             // U tile in accumulator order straight from the workspace.
             const bf16x4 u4 = *reinterpret_cast<const bf16x4 *>(
                 Ug + (((size_t)I * (DV / 16) + (v0 / 16 + cb)) * 64 + lane) * 4);
