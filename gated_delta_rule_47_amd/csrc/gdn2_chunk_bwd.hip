@@ -125,7 +125,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_rev_kernel(BwdArgs ba) 
     constexpr int DV = C::DV, NCB = C::NCB, LDKP = C::LDKP, L64 = C::L64, NKD = DK / 32;
     const ChunkArgs &a = ba.c;
     __shared__ __attribute__((aligned(16))) bf16 sdSt[DVS * LDKP];  // [v][c] = dS'[c][v]
-    __shared__ __attribute__((aligned(16))) bf16 sdOt[DVS * L64];   // [v][i] = dO[i][v]
+    __shared__ __attribute__((aligned(16))) bf16 sdO[kChunk * C::LDV];  // [i][v] = dO[i][v]
     __shared__ __attribute__((aligned(16))) bf16 sdUt[DVS * L64];   // [v][i] = dU_eff[i][v]
     __shared__ __attribute__((aligned(16))) bf16 sdS[DK * C::LDV];  // [c][v] = dS'[c][v]
 
@@ -208,7 +208,8 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_rev_kernel(BwdArgs ba) 
             store_tile<bf16>(sdS + 16 * cblk * C::LDV + 16 * colb, C::LDV, dS[u], lane);
             store_tile_t<bf16>(sdSt + 16 * colb * LDKP + 16 * cblk, LDKP, dS[u], lane);
         }
-        // dO rows of the chunk (zero past its end), transposed.
+        // dO rows of the chunk (zero past its end), read through transposing
+        // LDS reads.
 #pragma unroll
         for (int q = 0; q < NE; ++q) {
             const int e = tid + q * kThreads, i = e / (DVS / 4), c4 = 4 * (e % (DVS / 4));
@@ -217,8 +218,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_rev_kernel(BwdArgs ba) 
 #pragma unroll
                 for (int t = 0; t < 4; ++t) v4[t] = static_cast<bf16>(0.0f);
             }
-#pragma unroll
-            for (int t = 0; t < 4; ++t) sdOt[(c4 + t) * L64 + i] = v4[t];
+            *reinterpret_cast<bf16x4 *>(sdO + i * C::LDV + c4) = v4;
         }
         __syncthreads();
         bf16 *dSc = ba.dSc + ch * DK * DV;
@@ -236,7 +236,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_rev_kernel(BwdArgs ba) 
             f32x4 acc = zero4();
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
-                acc = MB::mma(cur.fM[kk], load_frag<bf16>(sdOt + 16 * cb * L64 + 32 * kk, L64, lane), acc);
+                acc = MB::mma(cur.fM[kk], load_frag_tr(sdO, C::LDV, 32 * kk, 16 * cb, lane), acc);
 #pragma unroll
             for (int kk = 0; kk < NKD; ++kk)
                 acc = MB::mma(cur.fK[kk], load_frag<bf16>(sdSt + 16 * cb * LDKP + 32 * kk, LDKP, lane), acc);
@@ -251,7 +251,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_rev_kernel(BwdArgs ba) 
             f32x4 q = zero4(), wu = zero4();
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                q = MB::mma(cur.fQ[b][kk], load_frag<bf16>(sdOt + 16 * colb * L64 + 32 * kk, L64, lane), q);
+                q = MB::mma(cur.fQ[b][kk], load_frag_tr(sdO, C::LDV, 32 * kk, 16 * colb, lane), q);
                 wu = MB::mma(cur.fW[b][kk], load_frag<bf16>(sdUt + 16 * colb * L64 + 32 * kk, L64, lane), wu);
             }
             dS[u] = cur.gl[b] * dS[u] + q - wu;
