@@ -57,7 +57,7 @@ class WorkspaceLayout(ctypes.Structure):
                 ("off_Qhat", ctypes.c_size_t), ("off_KhatT", ctypes.c_size_t),
                 ("off_M", ctypes.c_size_t), ("off_U", ctypes.c_size_t),
                 ("off_gamma_last", ctypes.c_size_t),
-                ("off_plan", ctypes.c_size_t)]
+                ("off_plan", ctypes.c_size_t), ("total_bytes_with_Tinv", ctypes.c_size_t)]
 
 
 _lib = None
@@ -234,15 +234,65 @@ def _stream(stream):
     return stream.cuda_stream
 
 
-def _check(t, name, dtype=None):
-    if t is None:
-        return
-    if not t.is_cuda:
-        raise ValueError("%s must be a device tensor" % name)
-    if not t.is_contiguous():
-        raise ValueError("%s must be contiguous" % name)
-    if dtype is not None and t.dtype != dtype:
-        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+def _validate(specs, device=None):
+    """Validate tensor arguments before their addresses reach the library.
+
+    specs: (name, tensor or None, expected shape or None, dtype or None).
+    Every tensor's shape and dtype is checked first, then that each lives on
+    `device` and is contiguous: a tensor of the wrong size would otherwise
+    become out-of-bounds device reads or writes.
+    """
+    for name, t, shape, dtype in specs:
+        if t is None:
+            continue
+        if shape is not None and tuple(t.shape) != tuple(shape):
+            raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+        if dtype is not None and t.dtype != dtype:
+            raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    for name, t, _, _ in specs:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("%s must be a device tensor" % name)
+        if device is not None and t.device != device:
+            raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+
+
+def _check(t, name, shape=None, dtype=None, device=None):
+    _validate([(name, t, shape, dtype)], device)
+
+
+def _check_cu_seqlens(cu_seqlens, B, device):
+    """Packed calls: int32 [N+1] offsets on the device, with B == 1.  Returns N."""
+    import torch
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a 1-D tensor of N+1 offsets")
+    if B != 1:
+        raise ValueError("a packed call (cu_seqlens given) needs B == 1, got B = %d" % B)
+    _check(cu_seqlens, "cu_seqlens", dtype=torch.int32, device=device)
+    return cu_seqlens.numel() - 1
+
+
+def _workspace(workspace, nbytes, device):
+    """The caller's workspace (any dtype, contiguous, on the device) or a new one;
+    returns (tensor, size in bytes)."""
+    import torch
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    _check(workspace, "workspace", device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def _chunk_shapes(q, v, cu_seqlens):
+    """(B, T, H, Dk, Dv, N) of a chunk call, from q [B,T,H,Dk] and v [B,T,H,Dv]."""
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q and v must be [B, T, H, D] tensors")
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    N = B if cu_seqlens is None else _check_cu_seqlens(cu_seqlens, B, q.device)
+    return B, T, H, Dk, Dv, N
 
 
 def chunk_fwd(q, k, v, log_alpha, b, w, S0=None, cu_seqlens=None, o=None, S_final=None,
@@ -254,26 +304,28 @@ def chunk_fwd(q, k, v, log_alpha, b, w, S0=None, cu_seqlens=None, o=None, S_fina
     Returns (o [B,T,H,Dv] in q's dtype, S_final [N,H,Dk,Dv] float32 or None).
     """
     import torch
-    B, T, H, Dk = q.shape
-    Dv = v.shape[-1]
+    B, T, H, Dk, Dv, N = _chunk_shapes(q, v, cu_seqlens)
     io = _io_of(q)
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _check(t, name, q.dtype)
-    for name, t in (("log_alpha", log_alpha), ("b", b), ("w", w), ("S0", S0)):
-        _check(t, name, torch.float32)
-    _check(cu_seqlens, "cu_seqlens", torch.int32)
-    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    dev = q.device
+    tk, tv, st_shape = (B, T, H, Dk), (B, T, H, Dv), (N, H, Dk, Dv)
+    f32 = torch.float32
+    _validate([("q", q, tk, q.dtype), ("k", k, tk, q.dtype), ("v", v, tv, q.dtype),
+               ("o", o, tv, q.dtype), ("log_alpha", log_alpha, tk, f32), ("b", b, tk, f32),
+               ("w", w, tv, f32), ("S0", S0, st_shape, f32), ("S_final", S_final, st_shape, f32)],
+              dev)
     if o is None:
-        o = torch.empty((B, T, H, Dv), dtype=q.dtype, device=q.device)
+        o = torch.empty(tv, dtype=q.dtype, device=dev)
     if S_final is None and output_final_state:
-        S_final = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=q.device)
+        S_final = torch.empty(st_shape, dtype=torch.float32, device=dev)
     varlen = cu_seqlens is not None
     nbytes = gdn2_chunk_fwd_workspace_bytes(N, B, T, H, Dk, Dv, io, varlen)
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    if stages & GDN2_STAGE_STORE_T:
+        nbytes = gdn2_chunk_fwd_workspace_layout(N, B, T, H, Dk, Dv, io,
+                                                 varlen).total_bytes_with_Tinv
+    workspace, ws_bytes = _workspace(workspace, nbytes, dev)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(S0), _ptr(o),
             _ptr(S_final), _ptr(cu_seqlens), N, B, T, H, Dk, Dv, io, _ptr(workspace),
-            workspace.numel(), _stream(stream))
+            ws_bytes, _stream(stream))
     if stages == GDN2_STAGE_ALL:
         st = gdn2_chunk_fwd(*args)
     else:
@@ -286,15 +338,21 @@ def chunk_fwd(q, k, v, log_alpha, b, w, S0=None, cu_seqlens=None, o=None, S_fina
 def step(q, k, v, log_alpha, b, w, S, o=None, stream=None):
     """One decode token: q, k, log_alpha, b [B,H,Dk]; v, w [B,H,Dv]; S [B,H,Dk,Dv] f32 in place."""
     import torch
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError("q and v must be [B, H, D] tensors")
     B, H, Dk = q.shape
     Dv = v.shape[-1]
     io = _io_of(q)
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _check(t, name, q.dtype)
-    for name, t in (("log_alpha", log_alpha), ("b", b), ("w", w), ("S", S)):
-        _check(t, name, torch.float32)
+    dev = q.device
+    f32, dt = torch.float32, q.dtype
+    _validate([("q", q, (B, H, Dk), dt), ("k", k, (B, H, Dk), dt), ("v", v, (B, H, Dv), dt),
+               ("o", o, (B, H, Dv), dt), ("log_alpha", log_alpha, (B, H, Dk), f32),
+               ("b", b, (B, H, Dk), f32), ("w", w, (B, H, Dv), f32),
+               ("S", S, (B, H, Dk, Dv), f32)], dev)
+    if S is None:
+        raise ValueError("S (the state updated in place) is required")
     if o is None:
-        o = torch.empty((B, H, Dv), dtype=q.dtype, device=q.device)
+        o = torch.empty((B, H, Dv), dtype=q.dtype, device=dev)
     st = gdn2_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(S), _ptr(o),
                    B, H, Dk, Dv, io, _stream(stream))
     if st != GDN2_OK:
@@ -305,35 +363,34 @@ def step(q, k, v, log_alpha, b, w, S, o=None, stream=None):
 def chunk_bwd(q, k, v, log_alpha, b, w, dout, S0=None, dS_final=None, cu_seqlens=None,
               need_dS0=True, workspace=None, stream=None):
     """Gradients of chunk_fwd for upstream gradients dout (of o) and dS_final
-    (of S_final, None = zero).  Same shapes as chunk_fwd; bfloat16 q/k/v only.
+    (of S_final, None = zero).  Same shapes as chunk_fwd.
     Returns a dict: dq, dk, dv (q's dtype), dlog_alpha, db, dw (float32) and
     dS0 ([N,H,Dk,Dv] float32, or None when need_dS0 is False).
     """
     import torch
-    B, T, H, Dk = q.shape
-    Dv = v.shape[-1]
+    B, T, H, Dk, Dv, N = _chunk_shapes(q, v, cu_seqlens)
     io = _io_of(q)
-    for name, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
-        _check(t, name, q.dtype)
-    for name, t in (("log_alpha", log_alpha), ("b", b), ("w", w), ("S0", S0),
-                    ("dS_final", dS_final)):
-        _check(t, name, torch.float32)
-    _check(cu_seqlens, "cu_seqlens", torch.int32)
-    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    dev = q.device
+    tk, tv, st_shape = (B, T, H, Dk), (B, T, H, Dv), (N, H, Dk, Dv)
+    f32 = torch.float32
+    _validate([("q", q, tk, q.dtype), ("k", k, tk, q.dtype), ("v", v, tv, q.dtype),
+               ("dout", dout, tv, q.dtype), ("log_alpha", log_alpha, tk, f32),
+               ("b", b, tk, f32), ("w", w, tv, f32), ("S0", S0, st_shape, f32),
+               ("dS_final", dS_final, st_shape, f32)], dev)
+    if dout is None:
+        raise ValueError("dout is required")
     out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
                dlog_alpha=torch.empty_like(log_alpha), db=torch.empty_like(b),
                dw=torch.empty_like(w),
-               dS0=torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=q.device)
-               if need_dS0 else None)
+               dS0=torch.empty(st_shape, dtype=torch.float32, device=dev) if need_dS0 else None)
     varlen = cu_seqlens is not None
     nbytes = gdn2_chunk_bwd_workspace_bytes(N, B, T, H, Dk, Dv, io, varlen)
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    workspace, ws_bytes = _workspace(workspace, nbytes, dev)
     st = gdn2_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(S0),
                         _ptr(dout), _ptr(dS_final), _ptr(out["dq"]), _ptr(out["dk"]),
                         _ptr(out["dv"]), _ptr(out["dlog_alpha"]), _ptr(out["db"]),
                         _ptr(out["dw"]), _ptr(out["dS0"]), _ptr(cu_seqlens), N, B, T, H, Dk, Dv,
-                        io, _ptr(workspace), workspace.numel(), _stream(stream))
+                        io, _ptr(workspace), ws_bytes, _stream(stream))
     if st != GDN2_OK:
         raise Gdn2Error(st, "gdn2_chunk_bwd")
     return out
@@ -345,27 +402,26 @@ def chunk_fwd_gate_logits(q, k, v, log_alpha, b_logit, w_logit, S0=None, cu_seql
     """chunk_fwd with bfloat16 gate inputs: log_alpha itself and the logits of b
     and w (sigmoid taken in the kernel).  q, k, v must be bfloat16."""
     import torch
-    B, T, H, Dk = q.shape
-    Dv = v.shape[-1]
+    B, T, H, Dk, Dv, N = _chunk_shapes(q, v, cu_seqlens)
     io = _io_of(q)
-    for name, t in (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha), ("b_logit", b_logit),
-                    ("w_logit", w_logit)):
-        _check(t, name, torch.bfloat16)
-    _check(S0, "S0", torch.float32)
-    _check(cu_seqlens, "cu_seqlens", torch.int32)
-    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    dev = q.device
+    tk, tv, st_shape = (B, T, H, Dk), (B, T, H, Dv), (N, H, Dk, Dv)
+    bf, f32 = torch.bfloat16, torch.float32
+    _validate([("q", q, tk, bf), ("k", k, tk, bf), ("v", v, tv, bf),
+               ("log_alpha", log_alpha, tk, bf), ("b_logit", b_logit, tk, bf),
+               ("w_logit", w_logit, tv, bf), ("o", o, tv, bf), ("S0", S0, st_shape, f32),
+               ("S_final", S_final, st_shape, f32)], dev)
     if o is None:
-        o = torch.empty((B, T, H, Dv), dtype=q.dtype, device=q.device)
+        o = torch.empty(tv, dtype=q.dtype, device=dev)
     if S_final is None and output_final_state:
-        S_final = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=q.device)
+        S_final = torch.empty(st_shape, dtype=torch.float32, device=dev)
     varlen = cu_seqlens is not None
     nbytes = gdn2_chunk_fwd_workspace_bytes(N, B, T, H, Dk, Dv, io, varlen)
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    workspace, ws_bytes = _workspace(workspace, nbytes, dev)
     st = gdn2_chunk_fwd_gate_logits(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b_logit),
                                     _ptr(w_logit), _ptr(S0), _ptr(o), _ptr(S_final),
                                     _ptr(cu_seqlens), N, B, T, H, Dk, Dv, io, _ptr(workspace),
-                                    workspace.numel(), _stream(stream))
+                                    ws_bytes, _stream(stream))
     if st != GDN2_OK:
         raise Gdn2Error(st, "gdn2_chunk_fwd_gate_logits")
     return o, S_final
@@ -378,30 +434,29 @@ def layer_fwd(x, W_in, conv_w, alpha_bias, norm_w, W_o, H, Dk, Dv, norm_eps=1e-6
     [7*H*Dk, D] and W_o [D, H*Dv] are bfloat16; conv_w [3*H*Dk, L],
     alpha_bias [H*Dk] and norm_w [Dv] float32.  Returns (y, S_final)."""
     import torch
+    if x.dim() != 3:
+        raise ValueError("x must be a [B, T, D] tensor")
     B, T, D = x.shape
-    for name, t in (("x", x), ("W_in", W_in), ("W_o", W_o)):
-        _check(t, name, torch.bfloat16)
-    for name, t in (("conv_w", conv_w), ("alpha_bias", alpha_bias), ("norm_w", norm_w)):
-        _check(t, name, torch.float32)
-    _check(S0, "S0", torch.float32)
-    _check(cu_seqlens, "cu_seqlens", torch.int32)
-    if W_in.shape != (7 * H * Dk, D) or W_o.shape != (D, H * Dv) or conv_w.dim() != 2 \
-            or conv_w.shape[0] != 3 * H * Dk or alpha_bias.numel() != H * Dk \
-            or norm_w.numel() != Dv:
-        raise ValueError("layer weight shapes do not match H=%d, Dk=%d, Dv=%d, D=%d"
-                         % (H, Dk, Dv, D))
-    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    dev = x.device
+    if conv_w.dim() != 2:
+        raise ValueError("conv_w must be a [3*H*Dk, L] tensor")
+    N = B if cu_seqlens is None else _check_cu_seqlens(cu_seqlens, B, dev)
+    bf, f32 = torch.bfloat16, torch.float32
+    _validate([("x", x, (B, T, D), bf), ("W_in", W_in, (7 * H * Dk, D), bf),
+               ("W_o", W_o, (D, H * Dv), bf), ("y", y, (B, T, D), bf),
+               ("conv_w", conv_w, (3 * H * Dk, conv_w.shape[1]), f32),
+               ("alpha_bias", alpha_bias, (H * Dk,), f32), ("norm_w", norm_w, (Dv,), f32),
+               ("S0", S0, (N, H, Dk, Dv), f32), ("S_final", S_final, (N, H, Dk, Dv), f32)], dev)
     if y is None:
-        y = torch.empty((B, T, D), dtype=torch.bfloat16, device=x.device)
+        y = torch.empty((B, T, D), dtype=torch.bfloat16, device=dev)
     if S_final is None and output_final_state:
-        S_final = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=x.device)
+        S_final = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=dev)
     nbytes = gdn2_layer_fwd_workspace_bytes(N, B, T, H, Dk, Dv, D, cu_seqlens is not None)
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    workspace, ws_bytes = _workspace(workspace, nbytes, dev)
     wts = LayerWeights(_ptr(W_in), _ptr(conv_w), _ptr(alpha_bias), _ptr(norm_w), _ptr(W_o))
     st = gdn2_layer_fwd(_ptr(x), wts, conv_w.shape[1], float(norm_eps), _ptr(S0), _ptr(y),
                         _ptr(S_final), _ptr(cu_seqlens), N, B, T, H, Dk, Dv, D, _ptr(workspace),
-                        workspace.numel(), _stream(stream))
+                        ws_bytes, _stream(stream))
     if st != GDN2_OK:
         raise Gdn2Error(st, "gdn2_layer_fwd")
     return y, S_final
@@ -413,25 +468,28 @@ def swa_fwd(q, k, v, window, scale=None, cu_seqlens=None, o=None, lse=None, retu
     [B, T, H, D]; returns (o, lse) with lse float32 [B, H, T] (None if
     return_lse is False)."""
     import torch
+    if q.dim() != 4:
+        raise ValueError("q must be a [B, T, H, D] tensor")
     B, T, H, D = q.shape
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _check(t, name, torch.bfloat16)
-    _check(cu_seqlens, "cu_seqlens", torch.int32)
-    if k.shape != q.shape or v.shape != q.shape:
-        raise ValueError("q, k, v must have the same shape")
-    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    dev = q.device
+    N = B if cu_seqlens is None else _check_cu_seqlens(cu_seqlens, B, dev)
+    bf = torch.bfloat16
+    _validate([("q", q, (B, T, H, D), bf), ("k", k, (B, T, H, D), bf),
+               ("v", v, (B, T, H, D), bf), ("o", o, (B, T, H, D), bf),
+               ("lse", lse, (B, H, T), torch.float32)], dev)
     if scale is None:
         scale = D ** -0.5
     if o is None:
         o = torch.empty_like(q)
     if lse is None and return_lse:
-        lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
+        lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
     nbytes = gdn2_swa_fwd_workspace_bytes(N, cu_seqlens is not None)
-    if workspace is None and nbytes:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0
+    if workspace is not None or nbytes:
+        workspace, ws_bytes = _workspace(workspace, nbytes, dev)
     st = gdn2_swa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens), N, B, T,
-                      H, D, int(window), float(scale), _ptr(workspace),
-                      0 if workspace is None else workspace.numel(), _stream(stream))
+                      H, D, int(window), float(scale), _ptr(workspace), ws_bytes,
+                      _stream(stream))
     if st != GDN2_OK:
         raise Gdn2Error(st, "gdn2_swa_fwd")
     return o, lse
@@ -442,25 +500,26 @@ def swa_layer_fwd(x, W_qkv, W_o, H, D, window, scale=None, cu_seqlens=None, y=No
     """Sliding-window attention layer (gdn2_swa_layer_fwd).  x [B, T, Dm],
     W_qkv [3 H D, Dm], W_o [Dm, H D], all bfloat16.  Returns (y, lse)."""
     import torch
+    if x.dim() != 3:
+        raise ValueError("x must be a [B, T, Dm] tensor")
     B, T, Dm = x.shape
-    for name, t in (("x", x), ("W_qkv", W_qkv), ("W_o", W_o)):
-        _check(t, name, torch.bfloat16)
-    _check(cu_seqlens, "cu_seqlens", torch.int32)
-    if W_qkv.shape != (3 * H * D, Dm) or W_o.shape != (Dm, H * D):
-        raise ValueError("weight shapes do not match H=%d, D=%d, Dm=%d" % (H, D, Dm))
-    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    dev = x.device
+    N = B if cu_seqlens is None else _check_cu_seqlens(cu_seqlens, B, dev)
+    bf = torch.bfloat16
+    _validate([("x", x, (B, T, Dm), bf), ("W_qkv", W_qkv, (3 * H * D, Dm), bf),
+               ("W_o", W_o, (Dm, H * D), bf), ("y", y, (B, T, Dm), bf),
+               ("lse", lse, (B, H, T), torch.float32)], dev)
     if scale is None:
         scale = D ** -0.5
     if y is None:
-        y = torch.empty((B, T, Dm), dtype=torch.bfloat16, device=x.device)
+        y = torch.empty((B, T, Dm), dtype=torch.bfloat16, device=dev)
     if lse is None and return_lse:
-        lse = torch.empty((B, H, T), dtype=torch.float32, device=x.device)
+        lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
     nbytes = gdn2_swa_layer_fwd_workspace_bytes(N, B, T, H, D, Dm, cu_seqlens is not None)
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    workspace, ws_bytes = _workspace(workspace, nbytes, dev)
     st = gdn2_swa_layer_fwd(_ptr(x), _ptr(W_qkv), _ptr(W_o), _ptr(y), _ptr(lse), _ptr(cu_seqlens),
                             N, B, T, H, D, Dm, int(window), float(scale), _ptr(workspace),
-                            workspace.numel(), _stream(stream))
+                            ws_bytes, _stream(stream))
     if st != GDN2_OK:
         raise Gdn2Error(st, "gdn2_swa_layer_fwd")
     return y, lse

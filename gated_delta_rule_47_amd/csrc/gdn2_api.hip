@@ -14,7 +14,7 @@ using namespace gdn2;
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -45,7 +45,7 @@ int finish(hipError_t launch_err, hipStream_t stream) {
 namespace gdn2 {
 
 bool workspace_layout(int N, int B, int T, int H, int Dk, int Dv, size_t io_bytes, bool varlen,
-                      WorkspaceLayout *out) {
+                      WorkspaceLayout *out, bool for_bwd) {
     if (N < 0 || B < 0 || T < 0 || H < 0 || !supported_dims(Dk, Dv)) return false;
     const long long nc_seq = (T + kChunk - 1) / kChunk;
     long long max_chunks = varlen ? nc_seq + N : (long long)B * nc_seq;
@@ -60,16 +60,19 @@ bool workspace_layout(int N, int B, int T, int H, int Dk, int Dv, size_t io_byte
         off = align_up(off + bytes);
         return at;
     };
-    L.off_T = take(chd * kChunk * kChunk * io_bytes);
     L.off_W = take(chd * kChunk * Dk * io_bytes);
-    L.off_Qh = take(chd * kChunk * Dk * io_bytes);
+    // Qhat and M serve the output only: a backward call (no o) has no slots for them.
+    L.off_Qh = for_bwd ? kNoSlot : take(chd * kChunk * Dk * io_bytes);
     L.off_KhT = take(chd * Dk * kChunk * io_bytes);
-    L.off_M = take(chd * kChunk * kChunk * io_bytes);
+    L.off_M = for_bwd ? kNoSlot : take(chd * kChunk * kChunk * io_bytes);
     L.off_U = take(chd * kChunk * Dv * io_bytes);
     L.off_gl = take(chd * Dk * sizeof(float));
     L.plan_ints = varlen ? (size_t)N + 1 + 3 * (size_t)max_chunks : 0;
     L.off_plan = take(L.plan_ints * sizeof(int32_t));
     L.total = off;
+    // T itself is kept only on request (GDN2_STAGE_STORE_T), after everything else.
+    L.off_T = for_bwd ? kNoSlot : off;
+    L.total_T = for_bwd ? off : align_up(off + chd * kChunk * kChunk * io_bytes);
     *out = L;
     return true;
 }
@@ -77,7 +80,7 @@ bool workspace_layout(int N, int B, int T, int H, int Dk, int Dv, size_t io_byte
 bool bwd_layout(int N, int B, int T, int H, int Dk, int Dv, size_t io_bytes, bool varlen,
                 BwdLayout *out) {
     BwdLayout L;
-    if (!workspace_layout(N, B, T, H, Dk, Dv, io_bytes, varlen, &L.fwd)) return false;
+    if (!workspace_layout(N, B, T, H, Dk, Dv, io_bytes, varlen, &L.fwd, true)) return false;
     const size_t chd = (size_t)L.fwd.max_chunks * (size_t)H;
     size_t off = align_up(L.fwd.total);
     auto take = [&](size_t bytes) {
@@ -139,6 +142,7 @@ int gdn2_chunk_fwd_workspace_layout(int N, int B, int T, int H, int Dk, int Dv, 
     if (!workspace_layout(N, B, T, H, Dk, Dv, io_size(io), varlen != 0, &L))
         return GDN2_ERR_INVALID_ARGUMENT;
     out->total_bytes = L.total;
+    out->total_bytes_with_Tinv = L.total_T;
     out->max_chunks = L.max_chunks;
     out->off_Tinv = L.off_T;
     out->off_W = L.off_W;
@@ -179,13 +183,16 @@ static int chunk_fwd_impl(const void *q, const void *k, const void *v, const voi
     if ((S0 && !aligned16(S0)) || (S_final && !aligned16(S_final)) ||
         (cu_seqlens && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3)))
         return GDN2_ERR_INVALID_ARGUMENT;
-    if ((const void *)o == (const void *)S0 || (const void *)o == (const void *)S_final)
+    // (an empty call may pass o == NULL together with a NULL S0 or S_final)
+    if (o && ((const void *)o == (const void *)S0 || (const void *)o == (const void *)S_final))
         return GDN2_ERR_INVALID_ARGUMENT;
 
     WorkspaceLayout L;
     if (!workspace_layout(N, B, T, H, Dk, Dv, io_size(io), varlen, &L))
         return GDN2_ERR_INVALID_ARGUMENT;
-    if (L.total > 0 && (!workspace || workspace_bytes < L.total)) return GDN2_ERR_WORKSPACE;
+    const bool store_T = (stages & GDN2_STAGE_STORE_T) && (stages & GDN2_STAGE_FACTORS);
+    const size_t need = store_T ? L.total_T : L.total;
+    if (need > 0 && (!workspace || workspace_bytes < need)) return GDN2_ERR_WORKSPACE;
     if (workspace && (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)))
         return GDN2_ERR_WORKSPACE;
 
@@ -213,13 +220,13 @@ static int chunk_fwd_impl(const void *q, const void *k, const void *v, const voi
     a.NC = (T + kChunk - 1) / kChunk;
     a.max_chunks = L.max_chunks;
     a.plan = varlen ? reinterpret_cast<int32_t *>(ws + L.off_plan) : nullptr;
-    a.ws_T = ws + L.off_T;
+    a.ws_T = store_T ? ws + L.off_T : nullptr;
     a.ws_W = ws + L.off_W;
     a.ws_Qh = ws + L.off_Qh;
     a.ws_KhT = ws + L.off_KhT;
     a.ws_M = ws + L.off_M;
     a.ws_U = ws + L.off_U;
-    a.store_T = (stages & GDN2_STAGE_STORE_T) ? 1 : 0;
+    a.store_T = store_T ? 1 : 0;
     a.ws_gl = reinterpret_cast<float *>(ws + L.off_gl);
     const bool bf = io == GDN2_BF16;
 
@@ -337,11 +344,11 @@ int gdn2_chunk_bwd(const void *q, const void *k, const void *v, const float *log
     a.NC = (T + kChunk - 1) / kChunk;
     a.max_chunks = F.max_chunks;
     a.plan = varlen ? reinterpret_cast<int32_t *>(ws + F.off_plan) : nullptr;
-    a.ws_T = ws + F.off_T;
+    a.ws_T = nullptr;  // a backward call has no T, Qhat or M slots
     a.ws_W = ws + F.off_W;
-    a.ws_Qh = ws + F.off_Qh;
+    a.ws_Qh = nullptr;
     a.ws_KhT = ws + F.off_KhT;
-    a.ws_M = ws + F.off_M;
+    a.ws_M = nullptr;
     a.ws_U = ws + F.off_U;
     a.ws_gl = reinterpret_cast<float *>(ws + F.off_gl);
     a.store_T = 0;  // the backward kernels read T^T (ws_Tt) only

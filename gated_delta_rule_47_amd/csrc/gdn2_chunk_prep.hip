@@ -254,8 +254,10 @@ __device__ __forceinline__ float sigmoid1(float x) {
 // kLogits: the gates arrive as bf16 -- log alpha itself and the logits of b
 // and w, whose sigmoid is taken here.  kAlphaLogit (with kLogits): log_alpha
 // holds logits too, and log alpha = logsigmoid(logit + a.alpha_bias).
+// Two workgroups per CU where their LDS fits (fp32 with 128-wide heads needs
+// over 80 KB, so one workgroup runs per CU and may use all of its registers).
 template <typename E, int DK, bool kBwd, bool kLogits = false, bool kAlphaLogit = false>
-__global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(ChunkArgs a) {
+__global__ __launch_bounds__(kThreads, (PrepCfg<E, DK>::SMEM <= 80 * 1024 ? 2 : 1)) void chunk_prep_kernel(ChunkArgs a) {
     using C = PrepCfg<E, DK>;
     using M = Mma<E>;
     constexpr int TPG = C::TPG, LDT = C::LDT, LDC = C::LDC, LDA = C::LDA, LDX = C::LDX;
@@ -361,7 +363,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(ChunkArgs a) {
     for (int c = 0; c < 4; ++c) egr[c] = __expf(gr[c]);
 
     // ---- scaled tiles --------------------------------------------------------
-    E *Qh = reinterpret_cast<E *>(a.ws_Qh) + ch * kChunk * DK;
+    E *Qh = kBwd ? nullptr : reinterpret_cast<E *>(a.ws_Qh) + ch * kChunk * DK;
     E *KhT = reinterpret_cast<E *>(a.ws_KhT) + ch * DK * kChunk;
     Vec4<E> qp[TPG], qh[TPG];
 #pragma unroll
@@ -484,7 +486,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(ChunkArgs a) {
     }
     __syncthreads();
     if constexpr (!kBwd) stage_copy_out<E, C::NG>(Qh, sStg, tid);
-    E *Mg = reinterpret_cast<E *>(a.ws_M) + ch * kChunk * kChunk;
+    E *Mg = kBwd ? nullptr : reinterpret_cast<E *>(a.ws_M) + ch * kChunk * kChunk;
 #pragma unroll
     for (int u = 0; u < 3; ++u) {
         const int t = wave + 4 * u;

@@ -63,7 +63,6 @@ template <typename E, int DK, int DV, int DVS>
 __device__ __forceinline__ void load_chunk(ChunkFrags<E, DK, DVS> &f, const ChunkArgs &a, int n,
                                            int h, int cid, int cbeg, int col0, int wave,
                                            int lane) {
-    using M = Mma<E>;
     using C = PropCfg<E, DK, DVS>;
     using F = ChunkFrags<E, DK, DVS>;
     if (a.plan) {
@@ -109,8 +108,10 @@ __device__ __forceinline__ f32x4 to_f32x4(V4 x) {
     return f32x4{to_f32(x[0]), to_f32(x[1]), to_f32(x[2]), to_f32(x[3])};
 }
 
+// Two workgroups per CU where their LDS fits (fp32 with 64-column slabs of
+// 128-wide heads needs 85 KB: one workgroup per CU, all registers).
 template <typename E, int DK, int DV, int DVS>
-__global__ __launch_bounds__(kThreads, 2) void chunk_prop_kernel(ChunkArgs a) {
+__global__ __launch_bounds__(kThreads, (PropCfg<E, DK, DVS>::SMEM <= 80 * 1024 ? 2 : 1)) void chunk_prop_kernel(ChunkArgs a) {
     using C = PropCfg<E, DK, DVS>;
     using M = Mma<E>;
     using F = ChunkFrags<E, DK, DVS>;

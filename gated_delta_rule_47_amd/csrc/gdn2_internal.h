@@ -10,19 +10,25 @@ namespace gdn2 {
 
 typedef __bf16 bf16_t;
 
+// Offset of a workspace slot that a layout does not have.
+constexpr size_t kNoSlot = ~(size_t)0;
+
 // Per-chunk intermediates written by the chunk-factor kernel and consumed by
 // the state-propagation kernel.  All arrays are indexed [chunk id][head][...].
+// total covers every slot a forward call uses; total_T also covers T, which
+// is stored only on request and sits after everything else.
 struct WorkspaceLayout {
-    size_t total = 0;
+    size_t total = 0, total_T = 0;
     int max_chunks = 0;
     size_t off_T = 0, off_W = 0, off_Qh = 0, off_KhT = 0, off_M = 0, off_U = 0, off_gl = 0,
            off_plan = 0;
     size_t plan_ints = 0;
 };
 
-// Returns false when the sizes overflow or are invalid.
+// Returns false when the sizes overflow or are invalid.  for_bwd: the layout
+// a backward call needs (no T, Qhat or M slots; those offsets are kNoSlot).
 bool workspace_layout(int N, int B, int T, int H, int Dk, int Dv, size_t io_bytes, bool varlen,
-                      WorkspaceLayout *out);
+                      WorkspaceLayout *out, bool for_bwd = false);
 
 struct ChunkArgs {
     const void *q, *k, *v;
@@ -51,9 +57,8 @@ struct ChunkArgs {
     void *ws_Mt, *ws_Kh, *ws_Qt, *ws_Wt, *ws_Tt;
 };
 
-// The backward's workspace: the forward's layout (its T, Qhat and M regions
-// unused), the
-// transposed chunk factors (io dtype, fragment order), then arrays indexed
+// The backward's workspace: the forward's layout without its T, Qhat and M
+// slots, the transposed chunk factors (io dtype, fragment order), then arrays indexed
 // [chunk id][head][...]: every chunk's incoming state Sc and the gradient dSc
 // of its outgoing state (bf16 Dk x Dv, laid out by sc_index); the state-side
 // partial gradients

@@ -60,7 +60,8 @@ typedef enum gdn2_dtype {
     GDN2_BF16 = 1
 } gdn2_dtype;
 
-/* Version of this interface; bumped on any incompatible change. */
+/* Version of this interface; bumped on any incompatible change (2: the
+ * workspace layout reports the size with the optional T slot separately). */
 int gdn2_abi_version(void);
 
 /* Static, human-readable name of a status code (never NULL). */
@@ -106,7 +107,8 @@ size_t gdn2_chunk_fwd_workspace_bytes(int N, int B, int T, int H, int Dk, int Dv
  * The workspace (device memory, >= gdn2_chunk_fwd_workspace_bytes(...) bytes,
  * 256-byte aligned) holds the per-chunk intermediates; its layout is
  * described by gdn2_chunk_fwd_workspace_layout.  T == 0 or N == 0 is allowed:
- * then S_final = S0 (or zero) and o is untouched.
+ * then S_final = S0 (or zero) and o is untouched; with T == 0 the token
+ * pointers (q ... w, o) may be NULL.
  *
  * Precondition on the decay: within one 64-token chunk, the decay of any key
  * channel must stay below about 170 nats (half of it must be representable
@@ -131,7 +133,9 @@ int gdn2_chunk_fwd(const void *q, const void *k, const void *v,
 #define GDN2_STAGE_FACTORS 2    /* per chunk: cumulative decay, A, T = (I+A)^-1, W, U, M, Qhat, Khat */
 #define GDN2_STAGE_PROPAGATE 4  /* sequential state propagation: U_eff, o, S_final */
 #define GDN2_STAGE_ALL 7
-#define GDN2_STAGE_STORE_T 8    /* with FACTORS: also store T in the workspace (inspection only) */
+#define GDN2_STAGE_STORE_T 8    /* with FACTORS: also store T in the workspace (inspection only);
+                                   the workspace must then hold total_bytes_with_Tinv bytes
+                                   (gdn2_chunk_fwd_workspace_layout) */
 
 int gdn2_chunk_fwd_stages(const void *q, const void *k, const void *v,
                           const float *log_alpha, const float *b, const float *w,
@@ -162,7 +166,10 @@ int gdn2_chunk_fwd_gate_logits(const void *q, const void *k, const void *v,
 
 /*
  * Where gdn2_chunk_fwd keeps its per-chunk intermediates inside the
- * workspace, for inspection by tests.  Offsets are in bytes from the
+ * workspace, for inspection by tests.  total_bytes is what
+ * gdn2_chunk_fwd_workspace_bytes returns; total_bytes_with_Tinv also covers
+ * the Tinv slot, which lies after every other slot and is used only by
+ * calls whose stages include GDN2_STAGE_STORE_T.  Offsets are in bytes from the
  * workspace start; every array is indexed by (chunk id c, head h) as
  * [c][h][...], with chunk ids numbered sequence by sequence (dense: chunk c
  * of row n has id n * ceil(T/64) + c).  Element type is the io dtype unless
@@ -189,6 +196,7 @@ typedef struct gdn2_workspace_layout {
     size_t total_bytes;
     int max_chunks;          /* chunk-id capacity */
     size_t off_Tinv, off_W, off_Qhat, off_KhatT, off_M, off_U, off_gamma_last, off_plan;
+    size_t total_bytes_with_Tinv;
 } gdn2_workspace_layout;
 
 int gdn2_chunk_fwd_workspace_layout(int N, int B, int T, int H, int Dk, int Dv,

@@ -1,5 +1,4 @@
-"""Helpers for the GPU parity tests: upload seeded inputs, run the library,
-evaluate the oracle on sampled (sequence, head) pairs."""
+"""Helpers for the GPU parity tests: upload seeded inputs and the parity bound."""
 
 import sys
 
@@ -40,33 +39,3 @@ def upload_chunk(inp):
 def tol(io):
     """Parity bound on max|err| / max|ref|: 2e-2 for bf16 I/O, 1e-4 all-fp32."""
     return 2e-2 if io == W.BF16 else 1e-4
-
-
-def oracle_sampled(inp, pairs):
-    """Oracle outputs for (sequence n, head h) pairs.
-
-    Returns {(n, h): (o [L, Dv], S_final [Dk, Dv])}, where o covers the
-    sequence's tokens only.
-    """
-    cu = inp["cu_seqlens"]
-    out = {}
-    for n, h in pairs:
-        if cu is None:
-            row, t0, t1 = n, 0, inp["T"]
-        else:
-            row, t0, t1 = 0, int(cu[n]), int(cu[n + 1])
-        sl = (slice(row, row + 1), slice(t0, t1), slice(h, h + 1))
-        S0 = None if inp["S0"] is None else inp["S0"][n:n + 1, h:h + 1]
-        o, S = O.recurrence(*(inp[x][sl] for x in ("q", "k", "v", "log_alpha", "b", "w")), S0=S0)
-        out[(n, h)] = (o[0, :, 0], S[0, 0])
-    return out
-
-
-def gpu_slices(inp, o_gpu, S_gpu, n, h):
-    """The GPU outputs matching oracle_sampled's (n, h) entry, as float64 arrays."""
-    cu = inp["cu_seqlens"]
-    if cu is None:
-        o = o_gpu[n, :, h]
-    else:
-        o = o_gpu[0, int(cu[n]):int(cu[n + 1]), h]
-    return host(o), host(S_gpu[n, h])

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert g.gdn2_abi_version() == 1
+    assert g.gdn2_abi_version() == 2
     assert g.gdn2_status_string(g.GDN2_OK) == "GDN2_OK"
     assert g.gdn2_status_string(g.GDN2_ERR_WORKSPACE) == "GDN2_ERR_WORKSPACE"
     assert g.gdn2_status_string(99) == "GDN2_ERR_UNKNOWN"
@@ -42,11 +42,17 @@ def test_workspace_size_and_layout():
     L = g.gdn2_chunk_fwd_workspace_layout(8, 8, 4096, 16, 128, 128, g.GDN2_BF16, 0)
     assert L.total_bytes == n and L.max_chunks == 8 * 64
     chd = 8 * 64 * 16
-    # T, W, Qhat, KhatT, M in bf16 plus gamma_last in f32, each 256-byte aligned
-    assert L.off_W - L.off_Tinv == chd * 64 * 64 * 2
+    # W, Qhat, KhatT, M, U in bf16 plus gamma_last in f32, each 256-byte aligned;
+    # the optional T slot comes after everything else and is not in total_bytes
+    assert L.off_Qhat - L.off_W == chd * 64 * 128 * 2
     assert L.off_M - L.off_KhatT == chd * 128 * 64 * 2
+    assert L.off_Tinv == L.total_bytes
+    assert L.total_bytes_with_Tinv == L.total_bytes + chd * 64 * 64 * 2
     for off in (L.off_Tinv, L.off_W, L.off_Qhat, L.off_KhatT, L.off_M, L.off_gamma_last):
         assert off % 256 == 0
+    # the backward's workspace has no T, Qhat or M slots of its own
+    nb = g.gdn2_chunk_bwd_workspace_bytes(8, 8, 4096, 16, 128, 128, g.GDN2_BF16, 0)
+    assert 0 < nb < 2_000_000_000
     Lv = g.gdn2_chunk_fwd_workspace_layout(32, 1, 139000, 16, 128, 128, g.GDN2_BF16, 1)
     assert Lv.max_chunks == (139000 + 63) // 64 + 32
     assert Lv.total_bytes >= Lv.off_plan + 4 * (33 + 3 * Lv.max_chunks)
@@ -78,9 +84,26 @@ def test_chunk_fwd_validation():
     need = g.gdn2_chunk_fwd_workspace_bytes(1, 1, 64, 1, 128, 128, g.GDN2_BF16, 0)
     assert _chunk(workspace=P16, workspace_bytes=need - 1) == g.GDN2_ERR_WORKSPACE
     assert _chunk(workspace=P16 + 16, workspace_bytes=need) == g.GDN2_ERR_WORKSPACE  # not 256-aligned
+    # the T slot is required only when the stages ask for T
+    L = g.gdn2_chunk_fwd_workspace_layout(1, 1, 64, 1, 128, 128, g.GDN2_BF16, 0)
+    assert g.gdn2_chunk_fwd_stages(P16, P16, P16, P16, P16, P16, None, P16 + 4096, None, None, 1, 1,
+                                   64, 1, 128, 128, g.GDN2_BF16, P16, L.total_bytes, None,
+                                   g.GDN2_STAGE_ALL | g.GDN2_STAGE_STORE_T) == g.GDN2_ERR_WORKSPACE
     # empty calls succeed without touching the GPU
     assert _chunk(N=0, B=0) == g.GDN2_OK
     assert _chunk(H=0) == g.GDN2_OK
+
+
+def test_chunk_fwd_empty_call_without_buffers():
+    """T == 0 with o, S0 and the token pointers all NULL is a valid call (it
+    writes S_final = 0).  Validation must accept it; without a GPU the launch
+    that writes S_final is what fails here."""
+    none = dict(q=None, k=None, v=None, log_alpha=None, b=None, w=None, o=None, S0=None)
+    st = _chunk(T=0, S_final=P16 + 8192, **none)
+    assert st in (g.GDN2_OK, g.GDN2_ERR_HIP)
+    assert _chunk(T=0, S_final=None, **none) in (g.GDN2_OK, g.GDN2_ERR_HIP)
+    # a non-empty call still needs every token pointer
+    assert _chunk(T=64, S_final=P16 + 8192, **none) == g.GDN2_ERR_INVALID_ARGUMENT
 
 
 def _step(**kw):
@@ -189,3 +212,72 @@ def test_swa_layer_fwd_validation():
     assert need > 0 and g.gdn2_swa_layer_fwd_workspace_bytes(1, 1, 64, 1, 128, 100, 0) == 0
     assert _swa_layer(workspace=P16, workspace_bytes=need - 1) == g.GDN2_ERR_WORKSPACE
     assert _swa_layer(T=0) == g.GDN2_OK and _swa_layer(H=0) == g.GDN2_OK
+
+
+# ---------------------------------------------------------------------------
+# The binding's own checks: every tensor's shape, dtype and device is compared
+# with the sizes taken from q (or x) before an address reaches the library.
+# Metadata is checked before the device, so CPU tensors exercise these paths.
+# ---------------------------------------------------------------------------
+
+def _chunk_tensors(B=2, T=8, H=3, D=64, dtype="bfloat16"):
+    import torch
+    dt = getattr(torch, dtype)
+    tk = torch.zeros(B, T, H, D, dtype=dt)
+    f = torch.zeros(B, T, H, D, dtype=torch.float32)
+    return dict(q=tk, k=tk.clone(), v=tk.clone(), log_alpha=f, b=f.clone(), w=f.clone())
+
+
+@pytest.mark.parametrize("name,shape", [("k", (2, 8, 3, 32)), ("v", (2, 8, 2, 64)),
+                                        ("log_alpha", (2, 8, 3, 1)), ("b", (2, 7, 3, 64)),
+                                        ("w", (1, 8, 3, 64))])
+def test_binding_chunk_fwd_rejects_wrong_shapes(name, shape):
+    import torch
+    x = _chunk_tensors()
+    x[name] = torch.zeros(shape, dtype=x[name].dtype)
+    with pytest.raises(ValueError, match=name):
+        g.chunk_fwd(**x)
+
+
+def test_binding_chunk_fwd_rejects_wrong_outputs_and_states():
+    import torch
+    x = _chunk_tensors()
+    with pytest.raises(ValueError, match="S0"):
+        g.chunk_fwd(**x, S0=torch.zeros(2, 3, 64, 32))
+    with pytest.raises(TypeError, match="S0"):
+        g.chunk_fwd(**x, S0=torch.zeros(2, 3, 64, 64, dtype=torch.float64))
+    with pytest.raises(TypeError, match="o"):
+        g.chunk_fwd(**x, o=torch.zeros(2, 8, 3, 64, dtype=torch.float32))     # fp32 o, bf16 q
+    with pytest.raises(ValueError, match="S_final"):
+        g.chunk_fwd(**x, S_final=torch.zeros(1, 3, 64, 64))
+    with pytest.raises(TypeError, match="log_alpha"):
+        g.chunk_fwd(**dict(x, log_alpha=x["log_alpha"].to(torch.bfloat16)))
+    with pytest.raises(ValueError, match="device tensor"):   # right sizes, but host memory
+        g.chunk_fwd(**x)
+
+
+def test_binding_packed_calls_need_one_row():
+    import torch
+    x = _chunk_tensors()
+    with pytest.raises(ValueError, match="B == 1"):
+        g.chunk_fwd(**x, cu_seqlens=torch.tensor([0, 4, 8], dtype=torch.int32))
+
+
+def test_binding_step_and_bwd_reject_wrong_shapes():
+    import torch
+    bf = torch.bfloat16
+    q = torch.zeros(4, 2, 64, dtype=bf)
+    f = torch.zeros(4, 2, 64)
+    with pytest.raises(ValueError, match="S"):
+        g.step(q, q, q, f, f, f, torch.zeros(4, 2, 64, 32))
+    with pytest.raises(ValueError, match="b"):
+        g.step(q, q, q, f, torch.zeros(4, 1, 64), f, torch.zeros(4, 2, 64, 64))
+    with pytest.raises(TypeError, match="o"):
+        g.step(q, q, q, f, f, f, torch.zeros(4, 2, 64, 64), o=torch.zeros(4, 2, 64))
+    x = _chunk_tensors()
+    with pytest.raises(ValueError, match="dout"):
+        g.chunk_bwd(**x, dout=torch.zeros(2, 8, 3, 32, dtype=bf))
+    with pytest.raises(ValueError, match="dS_final"):
+        g.chunk_bwd(**x, dout=torch.zeros(2, 8, 3, 64, dtype=bf), dS_final=torch.zeros(3, 64, 64))
+    with pytest.raises(TypeError, match="w_logit"):
+        g.chunk_fwd_gate_logits(x["q"], x["k"], x["v"], x["q"], x["q"], x["w"])

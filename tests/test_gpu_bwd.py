@@ -8,14 +8,15 @@ import pytest
 import gated_delta_rule_47_amd as g
 import oracle as O
 import workloads as W
-from gpu_util import dev, host, log, upload_chunk
+from gpu_util import dev, host, log, tol, upload_chunk
 
 pytestmark = pytest.mark.gpu
 
 NAMES = ("dq", "dk", "dv", "dlog_alpha", "db", "dw", "dS0")
-# bf16 I/O: the forward's bf16 factors and the bf16 gradient outputs bound the
-# agreement at a few 1e-3 of the largest value; the bound leaves headroom.
-TOL = 3e-2
+# The forward's parity bound on max|err| / max|ref| for the io dtype (2e-2
+# for bf16), applied to every gradient: the bf16 factors and the bf16
+# gradient outputs keep the measured agreement within about 1e-2.
+TOL = tol(W.BF16)
 
 
 def _run_bwd(inp, grads):
@@ -125,20 +126,23 @@ def test_bwd_f32_unsupported():
 
 def test_bwd_full_batch_workload_sampled():
     """B=8, H=16, T=4096, d=128 (the batch workload) in the launch configuration
-    the benchmark times; sampled (sequence, head) pairs against the oracle's
-    chunk-form backward (pinned to the reverse recurrence on the CPU)."""
+    the benchmark times; sampled (sequence, head) pairs against the plain
+    reverse recurrence (oracle.recurrence_bwd)."""
     inp = W.make_chunk_inputs(W.BATCH_4K)
     grads = W.make_chunk_grads(inp, 1)
     out = _run_bwd(inp, grads)
-    for n, h in [(0, 0), (5, 9), (7, 15)]:
+    out = {n: host(t) for n, t in out.items()}
+    worst = {}
+    for n, h in [(0, 0), (2, 5), (5, 9), (7, 15)]:
         sl = (slice(n, n + 1), slice(None), slice(h, h + 1))
-        ref = O.chunked_bwd(*(inp[x][sl] for x in ("q", "k", "v", "log_alpha", "b", "w")),
-                            grads["dout"][sl], inp["S0"][n:n + 1, h:h + 1],
-                            grads["dS_final"][n:n + 1, h:h + 1])
+        ref = O.recurrence_bwd(*(inp[x][sl] for x in ("q", "k", "v", "log_alpha", "b", "w")),
+                               grads["dout"][sl], inp["S0"][n:n + 1, h:h + 1],
+                               grads["dS_final"][n:n + 1, h:h + 1])
         errs = {}
         for name in NAMES:
             got = out[name][n:n + 1, h:h + 1] if name == "dS0" else out[name][sl]
-            errs[name] = O.rel_max_err(host(got), ref[name])
+            errs[name] = O.rel_max_err(got, ref[name])
+            worst[name] = max(worst.get(name, 0.0), errs[name])
         log("bwd batch (%d,%d): %s" % (n, h, " ".join("%s %.2e" % kv for kv in errs.items())))
-        for name, e in errs.items():
-            assert e <= TOL, (name, e)
+    for name, e in worst.items():
+        assert e <= TOL, (name, e)

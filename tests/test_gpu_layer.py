@@ -46,7 +46,7 @@ def _oracle(inp, rows=None):
         S0 = None if S0 is None else S0[rows]
     return LO.layer_fwd(x, inp["W_in"], inp["conv_w"], inp["alpha_bias"], inp["norm_w"],
                         inp["W_o"], inp["H"], inp["Dk"], inp["Dv"], S0=S0,
-                        cu_seqlens=inp["cu_seqlens"])
+                        cu_seqlens=inp["cu_seqlens"], core=O.recurrence)
 
 
 def _check(inp, label):
