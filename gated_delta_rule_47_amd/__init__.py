@@ -35,7 +35,7 @@ EXPORTED = ("gdn2_abi_version", "gdn2_status_string", "gdn2_chunk_fwd_workspace_
             "gdn2_chunk_fwd_gate_logits", "gdn2_chunk_bwd_workspace_bytes", "gdn2_chunk_bwd",
             "gdn2_step", "gdn2_layer_fwd_workspace_bytes", "gdn2_layer_fwd",
             "gdn2_swa_fwd_workspace_bytes", "gdn2_swa_fwd", "gdn2_swa_layer_fwd_workspace_bytes",
-            "gdn2_swa_layer_fwd")
+            "gdn2_swa_layer_fwd", "gdn2_chunk_fwd_noalloc")
 
 
 class Gdn2Error(RuntimeError):
@@ -83,6 +83,8 @@ def load_library(path=LIB_PATH):
     lib.gdn2_chunk_fwd_workspace_layout.argtypes = [I] * 8 + [ctypes.POINTER(WorkspaceLayout)]
     lib.gdn2_chunk_fwd.restype = I
     lib.gdn2_chunk_fwd.argtypes = [P] * 10 + [I] * 7 + [P, Z, P]
+    lib.gdn2_chunk_fwd_noalloc.restype = I
+    lib.gdn2_chunk_fwd_noalloc.argtypes = [P] * 10 + [I] * 7 + [P]
     lib.gdn2_chunk_fwd_stages.restype = I
     lib.gdn2_chunk_fwd_stages.argtypes = [P] * 10 + [I] * 7 + [P, Z, P, I]
     lib.gdn2_chunk_fwd_gate_logits.restype = I
@@ -141,6 +143,14 @@ def gdn2_chunk_fwd(q, k, v, log_alpha, b, w, S0, o, S_final, cu_seqlens, N, B, T
     return load_library().gdn2_chunk_fwd(q, k, v, log_alpha, b, w, S0, o, S_final, cu_seqlens,
                                           N, B, T, H, Dk, Dv, io, workspace, workspace_bytes,
                                           stream)
+
+
+def gdn2_chunk_fwd_noalloc(q, k, v, log_alpha, b, w, S0, o, S_final, cu_seqlens, N, B, T, H, Dk,
+                           Dv, io, stream):
+    """Raw call of the chunk forward that allocates nothing (no workspace
+    argument; the library's own fixed device region holds the intermediates)."""
+    return load_library().gdn2_chunk_fwd_noalloc(q, k, v, log_alpha, b, w, S0, o, S_final,
+                                                  cu_seqlens, N, B, T, H, Dk, Dv, io, stream)
 
 
 def gdn2_layer_fwd_workspace_bytes(N, B, T, H, Dk, Dv, D, varlen):

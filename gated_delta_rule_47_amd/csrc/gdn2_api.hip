@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <climits>
+#include <mutex>
 
 #include "gdn2_device.h"
 #include "gdn2_internal.h"
@@ -256,6 +257,64 @@ int gdn2_chunk_fwd(const void *q, const void *k, const void *v, const float *log
                    void *workspace, size_t workspace_bytes, void *stream_ptr) {
     return chunk_fwd_impl(q, k, v, log_alpha, b, w, S0, o, S_final, cu_seqlens, N, B, T, H, Dk, Dv,
                           io, workspace, workspace_bytes, stream_ptr, GDN2_STAGE_ALL, false);
+}
+
+}  // extern "C"
+
+// ---- the chunk forward for callers that cannot allocate ------------------------
+
+// Device memory of gdn2_chunk_fwd_noalloc: the chunk forward's intermediates,
+// laid out as in a caller's workspace.  Each GPU holds its own copy from the
+// library's first use of it until the process ends; every call on a GPU uses
+// that copy, so calls that overlap on one GPU race.  In host code `scratch`
+// names a host-side stand-in: only the address scratch_address() returns may
+// reach a kernel.
+constexpr size_t kScratchBytes = size_t(128) << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+// The device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept; nullptr if the lookup fails.
+void *scratch_address() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        addr[dev] = p;
+    }
+    return addr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn2_chunk_fwd_noalloc(const void *q, const void *k, const void *v, const float *log_alpha,
+                           const float *b, const float *w, const float *S0, void *o,
+                           float *S_final, const int32_t *cu_seqlens, int N, int B, int T, int H,
+                           int Dk, int Dv, int io, void *stream_ptr) {
+    // A call whose intermediates do not fit the scratch is rejected first; a
+    // call with invalid sizes gets its error from the common validation.
+    void *ws = nullptr;
+    size_t ws_bytes = 0;
+    WorkspaceLayout L;
+    if ((io == GDN2_F32 || io == GDN2_BF16) && N > 0 && H > 0 &&
+        workspace_layout(N, B, T, H, Dk, Dv, io_size(io), cu_seqlens != nullptr, &L) &&
+        L.total > 0) {
+        if (L.total > kScratchBytes) return GDN2_ERR_WORKSPACE;
+        ws = scratch_address();
+        if (!ws) return GDN2_ERR_HIP;
+        ws_bytes = kScratchBytes;
+    }
+    return chunk_fwd_impl(q, k, v, log_alpha, b, w, S0, o, S_final, cu_seqlens, N, B, T, H, Dk, Dv,
+                          io, ws, ws_bytes, stream_ptr, GDN2_STAGE_ALL, false);
 }
 
 int gdn2_chunk_fwd_gate_logits(const void *q, const void *k, const void *v,

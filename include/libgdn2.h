@@ -122,6 +122,29 @@ int gdn2_chunk_fwd(const void *q, const void *k, const void *v,
                    void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * gdn2_chunk_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, serving loops and harnesses that forbid allocation): the
+ * same computation, arguments and results, but the per-chunk intermediates
+ * live in a fixed region of device memory that the library holds itself, one
+ * per GPU, from the first call on that GPU until the process ends (128 MiB,
+ * 134217728 bytes).  No allocator is called and no workspace is passed.
+ *   - A call needing more than that (gdn2_chunk_fwd_workspace_bytes(...) >
+ *     134217728; about 1800 chunk-heads at Dk = Dv = 128 in bf16, e.g.
+ *     B = 1, H = 16, T = 7168) returns GDN2_ERR_WORKSPACE before anything is
+ *     enqueued; gdn2_chunk_fwd with a caller's workspace has no such limit.
+ *   - Every call on one GPU shares that GPU's region and leaves its own
+ *     intermediates in it: calls that overlap on one GPU (on different
+ *     streams, or from several host threads) race and give undefined
+ *     results.  Calls enqueued on one stream are ordered and safe.
+ *   - GDN2_ERR_HIP if the region's device address cannot be obtained.
+ */
+int gdn2_chunk_fwd_noalloc(const void *q, const void *k, const void *v,
+                           const float *log_alpha, const float *b, const float *w,
+                           const float *S0, void *o, float *S_final,
+                           const int32_t *cu_seqlens, int N,
+                           int B, int T, int H, int Dk, int Dv, int io, void *stream);
+
+/*
  * The stages of gdn2_chunk_fwd, for profiling each kernel on its own and for
  * inspecting the intermediates.  gdn2_chunk_fwd == gdn2_chunk_fwd_stages(...,
  * GDN2_STAGE_ALL).  A later call with the same arguments and workspace may run
