@@ -8,12 +8,18 @@ step, 16 heads each).  The two kernels of the call (chunk factors, state
 propagation) are bracketed with HIP events on the stream they run on, which
 gives each kernel's duration and the roofline of the dominant one.
 
-Also measured in the same run (not part of the headline value):
-  decode: gdn2_step on B=256, H=16, d=128 (fp32 state, in place), GB/s of
-          its algorithmic traffic;
-  varlen: gdn2_chunk_fwd on 32 packed sequences of 512..8192 tokens.
-cpu_baseline: the fp64 numpy oracle on a bounded sample of the same workload,
-on this host's cores (rank 0, N=1 only).
+Also measured in the same run (each in its own object of the JSON line):
+  seq / tiny: gdn2_chunk_fwd on the single-sequence 4K workload (B=1, H=16,
+          16 chains of 64 dependent chunk steps) and on the tiny fp32 one;
+  context_sweep: the same 16K tokens as B x T = 8 x 2K, 4 x 4K, 2 x 8K, 1 x 16K;
+  decode: gdn2_step on B=256, H=16, d=128 (fp32 state, in place) over 1024
+          distinct pre-generated steps, GB/s of its algorithmic traffic;
+  varlen, gate_logits, backward, layer, swa (see the design doc's measurement section).
+cpu_baseline: the fp64 numpy oracle over the whole batch workload, its
+(sequence, head) chains spread over a process pool on this host's cores, plus
+one-core figures for the tiny and single-sequence workloads.  Work that starts
+worker processes (the baseline, the decode inputs) runs before the GPU is
+initialised.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
        python bench.py --calibrate-copy   (plain copy of known size, for PMC scaling)
@@ -45,11 +51,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-steps", type=int, default=1024)
-    ap.add_argument("--only", choices=["all", "chunk", "decode", "varlen", "bwd", "layer", "swa"],
-                    default="all")
+    ap.add_argument("--only", choices=["all", "chunk", "decode", "varlen", "bwd", "layer", "swa",
+                                       "seq", "sweep"], default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-rows", type=int, default=8,
-                    help="batch rows (4096 tokens x 16 heads each) the oracle runs on")
+    ap.add_argument("--workers", type=int, default=0,
+                    help="host worker processes (default: the usable cores, at most 16)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a plain device copy of 1 GiB (5 times) and exit")
     return ap.parse_args()
@@ -181,53 +187,126 @@ def time_chunk(d, inp, steps, warmup):
     return wall / steps * 1e3, f_ms, p_ms
 
 
-def time_decode(steps, pool=16):
-    """gdn2_step over the decode workload: a pool of distinct per-step inputs
-    is cycled; each launch is bracketed by events on its stream."""
+# ---------------------------------------------------------------------------
+# Host-side work done in worker processes, before the GPU is initialised
+# ---------------------------------------------------------------------------
+
+def host_workers(requested=0):
+    """Worker processes for host-side work: the usable cores, at most 16."""
+    n = len(os.sched_getaffinity(0))
+    return max(1, min(requested or n, n, 16))
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+_POOL_INP = None  # inputs shared with forked workers (read only)
+
+
+def _oracle_chain(nh):
+    """The oracle on one (sequence, head) chain of _POOL_INP."""
+    import oracle as O
+    n, h = nh
+    inp = _POOL_INP
+    sl = (slice(n, n + 1), slice(None), slice(h, h + 1))
+    S0 = None if inp["S0"] is None else inp["S0"][n:n + 1, h:h + 1]
+    _, S = O.recurrence(*(inp[x][sl] for x in ("q", "k", "v", "log_alpha", "b", "w")), S0=S0)
+    return float(abs(S).sum())
+
+
+def cpu_baseline(inp, workers):
+    """The oracle as it stands, timed on this host: every (sequence, head)
+    chain of the dense workload `inp`, spread over a pool of forked worker
+    processes (one numpy thread each).  Returns (tokens/s, seconds, tokens)."""
+    import multiprocessing as mp
+    global _POOL_INP
+    _POOL_INP = inp
+    units = [(n, h) for n in range(inp["B"]) for h in range(inp["H"])]
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(workers) as pool:
+        pool.map(_oracle_chain, units, chunksize=1)
+    dt = time.perf_counter() - t0
+    _POOL_INP = None
+    n_tokens = inp["B"] * inp["T"]
+    return n_tokens / dt, dt, n_tokens
+
+
+def cpu_one_core(inp):
+    """The oracle on a whole workload in this process (one core)."""
+    import oracle as O
+    t0 = time.perf_counter()
+    O.recurrence(*(inp[x] for x in ("q", "k", "v", "log_alpha", "b", "w")), S0=inp["S0"],
+                 cu_seqlens=inp["cu_seqlens"])
+    dt = time.perf_counter() - t0
+    return inp["B"] * inp["T"] / dt, dt
+
+
+def _decode_step_packed(s):
+    """Decode step s of the decode workload: bf16 bits of q, k, v (uint16) and
+    the fp32 gates."""
+    import workloads as W
+    x = W.make_decode_step(W.DECODE, s)
+    return (s, W.bf16_bits(x["q"]), W.bf16_bits(x["k"]), W.bf16_bits(x["v"]), x["log_alpha"],
+            x["b"], x["w"])
+
+
+def pregenerate_decode(steps, workers):
+    """All `steps` decode inputs (each step its own seeded stream), made by a
+    pool of forked workers: uint16 [steps, B, H, D] for q, k, v and float32
+    for log_alpha, b, w."""
+    import multiprocessing as mp
+    import workloads as W
+    wl = W.DECODE
+    shp = (steps, wl.B, wl.H, wl.Dk)
+    out = dict(q=np.empty(shp, np.uint16), k=np.empty(shp, np.uint16), v=np.empty(shp, np.uint16),
+               log_alpha=np.empty(shp, np.float32), b=np.empty(shp, np.float32),
+               w=np.empty(shp, np.float32))
+    with mp.get_context("fork").Pool(workers) as pool:
+        for s, *arrs in pool.imap_unordered(_decode_step_packed, range(steps), chunksize=4):
+            for name, arr in zip(("q", "k", "v", "log_alpha", "b", "w"), arrs):
+                out[name][s] = arr
+    return out
+
+
+def time_decode(pre):
+    """gdn2_step over the decode workload: every step reads its own
+    pre-generated inputs (uploaded before timing); each launch is bracketed
+    by events on the launch stream."""
     import torch
     import gated_delta_rule_47_amd as g
     import workloads as W
     wl = W.DECODE
-
-    def dev(x, io=None):
-        if io == W.BF16:
-            return torch.from_numpy(W.bf16_bits(x).view(np.int16)).to("cuda").view(torch.bfloat16)
-        return torch.from_numpy(np.ascontiguousarray(x)).to("cuda")
-    S = dev(W.make_decode_state(wl))
-    xs = []
-    for s in range(pool):
-        x = W.make_decode_step(wl, s)
-        xs.append(tuple(dev(x[k], wl.io if k in ("q", "k", "v") else None)
-                        for k in ("q", "k", "v", "log_alpha", "b", "w")))
+    steps = pre["q"].shape[0]
+    S = torch.from_numpy(W.make_decode_state(wl)).to("cuda")
+    dev = {}
+    for name in ("q", "k", "v"):
+        dev[name] = torch.from_numpy(pre[name].view(np.int16)).to("cuda").view(torch.bfloat16)
+    for name in ("log_alpha", "b", "w"):
+        dev[name] = torch.from_numpy(pre[name]).to("cuda")
+    xs = [tuple(dev[n][i] for n in ("q", "k", "v", "log_alpha", "b", "w")) for i in range(steps)]
     o = torch.empty((wl.B, wl.H, wl.Dv), dtype=torch.bfloat16, device="cuda")
+    S_warm = S.clone()
     for i in range(3):
-        g.step(*xs[i % pool], S, o=o)
+        g.step(*xs[i], S_warm, o=o)
     torch.cuda.synchronize()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     t0 = time.perf_counter()
     for i in range(steps):
         ev[i].record()
-        g.step(*xs[i % pool], S, o=o)
+        g.step(*xs[i], S, o=o)
     ev[steps].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
     assert torch.isfinite(S).all()
     return wall, float(np.mean(per)), float(np.median(per))
-
-
-def cpu_baseline(inp, rows):
-    """The oracle as it stands on a bounded sample: the first `rows` batch
-    rows (whole sequences, all heads), one numpy process."""
-    import oracle as O
-    sl = (slice(0, rows),)
-    args = [inp[x][sl] for x in ("q", "k", "v", "log_alpha", "b", "w")]
-    S0 = inp["S0"][0:rows] if inp["S0"] is not None else None
-    t0 = time.perf_counter()
-    O.recurrence(*args, S0=S0)
-    dt = time.perf_counter() - t0
-    n_tokens = rows * inp["T"]
-    return n_tokens / dt, dt, n_tokens
 
 
 def time_gate_logits(inp, steps, warmup):
@@ -404,6 +483,39 @@ def main():
         print("bench.py runs on one GPU only: libgdn2 has no multi-GPU path "
               "(--gpus %d requested)" % a.gpus, file=sys.stderr)
         sys.exit(2)
+    import workloads as W
+
+    # Host-side work that starts worker processes comes first: nothing below
+    # it initialises the GPU until it is done.
+    workers = host_workers(a.workers)
+    do_chunk = a.only in ("all", "chunk")
+    inp = None
+    cpu = None
+    if do_chunk and not a.calibrate_copy:
+        log("generating %s" % W.BATCH_4K.name)
+        inp = W.make_chunk_inputs(W.BATCH_4K)
+        if not a.no_cpu_baseline:
+            tps, dt, n = cpu_baseline(inp, workers)
+            log("cpu oracle: %.1f tokens/s (%d tokens, %d workers, %.1f s)" % (tps, n, workers, dt))
+            one = {}
+            for wl in (W.TINY_F32, W.SEQ_4K):
+                t1, d1 = cpu_one_core(W.make_chunk_inputs(wl))
+                one[wl.name] = {"tokens_per_s": t1, "seconds": d1}
+                log("cpu oracle, one core, %s: %.1f tokens/s (%.1f s)" % (wl.name, t1, d1))
+            cpu = {"value": tps, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+                   "cpu_model": cpu_model(),
+                   "sample": "fp64 numpy token recurrence over the whole %s workload (%d tokens "
+                             "x 16 heads, S0 as in the workload): its %d (sequence, head) chains "
+                             "on a pool of %d worker processes, one numpy thread each, %.1f s"
+                             % (W.BATCH_4K.name, n, inp["B"] * inp["H"], workers, workers, dt),
+                   "one_core": one}
+    decode_pre = None
+    if a.only in ("all", "decode") and not a.calibrate_copy:
+        t0 = time.perf_counter()
+        decode_pre = pregenerate_decode(a.decode_steps, workers)
+        log("decode inputs: %d steps generated in %.1f s" % (a.decode_steps,
+                                                             time.perf_counter() - t0))
+
     import torch
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -412,17 +524,14 @@ def main():
         calibrate_copy()
         return
     import gated_delta_rule_47_amd as g
-    import workloads as W
     g.load_library()
     out = {"metric": "tokens/s and MFMA util for gdn2_chunk_fwd (H16, d128, T4K); decode GB/s",
            "unit": "tokens/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic (seeded; shapes of a 1.3B-parameter layer: 16 heads, 128x128 state)"}
 
-    if a.only in ("all", "chunk"):
+    if do_chunk:
         wl = W.BATCH_4K
-        log("generating %s" % wl.name)
-        inp = W.make_chunk_inputs(wl)
         d = upload(inp)
         ms, f_ms, p_ms = time_chunk(d, inp, a.steps, a.warmup)
         tokens = inp["B"] * inp["T"]
@@ -443,6 +552,8 @@ def main():
             "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved,
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                          "traffic": stored_traffic(dom, wl.name, digest),
+                         "traffic_source": "committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary "
+                                           "of the same kernel source (null if it changed)",
                          "alg_bytes_per_launch": dbytes, "avg_launch_ms": dms},
             "kernels_ms": {"chunk_factors": f_ms, "chunk_propagate": p_ms},
             "path": {"alg_bytes": fa + pa, "alg_GBps": (fa + pa) / (ms * 1e-3) / 1e9,
@@ -453,15 +564,40 @@ def main():
         })
         log("chunk: %.3f ms/step (factors %.3f, propagate %.3f) -> %.3e tokens/s"
             % (ms, f_ms, p_ms, out["value"]))
-        if not a.no_cpu_baseline:
-            rows = max(1, min(a.cpu_sample_rows, inp["B"]))
-            tps, dt, n = cpu_baseline(inp, rows)
-            out["cpu_baseline"] = {"value": tps, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-                                   "sample": "fp64 numpy token recurrence on batch rows 0..%d "
-                                             "(%d tokens x 16 heads, S0 as in the workload), one "
-                                             "process, %.1f s" % (rows - 1, n, dt)}
-            log("cpu oracle: %.1f tokens/s (%d tokens in %.1f s)" % (tps, n, dt))
+        if cpu is not None:
+            out["cpu_baseline"] = cpu
         del d, inp
+
+    if a.only in ("all", "chunk", "seq"):
+        # The single-sequence 4K workload (16 chains of 64 dependent chunk steps)
+        # and the tiny fp32 one.
+        for key, wl in (("seq", W.SEQ_4K), ("tiny", W.TINY_F32)):
+            inp_s = W.make_chunk_inputs(wl)
+            ms, f_ms, p_ms = time_chunk(upload(inp_s), inp_s, a.steps, a.warmup)
+            tokens = inp_s["B"] * inp_s["T"]
+            nchunks = (inp_s["T"] + 63) // 64
+            out[key] = {"workload": wl.name, "io": wl.io, "ms": ms,
+                        "tokens_per_s": tokens / (ms * 1e-3),
+                        "kernels_ms": {"chunk_factors": f_ms, "chunk_propagate": p_ms},
+                        "chunk_steps_per_chain": nchunks,
+                        "us_per_chunk_step": p_ms * 1e3 / nchunks}
+            log("%s: %.3f ms (factors %.3f, propagate %.3f = %.2f us per chunk step)"
+                % (wl.name, ms, f_ms, p_ms, p_ms * 1e3 / nchunks))
+            del inp_s
+
+    if a.only in ("all", "sweep"):
+        # The same 16K tokens (16 heads) as B x T = 8 x 2K, 4 x 4K, 2 x 8K, 1 x 16K.
+        sweep = []
+        for B, T in ((8, 2048), (4, 4096), (2, 8192), (1, 16384)):
+            inp_s = W.make_chunk_inputs(W.BATCH_4K, B=B, T=T)
+            ms, f_ms, p_ms = time_chunk(upload(inp_s), inp_s, max(5, a.steps // 2), 2)
+            sweep.append({"B": B, "T": T, "ms": ms, "tokens_per_s": B * T / (ms * 1e-3),
+                          "kernels_ms": {"chunk_factors": f_ms, "chunk_propagate": p_ms}})
+            log("sweep B=%d T=%d: %.3f ms (factors %.3f, propagate %.3f) -> %.3e tokens/s"
+                % (B, T, ms, f_ms, p_ms, B * T / (ms * 1e-3)))
+            del inp_s
+        out["context_sweep"] = {"workload": "B x T = 16384 tokens, H16 d128, bf16, S0 != 0",
+                                "points": sweep}
 
     if a.only in ("all", "chunk"):
         # The same batch workload with bf16 gate inputs (log alpha and the b, w logits).
@@ -555,7 +691,8 @@ def main():
 
     if a.only in ("all", "decode"):
         wl = W.DECODE
-        wall, mean_ms, med_ms = time_decode(a.decode_steps)
+        wall, mean_ms, med_ms = time_decode(decode_pre)
+        del decode_pre
         nbytes = decode_alg_bytes(wl.B, wl.H, wl.Dk, 2)
         ddig = source_digest("gdn2_step.hip", "gdn2_device.h")
         dec = {"workload": wl.name, "steps": a.decode_steps, "us_per_step": mean_ms * 1e3,
@@ -567,6 +704,8 @@ def main():
                             "traffic": stored_traffic("decode_step", wl.name, ddig),
                             "alg_bytes_per_launch": nbytes, "avg_launch_ms": mean_ms},
                "alg_bytes_per_step": nbytes, "loop_wall_s": wall,
+               "inputs": "%d distinct pre-generated steps, uploaded before timing"
+                         % a.decode_steps,
                "tokens_per_s": wl.B * a.decode_steps / wall}
         out["decode"] = dec
         log("decode: %.1f us/step, %.0f GB/s (%.1f%% of HBM)"

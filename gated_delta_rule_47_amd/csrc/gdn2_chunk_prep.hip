@@ -287,66 +287,74 @@ __global__ __launch_bounds__(kThreads, (PrepCfg<E, DK>::SMEM <= 80 * 1024 ? 2 : 
     const E *v = reinterpret_cast<const E *>(a.v);
 
     // ---- stage 1: load, cumulative log-decay -------------------------------
-    // q and k stay in their input type (exact) until used.
-    f32x4 g[TPG], bk[TPG];
+    // Every token slot loads unconditionally (from the chunk's last token when
+    // the slot is past its length) and padding slots are zeroed afterwards
+    // (k = q = b = v = 0, log alpha = 0: an exact no-op).  A load under a
+    // per-token branch makes the merge with the other branch's zero wait for
+    // the load, which turned the loads into one memory round trip per token.
+    // The raw values (bf16 gate logits still bf16) are converted only after
+    // every load has been issued.  q and k stay in their input type (exact)
+    // until used.
+    using GR = typename std::conditional<kLogits, bf16x4, f32x4>::type;  // a gate as loaded
+    GR rla[TPG], rb[TPG];
     Vec4<E> kk[TPG], qq[TPG];
+    size_t src[TPG];  // element offset of each slot's token row (head h, channel c0)
+#pragma unroll
+    for (int j = 0; j < TPG; ++j) src[j] = (size_t)(tok0 + max(min(tg * TPG + j, len - 1), 0));
+#pragma unroll
+    for (int j = 0; j < TPG; ++j) {
+        const size_t off = (src[j] * H + h) * DK + c0;
+        if constexpr (kLogits) {
+            const size_t offg = src[j] * a.ld_gate + (size_t)h * DK + c0;
+            rla[j] = *reinterpret_cast<const GR *>(reinterpret_cast<const bf16 *>(a.log_alpha) + offg);
+            rb[j] = *reinterpret_cast<const GR *>(reinterpret_cast<const bf16 *>(a.b) + offg);
+        } else {
+            rla[j] = *reinterpret_cast<const GR *>(a.log_alpha + off);
+            rb[j] = *reinterpret_cast<const GR *>(a.b + off);
+        }
+        kk[j] = *reinterpret_cast<const Vec4<E> *>(k + off);
+        qq[j] = *reinterpret_cast<const Vec4<E> *>(q + off);
+    }
+    // w and v are multiplied only when (w v)^T is staged, after W: their loads
+    // stay in flight through the following phases.
+    using GW = GR;  // w, or its logit
+    GW zw[TPG];
+    Vec4<E> zv[TPG];
+#pragma unroll
+    for (int j = 0; j < TPG; ++j) {
+        const size_t off = (src[j] * H + h) * DK + c0;  // Dv == Dk
+        if constexpr (kLogits)
+            zw[j] = *reinterpret_cast<const GW *>(reinterpret_cast<const bf16 *>(a.w) +
+                                                  src[j] * a.ld_gate + (size_t)h * DK + c0);
+        else
+            zw[j] = *reinterpret_cast<const GW *>(a.w + off);
+        zv[j] = *reinterpret_cast<const Vec4<E> *>(v + off);
+    }
+    f32x4 g[TPG], bk[TPG];
     f32x4 abias = zero4();
     if constexpr (kAlphaLogit) abias = *reinterpret_cast<const f32x4 *>(a.alpha_bias + h * DK + c0);
 #pragma unroll
     for (int j = 0; j < TPG; ++j) {
-        const int i = tg * TPG + j;
-        if (i < len) {
-            const size_t off = ((size_t)(tok0 + i) * H + h) * DK + c0;
-            if constexpr (kLogits) {
-                const size_t offg = (size_t)(tok0 + i) * a.ld_gate + (size_t)h * DK + c0;
-                g[j] = to4(*reinterpret_cast<const bf16x4 *>(reinterpret_cast<const bf16 *>(a.log_alpha) + offg));
-                if constexpr (kAlphaLogit) {
+        const bool pad = tg * TPG + j >= len;
+        g[j] = to4(rla[j]);
+        if constexpr (kAlphaLogit) {
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) g[j][c] = logsigmoid_fast(g[j][c] + abias[c]);
-                }
-                const f32x4 bl = to4(*reinterpret_cast<const bf16x4 *>(reinterpret_cast<const bf16 *>(a.b) + offg));
+            for (int c = 0; c < 4; ++c) g[j][c] = logsigmoid_fast(g[j][c] + abias[c]);
+        }
+        bk[j] = to4(rb[j]);
+        if constexpr (kLogits) {
 #pragma unroll
-                for (int c = 0; c < 4; ++c) bk[j][c] = sigmoid1(bl[c]);
-            } else {
-                g[j] = *reinterpret_cast<const f32x4 *>(a.log_alpha + off);
-                bk[j] = *reinterpret_cast<const f32x4 *>(a.b + off);
-            }
-            kk[j] = *reinterpret_cast<const Vec4<E> *>(k + off);
-            qq[j] = *reinterpret_cast<const Vec4<E> *>(q + off);
-        } else {  // padding token: k = q = b = 0, log alpha = 0 (an exact no-op)
-            g[j] = bk[j] = zero4();
-            kk[j] = qq[j] = pack4<E>(zero4());
+            for (int c = 0; c < 4; ++c) bk[j][c] = sigmoid1(bk[j][c]);
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            g[j][c] = pad ? 0.0f : g[j][c];
+            bk[j][c] = pad ? 0.0f : bk[j][c];
         }
     }
 #pragma unroll
     for (int j = 1; j < TPG; ++j) g[j] += g[j - 1];
     *reinterpret_cast<f32x4 *>(sTot + tg * DK + c0) = g[TPG - 1];
-    // w and v are multiplied only when (w v)^T is staged, after W: their loads
-    // stay in flight through the following phases.
-    using GW = typename std::conditional<kLogits, bf16x4, f32x4>::type;  // w, or its logit
-    GW zw[TPG];
-    Vec4<E> zv[TPG];
-#pragma unroll
-    for (int j = 0; j < TPG; ++j) {
-        const int i = tg * TPG + j;
-        if (i < len) {
-            const size_t off = ((size_t)(tok0 + i) * H + h) * DK + c0;  // Dv == Dk
-            if constexpr (kLogits)
-                zw[j] = *reinterpret_cast<const bf16x4 *>(reinterpret_cast<const bf16 *>(a.w) +
-                                                          (size_t)(tok0 + i) * a.ld_gate + (size_t)h * DK + c0);
-            else
-                zw[j] = *reinterpret_cast<const f32x4 *>(a.w + off);
-            zv[j] = *reinterpret_cast<const Vec4<E> *>(v + off);
-        } else {  // padding token: v = 0 makes w v = 0 whatever w is
-            if constexpr (kLogits) {
-#pragma unroll
-                for (int c = 0; c < 4; ++c) zw[j][c] = static_cast<bf16>(0.0f);
-            } else {
-                zw[j] = zero4();
-            }
-            zv[j] = pack4<E>(zero4());
-        }
-    }
     __syncthreads();
     f32x4 goff = zero4(), glast = zero4();
 #pragma unroll
@@ -376,7 +384,13 @@ __global__ __launch_bounds__(kThreads, (PrepCfg<E, DK>::SMEM <= 80 * 1024 ? 2 : 
             ex[c] = __expf(gg[c] - gr[c]);   // e^{g - g_r}
             ei[c] = __expf(gr[c] - gg[c]);   // e^{g_r - g}
         }
-        const f32x4 kf = to4(kk[j]), qf = to4(qq[j]);
+        const bool pad = i >= len;  // padding: k = q = 0
+        f32x4 kf = to4(kk[j]), qf = to4(qq[j]);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            kf[c] = pad ? 0.0f : kf[c];
+            qf[c] = pad ? 0.0f : qf[c];
+        }
         bk[j] *= kf;
         store4<E>(sX + i * LDT + c0, bk[j] * ex);
         store4<E>(sKp + i * LDT + c0, kf * ei);
@@ -679,7 +693,7 @@ __global__ __launch_bounds__(kThreads, (PrepCfg<E, DK>::SMEM <= 80 * 1024 ? 2 : 
             float wv;
             if constexpr (kLogits) wv = sigmoid1(static_cast<float>(zw[j][c]));
             else wv = zw[j][c];
-            zt[j] = wv * elem<E>(zv[j], c);
+            zt[j] = tg * TPG + j < len ? wv * elem<E>(zv[j], c) : 0.0f;  // padding: v = 0
         }
         store_run_et<E, TPG>(sEt + (c0 + c) * LDC, c0 + c, tg * TPG, zt);
     }
