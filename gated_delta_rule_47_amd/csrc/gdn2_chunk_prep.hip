@@ -528,16 +528,27 @@ __global__ __launch_bounds__(kThreads, (PrepCfg<E, DK>::SMEM <= 80 * 1024 ? 2 : 
         }
     }
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {  // the zero upper blocks of M (read by the propagation)
+    for (int u = 0; u < 2; ++u) {  // zero blocks of M above the diagonal
         const int t = wave + 4 * u;
         if (t < 6) {
             int I, J;
             upper_tile(t, I, J);
-            if constexpr (!kBwd)
-                store4_frag<E>(Mg, kChunk, 16 * I + (lane & 15), 16 * J + 4 * (lane >> 4), zero4());
-            else  // the zero lower blocks of M^T
+            // Only the zero blocks inside an operand fragment that also holds
+            // elements on or below the diagonal are written (and read): the
+            // fragments wholly above it are skipped by the propagation.
+            if constexpr (!kBwd) {
+                if (m_frag_used<E>(I, 16 * J)) {
+                    // A zero made here: a loop-invariant zero register would be
+                    // spilled, and its reload waits for every load in flight.
+                    float z;
+                    asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+                    store4_frag<E>(Mg, kChunk, 16 * I + (lane & 15), 16 * J + 4 * (lane >> 4),
+                                   f32x4{z, z, z, z});
+                }
+            } else {  // the zero lower blocks of M^T
                 store4_frag<E>(reinterpret_cast<E *>(a.ws_Mt) + ch * kChunk * kChunk, kChunk,
                                16 * J + (lane & 15), 16 * I + 4 * (lane >> 4), zero4());
+            }
         }
     }
     __syncthreads();  // the token-major tiles are dead: region 1 becomes the solve buffers

@@ -63,6 +63,7 @@ template <typename E, int DK, int DV, int DVS>
 __device__ __forceinline__ void load_chunk(ChunkFrags<E, DK, DVS> &f, const ChunkArgs &a, int n,
                                            int h, int cid, int cbeg, int col0, int wave,
                                            int lane) {
+    using M = Mma<E>;
     using C = PropCfg<E, DK, DVS>;
     using F = ChunkFrags<E, DK, DVS>;
     if (a.plan) {
@@ -90,7 +91,9 @@ __device__ __forceinline__ void load_chunk(ChunkFrags<E, DK, DVS> &f, const Chun
 #pragma unroll
     for (int kk = 0; kk < F::NKD; ++kk) f.w[kk] = load_frag_packed<E>(Wg, DK, wave, kk, lane);
 #pragma unroll
-    for (int kk = 0; kk < F::NK64; ++kk) f.m[kk] = load_frag_packed<E>(Mg, kChunk, wave, kk, lane);
+    for (int kk = 0; kk < F::NK64; ++kk)  // fragments wholly above the diagonal are not stored
+        f.m[kk] = m_frag_used<E>(wave, kk * M::KS) ? load_frag_packed<E>(Mg, kChunk, wave, kk, lane)
+                                                   : M::zero();
 #pragma unroll
     for (int kk = 0; kk < F::NKD; ++kk) f.qh[kk] = load_frag_packed<E>(Qg, DK, wave, kk, lane);
 #pragma unroll
@@ -192,8 +195,9 @@ __global__ __launch_bounds__(kThreads, (PropCfg<E, DK, DVS>::SMEM <= 80 * 1024 ?
                                  cur.qh[kk], acc);
 #pragma unroll
                 for (int kk = 0; kk < F::NK64; ++kk)
-                    acc = M::mma(load_frag<E>(sU + 16 * cb * LDU + kk * M::KS, LDU, lane),
-                                 cur.m[kk], acc);
+                    if (m_frag_used<E>(wave, kk * M::KS))
+                        acc = M::mma(load_frag<E>(sU + 16 * cb * LDU + kk * M::KS, LDU, lane),
+                                     cur.m[kk], acc);
                 if (i < cur.len) {
                     E *dst = out + ((size_t)(cur.tok0 + i) * H + h) * DV + col0 + 16 * cb +
                              4 * (lane >> 4);
@@ -570,7 +574,8 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_prop_ws_kernel(ChunkArg
             M::frag uf[NCB][NK64], mf[NK64], kf[C::KB_W][NK64];
 #pragma unroll
             for (int kk = 0; kk < NK64; ++kk) {
-                if constexpr (!kStates) mf[kk] = load_frag_packed<bf16>(Mf, kChunk, wave, kk, lane);
+                if (!kStates && m_frag_used<bf16>(wave, kk * M::KS))
+                    mf[kk] = load_frag_packed<bf16>(Mf, kChunk, wave, kk, lane);
 #pragma unroll
                 for (int b = 0; b < C::KB_W; ++b)
                     kf[b][kk] = load_frag_packed<bf16>(Kf, kChunk, wave * C::KB_W + b, kk, lane);
@@ -583,7 +588,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_prop_ws_kernel(ChunkArg
             for (int u = 0; u < C::S_TPW; ++u) d[u] = zero4();
 #pragma unroll
             for (int kk = 0; kk < NK64; ++kk) {
-                if constexpr (!kStates) {
+                if (!kStates && m_frag_used<bf16>(wave, kk * M::KS)) {  // M is zero above the diagonal
 #pragma unroll
                     for (int cb = 0; cb < NCB; ++cb) oacc[cb] = M::mma(uf[cb][kk], mf[kk], oacc[cb]);
                 }

@@ -149,6 +149,14 @@ __device__ __forceinline__ size_t frag_index(int r, int k, int K) {
            ((r & 15) + 16 * ((k % M::KS) / M::KPL)) * M::KPL + (k % M::KPL);
 }
 
+// The causal query-key matrix M of a chunk (64 x 64, zero above the diagonal)
+// is kept in fragment order without its fragments that lie wholly above the
+// diagonal: is the fragment of row block I (16 rows) holding column col used?
+template <typename E>
+__host__ __device__ constexpr bool m_frag_used(int I, int col) {
+    return (col / Mma<E>::KS) * Mma<E>::KS <= 16 * I + 15;
+}
+
 // Fragment (row block rb, column block kb) of a matrix stored in fragment order.
 template <typename E>
 __device__ __forceinline__ typename Mma<E>::frag load_frag_packed(const E *X, int K, int rb, int kb,

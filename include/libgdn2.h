@@ -204,7 +204,10 @@ int gdn2_chunk_fwd_gate_logits(const void *q, const void *k, const void *v,
  *   W      [64][Dk]  T (gamma * b * k)                  } in fragment order,
  *   Qhat   [64][Dk]  gamma * q                          } see below
  *   KhatT  [Dk][64]  (exp(g_last - g) * k)^T            }
- *   M      [64][64]  lower incl. diagonal, M_ij = sum_c q_i k_j exp(g_i - g_j)
+ *   M      [64][64]  lower incl. diagonal, M_ij = sum_c q_i k_j exp(g_i - g_j);
+ *                    its fragments wholly above the diagonal (16-row block rb,
+ *                    KS-column block kb with kb*KS > 16*rb + 15; for bf16 the
+ *                    columns 32..63 of rows 0..31) are not written
  *          Fragment order of an R x K matrix X: X[r][k] is element
  *            ((r/16)*(K/KS) + k/KS)*64*KPL + ((r%16) + 16*((k%KS)/KPL))*KPL + k%KPL
  *          with (KS, KPL) = (32, 8) for bf16 and (4, 1) for f32.

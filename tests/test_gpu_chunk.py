@@ -190,7 +190,8 @@ def test_chunk_factors_in_workspace(io, D, lengths):
     N, B, T, H = inp["N"], inp["B"], inp["T"], inp["H"]
     ioc = g.GDN2_BF16 if io == W.BF16 else g.GDN2_F32
     L = g.gdn2_chunk_fwd_workspace_layout(N, B, T, H, D, D, ioc, varlen)
-    ws = torch.zeros(L.total_bytes_with_Tinv, dtype=torch.uint8, device="cuda")
+    # NaN bytes everywhere first: whatever the kernel leaves unwritten shows up
+    ws = torch.full((L.total_bytes_with_Tinv,), 0xFF, dtype=torch.uint8, device="cuda")
     _run(inp, workspace=ws, stages=g.GDN2_STAGE_ALL | g.GDN2_STAGE_STORE_T)
     tdt = torch.bfloat16 if io == W.BF16 else torch.float32
     nch = L.max_chunks
@@ -200,6 +201,12 @@ def test_chunk_factors_in_workspace(io, D, lengths):
     Qw = _unfrag(host(_ws_view(ws, L.off_Qhat, nch * H * 64 * D, tdt, (nch, H, 64 * D))), 64, D, bf)
     Kw = _unfrag(host(_ws_view(ws, L.off_KhatT, nch * H * 64 * D, tdt, (nch, H, 64 * D))), D, 64, bf)
     Mw = _unfrag(host(_ws_view(ws, L.off_M, nch * H * 4096, tdt, (nch, H, 4096))), 64, 64, bf)
+    # M's fragments wholly above the diagonal (16-row block rb, KS-column block
+    # kb with kb*KS > 16*rb + 15) are not stored; everything else is
+    KS = 32 if bf else 4
+    rr, cc = np.meshgrid(np.arange(64), np.arange(64), indexing="ij")
+    m_unused = (cc // KS) * KS > 16 * (rr // 16) + 15
+    Mw = np.where(m_unused, 0.0, Mw)
     Gw = host(_ws_view(ws, L.off_gamma_last, nch * H * D, torch.float32, (nch, H, D)))
     # U is stored in MFMA accumulator order: [I][cb][lane][r] -> U[16I + 4(lane/16) + r][16cb + lane%16]
     Us = host(_ws_view(ws, L.off_U, nch * H * 64 * D, tdt, (nch, H, 4, D // 16, 4, 16, 4)))
@@ -215,6 +222,9 @@ def test_chunk_factors_in_workspace(io, D, lengths):
         for n in range(B):
             for t0 in range(0, T, 64):
                 chunks.append((n, t0, min(64, T - t0)))
+    Mraw = _unfrag(host(_ws_view(ws, L.off_M, nch * H * 4096, tdt, (nch, H, 4096))), 64, 64, bf)
+    assert np.isnan(Mraw[:len(chunks)][..., m_unused]).all()
+    assert not np.isnan(Mraw[:len(chunks)][..., ~m_unused]).any()
     bound = 1e-2 if io == W.BF16 else 1e-5
     worst = {}
     for cid, (row, t0, ln) in enumerate(chunks):
