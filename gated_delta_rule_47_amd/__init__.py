@@ -373,7 +373,8 @@ def step(q, k, v, log_alpha, b, w, S, o=None, stream=None):
 def chunk_bwd(q, k, v, log_alpha, b, w, dout, S0=None, dS_final=None, cu_seqlens=None,
               need_dS0=True, workspace=None, stream=None):
     """Gradients of chunk_fwd for upstream gradients dout (of o) and dS_final
-    (of S_final, None = zero).  Same shapes as chunk_fwd.
+    (of S_final, None = zero).  Same shapes and dtypes as chunk_fwd (bf16 or
+    fp32 q/k/v/dout).
     Returns a dict: dq, dk, dv (q's dtype), dlog_alpha, db, dw (float32) and
     dS0 ([N,H,Dk,Dv] float32, or None when need_dS0 is False).
     """

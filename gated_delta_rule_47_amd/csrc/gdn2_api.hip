@@ -107,6 +107,25 @@ bool bwd_layout(int N, int B, int T, int H, int Dk, int Dv, size_t io_bytes, boo
     return true;
 }
 
+bool bwd_f32_layout(int N, int B, int T, int H, int Dk, int Dv, bool varlen, BwdF32Layout *out) {
+    BwdF32Layout L;
+    if (!workspace_layout(N, B, T, H, Dk, Dv, sizeof(float), varlen, &L.fwd)) return false;
+    const size_t chd = (size_t)L.fwd.max_chunks * (size_t)H;
+    size_t off = align_up(L.fwd.total_T);  // after the T slot, which this backward uses
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off = align_up(off + bytes);
+        return at;
+    };
+    L.off_Sc = take(chd * Dk * Dv * sizeof(float));
+    L.off_dSp = take(chd * Dk * Dv * sizeof(float));
+    L.off_tiles = take(20 * chd * kChunk * Dk * sizeof(float));
+    L.off_sq = take(2 * chd * kChunk * kChunk * sizeof(float));
+    L.total = off;
+    *out = L;
+    return true;
+}
+
 }  // namespace gdn2
 
 extern "C" {
@@ -330,9 +349,91 @@ int gdn2_chunk_fwd_gate_logits(const void *q, const void *k, const void *v,
                           true);
 }
 
+}  // extern "C"
+
+// The fp32 backward (arguments already validated by gdn2_chunk_bwd): the chunk
+// factors with T, the propagation storing every chunk's incoming state, then
+// the fp32 reverse pass and per-chunk products.
+static int chunk_bwd_f32(const void *q, const void *k, const void *v, const float *log_alpha,
+                         const float *b, const float *w, const float *S0, const void *dout,
+                         const float *dS_final, void *dq, void *dk, void *dv, float *dlog_alpha,
+                         float *db, float *dw, float *dS0, const int32_t *cu_seqlens, int N, int B,
+                         int T, int H, int Dk, int Dv, void *workspace, size_t workspace_bytes,
+                         void *stream_ptr) {
+    const bool varlen = cu_seqlens != nullptr;
+    BwdF32Layout L;
+    if (!bwd_f32_layout(N, B, T, H, Dk, Dv, varlen, &L)) return GDN2_ERR_INVALID_ARGUMENT;
+    if (!workspace || workspace_bytes < L.total) return GDN2_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) return GDN2_ERR_WORKSPACE;
+    hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+    (void)hipGetLastError();  // a stale error left by other code is not ours to report
+    char *ws = static_cast<char *>(workspace);
+    const WorkspaceLayout &F = L.fwd;
+    BwdF32Args f{};
+    ChunkArgs &a = f.c;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.log_alpha = log_alpha;
+    a.b = b;
+    a.w = w;
+    a.S0 = S0;
+    a.o = nullptr;
+    a.S_final = nullptr;
+    a.cu_seqlens = cu_seqlens;
+    a.N = N;
+    a.B = B;
+    a.T = T;
+    a.H = H;
+    a.NC = (T + kChunk - 1) / kChunk;
+    a.max_chunks = F.max_chunks;
+    a.plan = varlen ? reinterpret_cast<int32_t *>(ws + F.off_plan) : nullptr;
+    a.ws_T = ws + F.off_T;
+    a.store_T = 1;
+    a.ws_W = ws + F.off_W;
+    a.ws_Qh = ws + F.off_Qh;
+    a.ws_KhT = ws + F.off_KhT;
+    a.ws_M = ws + F.off_M;
+    a.ws_U = ws + F.off_U;
+    a.ws_gl = reinterpret_cast<float *>(ws + F.off_gl);
+    a.ws_Sc32 = reinterpret_cast<float *>(ws + L.off_Sc);
+    f.dout = dout;
+    f.dS_final = dS_final;
+    f.dq = dq;
+    f.dk = dk;
+    f.dv = dv;
+    f.dla = dlog_alpha;
+    f.db = db;
+    f.dw = dw;
+    f.dS0 = dS0;
+    f.Sc = a.ws_Sc32;
+    f.dSp = reinterpret_cast<float *>(ws + L.off_dSp);
+    const size_t tile = (size_t)F.max_chunks * H * kChunk * Dk;  // floats per [64][D] array
+    float *t = reinterpret_cast<float *>(ws + L.off_tiles);
+    float **tiles[] = {&f.dUeff, &f.Qg, &f.Kg, &f.Vg, &f.Bg, &f.Wg, &f.dOg, &f.G, &f.Ep, &f.Kp,
+                       &f.Qp, &f.Ueff, &f.dQhat, &f.dKhat, &f.dW, &f.dZ, &f.dE, &f.dEp, &f.dQp, &f.dKp};
+    static_assert(sizeof(tiles) / sizeof(tiles[0]) == 20, "20 tile arrays");
+    for (int i = 0; i < 20; ++i) *tiles[i] = t + i * tile;
+    f.dM = reinterpret_cast<float *>(ws + L.off_sq);
+    f.dA = f.dM + (size_t)F.max_chunks * H * kChunk * kChunk;
+
+    hipError_t err = hipSuccess;
+    if (varlen) err = launch_plan(a, stream);
+    if (err == hipSuccess && F.max_chunks > 0) err = launch_chunk_prep(a, Dk, false, stream);
+    if (err == hipSuccess) err = launch_chunk_prop(a, Dk, false, stream);
+    if (err == hipSuccess) err = launch_chunk_bwd_f32(f, Dk, stream);
+    return finish(err, stream);
+}
+
+extern "C" {
+
 size_t gdn2_chunk_bwd_workspace_bytes(int N, int B, int T, int H, int Dk, int Dv, int io,
                                       int varlen) {
     if (io != GDN2_F32 && io != GDN2_BF16) return 0;
+    if (io == GDN2_F32) {
+        BwdF32Layout L32;
+        return bwd_f32_layout(N, B, T, H, Dk, Dv, varlen != 0, &L32) ? L32.total : 0;
+    }
     BwdLayout L;
     if (!bwd_layout(N, B, T, H, Dk, Dv, io_size(io), varlen != 0, &L)) return 0;
     return L.total;
@@ -346,7 +447,7 @@ int gdn2_chunk_bwd(const void *q, const void *k, const void *v, const float *log
                    void *stream_ptr) {
     if (io != GDN2_F32 && io != GDN2_BF16) return GDN2_ERR_INVALID_ARGUMENT;
     if (N < 0 || B < 0 || T < 0 || H < 0 || Dk <= 0 || Dv <= 0) return GDN2_ERR_INVALID_ARGUMENT;
-    if (!supported_dims(Dk, Dv) || io != GDN2_BF16) return GDN2_ERR_UNSUPPORTED;
+    if (!supported_dims(Dk, Dv)) return GDN2_ERR_UNSUPPORTED;
     const bool varlen = cu_seqlens != nullptr;
     if (varlen ? B != 1 : N != B) return GDN2_ERR_INVALID_ARGUMENT;
     if (N == 0 || H == 0) return GDN2_OK;
@@ -375,6 +476,10 @@ int gdn2_chunk_bwd(const void *q, const void *k, const void *v, const float *log
             if (all_out[i] == p) return GDN2_ERR_INVALID_ARGUMENT;
     }
 
+    if (io == GDN2_F32)
+        return chunk_bwd_f32(q, k, v, log_alpha, b, w, S0, dout, dS_final, dq, dk, dv, dlog_alpha,
+                             db, dw, dS0, cu_seqlens, N, B, T, H, Dk, Dv, workspace,
+                             workspace_bytes, stream_ptr);
     BwdLayout L;
     if (!bwd_layout(N, B, T, H, Dk, Dv, io_size(io), varlen, &L)) return GDN2_ERR_INVALID_ARGUMENT;
     if (!workspace || workspace_bytes < L.total) return GDN2_ERR_WORKSPACE;

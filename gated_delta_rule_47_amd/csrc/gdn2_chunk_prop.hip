@@ -170,6 +170,18 @@ __global__ __launch_bounds__(kThreads, (PropCfg<E, DK, DVS>::SMEM <= 80 * 1024 ?
         }
         const E *sS = sS0 + buf * (DVS * LDS_);
         E *sSn = sS0 + (buf ^ 1) * (DVS * LDS_);
+        if (a.ws_Sc32) {  // fp32 backward calls: this chunk's incoming state, row-major
+#pragma unroll
+            for (int u = 0; u < C::S_TPW; ++u) {
+                const int cblk = wave * C::KB_W + u / NCB, colb = u % NCB;
+                const int col = col0 + 16 * colb + (lane & 15);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int c = 16 * cblk + 4 * (lane >> 4) + r;
+                    a.ws_Sc32[(((size_t)cid * H + h) * DK + c) * DV + col] = Sacc[u][r];
+                }
+            }
+        }
 
         // U_eff rows of block `wave`:  U - W S.
 #pragma unroll
@@ -198,7 +210,7 @@ __global__ __launch_bounds__(kThreads, (PropCfg<E, DK, DVS>::SMEM <= 80 * 1024 ?
                     if (m_frag_used<E>(wave, kk * M::KS))
                         acc = M::mma(load_frag<E>(sU + 16 * cb * LDU + kk * M::KS, LDU, lane),
                                      cur.m[kk], acc);
-                if (i < cur.len) {
+                if (out && i < cur.len) {
                     E *dst = out + ((size_t)(cur.tok0 + i) * H + h) * DV + col0 + 16 * cb +
                              4 * (lane >> 4);
                     if constexpr (sizeof(E) == 2) {

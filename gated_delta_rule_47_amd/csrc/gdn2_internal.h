@@ -55,6 +55,9 @@ struct ChunkArgs {
     // If set (backward calls), the chunk-factor kernel also writes, in fragment
     // order: M^T [64][64], Khat [64][Dk], Qhat^T [Dk][64], W^T [Dk][64] and T^T [64][64].
     void *ws_Mt, *ws_Kh, *ws_Qt, *ws_Wt, *ws_Tt;
+    float *ws_Sc32;       // if set (fp32 backward calls), the fp32 propagation stores
+                          // every chunk's incoming state here, row-major
+                          // [chunk id][head][Dk][Dv]; o may then be NULL
 };
 
 // The backward's workspace: the forward's layout without its T, Qhat and M
@@ -92,6 +95,31 @@ struct BwdArgs {
     bf16_t *Sc, *dSc, *dWt, *dM, *dMt;
     bf16_t *dKh, *dAp;
     float *dG;
+};
+
+// The fp32 backward's workspace: the forward's layout including T, then per
+// chunk-head slot (all fp32, row-major): the incoming state Sc and the
+// gradient dSp of the outgoing state [Dk][Dv]; [64][D] tiles: dU_eff, the
+// gathered token rows Qg, Kg, Vg, Bg, Wg, dOg (zero past the chunk), the
+// cumulative log-decay G, the midpoint-scaled Ep, Kp, Qp, U_eff and the
+// products dQhat, dKhat, dW, dZ, dE, dEp, dQp, dKp; [64][64]: dM, dA.
+struct BwdF32Layout {
+    WorkspaceLayout fwd;
+    size_t off_Sc = 0, off_dSp = 0, off_tiles = 0, off_sq = 0;  // tiles: 20 x [64][D]; sq: 2 x [64][64]
+    size_t total = 0;
+};
+
+bool bwd_f32_layout(int N, int B, int T, int H, int Dk, int Dv, bool varlen, BwdF32Layout *out);
+
+struct BwdF32Args {
+    ChunkArgs c;          // forward arguments and chunk factors (c.o unused, c.ws_T set)
+    const void *dout;
+    const float *dS_final;
+    void *dq, *dk, *dv;
+    float *dla, *db, *dw, *dS0;
+    float *Sc, *dSp, *dUeff;
+    float *Qg, *Kg, *Vg, *Bg, *Wg, *dOg, *G, *Ep, *Kp, *Qp, *Ueff;
+    float *dQhat, *dKhat, *dW, *dZ, *dE, *dEp, *dQp, *dKp, *dM, *dA;
 };
 
 // Token-mixer layer: the element-wise kernels around the core.
@@ -138,6 +166,8 @@ hipError_t launch_chunk_prop(const ChunkArgs &a, int Dk, bool bf16_io, hipStream
 hipError_t launch_step(const StepArgs &a, int Dk, bool bf16_io, hipStream_t stream);
 // Backward (bf16 only): reverse state-gradient pass, then the two per-chunk kernels.
 hipError_t launch_chunk_bwd(const BwdArgs &a, int Dk, hipStream_t stream);
+// fp32 backward (after the chunk factors with T and the state-storing propagation).
+hipError_t launch_chunk_bwd_f32(const BwdF32Args &a, int Dk, hipStream_t stream);
 hipError_t launch_swa_fwd(const SwaArgs &a, int D, hipStream_t stream);
 hipError_t launch_swa_plan(const int32_t *cu, int N, int T, int H, int32_t *blk_start,
                            hipStream_t stream);

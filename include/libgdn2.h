@@ -259,8 +259,11 @@ size_t gdn2_chunk_bwd_workspace_bytes(int N, int B, int T, int H, int Dk, int Dv
  * Outputs must not alias each other or any input.  The workspace (>=
  * gdn2_chunk_bwd_workspace_bytes(...) bytes, 256-byte aligned) holds the
  * chunk factors, every chunk's incoming state and state gradient, and the
- * per-chunk partial gradients.  Only io = GDN2_BF16 is implemented;
- * GDN2_F32 returns GDN2_ERR_UNSUPPORTED.
+ * per-chunk partial gradients.  io = GDN2_BF16 runs the fast bf16-MFMA
+ * kernels (bf16 factors and intermediates, fp32 accumulation); io = GDN2_F32
+ * computes every product and intermediate in fp32 (fp32 MFMA), the precision
+ * reference of the same chain rule, with a larger workspace (about 1 MiB per
+ * chunk-head at Dk = 128).
  */
 int gdn2_chunk_bwd(const void *q, const void *k, const void *v,
                    const float *log_alpha, const float *b, const float *w,

@@ -1,6 +1,7 @@
 """GPU parity of gdn2_chunk_bwd against the fp64 oracle's reverse recurrence
 (oracle.recurrence_bwd): every gradient, dense and packed calls, ragged tails,
-with and without initial state and final-state gradient."""
+with and without initial state and final-state gradient, for bf16 I/O (bound
+2e-2) and fp32 I/O (bound 1e-4)."""
 
 import numpy as np
 import pytest
@@ -113,15 +114,68 @@ def test_bwd_deterministic_bitwise():
         assert torch.equal(a[n], b[n]), n
 
 
-def test_bwd_f32_unsupported():
-    import torch
-    wl = W.ChunkWorkload("bwd_f32", 1, 64, 1, 64, 64, W.F32, 4747)
+# ---------------------------------------------------------------------------
+# fp32 I/O: the same gradients at the all-fp32 bound (1e-4 of max |ref|)
+# ---------------------------------------------------------------------------
+
+def _check_f32(inp, grads, label):
+    out = _run_bwd(inp, grads)
+    ref = O.recurrence_bwd(*(inp[x] for x in ("q", "k", "v", "log_alpha", "b", "w")),
+                           grads["dout"], inp["S0"], grads["dS_final"], inp["cu_seqlens"])
+    errs = {n: O.rel_max_err(host(out[n]), ref[n]) for n in NAMES}
+    log("%s: %s" % (label, " ".join("%s %.2e" % kv for kv in errs.items())))
+    for n, e in errs.items():
+        assert e <= tol(W.F32), (n, e)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_bwd_f32_dense_ragged(D):
+    """fp32: T = 150 (a 22-token tail), S0 and dS_final nonzero."""
+    wl = W.ChunkWorkload("bwd_f32_dense", 2, 150, 2, D, D, W.F32, 5242 + D, with_S0=True)
     inp = W.make_chunk_inputs(wl)
-    d = upload_chunk(inp)
-    dout = torch.zeros_like(d["q"])
-    with pytest.raises(g.Gdn2Error) as e:
-        g.chunk_bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], dout)
-    assert e.value.status == g.GDN2_ERR_UNSUPPORTED
+    _check_f32(inp, W.make_chunk_grads(inp, 21 + D), "bwd f32 dense D=%d" % D)
+
+
+def test_bwd_f32_no_state_no_final_grad():
+    wl = W.ChunkWorkload("bwd_f32_nostate", 1, 40, 2, 128, 128, W.F32, 5343)
+    inp = W.make_chunk_inputs(wl)
+    _check_f32(inp, W.make_chunk_grads(inp, 22, with_dS_final=False), "bwd f32 no state")
+
+
+def test_bwd_f32_varlen_edge_lengths():
+    wl = W.ChunkWorkload("bwd_f32_varlen", 1, 0, 2, 128, 128, W.F32, 5444, with_S0=True,
+                         n_seqs=7)
+    inp = W.make_chunk_inputs(wl, lengths=[1, 63, 64, 65, 130, 0, 7])
+    _check_f32(inp, W.make_chunk_grads(inp, 23), "bwd f32 varlen")
+
+
+def test_bwd_f32_many_chains():
+    """16 chains over 3 chunks each, d = 64."""
+    wl = W.ChunkWorkload("bwd_f32_many", 4, 130, 4, 64, 64, W.F32, 5545, with_S0=True)
+    inp = W.make_chunk_inputs(wl)
+    _check_f32(inp, W.make_chunk_grads(inp, 24), "bwd f32 16 chains")
+
+
+def test_bwd_f32_erase_gate_to_two():
+    wl = W.ChunkWorkload("bwd_f32_b2", 1, 128, 2, 128, 128, W.F32, 5646, with_S0=True)
+    inp = W.make_chunk_inputs(wl, b_scale=2.0)
+    _check_f32(inp, W.make_chunk_grads(inp, 25), "bwd f32 b in [0,2]")
+
+
+@pytest.mark.parametrize("case", ["no_decay_no_erase", "strong_decay"])
+def test_bwd_f32_degenerate_gates(case):
+    wl = W.ChunkWorkload("bwd_f32_degen", 2, 150, 2, 128, 128, W.F32, 5747, with_S0=True)
+    if case == "no_decay_no_erase":
+        inp = W.make_chunk_inputs(wl, log_alpha_range=(0.0, 0.0), b_scale=0.0)
+    else:
+        inp = W.make_chunk_inputs(wl, log_alpha_range=(-2.5, -2.0))
+    _check_f32(inp, W.make_chunk_grads(inp, 26), "bwd f32 %s" % case)
+
+
+def test_bwd_f32_tiny_workload():
+    """The tiny fp32 workload (B=1, H=2, T=256, d=64) with upstream gradients."""
+    inp = W.make_chunk_inputs(W.TINY_F32)
+    _check_f32(inp, W.make_chunk_grads(inp, 27), "bwd f32 tiny workload")
 
 
 def test_bwd_full_batch_workload_sampled():
