@@ -55,7 +55,8 @@ def parse():
                                        "seq", "sweep"], default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workers", type=int, default=0,
-                    help="host worker processes (default: the usable cores, at most 16)")
+                    help="host worker processes (default: the usable cores, at most 16; "
+                         "1 runs the host-side work in this process, as profiled runs need)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a plain device copy of 1 GiB (5 times) and exit")
     return ap.parse_args()
@@ -230,8 +231,12 @@ def cpu_baseline(inp, workers):
     _POOL_INP = inp
     units = [(n, h) for n in range(inp["B"]) for h in range(inp["H"])]
     t0 = time.perf_counter()
-    with mp.get_context("fork").Pool(workers) as pool:
-        pool.map(_oracle_chain, units, chunksize=1)
+    if workers == 1:  # in this process (profiled runs: no worker processes)
+        for u in units:
+            _oracle_chain(u)
+    else:
+        with mp.get_context("fork").Pool(workers) as pool:
+            pool.map(_oracle_chain, units, chunksize=1)
     dt = time.perf_counter() - t0
     _POOL_INP = None
     n_tokens = inp["B"] * inp["T"]
@@ -268,10 +273,16 @@ def pregenerate_decode(steps, workers):
     out = dict(q=np.empty(shp, np.uint16), k=np.empty(shp, np.uint16), v=np.empty(shp, np.uint16),
                log_alpha=np.empty(shp, np.float32), b=np.empty(shp, np.float32),
                w=np.empty(shp, np.float32))
+    def keep(s, *arrs):
+        for name, arr in zip(("q", "k", "v", "log_alpha", "b", "w"), arrs):
+            out[name][s] = arr
+    if workers == 1:  # in this process (profiled runs: no worker processes)
+        for s in range(steps):
+            keep(*_decode_step_packed(s))
+        return out
     with mp.get_context("fork").Pool(workers) as pool:
-        for s, *arrs in pool.imap_unordered(_decode_step_packed, range(steps), chunksize=4):
-            for name, arr in zip(("q", "k", "v", "log_alpha", "b", "w"), arrs):
-                out[name][s] = arr
+        for res in pool.imap_unordered(_decode_step_packed, range(steps), chunksize=4):
+            keep(*res)
     return out
 
 
@@ -507,7 +518,7 @@ def main():
                    "sample": "fp64 numpy token recurrence over the whole %s workload (%d tokens "
                              "x 16 heads, S0 as in the workload): its %d (sequence, head) chains "
                              "on a pool of %d worker processes, one numpy thread each, %.1f s"
-                             % (W.BATCH_4K.name, n, inp["B"] * inp["H"], workers, workers, dt),
+                             % (W.BATCH_4K.name, n, inp["B"] * inp["H"], workers, dt),
                    "one_core": one}
     decode_pre = None
     if a.only in ("all", "decode") and not a.calibrate_copy:
