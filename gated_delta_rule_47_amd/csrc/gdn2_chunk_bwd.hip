@@ -139,15 +139,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_rev_kernel(BwdArgs ba) 
     seq_chunks(a, n, cbeg, cend);
 
     f32x4 dS[C::S_TPW];
-#pragma unroll
-    for (int u = 0; u < C::S_TPW; ++u) {
-        const int cblk = wave * C::KB_W + u / NCB, colb = u % NCB;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = 16 * cblk + 4 * (lane >> 4) + r, col = col0 + 16 * colb + (lane & 15);
-            dS[u][r] = ba.dS_final ? ba.dS_final[((size_t)chain * DK + row) * DV + col] : 0.0f;
-        }
-    }
+    load_state_tiles<DK, DV, C::KB_W, NCB>(dS, ba.dS_final, chain, wave, col0, lane);
     const bf16 *dout = reinterpret_cast<const bf16 *>(ba.dout);
     // Everything a chunk reads from global memory: M^T and Khat rows of block
     // `wave`, Qhat^T and W^T rows of this wave's state row blocks, gamma_last,
@@ -320,15 +312,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_bwd_rev2_kernel(BwdArgs
     seq_chunks(a, n, cbeg, cend);
 
     f32x4 dS[C::S_TPW];
-#pragma unroll
-    for (int u = 0; u < C::S_TPW; ++u) {
-        const int cblk = wl * C::KB_W + u / NCB, colb = u % NCB;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = 16 * cblk + 4 * (lane >> 4) + r, col = col0 + hc + 16 * colb + (lane & 15);
-            dS[u][r] = ba.dS_final ? ba.dS_final[((size_t)chain * DK + row) * DV + col] : 0.0f;
-        }
-    }
+    load_state_tiles<DK, DV, C::KB_W, NCB>(dS, ba.dS_final, chain, wl, col0 + hc, lane);
     const bf16 *dout = reinterpret_cast<const bf16 *>(ba.dout);
     // One chunk's global operands: its factor granules (thread t holds
     // granules t, t + 512, ...), dO granules (8 columns of one token row; rows

@@ -148,15 +148,10 @@ __global__ __launch_bounds__(kThreads, (PropCfg<E, DK, DVS>::SMEM <= 80 * 1024 ?
 
     // Initial state (fp32 accumulators) and its operand copy.
     f32x4 Sacc[C::S_TPW];
+    load_state_tiles<DK, DV, C::KB_W, NCB>(Sacc, a.S0, chain, wave, col0, lane);
 #pragma unroll
     for (int u = 0; u < C::S_TPW; ++u) {
         const int cblk = wave * C::KB_W + u / NCB, colb = u % NCB;
-        const int col = col0 + 16 * colb + (lane & 15);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int c = 16 * cblk + 4 * (lane >> 4) + r;
-            Sacc[u][r] = a.S0 ? a.S0[((size_t)chain * DK + c) * DV + col] : 0.0f;
-        }
         store_tile_t<E>(sS0 + 16 * colb * LDS_ + 16 * cblk, LDS_, Sacc[u], lane);
     }
     __syncthreads();
@@ -524,15 +519,10 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_prop_ws_kernel(ChunkArg
     load_own(nxt, min(cbeg + 1, cend - 1));
 
     f32x4 Sacc[C::S_TPW];
+    load_state_tiles<DK, DV, C::KB_W, NCB>(Sacc, a.S0, chain, wave, col0, lane);
 #pragma unroll
     for (int u = 0; u < C::S_TPW; ++u) {
         const int cblk = wave * C::KB_W + u / NCB, colb = u % NCB;
-        const int col = col0 + 16 * colb + (lane & 15);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int c = 16 * cblk + 4 * (lane >> 4) + r;
-            Sacc[u][r] = a.S0 ? a.S0[((size_t)chain * DK + c) * DV + col] : 0.0f;
-        }
         store_tile_t<bf16>(sS + 16 * colb * LDS_ + 16 * cblk, LDS_, Sacc[u], lane);
         if constexpr (kStates) store_state_rows<DVS>(sSr, cblk, colb, Sacc[u], lane);
     }

@@ -204,4 +204,26 @@ __device__ __forceinline__ void store_tile(E *dst, int ld, f32x4 acc, int lane) 
     for (int r = 0; r < 4; ++r) p[r * ld] = from_f32<E>(acc[r]);
 }
 
+// The state tiles a wave owns, in accumulator order, from an fp32 [chains, DK,
+// DV] array (or zeros when src is NULL): tile u covers rows 16 (w KB_W + u/NCB)
+// .. +15 and columns col0 + 16 (u%NCB) .. +15 of chain `chain`.  The NULL test
+// is one branch around every load: a per-element select makes the compiler
+// wait for each load before issuing the next.
+template <int DK, int DV, int KB_W, int NCB>
+__device__ __forceinline__ void load_state_tiles(f32x4 (&acc)[KB_W * NCB], const float *src, int chain,
+                                                 int w, int col0, int lane) {
+    if (src) {
+#pragma unroll
+        for (int u = 0; u < KB_W * NCB; ++u) {
+            const int cblk = w * KB_W + u / NCB, col = col0 + 16 * (u % NCB) + (lane & 15);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                acc[u][r] = src[((size_t)chain * DK + 16 * cblk + 4 * (lane >> 4) + r) * DV + col];
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < KB_W * NCB; ++u) acc[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+}
+
 }  // namespace gdn2
