@@ -540,6 +540,18 @@ def main():
            "unit": "tokens/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic (seeded; shapes of a 1.3B-parameter layer: 16 heads, 128x128 state)"}
+    # The part's own figures beside the published peaks used in the rooflines:
+    # a gfx950 CU retires 4096 dense bf16 MFMA flops and 256 fp32 vector flops
+    # per clock.
+    props = torch.cuda.get_device_properties(0)
+    cus, khz = g.device_info(0)
+    out["device"] = {"name": props.name, "arch": props.gcnArchName, "compute_units": cus,
+                     "peak_clock_mhz": khz / 1e3, "hbm_gib": props.total_memory / 2**30,
+                     "bf16_mfma_peak_tflops_from_clock": cus * 4096 * khz * 1e3 / 1e12,
+                     "fp32_vector_peak_tflops_from_clock": cus * 256 * khz * 1e3 / 1e12,
+                     "published_peaks": {"hbm_GBps": HBM_PEAK_GBS, "bf16_mfma_tflops": MFMA_BF16_PEAK_TFLOPS}}
+    log("device: %s, %d CUs at %.0f MHz -> bf16 MFMA %.0f TFLOP/s from the clock"
+        % (props.gcnArchName, cus, khz / 1e3, out["device"]["bf16_mfma_peak_tflops_from_clock"]))
 
     if do_chunk:
         wl = W.BATCH_4K

@@ -35,7 +35,7 @@ EXPORTED = ("gdn2_abi_version", "gdn2_status_string", "gdn2_chunk_fwd_workspace_
             "gdn2_chunk_fwd_gate_logits", "gdn2_chunk_bwd_workspace_bytes", "gdn2_chunk_bwd",
             "gdn2_step", "gdn2_layer_fwd_workspace_bytes", "gdn2_layer_fwd",
             "gdn2_swa_fwd_workspace_bytes", "gdn2_swa_fwd", "gdn2_swa_layer_fwd_workspace_bytes",
-            "gdn2_swa_layer_fwd", "gdn2_chunk_fwd_noalloc")
+            "gdn2_swa_layer_fwd", "gdn2_chunk_fwd_noalloc", "gdn2_device_info")
 
 
 class Gdn2Error(RuntimeError):
@@ -77,6 +77,8 @@ def load_library(path=LIB_PATH):
     lib.gdn2_abi_version.argtypes = []
     lib.gdn2_status_string.restype = ctypes.c_char_p
     lib.gdn2_status_string.argtypes = [I]
+    lib.gdn2_device_info.restype = I
+    lib.gdn2_device_info.argtypes = [I, ctypes.POINTER(I), ctypes.POINTER(I)]
     lib.gdn2_chunk_fwd_workspace_bytes.restype = Z
     lib.gdn2_chunk_fwd_workspace_bytes.argtypes = [I] * 8
     lib.gdn2_chunk_fwd_workspace_layout.restype = I
@@ -118,6 +120,15 @@ def load_library(path=LIB_PATH):
 
 def gdn2_abi_version():
     return load_library().gdn2_abi_version()
+
+
+def device_info(device=0):
+    """(compute units, peak engine clock in kHz) of a device, from the HIP runtime."""
+    cus, khz = ctypes.c_int(0), ctypes.c_int(0)
+    st = load_library().gdn2_device_info(int(device), ctypes.byref(cus), ctypes.byref(khz))
+    if st != 0:
+        raise Gdn2Error(st, "gdn2_device_info")
+    return cus.value, khz.value
 
 
 def gdn2_status_string(status):

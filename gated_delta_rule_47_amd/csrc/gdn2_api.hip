@@ -90,9 +90,7 @@ bool bwd_layout(int N, int B, int T, int H, int Dk, int Dv, size_t io_bytes, boo
         return at;
     };
     L.off_Mt = take(chd * kChunk * kChunk * io_bytes);
-    L.off_Kh = take(chd * kChunk * Dk * io_bytes);
     L.off_Qt = take(chd * Dk * kChunk * io_bytes);
-    L.off_Wt = take(chd * Dk * kChunk * io_bytes);
     L.off_Tt = take(chd * kChunk * kChunk * io_bytes);
     L.off_Sc = take(chd * Dk * Dv * 2);
     L.off_dSc = take(chd * Dk * Dv * 2);
@@ -141,6 +139,16 @@ const char *gdn2_status_string(int status) {
         case GDN2_ERR_HIP: return "GDN2_ERR_HIP";
         default: return "GDN2_ERR_UNKNOWN";
     }
+}
+
+int gdn2_device_info(int device, int *compute_units, int *peak_clock_khz) {
+    int cus = 0, khz = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
+        hipDeviceGetAttribute(&khz, hipDeviceAttributeClockRate, device) != hipSuccess)
+        return GDN2_ERR_HIP;
+    if (compute_units) *compute_units = cus;
+    if (peak_clock_khz) *peak_clock_khz = khz;
+    return GDN2_OK;
 }
 
 static size_t io_size(int io) { return io == GDN2_BF16 ? 2 : 4; }
@@ -518,9 +526,7 @@ int gdn2_chunk_bwd(const void *q, const void *k, const void *v, const float *log
     a.store_T = 0;  // the backward kernels read T^T (ws_Tt) only
     a.ws_Sc = reinterpret_cast<bf16_t *>(ws + L.off_Sc);
     a.ws_Mt = ws + L.off_Mt;
-    a.ws_Kh = ws + L.off_Kh;
     a.ws_Qt = ws + L.off_Qt;
-    a.ws_Wt = ws + L.off_Wt;
     a.ws_Tt = ws + L.off_Tt;
     ba.dout = dout;
     ba.dS_final = dS_final;

@@ -99,35 +99,55 @@ __device__ __forceinline__ Mma<bf16>::frag load_frag_tr(const bf16 *X, int ld, i
     return __builtin_bit_cast(Mma<bf16>::frag, both);
 }
 
+// Operand fragment of X^T where X (K columns) lies in LDS in the chunk
+// factors' fragment order: lane l receives X[r0 + 8 (l/16) + t][c0 + l%16],
+// t = 0..7, i.e. the fragment of X^T at rows c0.., contraction index r0...
+// Four consecutive columns of an X row are 8 contiguous bytes of that order,
+// so the two transposing reads work on it as on a row-major tile.
+__device__ __forceinline__ Mma<bf16>::frag load_frag_tr_fo(const bf16 *X, int K, int r0, int c0, int lane) {
+    const int j = lane & 15, row = r0 + 8 * (lane >> 4) + (j >> 2), col = c0 + 4 * (j & 3);
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16 *)(X + frag_index<bf16>(row, col, K)));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16 *)(X + frag_index<bf16>(row + 4, col, K)));
+    const v8i16 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(Mma<bf16>::frag, both);
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
 // Reverse pass: one workgroup per (sequence, head, DVS-column slab), the
 // chunks of the sequence from last to first, bf16 MFMA.  dS' lives in fp32
 // accumulators (wave w owns state rows 16 (w*KB_W + b) .. of the slab, like
-// the forward); its bf16 transpose in LDS is the operand of Khat dS'.  The
-// factors are the transposed copies the chunk-factor kernel writes for
-// backward calls (M^T, Khat, Qhat^T, W^T), loaded as fragments.
+// the forward); its bf16 copy in LDS, read through transposing LDS reads, is
+// the operand of Khat dS'.  M^T and Qhat^T (written for backward calls) are
+// loaded as fragments; Khat and W^T come from the Khat^T and W images the
+// forward propagation reads, staged in LDS and read transposed.
 // ---------------------------------------------------------------------------
 template <int DK, int DVS>
 struct RevCfg {
     static constexpr int DV = DK, NS = DV / DVS, NCB = DVS / 16, NKB = DK / 16;
     static constexpr int KB_W = NKB / 4, S_TPW = KB_W * NCB;
-    static constexpr int LDKP = DK + 8, L64 = kChunk + 8, LDV = DVS + 8;
+    static constexpr int L64 = kChunk + 8, LDV = DVS + 8;
     static constexpr int NP = DK * DVS / 8;                   // 16-byte pieces of dS'
     static constexpr int NPC = (NP + kThreads - 1) / kThreads;  // per thread
+    static constexpr int GK = kChunk * DK / 8;                 // 16-byte granules of Khat^T, of W
+    static constexpr int NKW = 2 * GK / kThreads;              // per thread
+    static_assert(NKW * kThreads == 2 * GK, "Khat^T and W split");
 };
 
 template <int DK, int DVS>
 __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_rev_kernel(BwdArgs ba) {
     using C = RevCfg<DK, DVS>;
     using MB = Mma<bf16>;
-    constexpr int DV = C::DV, NCB = C::NCB, LDKP = C::LDKP, L64 = C::L64, NKD = DK / 32;
+    constexpr int DV = C::DV, NCB = C::NCB, L64 = C::L64, NKD = DK / 32;
     const ChunkArgs &a = ba.c;
-    __shared__ __attribute__((aligned(16))) bf16 sdSt[DVS * LDKP];  // [v][c] = dS'[c][v]
+    __shared__ __attribute__((aligned(16))) bf16 sKW[2 * C::GK * 8];  // Khat^T | W, fragment order
     __shared__ __attribute__((aligned(16))) bf16 sdO[kChunk * C::LDV];  // [i][v] = dO[i][v]
     __shared__ __attribute__((aligned(16))) bf16 sdUt[DVS * L64];   // [v][i] = dU_eff[i][v]
     __shared__ __attribute__((aligned(16))) bf16 sdS[DK * C::LDV];  // [c][v] = dS'[c][v]
+    const bf16 *sKt = sKW, *sW = sKW + C::GK * 8;
 
     const int H = a.H;
     const int x = blockIdx.x, xcd = x & 7, rest = x >> 3;
@@ -141,14 +161,15 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_rev_kernel(BwdArgs ba) 
     f32x4 dS[C::S_TPW];
     load_state_tiles<DK, DV, C::KB_W, NCB>(dS, ba.dS_final, chain, wave, col0, lane);
     const bf16 *dout = reinterpret_cast<const bf16 *>(ba.dout);
-    // Everything a chunk reads from global memory: M^T and Khat rows of block
-    // `wave`, Qhat^T and W^T rows of this wave's state row blocks, gamma_last,
-    // and this thread's dO pieces (raw; rows past the chunk's end read row 0,
-    // zeroed at use).
+    // Everything a chunk reads from global memory: M^T rows of block `wave`,
+    // Qhat^T rows of this wave's state row blocks, this thread's granules of
+    // the Khat^T and W images, gamma_last, and this thread's dO pieces (raw;
+    // rows past the chunk's end read row 0, zeroed at use).
     constexpr int NE = kChunk * DVS / 4 / kThreads;
     static_assert(NE * kThreads * 4 == kChunk * DVS, "dO split");
     struct RevIn {
-        MB::frag fM[2], fK[NKD], fQ[C::KB_W][2], fW[C::KB_W][2];
+        MB::frag fM[2], fQ[C::KB_W][2];
+        granule_t kw[C::NKW];
         f32x4 gl[C::KB_W];
         bf16x4 o[NE];
         int len;
@@ -159,21 +180,21 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_rev_kernel(BwdArgs ba) 
         chunk_span_of(a, cid, cbeg, n, tok0, len);
         x.len = len;
         const bf16 *Mt = reinterpret_cast<const bf16 *>(a.ws_Mt) + ch * kChunk * kChunk;
-        const bf16 *Kh = reinterpret_cast<const bf16 *>(a.ws_Kh) + ch * kChunk * DK;
         const bf16 *Qt = reinterpret_cast<const bf16 *>(a.ws_Qt) + ch * DK * kChunk;
-        const bf16 *Wt = reinterpret_cast<const bf16 *>(a.ws_Wt) + ch * DK * kChunk;
+        const granule_t *Kt = reinterpret_cast<const granule_t *>(a.ws_KhT) + ch * C::GK;
+        const granule_t *Wg = reinterpret_cast<const granule_t *>(a.ws_W) + ch * C::GK;
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) x.fM[kk] = load_frag_packed<bf16>(Mt, kChunk, wave, kk, lane);
 #pragma unroll
-        for (int kk = 0; kk < NKD; ++kk) x.fK[kk] = load_frag_packed<bf16>(Kh, DK, wave, kk, lane);
+        for (int j = 0; j < C::NKW; ++j) {
+            const int g = j * kThreads + tid;
+            x.kw[j] = g < C::GK ? Kt[g] : Wg[g - C::GK];
+        }
 #pragma unroll
         for (int b = 0; b < C::KB_W; ++b) {
             const int cblk = wave * C::KB_W + b;
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                x.fQ[b][kk] = load_frag_packed<bf16>(Qt, kChunk, cblk, kk, lane);
-                x.fW[b][kk] = load_frag_packed<bf16>(Wt, kChunk, cblk, kk, lane);
-            }
+            for (int kk = 0; kk < 2; ++kk) x.fQ[b][kk] = load_frag_packed<bf16>(Qt, kChunk, cblk, kk, lane);
             x.gl[b] = *reinterpret_cast<const f32x4 *>(a.ws_gl + ch * DK + 16 * cblk + 4 * (lane >> 4));
         }
 #pragma unroll
@@ -190,16 +211,17 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_rev_kernel(BwdArgs ba) 
         const size_t ch = (size_t)cid * H + h;
         load_in(cur, cid);
         const int len = cur.len;
-        // dS' of this chunk to LDS (bf16), as it is and transposed; the plain
-        // copy goes on to the workspace for the per-chunk kernels in 16-byte
-        // row pieces (2-byte stores straight from the accumulators cost more
-        // than the rest of the chunk's work).
+        // dS' of this chunk to LDS (bf16); the copy goes on to the workspace
+        // for the per-chunk kernels in 16-byte row pieces (2-byte stores
+        // straight from the accumulators cost more than the rest of the
+        // chunk's work).  The chunk's Khat^T and W images to LDS.
 #pragma unroll
         for (int u = 0; u < C::S_TPW; ++u) {
             const int cblk = wave * C::KB_W + u / NCB, colb = u % NCB;
             store_tile<bf16>(sdS + 16 * cblk * C::LDV + 16 * colb, C::LDV, dS[u], lane);
-            store_tile_t<bf16>(sdSt + 16 * colb * LDKP + 16 * cblk, LDKP, dS[u], lane);
         }
+#pragma unroll
+        for (int j = 0; j < C::NKW; ++j) *reinterpret_cast<granule_t *>(sKW + (j * kThreads + tid) * 8) = cur.kw[j];
         // dO rows of the chunk (zero past its end), read through transposing
         // LDS reads.
 #pragma unroll
@@ -223,20 +245,31 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_rev_kernel(BwdArgs ba) 
         }
 
         // dU_eff rows of block `wave`:  M^T dO + Khat dS'.
+        {
+            MB::frag fK[NKD];  // Khat rows of block `wave` = columns of Khat^T
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-            f32x4 acc = zero4();
+            for (int kk = 0; kk < NKD; ++kk) fK[kk] = load_frag_tr_fo(sKt, kChunk, 32 * kk, 16 * wave, lane);
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-                acc = MB::mma(cur.fM[kk], load_frag_tr(sdO, C::LDV, 32 * kk, 16 * cb, lane), acc);
+            for (int cb = 0; cb < NCB; ++cb) {
+                f32x4 acc = zero4();
 #pragma unroll
-            for (int kk = 0; kk < NKD; ++kk)
-                acc = MB::mma(cur.fK[kk], load_frag<bf16>(sdSt + 16 * cb * LDKP + 32 * kk, LDKP, lane), acc);
-            store_tile_t<bf16>(sdUt + 16 * cb * L64 + 16 * wave, L64, acc, lane);
+                for (int kk = 0; kk < 2; ++kk)
+                    acc = MB::mma(cur.fM[kk], load_frag_tr(sdO, C::LDV, 32 * kk, 16 * cb, lane), acc);
+#pragma unroll
+                for (int kk = 0; kk < NKD; ++kk)
+                    acc = MB::mma(fK[kk], load_frag_tr(sdS, C::LDV, 32 * kk, 16 * cb, lane), acc);
+                store_tile_t<bf16>(sdUt + 16 * cb * L64 + 16 * wave, L64, acc, lane);
+            }
         }
         __syncthreads();
 
         // dS <- Diag(gl) dS' + Qhat^T dO - W^T dU_eff.
+        MB::frag fW[C::KB_W][2];  // W^T rows of the wave's state row blocks = columns of W
+#pragma unroll
+        for (int b = 0; b < C::KB_W; ++b)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+                fW[b][kk] = load_frag_tr_fo(sW, DK, 32 * kk, 16 * (wave * C::KB_W + b), lane);
 #pragma unroll
         for (int u = 0; u < C::S_TPW; ++u) {
             const int b = u / NCB, colb = u % NCB;
@@ -244,7 +277,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_rev_kernel(BwdArgs ba) 
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 q = MB::mma(cur.fQ[b][kk], load_frag_tr(sdO, C::LDV, 32 * kk, 16 * colb, lane), q);
-                wu = MB::mma(cur.fW[b][kk], load_frag<bf16>(sdUt + 16 * colb * L64 + 32 * kk, L64, lane), wu);
+                wu = MB::mma(fW[b][kk], load_frag<bf16>(sdUt + 16 * colb * L64 + 32 * kk, L64, lane), wu);
             }
             dS[u] = cur.gl[b] * dS[u] + q - wu;
         }
@@ -266,10 +299,11 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_rev_kernel(BwdArgs ba) 
 // ---------------------------------------------------------------------------
 // Reverse pass with shared factor reads: one workgroup of 8 waves per
 // (sequence, head, 2*SUB-column slab).  Waves 0-3 and 4-7 each run the form
-// above on SUB columns.  The chunk's factors (M^T, Khat, Qhat^T, W^T in
+// above on SUB columns.  The chunk's factors (M^T, Khat^T, Qhat^T, W in
 // fragment order) are read from the workspace once per workgroup, by all
 // 512 threads, into registers one chunk ahead, and staged in LDS at the
-// chunk's start; the four waves of a half read their fragments from there.
+// chunk's start; the four waves of a half read their fragments from there
+// (those of Khat and W^T through transposing reads).
 // The per-CU vector-memory path bounds this pass, and the two halves now
 // share one read of the factors.
 // ---------------------------------------------------------------------------
@@ -279,7 +313,7 @@ struct Rev2Cfg {
     static constexpr int KB_W = NKB / 4, S_TPW = KB_W * NCB;
     static constexpr int LDKP = DK + 8, L64 = kChunk + 8, LDV = WC + 8;
     static constexpr int NT = 2 * kThreads;
-    // 16-byte granules of M^T, and of each of Khat, Qhat^T, W^T
+    // 16-byte granules of M^T, and of each of Khat^T, Qhat^T, W
     static constexpr int GM = kChunk * kChunk / 8, GK = kChunk * DK / 8;
     static constexpr int NG = GM + 3 * GK, NJ = NG / NT;
     static constexpr int NGO = kChunk * WC / 8, NJO = (NGO + NT - 1) / NT;  // dO granules
@@ -294,12 +328,12 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_bwd_rev2_kernel(BwdArgs
     constexpr int DV = C::DV, WC = C::WC, NCB = C::NCB, LDKP = C::LDKP, L64 = C::L64, LDV = C::LDV;
     constexpr int NKD = DK / 32, NT = C::NT;
     const ChunkArgs &a = ba.c;
-    __shared__ __attribute__((aligned(16))) bf16 sF[C::NG * 8];     // M^T | Khat | Qhat^T | W^T
+    __shared__ __attribute__((aligned(16))) bf16 sF[C::NG * 8];     // M^T | Khat^T | Qhat^T | W
     __shared__ __attribute__((aligned(16))) bf16 sdSt[WC * LDKP];   // [v][c] = dS'[c][v]
     __shared__ __attribute__((aligned(16))) bf16 sdO[kChunk * LDV];  // [i][v] = dO[i][v]
     __shared__ __attribute__((aligned(16))) bf16 sdUt[WC * L64];    // [v][i] = dU_eff[i][v]
     __shared__ __attribute__((aligned(16))) bf16 sdS[DK * LDV];     // [c][v] = dS'[c][v]
-    const bf16 *sMt = sF, *sKh = sF + C::GM * 8, *sQt = sKh + C::GK * 8, *sWt = sQt + C::GK * 8;
+    const bf16 *sMt = sF, *sKt = sF + C::GM * 8, *sQt = sKt + C::GK * 8, *sW = sQt + C::GK * 8;
 
     const int H = a.H;
     const int x = blockIdx.x, xcd = x & 7, rest = x >> 3;
@@ -326,16 +360,16 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_bwd_rev2_kernel(BwdArgs
     auto load_f = [&](In &x, int cid) {
         const size_t ch = (size_t)cid * H + h;
         const granule_t *Mt = reinterpret_cast<const granule_t *>(a.ws_Mt) + ch * C::GM;
-        const granule_t *Kh = reinterpret_cast<const granule_t *>(a.ws_Kh) + ch * C::GK;
+        const granule_t *Kt = reinterpret_cast<const granule_t *>(a.ws_KhT) + ch * C::GK;
         const granule_t *Qt = reinterpret_cast<const granule_t *>(a.ws_Qt) + ch * C::GK;
-        const granule_t *Wt = reinterpret_cast<const granule_t *>(a.ws_Wt) + ch * C::GK;
+        const granule_t *Wg = reinterpret_cast<const granule_t *>(a.ws_W) + ch * C::GK;
 #pragma unroll
         for (int j = 0; j < C::NJ; ++j) {
             const int g = j * NT + tid;
             if (j * NT < C::GM) x.f[j] = Mt[g];
-            else if (j * NT < C::GM + C::GK) x.f[j] = Kh[g - C::GM];
+            else if (j * NT < C::GM + C::GK) x.f[j] = Kt[g - C::GM];
             else if (j * NT < C::GM + 2 * C::GK) x.f[j] = Qt[g - C::GM - C::GK];
-            else x.f[j] = Wt[g - C::GM - 2 * C::GK];
+            else x.f[j] = Wg[g - C::GM - 2 * C::GK];
         }
     };
     auto load_o = [&](In &x, int cid) {
@@ -406,7 +440,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_bwd_rev2_kernel(BwdArgs
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) fM[kk] = load_frag_packed<bf16>(sMt, kChunk, wl, kk, lane);
 #pragma unroll
-            for (int kk = 0; kk < NKD; ++kk) fK[kk] = load_frag_packed<bf16>(sKh, DK, wl, kk, lane);
+            for (int kk = 0; kk < NKD; ++kk) fK[kk] = load_frag_tr_fo(sKt, kChunk, 32 * kk, 16 * wl, lane);
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) {
                 const int v = hc + 16 * cb;
@@ -430,7 +464,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_bwd_rev2_kernel(BwdArgs
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 fQ[kk] = load_frag_packed<bf16>(sQt, kChunk, cblk, kk, lane);
-                fW[kk] = load_frag_packed<bf16>(sWt, kChunk, cblk, kk, lane);
+                fW[kk] = load_frag_tr_fo(sW, DK, 32 * kk, 16 * cblk, lane);
             }
 #pragma unroll
             for (int colb = 0; colb < NCB; ++colb) {
@@ -498,7 +532,9 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_state_kernel(BwdArgs ba
     constexpr int DV = C::DV, SW = C::SW, NKB = C::NKB, LSW = C::LSW, L64 = C::L64;
     constexpr int NKD = DK / 32;
     const ChunkArgs &a = ba.c;
-    // per slab (W, M^T, Khat and T^T are loaded as fragments from the workspace)
+    // per slab (W, M^T and T^T are loaded as fragments from the workspace,
+    // Khat through the Khat^T image in sKt)
+    __shared__ __attribute__((aligned(16))) bf16 sKt[DK * kChunk];   // Khat^T, fragment order
     __shared__ __attribute__((aligned(16))) bf16 sS[DK * LSW];       // [c][v]
     __shared__ __attribute__((aligned(16))) bf16 sdS[DK * LSW];      // [c][v]
     __shared__ __attribute__((aligned(16))) bf16 sdO[kChunk * LSW];  // [i][v]
@@ -522,7 +558,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_state_kernel(BwdArgs ba
 
     const bf16 *Wg = reinterpret_cast<const bf16 *>(a.ws_W) + ch * kChunk * DK;
     const bf16 *Mtg = reinterpret_cast<const bf16 *>(a.ws_Mt) + ch * kChunk * kChunk;
-    const bf16 *Khg = reinterpret_cast<const bf16 *>(a.ws_Kh) + ch * kChunk * DK;
+    const granule_t *Ktg = reinterpret_cast<const granule_t *>(a.ws_KhT) + ch * (DK * kChunk / 8);
     const bf16 *Ttg = reinterpret_cast<const bf16 *>(a.ws_Tt) + ch * kChunk * kChunk;
 
     f32x4 dWt[NKB], dKh[NKB], dMa[4], dAp[4];
@@ -535,16 +571,25 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_state_kernel(BwdArgs ba
     // The wave's rows of W, Khat, M^T and T^T, held in registers across the
     // slabs (reloading them per slab re-reads them from HBM once the working
     // set of the resident workgroups has left L2).
+    // Khat's rows are columns of the Khat^T image, staged in LDS once.
+    constexpr int NKG = DK * kChunk / 8 / kThreads;  // granules of Khat^T per thread
     MB::frag fW[NKD], fKh[NKD], fMt[2], fTt[2];
+    {
+        granule_t kg[NKG];
 #pragma unroll
-    for (int kk = 0; kk < NKD; ++kk) {
-        fW[kk] = load_frag_packed<bf16>(Wg, DK, I, kk, lane);
-        fKh[kk] = load_frag_packed<bf16>(Khg, DK, I, kk, lane);
-    }
+        for (int j = 0; j < NKG; ++j) kg[j] = Ktg[j * kThreads + tid];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-        fMt[kk] = load_frag_packed<bf16>(Mtg, kChunk, I, kk, lane);
-        fTt[kk] = load_frag_packed<bf16>(Ttg, kChunk, I, kk, lane);
+        for (int kk = 0; kk < NKD; ++kk) fW[kk] = load_frag_packed<bf16>(Wg, DK, I, kk, lane);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            fMt[kk] = load_frag_packed<bf16>(Mtg, kChunk, I, kk, lane);
+            fTt[kk] = load_frag_packed<bf16>(Ttg, kChunk, I, kk, lane);
+        }
+#pragma unroll
+        for (int j = 0; j < NKG; ++j) *reinterpret_cast<granule_t *>(sKt + (j * kThreads + tid) * 8) = kg[j];
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < NKD; ++kk) fKh[kk] = load_frag_tr_fo(sKt, kChunk, 32 * kk, 16 * I, lane);
     }
     // Thread t stages row c = t / TPR of S and dS' (columns CPT (t % TPR) .. of
     // each slab) and accumulates dgl[c] = sum_v dS'[c][v] S[c][v] over the slabs.

@@ -250,7 +250,8 @@ __device__ __forceinline__ float sigmoid1(float x) {
 }
 
 // kBwd: also write the transposed factors a backward call needs (a.ws_Mt,
-// ws_Kh, ws_Qt, ws_Wt, ws_Tt), and not Qhat or M, which only o needs.
+// ws_Qt, ws_Tt), and not Qhat or M, which only o needs (its kernels read
+// Khat and W^T from Khat^T and W with transposing LDS reads).
 // kLogits: the gates arrive as bf16 -- log alpha itself and the logits of b
 // and w, whose sigmoid is taken here.  kAlphaLogit (with kLogits): log_alpha
 // holds logits too, and log alpha = logsigmoid(logit + a.alpha_bias).
@@ -408,11 +409,8 @@ __global__ __launch_bounds__(kThreads, (PrepCfg<E, DK>::SMEM <= 80 * 1024 ? 2 : 
         for (int j = 0; j < TPG; ++j) et[j] = bk[j][c];
         store_run_et<E, TPG>(sEt + (c0 + c) * LDC, c0 + c, tg * TPG, et);
     }
-    if constexpr (kBwd) {  // backward calls: Khat token-major and Qhat^T, fragment order
-        E *KhG = reinterpret_cast<E *>(a.ws_Kh) + ch * kChunk * DK;
+    if constexpr (kBwd) {  // backward calls: Qhat^T, fragment order
         E *QtG = reinterpret_cast<E *>(a.ws_Qt) + ch * DK * kChunk;
-#pragma unroll
-        for (int j = 0; j < TPG; ++j) store4_frag<E>(KhG, DK, tg * TPG + j, c0, g[j]);
 #pragma unroll
         for (int c = 0; c < 4; ++c)
 #pragma unroll
@@ -685,12 +683,6 @@ __global__ __launch_bounds__(kThreads, (PrepCfg<E, DK>::SMEM <= 80 * 1024 ? 2 : 
                 f32x4 acc = mma_tile_swz<E>(zero4(), sEt + 16 * cblk * LDC, LDC, cblk & 7,
                                             sTb + 16 * I * LDC, LDC, 0, K, lane);
                 store4_frag_nt<E>(Wg, DK, 16 * I + (lane & 15), 16 * cblk + 4 * (lane >> 4), acc);
-                if constexpr (kBwd) {  // W^T: the same tile with the operands swapped
-                    const f32x4 t = mma_tile_swz<E>(zero4(), sTb + 16 * I * LDC, LDC, 0,
-                                                    sEt + 16 * cblk * LDC, LDC, cblk & 7, K, lane);
-                    store4_frag<E>(reinterpret_cast<E *>(a.ws_Wt) + ch * DK * kChunk, kChunk,
-                                   16 * cblk + (lane & 15), 16 * I + 4 * (lane >> 4), t);
-                }
             }
         }
     }

@@ -53,8 +53,8 @@ struct ChunkArgs {
                           // state here (bf16 [chunk id][head], layout of sc_index)
                           // and writes no o
     // If set (backward calls), the chunk-factor kernel also writes, in fragment
-    // order: M^T [64][64], Khat [64][Dk], Qhat^T [Dk][64], W^T [Dk][64] and T^T [64][64].
-    void *ws_Mt, *ws_Kh, *ws_Qt, *ws_Wt, *ws_Tt;
+    // order: M^T [64][64], Qhat^T [Dk][64] and T^T [64][64].
+    void *ws_Mt, *ws_Qt, *ws_Tt;
     float *ws_Sc32;       // if set (fp32 backward calls), the fp32 propagation stores
                           // every chunk's incoming state here, row-major
                           // [chunk id][head][Dk][Dv]; o may then be NULL
@@ -77,7 +77,7 @@ __host__ __device__ inline size_t sc_index(int c, int v, int Dk) {
 
 struct BwdLayout {
     WorkspaceLayout fwd;
-    size_t off_Mt = 0, off_Kh = 0, off_Qt = 0, off_Wt = 0, off_Tt = 0;
+    size_t off_Mt = 0, off_Qt = 0, off_Tt = 0;
     size_t off_Sc = 0, off_dSc = 0, off_dKh = 0, off_dWt = 0, off_dM = 0,
            off_dMt = 0, off_dAp = 0, off_dG = 0;
     size_t total = 0;

@@ -68,6 +68,15 @@ int gdn2_abi_version(void);
 const char *gdn2_status_string(int status);
 
 /*
+ * The device's compute-unit count and peak engine clock (kHz), as the HIP
+ * runtime reports them, for stating peak rates from the part's own figures
+ * (a gfx950 CU retires 4096 dense bf16 MFMA flops and 256 fp32 vector flops
+ * per clock).  Outputs may be NULL.  Returns GDN2_ERR_HIP when the runtime
+ * query fails (no such device), GDN2_OK otherwise.
+ */
+int gdn2_device_info(int device, int *compute_units, int *peak_clock_khz);
+
+/*
  * Workspace bytes gdn2_chunk_fwd needs for a call with these sizes.
  * varlen != 0 sizes it for a packed call with N sequences and T total tokens
  * (B must then be 1).  Returns 0 for unsupported or invalid sizes.
