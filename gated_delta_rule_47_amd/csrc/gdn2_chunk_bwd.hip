@@ -99,17 +99,28 @@ __device__ __forceinline__ Mma<bf16>::frag load_frag_tr(const bf16 *X, int ld, i
     return __builtin_bit_cast(Mma<bf16>::frag, both);
 }
 
+// LDS slot of 16-byte granule g of a fragment-ordered image that is read
+// transposed: granules whose bit 4 is set trade places with the granule 4
+// away, so that a transposing read's two column groups of the same rows (16
+// granules apart) land on different banks.
+__device__ __forceinline__ int fo_slot(int g) { return g ^ (((g >> 4) & 1) << 2); }
+
 // Operand fragment of X^T where X (K columns) lies in LDS in the chunk
-// factors' fragment order: lane l receives X[r0 + 8 (l/16) + t][c0 + l%16],
-// t = 0..7, i.e. the fragment of X^T at rows c0.., contraction index r0...
-// Four consecutive columns of an X row are 8 contiguous bytes of that order,
-// so the two transposing reads work on it as on a row-major tile.
+// factors' fragment order, granules placed by fo_slot: lane l receives
+// X[r0 + 8 (l/16) + t][c0 + l%16], t = 0..7, i.e. the fragment of X^T at rows
+// c0.., contraction index r0...  Four consecutive columns of an X row are 8
+// contiguous bytes of that order, so the two transposing reads work on it as
+// on a row-major tile.
+__device__ __forceinline__ const bf16 *fo_at(const bf16 *X, int r, int k, int K) {
+    const int e = (int)frag_index<bf16>(r, k, K);
+    return X + fo_slot(e >> 3) * 8 + (e & 7);
+}
 __device__ __forceinline__ Mma<bf16>::frag load_frag_tr_fo(const bf16 *X, int K, int r0, int c0, int lane) {
     const int j = lane & 15, row = r0 + 8 * (lane >> 4) + (j >> 2), col = c0 + 4 * (j & 3);
     const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) v4i16 *)(X + frag_index<bf16>(row, col, K)));
+        (__attribute__((address_space(3))) v4i16 *)fo_at(X, row, col, K));
     const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) v4i16 *)(X + frag_index<bf16>(row + 4, col, K)));
+        (__attribute__((address_space(3))) v4i16 *)fo_at(X, row + 4, col, K));
     const v8i16 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     return __builtin_bit_cast(Mma<bf16>::frag, both);
 }
@@ -221,7 +232,8 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_rev_kernel(BwdArgs ba) 
             store_tile<bf16>(sdS + 16 * cblk * C::LDV + 16 * colb, C::LDV, dS[u], lane);
         }
 #pragma unroll
-        for (int j = 0; j < C::NKW; ++j) *reinterpret_cast<granule_t *>(sKW + (j * kThreads + tid) * 8) = cur.kw[j];
+        for (int j = 0; j < C::NKW; ++j)
+            *reinterpret_cast<granule_t *>(sKW + fo_slot(j * kThreads + tid) * 8) = cur.kw[j];
         // dO rows of the chunk (zero past its end), read through transposing
         // LDS reads.
 #pragma unroll
@@ -402,7 +414,11 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_bwd_rev2_kernel(BwdArgs
         // zero past the chunk's end; read through transposing LDS reads)
         // into LDS.
 #pragma unroll
-        for (int j = 0; j < C::NJ; ++j) *reinterpret_cast<granule_t *>(sF + (j * NT + tid) * 8) = x.f[j];
+        for (int j = 0; j < C::NJ; ++j) {  // Khat^T and W (read transposed) placed by fo_slot
+            const int g = j * NT + tid;
+            const bool tr = (j * NT >= C::GM && j * NT < C::GM + C::GK) || j * NT >= C::GM + 2 * C::GK;
+            *reinterpret_cast<granule_t *>(sF + (tr ? fo_slot(g) : g) * 8) = x.f[j];
+        }
         load_f(x, nxt2);
 #pragma unroll
         for (int u = 0; u < C::S_TPW; ++u) {
@@ -586,7 +602,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_state_kernel(BwdArgs ba
             fTt[kk] = load_frag_packed<bf16>(Ttg, kChunk, I, kk, lane);
         }
 #pragma unroll
-        for (int j = 0; j < NKG; ++j) *reinterpret_cast<granule_t *>(sKt + (j * kThreads + tid) * 8) = kg[j];
+        for (int j = 0; j < NKG; ++j) *reinterpret_cast<granule_t *>(sKt + fo_slot(j * kThreads + tid) * 8) = kg[j];
         __syncthreads();
 #pragma unroll
         for (int kk = 0; kk < NKD; ++kk) fKh[kk] = load_frag_tr_fo(sKt, kChunk, 32 * kk, 16 * I, lane);
