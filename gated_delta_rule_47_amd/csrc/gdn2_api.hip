@@ -97,7 +97,6 @@ bool bwd_layout(int N, int B, int T, int H, int Dk, int Dv, size_t io_bytes, boo
     L.off_dKh = take(chd * kChunk * Dk * 2);
     L.off_dWt = take(chd * Dk * kChunk * 2);
     L.off_dM = take(chd * kChunk * kChunk * 2);
-    L.off_dMt = take(chd * kChunk * kChunk * 2);
     L.off_dAp = take(chd * kChunk * kChunk * 2);
     L.off_dG = take(chd * Dk * sizeof(float));
     L.total = off;
@@ -542,7 +541,6 @@ int gdn2_chunk_bwd(const void *q, const void *k, const void *v, const float *log
     ba.dKh = reinterpret_cast<bf16_t *>(ws + L.off_dKh);
     ba.dWt = reinterpret_cast<bf16_t *>(ws + L.off_dWt);
     ba.dM = reinterpret_cast<bf16_t *>(ws + L.off_dM);
-    ba.dMt = reinterpret_cast<bf16_t *>(ws + L.off_dMt);
     ba.dAp = reinterpret_cast<bf16_t *>(ws + L.off_dAp);
     ba.dG = reinterpret_cast<float *>(ws + L.off_dG);
 

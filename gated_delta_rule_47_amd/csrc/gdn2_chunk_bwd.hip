@@ -747,8 +747,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_state_kernel(BwdArgs ba
     bf16 *oK = ba.dKh + ch * kChunk * DK;
     bf16 *oA = ba.dAp + ch * kChunk * kChunk;
     bf16 *oWt = ba.dWt + ch * DK * kChunk;      // dW^T, fragment order
-    bf16 *oM = ba.dM + ch * kChunk * kChunk;    // dM, fragment order
-    bf16 *oMt = ba.dMt + ch * kChunk * kChunk;  // dM^T, fragment order
+    bf16 *oM = ba.dM + ch * kChunk * kChunk;    // dM, fragment order (zero above the diagonal)
     // Row-major and row-fragment results leave as row pieces after a quad
     // transpose (row it, columns 4 lq ..); the transposed ones as they are.
     const int i0 = 16 * I + 4 * (lane >> 4), it = 16 * I + 4 * (lane >> 4) + (lane & 3);
@@ -768,7 +767,6 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_state_kernel(BwdArgs ba
         f32x4 m;
 #pragma unroll
         for (int r = 0; r < 4; ++r) m[r] = j <= i0 + r ? dMa[J][r] : 0.0f;
-        store4_frag<bf16>(oMt, kChunk, j, i0, m);
         const f32x4 at = quad_transpose(dAp[J], lane);
         *reinterpret_cast<bf16x4 *>(oA + it * kChunk + 16 * J + 4 * lq) =
             bf16x4{static_cast<bf16>(at[0]), static_cast<bf16>(at[1]), static_cast<bf16>(at[2]),
@@ -858,14 +856,19 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_factor_kernel(BwdArgs b
 
     for (int c = tid; c < DK; c += kThreads) sDG[c] = ba.dG[ch * DK + c];
     const bf16 *dWtg = ba.dWt + ch * DK * kChunk;
-    const bf16 *dMg = ba.dM + ch * kChunk * kChunk, *dMtg = ba.dMt + ch * kChunk * kChunk;
+    const granule_t *dMg = reinterpret_cast<const granule_t *>(ba.dM + ch * kChunk * kChunk);
 
     const bf16 *Ttg = reinterpret_cast<const bf16 *>(a.ws_Tt) + ch * kChunk * kChunk;
     const bf16 *Wg = reinterpret_cast<const bf16 *>(a.ws_W) + ch * kChunk * DK;
     // Global operands of dA and of the per-half products, issued before dE so
     // that their loads are in flight together.  Token rows past the chunk's end
-    // read row 0 (always valid) and are zeroed or skipped where used.
-    MB::frag fWd[4][NKD], fM[2], fMt[2], fdO[NKD];
+    // read row 0 (always valid) and are zeroed or skipped where used.  dM
+    // comes as this thread's granules of its fragment-ordered image, staged in
+    // LDS (the g region, free until the halves) and read there as dM and,
+    // transposed, as dM^T.
+    constexpr int NMG = kChunk * kChunk / 8 / kThreads;  // dM granules per thread
+    MB::frag fWd[4][NKD], fdO[NKD];
+    granule_t mg[NMG];
     bf16 apv[4][4];  // raw, converted where used
     {
         const bf16 *Ap = ba.dAp + ch * kChunk * kChunk;
@@ -878,10 +881,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_factor_kernel(BwdArgs b
                 apv[J][r] = Ap[(size_t)(16 * I + 4 * (lane >> 4) + r) * kChunk + 16 * J + (lane & 15)];
         }
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            fM[kk] = load_frag_packed<bf16>(dMg, kChunk, I, kk, lane);
-            fMt[kk] = load_frag_packed<bf16>(dMtg, kChunk, I, kk, lane);
-        }
+        for (int j = 0; j < NMG; ++j) mg[j] = dMg[j * kThreads + tid];
         const bf16 *dout = reinterpret_cast<const bf16 *>(ba.dout);
         const int row = 16 * I + (lane & 15);
         const bf16 *src = dout + ((size_t)(tok0 + (row < len ? row : 0)) * H + h) * DK + 8 * (lane >> 4);
@@ -902,9 +902,18 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_factor_kernel(BwdArgs b
             store_tile<bf16>(sdE + 16 * I * LDKP + 16 * cb, LDKP, d, lane);
         }
     }
-    // (each wave reads back only its own rows of dE: a wave-level fence suffices,
-    // but the block barrier below also orders sDG)
+    bf16 *sMi = reinterpret_cast<bf16 *>(smem + C::OFF_G);  // dM image (until the halves)
+#pragma unroll
+    for (int j = 0; j < NMG; ++j) *reinterpret_cast<granule_t *>(sMi + fo_slot(j * kThreads + tid) * 8) = mg[j];
+    // (each wave reads back only its own rows of dE; the block barrier orders
+    // sDG and the dM image)
     __syncthreads();
+    MB::frag fM[2], fMt[2];  // dM and dM^T rows of block I
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        fM[kk] = *reinterpret_cast<const MB::frag *>(sMi + fo_slot((2 * I + kk) * 64 + lane) * 8);
+        fMt[kk] = load_frag_tr_fo(sMi, kChunk, 32 * kk, 16 * I, lane);
+    }
     // ---- dA = -strict_tril(dZ U^T + dE W^T), both orientations --------------
     {
         MB::frag fe_[NKD];
