@@ -94,9 +94,14 @@ bool bwd_layout(int N, int B, int T, int H, int Dk, int Dv, size_t io_bytes, boo
     L.off_Tt = take(chd * kChunk * kChunk * io_bytes);
     L.off_Sc = take(chd * Dk * Dv * 2);
     L.off_dSc = take(chd * Dk * Dv * 2);
-    L.off_dKh = take(chd * kChunk * Dk * 2);
-    L.off_dWt = take(chd * Dk * kChunk * 2);
-    L.off_dM = take(chd * kChunk * kChunk * 2);
+    // The state-side kernel writes three of its partial gradients over inputs
+    // that no later kernel reads, each chunk-head's slot by the workgroup that
+    // has already read it: dKhat over Qhat^T (read by the reverse pass only),
+    // dW^T over U and dM over M^T (both read by that workgroup before it
+    // writes).  All three pairs have the same size (bf16, Dk == Dv).
+    L.off_dKh = L.off_Qt;
+    L.off_dWt = L.fwd.off_U;
+    L.off_dM = L.off_Mt;
     L.off_dAp = take(chd * kChunk * kChunk * 2);
     L.off_dG = take(chd * Dk * sizeof(float));
     L.total = off;
