@@ -269,7 +269,8 @@ size_t gdn2_chunk_bwd_workspace_bytes(int N, int B, int T, int H, int Dk, int Dv
  * gdn2_chunk_bwd_workspace_bytes(...) bytes, 256-byte aligned) holds the
  * chunk factors, every chunk's incoming state and state gradient, and the
  * per-chunk partial gradients.  io = GDN2_BF16 runs the fast bf16-MFMA
- * kernels (bf16 factors and intermediates, fp32 accumulation); io = GDN2_F32
+ * kernels (bf16 factors and intermediates, fp32 accumulation; about 157 KiB
+ * of workspace per chunk-head at Dk = 128); io = GDN2_F32
  * computes every product and intermediate in fp32 (fp32 MFMA), the precision
  * reference of the same chain rule, with a larger workspace (about 1 MiB per
  * chunk-head at Dk = 128).
