@@ -94,16 +94,10 @@ bool bwd_layout(int N, int B, int T, int H, int Dk, int Dv, size_t io_bytes, boo
     L.off_Tt = take(chd * kChunk * kChunk * io_bytes);
     L.off_Sc = take(chd * Dk * Dv * 2);
     L.off_dSc = take(chd * Dk * Dv * 2);
-    // The state-side kernel writes three of its partial gradients over inputs
-    // that no later kernel reads, each chunk-head's slot by the workgroup that
-    // has already read it: dKhat over Qhat^T (read by the reverse pass only),
-    // dW^T over U and dM over M^T (both read by that workgroup before it
-    // writes).  All three pairs have the same size (bf16, Dk == Dv).
+    // The per-chunk kernel hands dKhat from its state side to its factor side
+    // through the slot of Qhat^T, which only the reverse pass (finished by
+    // then) reads; same size (bf16, Dk == Dv).
     L.off_dKh = L.off_Qt;
-    L.off_dWt = L.fwd.off_U;
-    L.off_dM = L.off_Mt;
-    L.off_dAp = take(chd * kChunk * kChunk * 2);
-    L.off_dG = take(chd * Dk * sizeof(float));
     L.total = off;
     *out = L;
     return true;
@@ -544,10 +538,6 @@ int gdn2_chunk_bwd(const void *q, const void *k, const void *v, const float *log
     ba.Sc = a.ws_Sc;
     ba.dSc = reinterpret_cast<bf16_t *>(ws + L.off_dSc);
     ba.dKh = reinterpret_cast<bf16_t *>(ws + L.off_dKh);
-    ba.dWt = reinterpret_cast<bf16_t *>(ws + L.off_dWt);
-    ba.dM = reinterpret_cast<bf16_t *>(ws + L.off_dM);
-    ba.dAp = reinterpret_cast<bf16_t *>(ws + L.off_dAp);
-    ba.dG = reinterpret_cast<float *>(ws + L.off_dG);
 
     hipError_t err = hipSuccess;
     if (varlen) err = launch_plan(a, stream);

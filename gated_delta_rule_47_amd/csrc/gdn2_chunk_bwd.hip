@@ -24,14 +24,14 @@
 //   dg = E dE + Ep dEp + Qhat dQhat + Qp dQp - Kp dKp - Khat dKhat,
 //   dlog_alpha_j = sum_{i>=j} dg_i + gl dgl + sum_i Khat_i dKhat_i.
 //
-// Three kernels after the forward (the chunk factors a backward call needs:
-// W, Khat^T, U, gamma_last and the transposes M^T, Khat, Qhat^T, W^T, T^T; the
+// Two kernels after the forward (the chunk factors a backward call needs:
+// W, Khat^T, U, gamma_last and the transposes M^T, Qhat^T, T^T; the
 // propagation storing every chunk's incoming state and forming no o):
 //   chunk_bwd_rev2_kernel    sequential over the chunks of a sequence, in
 //   (chunk_bwd_rev_kernel    reverse: dU_eff and dS, storing each chunk's dS'
 //    with 256+ chains)
-//   chunk_bwd_state_kernel   per chunk: the state-side products, dv and dw
-//   chunk_bwd_factor_kernel  per chunk: the factor side, dq, dk, db, dlog_alpha
+//   chunk_bwd_local_kernel   per chunk: the state-side products with dv and dw,
+//                            then the factor side with dq, dk, db, dlog_alpha
 // All products are bf16 MFMA (16x16x32) with fp32 accumulation; each operand is
 // either a fragment-ordered factor from the workspace or staged in LDS with its
 // contraction index contiguous.
@@ -539,10 +539,61 @@ struct StateCfg {
     static constexpr int DV = DK, SW = 32, NSL = DV / SW, NKB = DK / 16;
     static constexpr int LSW = SW + 8;     // [..][SW] bf16 rows
     static constexpr int L64 = kChunk + 8; // [..][64] bf16 rows
+    // LDS (bf16 elements): Khat^T image, S and dS' [c][v], dO, U, U_eff, dU_eff
+    // and dZ [i][v], dU_eff^T [v][i]
+    static constexpr int E_KT = DK * kChunk, E_S = DK * LSW, E_R = kChunk * LSW, E_UT = SW * L64;
+    static constexpr size_t SMEM = size_t(E_KT + 2 * E_S + 5 * E_R + E_UT) * 2;
+    static_assert(E_KT % 8 == 0 && E_S % 8 == 0 && E_R % 8 == 0, "16-byte aligned arrays");
 };
 
 template <int DK>
-__global__ __launch_bounds__(kThreads, 2) void chunk_bwd_state_kernel(BwdArgs ba) {
+struct FacCfg {
+    static constexpr int DH = DK / 2;                 // channels per half
+    static constexpr int NQUAD = DH / 4, NTG = kThreads / NQUAD, TPG = kChunk / NTG;
+    // the loops over the NTG token groups' partial sums: fully unrolled for
+    // 128-wide heads; by 4 for 64-wide ones, whose 32 groups would otherwise
+    // hold 32 LDS reads in flight and spill
+    static constexpr int NTG_UNROLL = NTG > 16 ? 4 : NTG;
+    static constexpr int L64 = kChunk + 8;            // bf16 [..][64]
+    static constexpr int LDKP = DK + 8;               // bf16 [..][DK]
+    static constexpr int LDG = DH + 4;                // fp32 [64][LDG]
+    static constexpr size_t SZ_CT = size_t(DH) * L64 * 2;       // [DH][64] bf16
+    static constexpr size_t SZ_64 = size_t(kChunk) * L64 * 2;    // [64][64] bf16
+    static constexpr size_t SZ_DE = size_t(kChunk) * LDKP * 2;   // dE bf16 [64][LDKP]
+    static constexpr size_t SZ_T3 = 3 * SZ_CT;                   // Kp^T, Ep^T, Qp^T of a half
+    static constexpr size_t OFF_T = 0;                           // dE, then the half's tiles
+    static constexpr size_t OFF_A = OFF_T + (SZ_DE > SZ_T3 ? SZ_DE : SZ_T3);  // dA, dA^T
+    static constexpr size_t OFF_G = OFF_A + 2 * SZ_64;           // g, then dg of a half (fp32)
+    static constexpr size_t OFF_R = OFF_G + size_t(kChunk) * LDG * 4;
+    static constexpr size_t SZ_R = size_t(2 * NTG + 4) * DH * 4 + size_t(2) * DK * 4;
+    static constexpr size_t OFF_DG = OFF_R + size_t(2 * NTG + 4) * DH * 4;  // dgl [DK] (in the R region)
+    static constexpr size_t SMEM = OFF_R + SZ_R;
+    static_assert(SMEM <= 80 * 1024, "two workgroups per CU");
+};
+
+// What the state side hands to the factor side in registers, per wave (rows
+// of block I, MFMA accumulator order): dU_eff S^T (= -dW), dO U_eff^T (dM
+// before its mask), dZ U^T, and the wave's T^T fragments.  Its gamma_last
+// gradient goes to the factor side's LDS slot directly, and dKhat through the
+// workspace.
+template <int DK>
+struct StateOut {
+    f32x4 dWn[DK / 16], dM[4], dAp[4];
+    Mma<bf16>::frag fTt[2];
+};
+
+// LDS of the per-chunk kernel, sized for 128-wide heads (the larger): the
+// state side's tiles, then the factor side's in the same bytes.
+constexpr size_t kBwdSmem = StateCfg<128>::SMEM > FacCfg<128>::SMEM ? StateCfg<128>::SMEM : FacCfg<128>::SMEM;
+static_assert(kBwdSmem <= 80 * 1024, "two workgroups per CU");
+__shared__ __attribute__((aligned(16))) char bwd_smem[kBwdSmem];
+
+// The state side of one (chunk, head), the first part of
+// chunk_bwd_local_kernel, in bwd_smem (StateCfg<DK>::SMEM bytes).
+template <int DK>
+__device__ __forceinline__ void bwd_state_side(const BwdArgs &ba, StateOut<DK> &out) {
+    char *smem = bwd_smem;
+    static_assert(FacCfg<DK>::OFF_DG >= StateCfg<DK>::SMEM, "the gamma_last gradient slot is clear of the state side's tiles");
     using C = StateCfg<DK>;
     using MB = Mma<bf16>;
     constexpr int DV = C::DV, SW = C::SW, NKB = C::NKB, LSW = C::LSW, L64 = C::L64;
@@ -550,15 +601,15 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_state_kernel(BwdArgs ba
     const ChunkArgs &a = ba.c;
     // per slab (W, M^T and T^T are loaded as fragments from the workspace,
     // Khat through the Khat^T image in sKt)
-    __shared__ __attribute__((aligned(16))) bf16 sKt[DK * kChunk];   // Khat^T, fragment order
-    __shared__ __attribute__((aligned(16))) bf16 sS[DK * LSW];       // [c][v]
-    __shared__ __attribute__((aligned(16))) bf16 sdS[DK * LSW];      // [c][v]
-    __shared__ __attribute__((aligned(16))) bf16 sdO[kChunk * LSW];  // [i][v]
-    __shared__ __attribute__((aligned(16))) bf16 sU[kChunk * LSW];   // [j][v] = U[j][v]
-    __shared__ __attribute__((aligned(16))) bf16 sUe[kChunk * LSW];  // [i][v] = U_eff
-    __shared__ __attribute__((aligned(16))) bf16 sdUt[SW * L64];     // [v][i] = dU_eff[i][v]
-    __shared__ __attribute__((aligned(16))) bf16 sdU[kChunk * LSW];  // [i][v]
-    __shared__ __attribute__((aligned(16))) bf16 sdZ[kChunk * LSW];  // [i][v]
+    bf16 *sKt = reinterpret_cast<bf16 *>(smem);  // Khat^T, fragment order
+    bf16 *sS = sKt + C::E_KT;                     // [c][v]
+    bf16 *sdS = sS + C::E_S;                      // [c][v]
+    bf16 *sdO = sdS + C::E_S;                     // [i][v]
+    bf16 *sU = sdO + C::E_R;                      // [j][v] = U[j][v]
+    bf16 *sUe = sU + C::E_R;                      // [i][v] = U_eff
+    bf16 *sdU = sUe + C::E_R;                     // [i][v]
+    bf16 *sdZ = sdU + C::E_R;                     // [i][v]
+    bf16 *sdUt = sdZ + C::E_R;                    // [v][i] = dU_eff[i][v]
 
     const int H = a.H, cid = blockIdx.x / H, h = blockIdx.x % H;
     if (a.plan && cid >= a.plan[a.N]) return;
@@ -743,36 +794,26 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_state_kernel(BwdArgs ba
     // dgl: the TPR threads staging a row are consecutive lanes.
 #pragma unroll
     for (int o = 1; o < TPR; o <<= 1) dgp += __shfl_xor(dgp, o, TPR);
-    if ((tid % TPR) == 0) ba.dG[ch * DK + srow] = dgp;
+    if ((tid % TPR) == 0) reinterpret_cast<float *>(smem + FacCfg<DK>::OFF_DG)[srow] = dgp;
+    // dKhat leaves as row pieces after a quad transpose (row it, columns 4 lq ..).
     bf16 *oK = ba.dKh + ch * kChunk * DK;
-    bf16 *oA = ba.dAp + ch * kChunk * kChunk;
-    bf16 *oWt = ba.dWt + ch * DK * kChunk;      // dW^T, fragment order
-    bf16 *oM = ba.dM + ch * kChunk * kChunk;    // dM, fragment order (zero above the diagonal)
-    // Row-major and row-fragment results leave as row pieces after a quad
-    // transpose (row it, columns 4 lq ..); the transposed ones as they are.
-    const int i0 = 16 * I + 4 * (lane >> 4), it = 16 * I + 4 * (lane >> 4) + (lane & 3);
-    const int lq = (lane >> 2) & 3;
+    const int it = 16 * I + 4 * (lane >> 4) + (lane & 3), lq = (lane >> 2) & 3;
 #pragma unroll
     for (int cb = 0; cb < NKB; ++cb) {
-        const int c = 16 * cb + (lane & 15);
         const f32x4 kt = quad_transpose(dKh[cb], lane);
         *reinterpret_cast<bf16x4 *>(oK + it * DK + 16 * cb + 4 * lq) =
             bf16x4{static_cast<bf16>(kt[0]), static_cast<bf16>(kt[1]), static_cast<bf16>(kt[2]),
                    static_cast<bf16>(kt[3])};
-        store4_frag<bf16>(oWt, kChunk, c, i0, -dWt[cb]);
     }
+#pragma unroll
+    for (int cb = 0; cb < NKB; ++cb) out.dWn[cb] = dWt[cb];
 #pragma unroll
     for (int J = 0; J < 4; ++J) {
-        const int j = 16 * J + (lane & 15);
-        f32x4 m;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) m[r] = j <= i0 + r ? dMa[J][r] : 0.0f;
-        const f32x4 at = quad_transpose(dAp[J], lane);
-        *reinterpret_cast<bf16x4 *>(oA + it * kChunk + 16 * J + 4 * lq) =
-            bf16x4{static_cast<bf16>(at[0]), static_cast<bf16>(at[1]), static_cast<bf16>(at[2]),
-                   static_cast<bf16>(at[3])};
-        store4_frag<bf16>(oM, kChunk, it, 16 * J + 4 * lq, quad_transpose(m, lane));
+        out.dM[J] = dMa[J];
+        out.dAp[J] = dAp[J];
     }
+    out.fTt[0] = fTt[0];
+    out.fTt[1] = fTt[1];
 }
 
 // ---------------------------------------------------------------------------
@@ -799,38 +840,17 @@ __device__ __forceinline__ bf16x8 load_frag_fac(const bf16 *tile, int ld, int rb
     return *reinterpret_cast<const bf16x8 *>(tile + (lane & 15) * ld + (((4 * kk + (lane >> 4)) ^ (rb & 7)) << 3));
 }
 
-template <int DK>
-struct FacCfg {
-    static constexpr int DH = DK / 2;                 // channels per half
-    static constexpr int NQUAD = DH / 4, NTG = kThreads / NQUAD, TPG = kChunk / NTG;
-    // the loops over the NTG token groups' partial sums: fully unrolled for
-    // 128-wide heads; by 4 for 64-wide ones, whose 32 groups would otherwise
-    // hold 32 LDS reads in flight and spill
-    static constexpr int NTG_UNROLL = NTG > 16 ? 4 : NTG;
-    static constexpr int L64 = kChunk + 8;            // bf16 [..][64]
-    static constexpr int LDKP = DK + 8;               // bf16 [..][DK]
-    static constexpr int LDG = DH + 4;                // fp32 [64][LDG]
-    static constexpr size_t SZ_CT = size_t(DH) * L64 * 2;       // [DH][64] bf16
-    static constexpr size_t SZ_64 = size_t(kChunk) * L64 * 2;    // [64][64] bf16
-    static constexpr size_t SZ_DE = size_t(kChunk) * LDKP * 2;   // dE bf16 [64][LDKP]
-    static constexpr size_t SZ_T3 = 3 * SZ_CT;                   // Kp^T, Ep^T, Qp^T of a half
-    static constexpr size_t OFF_T = 0;                           // dE, then the half's tiles
-    static constexpr size_t OFF_A = OFF_T + (SZ_DE > SZ_T3 ? SZ_DE : SZ_T3);  // dA, dA^T
-    static constexpr size_t OFF_G = OFF_A + 2 * SZ_64;           // g, then dg of a half (fp32)
-    static constexpr size_t OFF_R = OFF_G + size_t(kChunk) * LDG * 4;
-    static constexpr size_t SZ_R = size_t(2 * NTG + 4) * DH * 4 + size_t(2) * DK * 4;
-    static constexpr size_t SMEM = OFF_R + SZ_R;
-    static_assert(SMEM <= 80 * 1024, "two workgroups per CU");
-};
 
+// The factor side of one (chunk, head), the second part of
+// chunk_bwd_local_kernel, in bwd_smem (FacCfg<DK>::SMEM bytes).
 template <int DK>
-__global__ __launch_bounds__(kThreads, 2) void chunk_bwd_factor_kernel(BwdArgs ba) {
+__device__ __forceinline__ void bwd_factor_side(const BwdArgs &ba, const StateOut<DK> &st) {
+    char *smem = bwd_smem;
     using C = FacCfg<DK>;
     using MB = Mma<bf16>;
     constexpr int DH = C::DH, L64 = C::L64, LDKP = C::LDKP, LDG = C::LDG, TPG = C::TPG;
     constexpr int NKB = DK / 16, NKD = DK / 32, NHB = DH / 16;
     const ChunkArgs &a = ba.c;
-    __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
     bf16 *sdE = reinterpret_cast<bf16 *>(smem + C::OFF_T);     // [i][c] (until dA is formed)
     bf16 *sKpt = reinterpret_cast<bf16 *>(smem + C::OFF_T);    // [c][j] = Kp[j][c], half
     bf16 *sEpt = sKpt + DH * L64;                               // [c][i] = Ep[i][c]
@@ -854,34 +874,21 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_factor_kernel(BwdArgs b
     const int qd = tid % C::NQUAD, tg = tid / C::NQUAD, cq = 4 * qd;  // channel quad within a half
     const bf16 *kin = reinterpret_cast<const bf16 *>(a.k), *qin = reinterpret_cast<const bf16 *>(a.q);
 
-    for (int c = tid; c < DK; c += kThreads) sDG[c] = ba.dG[ch * DK + c];
-    const bf16 *dWtg = ba.dWt + ch * DK * kChunk;
-    const granule_t *dMg = reinterpret_cast<const granule_t *>(ba.dM + ch * kChunk * kChunk);
+    // (sDG holds the state side's gamma_last gradient; the dW^T image lies in
+    // the dA region and the dM image in the g region until they are read)
+    const bf16 *sWt = reinterpret_cast<const bf16 *>(smem + C::OFF_A);
+    const bf16 *sMi = reinterpret_cast<const bf16 *>(smem + C::OFF_G);
 
-    const bf16 *Ttg = reinterpret_cast<const bf16 *>(a.ws_Tt) + ch * kChunk * kChunk;
     const bf16 *Wg = reinterpret_cast<const bf16 *>(a.ws_W) + ch * kChunk * DK;
     // Global operands of dA and of the per-half products, issued before dE so
     // that their loads are in flight together.  Token rows past the chunk's end
-    // read row 0 (always valid) and are zeroed or skipped where used.  dM
-    // comes as this thread's granules of its fragment-ordered image, staged in
-    // LDS (the g region, free until the halves) and read there as dM and,
-    // transposed, as dM^T.
-    constexpr int NMG = kChunk * kChunk / 8 / kThreads;  // dM granules per thread
+    // read row 0 (always valid) and are zeroed or skipped where used.
     MB::frag fWd[4][NKD], fdO[NKD];
-    granule_t mg[NMG];
-    bf16 apv[4][4];  // raw, converted where used
     {
-        const bf16 *Ap = ba.dAp + ch * kChunk * kChunk;
 #pragma unroll
-        for (int J = 0; J < 4; ++J) {
+        for (int J = 0; J < 4; ++J)
 #pragma unroll
             for (int kk = 0; kk < NKD; ++kk) fWd[J][kk] = load_frag_packed<bf16>(Wg, DK, J, kk, lane);
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                apv[J][r] = Ap[(size_t)(16 * I + 4 * (lane >> 4) + r) * kChunk + 16 * J + (lane & 15)];
-        }
-#pragma unroll
-        for (int j = 0; j < NMG; ++j) mg[j] = dMg[j * kThreads + tid];
         const bf16 *dout = reinterpret_cast<const bf16 *>(ba.dout);
         const int row = 16 * I + (lane & 15);
         const bf16 *src = dout + ((size_t)(tok0 + (row < len ? row : 0)) * H + h) * DK + 8 * (lane >> 4);
@@ -891,22 +898,15 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_factor_kernel(BwdArgs b
 
     // ---- dE = T^T dW (rows of block I), kept in registers and as bf16 --------
     f32x4 dE[NKB];
-    {
-        const MB::frag t0 = load_frag_packed<bf16>(Ttg, kChunk, I, 0, lane);
-        const MB::frag t1 = load_frag_packed<bf16>(Ttg, kChunk, I, 1, lane);
 #pragma unroll
-        for (int cb = 0; cb < NKB; ++cb) {
-            f32x4 d = MB::mma(t0, load_frag_packed<bf16>(dWtg, kChunk, cb, 0, lane), zero4());
-            d = MB::mma(t1, load_frag_packed<bf16>(dWtg, kChunk, cb, 1, lane), d);
-            dE[cb] = d;
-            store_tile<bf16>(sdE + 16 * I * LDKP + 16 * cb, LDKP, d, lane);
-        }
+    for (int cb = 0; cb < NKB; ++cb) {
+        f32x4 d = MB::mma(st.fTt[0], load_frag_packed<bf16>(sWt, kChunk, cb, 0, lane), zero4());
+        d = MB::mma(st.fTt[1], load_frag_packed<bf16>(sWt, kChunk, cb, 1, lane), d);
+        dE[cb] = d;
+        store_tile<bf16>(sdE + 16 * I * LDKP + 16 * cb, LDKP, d, lane);
     }
-    bf16 *sMi = reinterpret_cast<bf16 *>(smem + C::OFF_G);  // dM image (until the halves)
-#pragma unroll
-    for (int j = 0; j < NMG; ++j) *reinterpret_cast<granule_t *>(sMi + fo_slot(j * kThreads + tid) * 8) = mg[j];
-    // (each wave reads back only its own rows of dE; the block barrier orders
-    // sDG and the dM image)
+    // (each wave reads back only its own rows of dE; the barrier orders the
+    // reads of the dW^T image before dA overwrites it)
     __syncthreads();
     MB::frag fM[2], fMt[2];  // dM and dM^T rows of block I
 #pragma unroll
@@ -927,7 +927,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_factor_kernel(BwdArgs b
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = 16 * I + 4 * (lane >> 4) + r, j = 16 * J + (lane & 15);
-                d[r] = j < i ? -(static_cast<float>(apv[J][r]) + d[r]) : 0.0f;
+                d[r] = j < i ? -(st.dAp[J][r] + d[r]) : 0.0f;
             }
             store_tile<bf16>(sdA + 16 * I * L64 + 16 * J, L64, d, lane);
             store_tile_t<bf16>(sdAt + 16 * I + 16 * J * L64, L64, d, lane);
@@ -1150,6 +1150,46 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_factor_kernel(BwdArgs b
     }
 }
 
+// Both per-chunk sides of one (chunk, head) on one workgroup, one after the
+// other.  The state side's partial gradients reach the factor side in
+// registers (dU_eff S^T, dO U_eff^T, dZ U^T, T^T fragments), through LDS (the
+// gamma_last gradient; dW^T and dM as fragment-ordered images written between
+// the two sides) or, for dKhat, through the workspace; the operands both
+// sides read (S, dO, W) come back from the caches.
+template <int DK>
+__global__ __launch_bounds__(kThreads, 2) void chunk_bwd_local_kernel(BwdArgs ba) {
+    const ChunkArgs &a = ba.c;
+    const int cid = blockIdx.x / a.H;
+    if (a.plan && cid >= a.plan[a.N]) return;
+    int tok0, len;
+    dense_span(a, cid, tok0, len);
+    if (len <= 0) return;  // (a malformed table only) no token: nothing to write
+    StateOut<DK> st;
+    bwd_state_side<DK>(ba, st);
+    __syncthreads();  // the state side's tiles are dead
+    {
+        bf16 *sWt = reinterpret_cast<bf16 *>(bwd_smem + FacCfg<DK>::OFF_A);  // dW^T [DK][64]
+        bf16 *sMi = reinterpret_cast<bf16 *>(bwd_smem + FacCfg<DK>::OFF_G);  // dM [64][64], fo_slot
+        const int lane = threadIdx.x & 63, I = threadIdx.x >> 6;
+        const int i0 = 16 * I + 4 * (lane >> 4), it = i0 + (lane & 3), lq = (lane >> 2) & 3;
+#pragma unroll
+        for (int cb = 0; cb < DK / 16; ++cb) store4_frag<bf16>(sWt, kChunk, 16 * cb + (lane & 15), i0, -st.dWn[cb]);
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+            const int j = 16 * J + (lane & 15);
+            f32x4 m;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) m[r] = j <= i0 + r ? st.dM[J][r] : 0.0f;  // dM is zero above the diagonal
+            m = quad_transpose(m, lane);
+            *reinterpret_cast<bf16x4 *>(const_cast<bf16 *>(fo_at(sMi, it, 16 * J + 4 * lq, kChunk))) =
+                bf16x4{static_cast<bf16>(m[0]), static_cast<bf16>(m[1]), static_cast<bf16>(m[2]),
+                       static_cast<bf16>(m[3])};
+        }
+    }
+    __syncthreads();
+    bwd_factor_side<DK>(ba, st);
+}
+
 template <int D>
 static void launch_bwd_d(const BwdArgs &a, hipStream_t stream) {
     const int chains = a.c.N * a.c.H, groups = (chains + 7) / 8;
@@ -1164,8 +1204,7 @@ static void launch_bwd_d(const BwdArgs &a, hipStream_t stream) {
                            0, stream, a);
     if (a.c.max_chunks == 0) return;
     const dim3 grid((unsigned)((size_t)a.c.max_chunks * a.c.H));
-    hipLaunchKernelGGL((chunk_bwd_state_kernel<D>), grid, block, 0, stream, a);
-    hipLaunchKernelGGL((chunk_bwd_factor_kernel<D>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((chunk_bwd_local_kernel<D>), grid, block, 0, stream, a);
 }
 
 hipError_t launch_chunk_bwd(const BwdArgs &a, int Dk, hipStream_t stream) {

@@ -64,10 +64,8 @@ struct ChunkArgs {
 // slots, the transposed chunk factors M^T, Qhat^T, T^T (io dtype, fragment
 // order), then arrays indexed [chunk id][head][...]: every chunk's incoming
 // state Sc and the gradient dSc of its outgoing state (bf16 Dk x Dv, laid out
-// by sc_index); the state-side partial gradients dKh (bf16 [64][Dk]), dW^T
-// (bf16 fragment order [Dk][64]), dM (bf16 fragment order [64][64], zero
-// above the diagonal), dAp = dZ U^T (bf16 [64][64]) and dG = rowsum(dSc * Sc)
-// (fp32 [Dk]).
+// by sc_index).  The per-chunk kernel's dKhat (bf16 [64][Dk]) goes over
+// Qhat^T.
 // Element (c, v) of a per-chunk bf16 state (Sc, dSc) of Dk rows: 32-column
 // slabs [v / 32][c][v % 32], so that a slab is one contiguous block and a
 // row's part of it is 64 contiguous bytes.
@@ -78,7 +76,7 @@ __host__ __device__ inline size_t sc_index(int c, int v, int Dk) {
 struct BwdLayout {
     WorkspaceLayout fwd;
     size_t off_Mt = 0, off_Qt = 0, off_Tt = 0;
-    size_t off_Sc = 0, off_dSc = 0, off_dKh = 0, off_dWt = 0, off_dM = 0, off_dAp = 0, off_dG = 0;
+    size_t off_Sc = 0, off_dSc = 0, off_dKh = 0;
     size_t total = 0;
 };
 
@@ -91,9 +89,7 @@ struct BwdArgs {
     const float *dS_final;
     void *dq, *dk, *dv;
     float *dla, *db, *dw, *dS0;
-    bf16_t *Sc, *dSc, *dWt, *dM;
-    bf16_t *dKh, *dAp;
-    float *dG;
+    bf16_t *Sc, *dSc, *dKh;
 };
 
 // The fp32 backward's workspace: the forward's layout including T, then per
