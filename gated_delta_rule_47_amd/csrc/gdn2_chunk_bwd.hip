@@ -573,13 +573,15 @@ struct FacCfg {
 
 // What the state side hands to the factor side in registers, per wave (rows
 // of block I, MFMA accumulator order): dU_eff S^T (= -dW), dO U_eff^T (dM
-// before its mask), dZ U^T, and the wave's T^T fragments.  Its gamma_last
-// gradient goes to the factor side's LDS slot directly, and dKhat through the
-// workspace.
+// before its mask), dZ U^T, and the wave's T^T fragments; also the factor
+// side's first global operands (every row block of W, the wave's dO rows),
+// issued by the state side as it finishes so that they arrive during the
+// hand-over.  Its gamma_last gradient goes to the factor side's LDS slot
+// directly, and dKhat through the workspace.
 template <int DK>
 struct StateOut {
     f32x4 dWn[DK / 16], dM[4], dAp[4];
-    Mma<bf16>::frag fTt[2];
+    Mma<bf16>::frag fTt[2], fWd[4][DK / 32], fdO[DK / 32];
 };
 
 // LDS of the per-chunk kernel, sized for 128-wide heads (the larger): the
@@ -814,6 +816,18 @@ __device__ __forceinline__ void bwd_state_side(const BwdArgs &ba, StateOut<DK> &
     }
     out.fTt[0] = fTt[0];
     out.fTt[1] = fTt[1];
+    // The factor side's operands of dA (W, every row block) and of dQhat (the
+    // wave's dO rows; rows past the chunk's end read row 0, zeroed at use).
+#pragma unroll
+    for (int J = 0; J < 4; ++J)
+#pragma unroll
+        for (int kk = 0; kk < NKD; ++kk) out.fWd[J][kk] = load_frag_packed<bf16>(Wg, DK, J, kk, lane);
+    {
+        const int row = 16 * I + (lane & 15);
+        const bf16 *src = dout + ((size_t)(tok0 + (row < len ? row : 0)) * H + h) * DV + 8 * (lane >> 4);
+#pragma unroll
+        for (int kk = 0; kk < NKD; ++kk) out.fdO[kk] = *reinterpret_cast<const MB::frag *>(src + 32 * kk);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -879,22 +893,12 @@ __device__ __forceinline__ void bwd_factor_side(const BwdArgs &ba, const StateOu
     const bf16 *sWt = reinterpret_cast<const bf16 *>(smem + C::OFF_A);
     const bf16 *sMi = reinterpret_cast<const bf16 *>(smem + C::OFF_G);
 
-    const bf16 *Wg = reinterpret_cast<const bf16 *>(a.ws_W) + ch * kChunk * DK;
-    // Global operands of dA and of the per-half products, issued before dE so
-    // that their loads are in flight together.  Token rows past the chunk's end
-    // read row 0 (always valid) and are zeroed or skipped where used.
-    MB::frag fWd[4][NKD], fdO[NKD];
-    {
+    // W (every row block, for dA) and the wave's dO rows (for dQhat), loaded
+    // by the state side as it finished.
+    const auto &fWd = st.fWd;
+    MB::frag fdO[NKD];
 #pragma unroll
-        for (int J = 0; J < 4; ++J)
-#pragma unroll
-            for (int kk = 0; kk < NKD; ++kk) fWd[J][kk] = load_frag_packed<bf16>(Wg, DK, J, kk, lane);
-        const bf16 *dout = reinterpret_cast<const bf16 *>(ba.dout);
-        const int row = 16 * I + (lane & 15);
-        const bf16 *src = dout + ((size_t)(tok0 + (row < len ? row : 0)) * H + h) * DK + 8 * (lane >> 4);
-#pragma unroll
-        for (int kk = 0; kk < NKD; ++kk) fdO[kk] = *reinterpret_cast<const MB::frag *>(src + 32 * kk);
-    }
+    for (int kk = 0; kk < NKD; ++kk) fdO[kk] = st.fdO[kk];
 
     // ---- dE = T^T dW (rows of block I), kept in registers and as bf16 --------
     f32x4 dE[NKB];
