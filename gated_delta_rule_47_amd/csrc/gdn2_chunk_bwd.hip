@@ -637,12 +637,12 @@ __device__ __forceinline__ void bwd_state_side(const BwdArgs &ba, StateOut<DK> &
     for (int j = 0; j < 4; ++j) dMa[j] = dAp[j] = zero4();
     const bf16 *Sc = ba.Sc + ch * DK * DV;
     const bf16 *dSc = ba.dSc + ch * DK * DV;
-    // The wave's rows of W, Khat, M^T and T^T, held in registers across the
-    // slabs (reloading them per slab re-reads them from HBM once the working
-    // set of the resident workgroups has left L2).
-    // Khat's rows are columns of the Khat^T image, staged in LDS once.
+    // The wave's rows of W, M^T and T^T, held in registers across the slabs
+    // (reloading them per slab re-reads them from HBM once the working set of
+    // the resident workgroups has left L2).  Khat's rows are columns of the
+    // Khat^T image, staged in LDS once and read per use.
     constexpr int NKG = DK * kChunk / 8 / kThreads;  // granules of Khat^T per thread
-    MB::frag fW[NKD], fKh[NKD], fMt[2], fTt[2];
+    MB::frag fW[NKD], fMt[2], fTt[2];
     {
         granule_t kg[NKG];
 #pragma unroll
@@ -656,9 +656,7 @@ __device__ __forceinline__ void bwd_state_side(const BwdArgs &ba, StateOut<DK> &
         }
 #pragma unroll
         for (int j = 0; j < NKG; ++j) *reinterpret_cast<granule_t *>(sKt + fo_slot(j * kThreads + tid) * 8) = kg[j];
-        __syncthreads();
-#pragma unroll
-        for (int kk = 0; kk < NKD; ++kk) fKh[kk] = load_frag_tr_fo(sKt, kChunk, 32 * kk, 16 * I, lane);
+        // (the first slab's staging barrier orders these stores before their reads)
     }
     // Thread t stages row c = t / TPR of S and dS' (columns CPT (t % TPR) .. of
     // each slab) and accumulates dgl[c] = sum_v dS'[c][v] S[c][v] over the slabs.
@@ -667,15 +665,61 @@ __device__ __forceinline__ void bwd_state_side(const BwdArgs &ba, StateOut<DK> &
     const int srow = tid / TPR, scol = CPT * (tid % TPR);
     float dgp = 0.0f;
 
+    constexpr int NCS = SW / 16;
+    // This lane's row piece (token iq, columns 4 lq4 .. +3 of each 16-column
+    // block) of w and v, and of the dv and dw it writes.
+    const int iq = 16 * I + 4 * (lane >> 4) + (lane & 3), lq4 = 4 * ((lane >> 2) & 3);
+    const size_t oq = ((size_t)(tok0 + (iq < len ? iq : 0)) * H + h) * DV + lq4;
+
+    // A slab's global operands, loaded one slab ahead: the next slab's are
+    // issued as soon as this slab's are staged in LDS, so their latency
+    // overlaps this slab's products.  Thread t holds CPT columns of row
+    // t / TPR of S and dS', NDO dO row pieces (row e / (SW/4), e = t + 256 p;
+    // rows past the chunk read row 0 and are zeroed when staged), and its
+    // lane's U tiles (accumulator order).
+    constexpr int NP8 = CPT / 8, NDO = kChunk * SW / 4 / kThreads;
+    static_assert(NDO * kThreads == kChunk * SW / 4, "dO row pieces split evenly");
+    struct SlabIn {
+        bf16x8 sb[NP8], db[NP8];
+        bf16x4 o4[NDO], u4[NCS];
+    };
+    auto load_slab = [&](SlabIn &x, int v0) {
+#pragma unroll
+        for (int p = 0; p < NP8; ++p) {
+            x.sb[p] = *reinterpret_cast<const bf16x8 *>(Sc + sc_index(srow, v0 + scol + 8 * p, DK));
+            x.db[p] = *reinterpret_cast<const bf16x8 *>(dSc + sc_index(srow, v0 + scol + 8 * p, DK));
+        }
+#pragma unroll
+        for (int p = 0; p < NDO; ++p) {
+            const int e = tid + kThreads * p, i = e / (SW / 4), v4 = 4 * (e % (SW / 4));
+            x.o4[p] = *reinterpret_cast<const bf16x4 *>(dout + ((size_t)(tok0 + (i < len ? i : 0)) * H + h) * DV +
+                                                        v0 + v4);
+        }
+#pragma unroll
+        for (int cb = 0; cb < NCS; ++cb) {
+            x.u4[cb] = *reinterpret_cast<const bf16x4 *>(Ug + (((size_t)I * (DV / 16) + (v0 / 16 + cb)) * 64 + lane) * 4);
+        }
+    };
+    SlabIn cur;
+    load_slab(cur, 0);
+
     for (int sl = 0; sl < C::NSL; ++sl) {
         const int v0 = sl * SW;
-        // S and dS' columns v0..v0+SW, [c][v] (products contracting over c
-        // read them with transposing LDS reads).
+        // w and v row pieces of the slab (rows past the chunk read row 0 and
+        // are not stored), used after the dZ product
+        f32x4 wq[NCS];
+        bf16x4 vq[NCS];
 #pragma unroll
-        for (int p8 = 0; p8 < CPT; p8 += 8) {
-            const int v = scol + p8;
-            const bf16x8 sb = *reinterpret_cast<const bf16x8 *>(Sc + sc_index(srow, v0 + v, DK));
-            const bf16x8 db = *reinterpret_cast<const bf16x8 *>(dSc + sc_index(srow, v0 + v, DK));
+        for (int cb = 0; cb < NCS; ++cb) {
+            wq[cb] = *reinterpret_cast<const f32x4 *>(a.w + oq + v0 + 16 * cb);
+            vq[cb] = *reinterpret_cast<const bf16x4 *>(vin + oq + v0 + 16 * cb);
+        }
+        // S and dS' columns v0..v0+SW, [c][v] (products contracting over c
+        // read them with transposing LDS reads); dO rows [i][v].
+#pragma unroll
+        for (int p = 0; p < NP8; ++p) {
+            const int v = scol + 8 * p;
+            const bf16x8 sb = cur.sb[p], db = cur.db[p];
 #pragma unroll
             for (int t = 0; t < 8; ++t) dgp += static_cast<float>(sb[t]) * static_cast<float>(db[t]);
             *reinterpret_cast<bf16x4 *>(sS + srow * LSW + v) = bf16x4{sb[0], sb[1], sb[2], sb[3]};
@@ -683,25 +727,19 @@ __device__ __forceinline__ void bwd_state_side(const BwdArgs &ba, StateOut<DK> &
             *reinterpret_cast<bf16x4 *>(sdS + srow * LSW + v) = bf16x4{db[0], db[1], db[2], db[3]};
             *reinterpret_cast<bf16x4 *>(sdS + srow * LSW + v + 4) = bf16x4{db[4], db[5], db[6], db[7]};
         }
-        // dO rows (zero past the chunk), [i][v]; U, [j][v].
-        for (int e = tid; e < kChunk * SW / 4; e += kThreads) {
-            const int i = e / (SW / 4), v4 = 4 * (e % (SW / 4));
-            bf16x4 o4;
-            if (i < len) {
-                o4 = *reinterpret_cast<const bf16x4 *>(dout + ((size_t)(tok0 + i) * H + h) * DV + v0 + v4);
-            } else {
+#pragma unroll
+        for (int p = 0; p < NDO; ++p) {
+            const int e = tid + kThreads * p, i = e / (SW / 4), v4 = 4 * (e % (SW / 4));
+            bf16x4 o4 = cur.o4[p];
+            if (i >= len) {
 #pragma unroll
                 for (int t = 0; t < 4; ++t) o4[t] = static_cast<bf16>(0.0f);
             }
             *reinterpret_cast<bf16x4 *>(sdO + i * LSW + v4) = o4;
-            // U in accumulator order: [I][cb][lane][r] = U[16I + 4(lane/16) + r][16cb + lane%16]
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int col = v0 + v4 + t, ul = 16 * ((i & 15) >> 2) + (col & 15);
-                sU[i * LSW + v4 + t] = Ug[(((size_t)(i >> 4) * (DV / 16) + (col >> 4)) * 64 + ul) * 4 + (i & 3)];
-            }
         }
         __syncthreads();
+        SlabIn nxt;
+        if (sl + 1 < C::NSL) load_slab(nxt, v0 + SW);
 
         // U_eff = U - W S and dU_eff = M^T dO + Khat dS' on this slab (rows of block I).
 #pragma unroll
@@ -710,63 +748,50 @@ __device__ __forceinline__ void bwd_state_side(const BwdArgs &ba, StateOut<DK> &
 #pragma unroll
             for (int kk = 0; kk < NKD; ++kk) {
                 ws = MB::mma(fW[kk], load_frag_tr(sS, LSW, 32 * kk, 16 * cb, lane), ws);
-                du = MB::mma(fKh[kk], load_frag_tr(sdS, LSW, 32 * kk, 16 * cb, lane), du);
+                du = MB::mma(load_frag_tr_fo(sKt, kChunk, 32 * kk, 16 * I, lane),
+                             load_frag_tr(sdS, LSW, 32 * kk, 16 * cb, lane), du);
             }
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
                 du = MB::mma(fMt[kk], load_frag_tr(sdO, LSW, 32 * kk, 16 * cb, lane), du);
-            // U tile in accumulator order straight from the workspace.
-            const bf16x4 u4 = *reinterpret_cast<const bf16x4 *>(
-                Ug + (((size_t)I * (DV / 16) + (v0 / 16 + cb)) * 64 + lane) * 4);
-            f32x4 ue;
+            // U tile in accumulator order straight from the workspace (also
+            // kept as rows [j][v] for dZ U^T).
+            const bf16x4 u4 = cur.u4[cb];
+            f32x4 ue, uf;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) ue[r] = static_cast<float>(u4[r]) - ws[r];
+            for (int r = 0; r < 4; ++r) {
+                uf[r] = static_cast<float>(u4[r]);
+                ue[r] = uf[r] - ws[r];
+            }
+            store_tile<bf16>(sU + 16 * I * LSW + 16 * cb, LSW, uf, lane);
             store_tile<bf16>(sUe + 16 * I * LSW + 16 * cb, LSW, ue, lane);
             store_tile<bf16>(sdU + 16 * I * LSW + 16 * cb, LSW, du, lane);
             store_tile_t<bf16>(sdUt + 16 * cb * L64 + 16 * I, L64, du, lane);
         }
         __syncthreads();
 
-        // dZ = T^T dU_eff; dv = w dZ, dw = v dZ (w and v of both column blocks
-        // loaded first; rows past the chunk read row 0 and are not stored).
-        {
-            constexpr int NCS = SW / 16;
-            float wv[NCS][4];
-            bf16 vv_[NCS][4];
+        // dZ = T^T dU_eff; dv = w dZ, dw = v dZ as row pieces (dZ quad
+        // transposed: 4 columns of one token per lane, the layout of w and v).
 #pragma unroll
-            for (int cb = 0; cb < NCS; ++cb)
+        for (int cb = 0; cb < NCS; ++cb) {
+            f32x4 dz = zero4();
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int i = 16 * I + 4 * (lane >> 4) + r;
-                    const size_t o = ((size_t)(tok0 + (i < len ? i : 0)) * H + h) * DV + v0 + 16 * cb + (lane & 15);
-                    wv[cb][r] = a.w[o];
-                    vv_[cb][r] = vin[o];
-                }
+            for (int kk = 0; kk < 2; ++kk)
+                dz = MB::mma(fTt[kk], load_frag<bf16>(sdUt + 16 * cb * L64 + 32 * kk, L64, lane), dz);
+            store_tile<bf16>(sdZ + 16 * I * LSW + 16 * cb, LSW, dz, lane);
+            const f32x4 zt = quad_transpose(dz, lane);
+            f32x4 dvv, dwv;
 #pragma unroll
-            for (int cb = 0; cb < NCS; ++cb) {
-                f32x4 dz = zero4();
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk)
-                    dz = MB::mma(fTt[kk],
-                                 load_frag<bf16>(sdUt + 16 * cb * L64 + 32 * kk, L64, lane), dz);
-                store_tile<bf16>(sdZ + 16 * I * LSW + 16 * cb, LSW, dz, lane);
-                // dv and dw as row pieces (quad transpose: 4 columns of one token per lane)
-                f32x4 dvv, dwv;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    dvv[r] = wv[cb][r] * dz[r];
-                    dwv[r] = static_cast<float>(vv_[cb][r]) * dz[r];
-                }
-                const int i = 16 * I + 4 * (lane >> 4) + (lane & 3);
-                const size_t o = ((size_t)(tok0 + (i < len ? i : 0)) * H + h) * DV + v0 + 16 * cb +
-                                 4 * ((lane >> 2) & 3);
-                dvv = quad_transpose(dvv, lane);
-                if (i < len)
-                    *reinterpret_cast<bf16x4 *>(dv + o) =
-                        bf16x4{static_cast<bf16>(dvv[0]), static_cast<bf16>(dvv[1]), static_cast<bf16>(dvv[2]),
-                               static_cast<bf16>(dvv[3])};
-                dwv = quad_transpose(dwv, lane);
-                if (i < len) *reinterpret_cast<f32x4 *>(ba.dw + o) = dwv;
+            for (int r = 0; r < 4; ++r) {
+                dvv[r] = wq[cb][r] * zt[r];
+                dwv[r] = static_cast<float>(vq[cb][r]) * zt[r];
+            }
+            if (iq < len) {
+                const size_t o = oq + v0 + 16 * cb;
+                *reinterpret_cast<bf16x4 *>(dv + o) =
+                    bf16x4{static_cast<bf16>(dvv[0]), static_cast<bf16>(dvv[1]), static_cast<bf16>(dvv[2]),
+                           static_cast<bf16>(dvv[3])};
+                *reinterpret_cast<f32x4 *>(ba.dw + o) = dwv;
             }
         }
         // Products accumulated over the slabs (k = the slab's 32 columns).
@@ -791,6 +816,7 @@ __device__ __forceinline__ void bwd_state_side(const BwdArgs &ba, StateOut<DK> &
                 dAp[J] = MB::mma(fdZ, load_frag<bf16>(sU + 16 * J * LSW, LSW, lane), dAp[J]);
         }
         __syncthreads();  // before the next slab is staged
+        cur = nxt;
     }
 
     // dgl: the TPR threads staging a row are consecutive lanes.
