@@ -10,10 +10,9 @@
 //   forward   U_eff = U - W S,  O = Qhat S + M U_eff,  S' = Diag(gl) S + Khat^T U_eff
 //   reverse   dU_eff = M^T dO + Khat dS'
 //             dS     = Diag(gl) dS' + Qhat^T dO - W^T dU_eff        (carried to the previous chunk)
-//   state side   dQhat = dO S^T,  dW = -dU_eff S^T,  dKhat = U_eff dS'^T,
-//                dM = tril(dO U_eff^T),  dgl = rowsum(dS' * S),  dZ = T^T dU_eff,
-//                dv = w * dZ,  dw = v * dZ
-//   factor side  dE = T^T dW,  dA = -strict_tril(dZ U^T + dE W^T),
+//   state side   dW = -dU_eff S^T,  dKhat = U_eff dS'^T,  dM = tril(dO U_eff^T),
+//                dgl = rowsum(dS' * S),  dZ = T^T dU_eff,  dv = w * dZ,  dw = v * dZ
+//   factor side  dQhat = dO S^T,  dE = T^T dW,  dA = -strict_tril(dZ U^T + dE W^T),
 //                dEp = dA Kp,  dQp = dM Kp,  dKp = dA^T Ep + dM^T Qp
 // where T = (I + A)^-1, W = T E, U = T Z, E = gamma*b*k, Z = w*v, and Ep, Kp, Qp
 // are the midpoint-scaled tiles of the forward (A = strict_tril(Ep Kp^T),
@@ -531,8 +530,9 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_bwd_rev2_kernel(BwdArgs
 // Every operand is staged in LDS in the orientation its fragment load wants
 // (k contiguous), transposing on the way in where needed; S and dS' are
 // staged once, [c][v], and read through transposing LDS reads where the
-// contraction runs over c.  Wave w owns token rows 16w .. 16w+15 of every
-// 64-row result.
+// contraction runs over c.  A slab's global operands are loaded during the
+// previous slab.  Wave w owns token rows 16w .. 16w+15 of every 64-row
+// result.
 // ---------------------------------------------------------------------------
 template <int DK>
 struct StateCfg {
