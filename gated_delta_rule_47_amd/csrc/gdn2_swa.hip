@@ -55,16 +55,48 @@ __device__ __forceinline__ int v_chunk(int r, int c) { return c ^ ((2 * r) & (Sw
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
-// Issue the direct global->LDS loads of key tile [k0, k0+BN) (rows clamped
-// to the sequence; rows past it are masked by the caller).  Wave w fills
-// chunks [(w*LOADS + i)*64, +64) of each tile, lane t chunk +t.
+// The direct global->LDS loads of key tile [k0, k0+BN).  Wave w fills
+// chunks [(w*LOADS + i)*64, +64) of each tile, lane t chunk +t.  A lane's
+// element offsets from the tile's first key row do not change from tile to
+// tile, so they are formed once; a tile that runs past the sequence's end
+// (its last one) takes the rows clamped to the sequence instead (rows past
+// it are masked by the caller).
 template <int D>
-__device__ __forceinline__ void swa_issue(const SwaArgs &a, int h, int s0, int s1, int k0,
-                                          bf16 *tK, bf16 *tV, int wave, int lane) {
+struct SwaFeed {
+    unsigned offK[SwaCfg<D>::LOADS], offV[SwaCfg<D>::LOADS];
+};
+
+template <int D>
+__device__ __forceinline__ SwaFeed<D> swa_feed(const SwaArgs &a, int h, int wave, int lane) {
+    using C = SwaCfg<D>;
+    SwaFeed<D> f;
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i) {
+        const int p = (wave * C::LOADS + i) * 64 + lane, row = p / C::CPR, pc = p % C::CPR;
+        const unsigned r0 = (unsigned)row * (unsigned)a.ldkv + (unsigned)(h * D);
+        f.offK[i] = r0 + 8 * k_chunk<D>(row, pc);
+        f.offV[i] = r0 + 8 * v_chunk<D>(row, pc);
+    }
+    return f;
+}
+
+template <int D>
+__device__ __forceinline__ void swa_issue(const SwaArgs &a, const SwaFeed<D> &f, int h, int s0, int s1,
+                                          int k0, bf16 *tK, bf16 *tV, int wave, int lane) {
     using C = SwaCfg<D>;
     const bf16 *K = reinterpret_cast<const bf16 *>(a.k);
     const bf16 *V = reinterpret_cast<const bf16 *>(a.v);
     const size_t ld = (size_t)a.ldkv;
+    if (k0 + C::BN <= s1) {  // every row inside the sequence
+        const bf16 *Kb = K + (size_t)k0 * ld, *Vb = V + (size_t)k0 * ld;
+#pragma unroll
+        for (int i = 0; i < C::LOADS; ++i) {
+            const int base = (wave * C::LOADS + i) * 64;
+            __builtin_amdgcn_global_load_lds(Kb + f.offK[i], (lds_void *)(tK + 8 * base), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(Vb + f.offV[i], (lds_void *)(tV + 8 * base), 16, 0, 0);
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
         const int base = (wave * C::LOADS + i) * 64, p = base + lane;
@@ -83,7 +115,9 @@ __global__ __launch_bounds__(kThreads, 2) void swa_fwd_kernel(SwaArgs a) {
     using C = SwaCfg<D>;
     using MB = Mma<bf16>;
     __shared__ __attribute__((aligned(16))) bf16 smem[4 * C::SZ];  // 2 x (K tile, V tile)
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // (the wave index as a uniform value: the LDS addresses of the direct
+    // loads are then formed in scalar registers)
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 15, grp = lane >> 4;
 
     // XCD-contiguous work mapping: work item w = (sequence, head, query block)
@@ -147,7 +181,8 @@ __global__ __launch_bounds__(kThreads, 2) void swa_fwd_kernel(SwaArgs a) {
     float m_run[2] = {-1e30f, -1e30f}, l_run[2] = {0.0f, 0.0f};
     const float cs = a.scale * kLog2eF;  // scores in base-2 units
 
-    swa_issue<D>(a, h, s0, s1, kstart, smem, smem + C::SZ, wave, lane);
+    const SwaFeed<D> feed = swa_feed<D>(a, h, wave, lane);
+    swa_issue<D>(a, feed, h, s0, s1, kstart, smem, smem + C::SZ, wave, lane);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
@@ -218,7 +253,7 @@ __global__ __launch_bounds__(kThreads, 2) void swa_fwd_kernel(SwaArgs a) {
         // softmax and the first group of MFMAs.
         if (j + 1 < ntiles) {
             bf16 *nK = smem + ((j + 1) & 1) * BUF;
-            swa_issue<D>(a, h, s0, s1, k0 + C::BN, nK, nK + C::SZ, wave, lane);
+            swa_issue<D>(a, feed, h, s0, s1, k0 + C::BN, nK, nK + C::SZ, wave, lane);
         }
         // mask the tile unless every key is inside every query's window
         const bool full = (k0 + C::BN - 1 <= wq0) && (k0 > wq_hi - W);
