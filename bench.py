@@ -395,6 +395,67 @@ def time_bwd(d, inp, steps, warmup):
     return e0.elapsed_time(e1) / steps, ws.numel()
 
 
+def time_train(d, inp, steps, warmup):
+    """A training step's chunk core both ways: gdn2_chunk_fwd + gdn2_chunk_bwd
+    (the backward recomputes the forward's factors and states) against
+    gdn2_chunk_fwd_train + gdn2_chunk_bwd_saved (the backward reuses them).
+    Events on the launch stream around each call; returns a dict of ms."""
+    import torch
+    import gated_delta_rule_47_amd as g
+    import workloads as W
+    gr = W.make_chunk_grads(inp, 1)
+    dout = torch.from_numpy(W.bf16_bits(gr["dout"]).view(np.int16)).to("cuda").view(torch.bfloat16)
+    dSf = torch.from_numpy(gr["dS_final"]).to("cuda")
+    x = (d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"])
+    B, T, H, D, N = inp["B"], inp["T"], inp["H"], inp["Dk"], inp["N"]
+    varlen = d["cu_seqlens"] is not None
+    o = torch.empty((B, T, H, D), dtype=d["q"].dtype, device="cuda")
+    S = torch.empty((N, H, D, D), dtype=torch.float32, device="cuda")
+    ws_f = torch.empty(g.gdn2_chunk_fwd_workspace_bytes(N, B, T, H, D, D, g.GDN2_BF16, varlen),
+                       dtype=torch.uint8, device="cuda")
+    ws_b = torch.empty(g.gdn2_chunk_bwd_workspace_bytes(N, B, T, H, D, D, g.GDN2_BF16, varlen),
+                       dtype=torch.uint8, device="cuda")
+    ws_t = torch.empty(g.gdn2_chunk_train_workspace_bytes(N, B, T, H, D, D, g.GDN2_BF16, varlen),
+                       dtype=torch.uint8, device="cuda")
+    kw = dict(S0=d["S0"], cu_seqlens=d["cu_seqlens"])
+
+    def recompute():
+        g.chunk_fwd(*x, **kw, o=o, S_final=S, workspace=ws_f)
+        return g.chunk_bwd(*x, dout, **kw, dS_final=dSf, workspace=ws_b)
+
+    def saved():
+        g.chunk_fwd_train(*x, **kw, o=o, S_final=S, workspace=ws_t)
+        return g.chunk_bwd_saved(*x, dout, ws_t, dS_final=dSf, cu_seqlens=d["cu_seqlens"])
+
+    def timed(f0, f1):
+        for _ in range(warmup):
+            f0()
+            f1()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        for i in range(steps):
+            ev[i][0].record()
+            f0()
+            ev[i][1].record()
+            f1()
+            ev[i][2].record()
+        torch.cuda.synchronize()
+        return (float(np.mean([e[0].elapsed_time(e[1]) for e in ev])),
+                float(np.mean([e[1].elapsed_time(e[2]) for e in ev])))
+
+    fwd_ms, bwd_ms = timed(lambda: g.chunk_fwd(*x, **kw, o=o, S_final=S, workspace=ws_f),
+                           lambda: g.chunk_bwd(*x, dout, **kw, dS_final=dSf, workspace=ws_b))
+    ftr_ms, bsv_ms = timed(lambda: g.chunk_fwd_train(*x, **kw, o=o, S_final=S, workspace=ws_t),
+                           lambda: g.chunk_bwd_saved(*x, dout, ws_t, dS_final=dSf,
+                                                     cu_seqlens=d["cu_seqlens"]))
+    # the two ways give the same gradients
+    a, b = recompute(), saved()
+    torch.cuda.synchronize()
+    assert all(torch.equal(a[n], b[n]) for n in a if a[n] is not None), "training pair differs"
+    return dict(fwd_ms=fwd_ms, bwd_ms=bwd_ms, step_ms=fwd_ms + bwd_ms, fwd_train_ms=ftr_ms,
+                bwd_saved_ms=bsv_ms, train_step_ms=ftr_ms + bsv_ms, workspace_bytes=ws_t.numel())
+
+
 def time_layer(inp, steps, warmup):
     """Time `steps` gdn2_layer_fwd calls on the token-mixer layer workload
     (events on the launch stream).  Returns (ms, workspace bytes)."""
@@ -648,6 +709,20 @@ def main():
         ms, ws_bytes = time_bwd(d, inp, max(3, a.steps // 4), 2)
         tokens = inp["B"] * inp["T"]
         nb = bwd_alg_bytes(tokens * inp["H"], inp["N"] * inp["H"], inp["Dk"], 2)
+        tr = time_train(d, inp, max(3, a.steps // 4), 2)
+        tokens_ = inp["B"] * inp["T"]
+        out["training_step"] = {
+            "workload": wl.name,
+            "recompute": {"entries": "gdn2_chunk_fwd + gdn2_chunk_bwd", "fwd_ms": tr["fwd_ms"],
+                          "bwd_ms": tr["bwd_ms"], "step_ms": tr["step_ms"]},
+            "saved": {"entries": "gdn2_chunk_fwd_train + gdn2_chunk_bwd_saved",
+                      "fwd_ms": tr["fwd_train_ms"], "bwd_ms": tr["bwd_saved_ms"],
+                      "step_ms": tr["train_step_ms"], "workspace_bytes": tr["workspace_bytes"],
+                      "tokens_per_s": tokens_ / (tr["train_step_ms"] * 1e-3)}}
+        log("training step: forward + recomputing backward %.3f + %.3f = %.3f ms; "
+            "training forward + saved-state backward %.3f + %.3f = %.3f ms (%.2f GB kept)"
+            % (tr["fwd_ms"], tr["bwd_ms"], tr["step_ms"], tr["fwd_train_ms"], tr["bwd_saved_ms"],
+               tr["train_step_ms"], tr["workspace_bytes"] / 1e9))
         out["backward"] = {"workload": wl.name, "entry": "gdn2_chunk_bwd", "ms": ms,
                            "tokens_per_s": tokens / (ms * 1e-3), "alg_bytes": nb,
                            "alg_GBps": nb / (ms * 1e-3) / 1e9,

@@ -35,7 +35,8 @@ EXPORTED = ("gdn2_abi_version", "gdn2_status_string", "gdn2_chunk_fwd_workspace_
             "gdn2_chunk_fwd_gate_logits", "gdn2_chunk_bwd_workspace_bytes", "gdn2_chunk_bwd",
             "gdn2_step", "gdn2_layer_fwd_workspace_bytes", "gdn2_layer_fwd",
             "gdn2_swa_fwd_workspace_bytes", "gdn2_swa_fwd", "gdn2_swa_layer_fwd_workspace_bytes",
-            "gdn2_swa_layer_fwd", "gdn2_chunk_fwd_noalloc", "gdn2_device_info")
+            "gdn2_swa_layer_fwd", "gdn2_chunk_fwd_noalloc", "gdn2_device_info",
+            "gdn2_chunk_train_workspace_bytes", "gdn2_chunk_fwd_train", "gdn2_chunk_bwd_saved")
 
 
 class Gdn2Error(RuntimeError):
@@ -95,6 +96,12 @@ def load_library(path=LIB_PATH):
     lib.gdn2_chunk_bwd_workspace_bytes.argtypes = [I] * 8
     lib.gdn2_chunk_bwd.restype = I
     lib.gdn2_chunk_bwd.argtypes = [P] * 17 + [I] * 7 + [P, Z, P]
+    lib.gdn2_chunk_train_workspace_bytes.restype = Z
+    lib.gdn2_chunk_train_workspace_bytes.argtypes = [I] * 8
+    lib.gdn2_chunk_fwd_train.restype = I
+    lib.gdn2_chunk_fwd_train.argtypes = [P] * 10 + [I] * 7 + [P, Z, P]
+    lib.gdn2_chunk_bwd_saved.restype = I
+    lib.gdn2_chunk_bwd_saved.argtypes = [P] * 16 + [I] * 7 + [P, Z, P]
     lib.gdn2_step.restype = I
     lib.gdn2_step.argtypes = [P] * 8 + [I] * 5 + [P]
     lib.gdn2_layer_fwd_workspace_bytes.restype = Z
@@ -224,6 +231,27 @@ def gdn2_chunk_bwd(q, k, v, log_alpha, b, w, S0, dout, dS_final, dq, dk, dv, dlo
     return load_library().gdn2_chunk_bwd(q, k, v, log_alpha, b, w, S0, dout, dS_final, dq, dk,
                                           dv, dlog_alpha, db, dw, dS0, cu_seqlens, N, B, T, H,
                                           Dk, Dv, io, workspace, workspace_bytes, stream)
+
+
+def gdn2_chunk_train_workspace_bytes(N, B, T, H, Dk, Dv, io, varlen):
+    return load_library().gdn2_chunk_train_workspace_bytes(N, B, T, H, Dk, Dv, io, int(varlen))
+
+
+def gdn2_chunk_fwd_train(q, k, v, log_alpha, b, w, S0, o, S_final, cu_seqlens, N, B, T, H, Dk,
+                         Dv, io, workspace, workspace_bytes, stream):
+    """Raw call: every pointer argument is an int (device address) or None."""
+    return load_library().gdn2_chunk_fwd_train(q, k, v, log_alpha, b, w, S0, o, S_final,
+                                                cu_seqlens, N, B, T, H, Dk, Dv, io, workspace,
+                                                workspace_bytes, stream)
+
+
+def gdn2_chunk_bwd_saved(q, k, v, log_alpha, b, w, dout, dS_final, dq, dk, dv, dlog_alpha, db, dw,
+                         dS0, cu_seqlens, N, B, T, H, Dk, Dv, io, workspace, workspace_bytes,
+                         stream):
+    """Raw call: every pointer argument is an int (device address) or None."""
+    return load_library().gdn2_chunk_bwd_saved(q, k, v, log_alpha, b, w, dout, dS_final, dq, dk,
+                                                dv, dlog_alpha, db, dw, dS0, cu_seqlens, N, B, T,
+                                                H, Dk, Dv, io, workspace, workspace_bytes, stream)
 
 
 def gdn2_step(q, k, v, log_alpha, b, w, S, o, B, H, Dk, Dv, io, stream):
@@ -415,6 +443,69 @@ def chunk_bwd(q, k, v, log_alpha, b, w, dout, S0=None, dS_final=None, cu_seqlens
                         io, _ptr(workspace), ws_bytes, _stream(stream))
     if st != GDN2_OK:
         raise Gdn2Error(st, "gdn2_chunk_bwd")
+    return out
+
+
+def chunk_fwd_train(q, k, v, log_alpha, b, w, S0=None, cu_seqlens=None, o=None, S_final=None,
+                    output_final_state=True, workspace=None, stream=None):
+    """chunk_fwd (bf16 only) that also keeps, in `workspace`, what
+    chunk_bwd_saved needs.  Returns (o, S_final, workspace); hold the
+    workspace until the backward."""
+    import torch
+    B, T, H, Dk, Dv, N = _chunk_shapes(q, v, cu_seqlens)
+    io = _io_of(q)
+    dev = q.device
+    tk, tv, st_shape = (B, T, H, Dk), (B, T, H, Dv), (N, H, Dk, Dv)
+    f32 = torch.float32
+    _validate([("q", q, tk, q.dtype), ("k", k, tk, q.dtype), ("v", v, tv, q.dtype),
+               ("o", o, tv, q.dtype), ("log_alpha", log_alpha, tk, f32), ("b", b, tk, f32),
+               ("w", w, tv, f32), ("S0", S0, st_shape, f32), ("S_final", S_final, st_shape, f32)],
+              dev)
+    if o is None:
+        o = torch.empty(tv, dtype=q.dtype, device=dev)
+    if S_final is None and output_final_state:
+        S_final = torch.empty(st_shape, dtype=torch.float32, device=dev)
+    nbytes = gdn2_chunk_train_workspace_bytes(N, B, T, H, Dk, Dv, io, cu_seqlens is not None)
+    if nbytes == 0:
+        raise Gdn2Error(GDN2_ERR_UNSUPPORTED, "gdn2_chunk_train_workspace_bytes")
+    workspace, ws_bytes = _workspace(workspace, nbytes, dev)
+    st = gdn2_chunk_fwd_train(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
+                              _ptr(S0), _ptr(o), _ptr(S_final), _ptr(cu_seqlens), N, B, T, H, Dk,
+                              Dv, io, _ptr(workspace), ws_bytes, _stream(stream))
+    if st != GDN2_OK:
+        raise Gdn2Error(st, "gdn2_chunk_fwd_train")
+    return o, S_final, workspace
+
+
+def chunk_bwd_saved(q, k, v, log_alpha, b, w, dout, workspace, dS_final=None, cu_seqlens=None,
+                    need_dS0=True, stream=None):
+    """chunk_bwd's gradients from the workspace of a chunk_fwd_train call on the
+    same inputs (S0 entered through the saved states).  Returns the dict of
+    chunk_bwd."""
+    import torch
+    B, T, H, Dk, Dv, N = _chunk_shapes(q, v, cu_seqlens)
+    io = _io_of(q)
+    dev = q.device
+    tk, tv, st_shape = (B, T, H, Dk), (B, T, H, Dv), (N, H, Dk, Dv)
+    f32 = torch.float32
+    _validate([("q", q, tk, q.dtype), ("k", k, tk, q.dtype), ("v", v, tv, q.dtype),
+               ("dout", dout, tv, q.dtype), ("log_alpha", log_alpha, tk, f32),
+               ("b", b, tk, f32), ("w", w, tv, f32), ("dS_final", dS_final, st_shape, f32)], dev)
+    if dout is None or workspace is None:
+        raise ValueError("dout and the training forward's workspace are required")
+    out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+               dlog_alpha=torch.empty_like(log_alpha), db=torch.empty_like(b),
+               dw=torch.empty_like(w),
+               dS0=torch.empty(st_shape, dtype=torch.float32, device=dev) if need_dS0 else None)
+    nbytes = gdn2_chunk_train_workspace_bytes(N, B, T, H, Dk, Dv, io, cu_seqlens is not None)
+    workspace, ws_bytes = _workspace(workspace, nbytes, dev)
+    st = gdn2_chunk_bwd_saved(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
+                              _ptr(dout), _ptr(dS_final), _ptr(out["dq"]), _ptr(out["dk"]),
+                              _ptr(out["dv"]), _ptr(out["dlog_alpha"]), _ptr(out["db"]),
+                              _ptr(out["dw"]), _ptr(out["dS0"]), _ptr(cu_seqlens), N, B, T, H, Dk,
+                              Dv, io, _ptr(workspace), ws_bytes, _stream(stream))
+    if st != GDN2_OK:
+        raise Gdn2Error(st, "gdn2_chunk_bwd_saved")
     return out
 
 

@@ -15,7 +15,7 @@ using namespace gdn2;
 
 namespace {
 
-constexpr int kAbiVersion = 2;
+constexpr int kAbiVersion = 3;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -103,6 +103,28 @@ bool bwd_layout(int N, int B, int T, int H, int Dk, int Dv, size_t io_bytes, boo
     return true;
 }
 
+bool train_layout(int N, int B, int T, int H, int Dk, int Dv, size_t io_bytes, bool varlen,
+                  TrainLayout *out) {
+    TrainLayout L;
+    if (!workspace_layout(N, B, T, H, Dk, Dv, io_bytes, varlen, &L.fwd)) return false;
+    const size_t chd = (size_t)L.fwd.max_chunks * (size_t)H;
+    size_t off = align_up(L.fwd.total);  // (the T slot of the forward's layout is not used)
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off = align_up(off + bytes);
+        return at;
+    };
+    L.off_Mt = take(chd * kChunk * kChunk * io_bytes);
+    L.off_Qt = take(chd * Dk * kChunk * io_bytes);
+    L.off_Tt = take(chd * kChunk * kChunk * io_bytes);
+    L.off_Sc = take(chd * Dk * Dv * 2);
+    L.off_dSc = take(chd * Dk * Dv * 2);
+    L.off_dKh = take(chd * kChunk * Dk * 2);
+    L.total = off;
+    *out = L;
+    return true;
+}
+
 bool bwd_f32_layout(int N, int B, int T, int H, int Dk, int Dv, bool varlen, BwdF32Layout *out) {
     BwdF32Layout L;
     if (!workspace_layout(N, B, T, H, Dk, Dv, sizeof(float), varlen, &L.fwd)) return false;
@@ -184,13 +206,15 @@ int gdn2_chunk_fwd_workspace_layout(int N, int B, int T, int H, int Dk, int Dv, 
 }  // extern "C"
 
 // The chunk forward; gate_logits selects bf16 gate inputs (log alpha and the
-// logits of b and w) instead of fp32 gates.
+// logits of b and w) instead of fp32 gates.  train: the workspace has the
+// TrainLayout, and the forward also keeps there what a later backward reads
+// (the transposed factors and every chunk's incoming state).
 static int chunk_fwd_impl(const void *q, const void *k, const void *v, const void *log_alpha,
                           const void *b, const void *w, const float *S0, void *o, float *S_final,
                           const int32_t *cu_seqlens, int N, int B, int T, int H, int Dk, int Dv,
                           int io, void *workspace, size_t workspace_bytes, void *stream_ptr,
                           int stages, bool gate_logits, const float *alpha_bias = nullptr,
-                          long long ld_gate = 0) {
+                          long long ld_gate = 0, bool train = false) {
     if (stages & ~(GDN2_STAGE_ALL | GDN2_STAGE_STORE_T)) return GDN2_ERR_INVALID_ARGUMENT;
     if (io != GDN2_F32 && io != GDN2_BF16) return GDN2_ERR_INVALID_ARGUMENT;
     if (N < 0 || B < 0 || T < 0 || H < 0 || Dk <= 0 || Dv <= 0) return GDN2_ERR_INVALID_ARGUMENT;
@@ -214,10 +238,15 @@ static int chunk_fwd_impl(const void *q, const void *k, const void *v, const voi
         return GDN2_ERR_INVALID_ARGUMENT;
 
     WorkspaceLayout L;
-    if (!workspace_layout(N, B, T, H, Dk, Dv, io_size(io), varlen, &L))
+    TrainLayout TL;
+    if (train) {
+        if (!train_layout(N, B, T, H, Dk, Dv, io_size(io), varlen, &TL)) return GDN2_ERR_INVALID_ARGUMENT;
+        L = TL.fwd;
+    } else if (!workspace_layout(N, B, T, H, Dk, Dv, io_size(io), varlen, &L)) {
         return GDN2_ERR_INVALID_ARGUMENT;
-    const bool store_T = (stages & GDN2_STAGE_STORE_T) && (stages & GDN2_STAGE_FACTORS);
-    const size_t need = store_T ? L.total_T : L.total;
+    }
+    const bool store_T = !train && (stages & GDN2_STAGE_STORE_T) && (stages & GDN2_STAGE_FACTORS);
+    const size_t need = train ? TL.total : store_T ? L.total_T : L.total;
     if (need > 0 && (!workspace || workspace_bytes < need)) return GDN2_ERR_WORKSPACE;
     if (workspace && (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)))
         return GDN2_ERR_WORKSPACE;
@@ -254,6 +283,12 @@ static int chunk_fwd_impl(const void *q, const void *k, const void *v, const voi
     a.ws_U = ws + L.off_U;
     a.store_T = store_T ? 1 : 0;
     a.ws_gl = reinterpret_cast<float *>(ws + L.off_gl);
+    if (train) {  // both factor sets, and o together with every chunk's incoming state
+        a.ws_Mt = ws + TL.off_Mt;
+        a.ws_Qt = ws + TL.off_Qt;
+        a.ws_Tt = ws + TL.off_Tt;
+        a.ws_Sc = reinterpret_cast<bf16_t *>(ws + TL.off_Sc);
+    }
     const bool bf = io == GDN2_BF16;
 
     hipError_t err = hipSuccess;
@@ -282,6 +317,24 @@ int gdn2_chunk_fwd(const void *q, const void *k, const void *v, const float *log
                    void *workspace, size_t workspace_bytes, void *stream_ptr) {
     return chunk_fwd_impl(q, k, v, log_alpha, b, w, S0, o, S_final, cu_seqlens, N, B, T, H, Dk, Dv,
                           io, workspace, workspace_bytes, stream_ptr, GDN2_STAGE_ALL, false);
+}
+
+size_t gdn2_chunk_train_workspace_bytes(int N, int B, int T, int H, int Dk, int Dv, int io,
+                                        int varlen) {
+    if (io != GDN2_BF16) return 0;
+    TrainLayout L;
+    if (!train_layout(N, B, T, H, Dk, Dv, io_size(io), varlen != 0, &L)) return 0;
+    return L.total;
+}
+
+int gdn2_chunk_fwd_train(const void *q, const void *k, const void *v, const float *log_alpha,
+                         const float *b, const float *w, const float *S0, void *o, float *S_final,
+                         const int32_t *cu_seqlens, int N, int B, int T, int H, int Dk, int Dv,
+                         int io, void *workspace, size_t workspace_bytes, void *stream_ptr) {
+    if (io == GDN2_F32) return GDN2_ERR_UNSUPPORTED;  // (fp32 I/O backs the reference path only)
+    return chunk_fwd_impl(q, k, v, log_alpha, b, w, S0, o, S_final, cu_seqlens, N, B, T, H, Dk, Dv,
+                          io, workspace, workspace_bytes, stream_ptr, GDN2_STAGE_ALL, false, nullptr,
+                          0, true);
 }
 
 }  // extern "C"
@@ -431,32 +484,23 @@ static int chunk_bwd_f32(const void *q, const void *k, const void *v, const floa
     return finish(err, stream);
 }
 
-extern "C" {
-
-size_t gdn2_chunk_bwd_workspace_bytes(int N, int B, int T, int H, int Dk, int Dv, int io,
-                                      int varlen) {
-    if (io != GDN2_F32 && io != GDN2_BF16) return 0;
-    if (io == GDN2_F32) {
-        BwdF32Layout L32;
-        return bwd_f32_layout(N, B, T, H, Dk, Dv, varlen != 0, &L32) ? L32.total : 0;
-    }
-    BwdLayout L;
-    if (!bwd_layout(N, B, T, H, Dk, Dv, io_size(io), varlen != 0, &L)) return 0;
-    return L.total;
-}
-
-int gdn2_chunk_bwd(const void *q, const void *k, const void *v, const float *log_alpha,
-                   const float *b, const float *w, const float *S0, const void *dout,
-                   const float *dS_final, void *dq, void *dk, void *dv, float *dlog_alpha,
-                   float *db, float *dw, float *dS0, const int32_t *cu_seqlens, int N, int B, int T,
-                   int H, int Dk, int Dv, int io, void *workspace, size_t workspace_bytes,
-                   void *stream_ptr) {
+// Argument checks shared by the backward entry points (S0 may be NULL);
+// *empty is set when the call has nothing to compute.
+static int check_bwd_args(const void *q, const void *k, const void *v, const float *log_alpha,
+                          const float *b, const float *w, const float *S0, const void *dout,
+                          const float *dS_final, void *dq, void *dk, void *dv, float *dlog_alpha,
+                          float *db, float *dw, float *dS0, const int32_t *cu_seqlens, int N, int B,
+                          int T, int H, int Dk, int Dv, int io, bool *empty) {
+    *empty = false;
     if (io != GDN2_F32 && io != GDN2_BF16) return GDN2_ERR_INVALID_ARGUMENT;
     if (N < 0 || B < 0 || T < 0 || H < 0 || Dk <= 0 || Dv <= 0) return GDN2_ERR_INVALID_ARGUMENT;
     if (!supported_dims(Dk, Dv)) return GDN2_ERR_UNSUPPORTED;
     const bool varlen = cu_seqlens != nullptr;
     if (varlen ? B != 1 : N != B) return GDN2_ERR_INVALID_ARGUMENT;
-    if (N == 0 || H == 0) return GDN2_OK;
+    if (N == 0 || H == 0) {
+        *empty = true;
+        return GDN2_OK;
+    }
     if ((long long)B * T > INT_MAX / 2) return GDN2_ERR_UNSUPPORTED;
     const void *ins[] = {q, k, v, log_alpha, b, w, dout};
     const void *outs[] = {dq, dk, dv, dlog_alpha, db, dw};
@@ -481,20 +525,26 @@ int gdn2_chunk_bwd(const void *q, const void *k, const void *v, const float *log
         for (const void *p : all_in)
             if (all_out[i] == p) return GDN2_ERR_INVALID_ARGUMENT;
     }
+    return GDN2_OK;
+}
 
-    if (io == GDN2_F32)
-        return chunk_bwd_f32(q, k, v, log_alpha, b, w, S0, dout, dS_final, dq, dk, dv, dlog_alpha,
-                             db, dw, dS0, cu_seqlens, N, B, T, H, Dk, Dv, workspace,
-                             workspace_bytes, stream_ptr);
-    BwdLayout L;
-    if (!bwd_layout(N, B, T, H, Dk, Dv, io_size(io), varlen, &L)) return GDN2_ERR_INVALID_ARGUMENT;
-    if (!workspace || workspace_bytes < L.total) return GDN2_ERR_WORKSPACE;
-    if (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) return GDN2_ERR_WORKSPACE;
+// Byte offsets of the backward's own slots in a workspace.
+struct BwdSlots {
+    size_t Mt, Qt, Tt, Sc, dSc, dKh;
+};
 
+// The bf16 backward on a checked call.  recompute: first rebuild the chunk
+// table, the chunk factors (with their transposes) and every chunk's incoming
+// state; otherwise they are read as a training forward left them.
+static int chunk_bwd_bf16(const void *q, const void *k, const void *v, const float *log_alpha,
+                          const float *b, const float *w, const float *S0, const void *dout,
+                          const float *dS_final, void *dq, void *dk, void *dv, float *dlog_alpha,
+                          float *db, float *dw, float *dS0, const int32_t *cu_seqlens, int N, int B,
+                          int T, int H, int Dk, const WorkspaceLayout &F, const BwdSlots &sl, char *ws,
+                          bool recompute, void *stream_ptr) {
+    const bool varlen = cu_seqlens != nullptr;
     hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
     (void)hipGetLastError();  // a stale error left by other code is not ours to report
-    char *ws = static_cast<char *>(workspace);
-    const WorkspaceLayout &F = L.fwd;
     BwdArgs ba{};
     ChunkArgs &a = ba.c;
     a.q = q;
@@ -514,7 +564,7 @@ int gdn2_chunk_bwd(const void *q, const void *k, const void *v, const float *log
     a.NC = (T + kChunk - 1) / kChunk;
     a.max_chunks = F.max_chunks;
     a.plan = varlen ? reinterpret_cast<int32_t *>(ws + F.off_plan) : nullptr;
-    a.ws_T = nullptr;  // a backward call has no T, Qhat or M slots
+    a.ws_T = nullptr;  // the backward kernels read neither T, Qhat nor M
     a.ws_W = ws + F.off_W;
     a.ws_Qh = nullptr;
     a.ws_KhT = ws + F.off_KhT;
@@ -522,10 +572,10 @@ int gdn2_chunk_bwd(const void *q, const void *k, const void *v, const float *log
     a.ws_U = ws + F.off_U;
     a.ws_gl = reinterpret_cast<float *>(ws + F.off_gl);
     a.store_T = 0;  // the backward kernels read T^T (ws_Tt) only
-    a.ws_Sc = reinterpret_cast<bf16_t *>(ws + L.off_Sc);
-    a.ws_Mt = ws + L.off_Mt;
-    a.ws_Qt = ws + L.off_Qt;
-    a.ws_Tt = ws + L.off_Tt;
+    a.ws_Sc = reinterpret_cast<bf16_t *>(ws + sl.Sc);
+    a.ws_Mt = ws + sl.Mt;
+    a.ws_Qt = ws + sl.Qt;
+    a.ws_Tt = ws + sl.Tt;
     ba.dout = dout;
     ba.dS_final = dS_final;
     ba.dq = dq;
@@ -536,15 +586,77 @@ int gdn2_chunk_bwd(const void *q, const void *k, const void *v, const float *log
     ba.dw = dw;
     ba.dS0 = dS0;
     ba.Sc = a.ws_Sc;
-    ba.dSc = reinterpret_cast<bf16_t *>(ws + L.off_dSc);
-    ba.dKh = reinterpret_cast<bf16_t *>(ws + L.off_dKh);
+    ba.dSc = reinterpret_cast<bf16_t *>(ws + sl.dSc);
+    ba.dKh = reinterpret_cast<bf16_t *>(ws + sl.dKh);
 
     hipError_t err = hipSuccess;
-    if (varlen) err = launch_plan(a, stream);
-    if (err == hipSuccess && F.max_chunks > 0) err = launch_chunk_prep(a, Dk, true, stream);
-    if (err == hipSuccess && F.max_chunks > 0) err = launch_chunk_prop(a, Dk, true, stream);
+    if (recompute) {
+        if (varlen) err = launch_plan(a, stream);
+        if (err == hipSuccess && F.max_chunks > 0) err = launch_chunk_prep(a, Dk, true, stream);
+        if (err == hipSuccess && F.max_chunks > 0) err = launch_chunk_prop(a, Dk, true, stream);
+    }
     if (err == hipSuccess) err = launch_chunk_bwd(ba, Dk, stream);
     return finish(err, stream);
+}
+
+extern "C" {
+
+size_t gdn2_chunk_bwd_workspace_bytes(int N, int B, int T, int H, int Dk, int Dv, int io,
+                                      int varlen) {
+    if (io != GDN2_F32 && io != GDN2_BF16) return 0;
+    if (io == GDN2_F32) {
+        BwdF32Layout L32;
+        return bwd_f32_layout(N, B, T, H, Dk, Dv, varlen != 0, &L32) ? L32.total : 0;
+    }
+    BwdLayout L;
+    if (!bwd_layout(N, B, T, H, Dk, Dv, io_size(io), varlen != 0, &L)) return 0;
+    return L.total;
+}
+
+int gdn2_chunk_bwd(const void *q, const void *k, const void *v, const float *log_alpha,
+                   const float *b, const float *w, const float *S0, const void *dout,
+                   const float *dS_final, void *dq, void *dk, void *dv, float *dlog_alpha,
+                   float *db, float *dw, float *dS0, const int32_t *cu_seqlens, int N, int B, int T,
+                   int H, int Dk, int Dv, int io, void *workspace, size_t workspace_bytes,
+                   void *stream_ptr) {
+    bool empty = false;
+    const int st = check_bwd_args(q, k, v, log_alpha, b, w, S0, dout, dS_final, dq, dk, dv,
+                                  dlog_alpha, db, dw, dS0, cu_seqlens, N, B, T, H, Dk, Dv, io, &empty);
+    if (st != GDN2_OK || empty) return st;
+    const bool varlen = cu_seqlens != nullptr;
+    if (io == GDN2_F32)
+        return chunk_bwd_f32(q, k, v, log_alpha, b, w, S0, dout, dS_final, dq, dk, dv, dlog_alpha,
+                             db, dw, dS0, cu_seqlens, N, B, T, H, Dk, Dv, workspace,
+                             workspace_bytes, stream_ptr);
+    BwdLayout L;
+    if (!bwd_layout(N, B, T, H, Dk, Dv, io_size(io), varlen, &L)) return GDN2_ERR_INVALID_ARGUMENT;
+    if (!workspace || workspace_bytes < L.total) return GDN2_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) return GDN2_ERR_WORKSPACE;
+    const BwdSlots sl{L.off_Mt, L.off_Qt, L.off_Tt, L.off_Sc, L.off_dSc, L.off_dKh};
+    return chunk_bwd_bf16(q, k, v, log_alpha, b, w, S0, dout, dS_final, dq, dk, dv, dlog_alpha, db,
+                          dw, dS0, cu_seqlens, N, B, T, H, Dk, L.fwd, sl, static_cast<char *>(workspace),
+                          true, stream_ptr);
+}
+
+int gdn2_chunk_bwd_saved(const void *q, const void *k, const void *v, const float *log_alpha,
+                         const float *b, const float *w, const void *dout, const float *dS_final,
+                         void *dq, void *dk, void *dv, float *dlog_alpha, float *db, float *dw,
+                         float *dS0, const int32_t *cu_seqlens, int N, int B, int T, int H, int Dk,
+                         int Dv, int io, void *workspace, size_t workspace_bytes, void *stream_ptr) {
+    bool empty = false;
+    const int st = check_bwd_args(q, k, v, log_alpha, b, w, nullptr, dout, dS_final, dq, dk, dv,
+                                  dlog_alpha, db, dw, dS0, cu_seqlens, N, B, T, H, Dk, Dv, io, &empty);
+    if (st != GDN2_OK || empty) return st;
+    if (io != GDN2_BF16) return GDN2_ERR_UNSUPPORTED;
+    TrainLayout L;
+    if (!train_layout(N, B, T, H, Dk, Dv, io_size(io), cu_seqlens != nullptr, &L))
+        return GDN2_ERR_INVALID_ARGUMENT;
+    if (!workspace || workspace_bytes < L.total) return GDN2_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) return GDN2_ERR_WORKSPACE;
+    const BwdSlots sl{L.off_Mt, L.off_Qt, L.off_Tt, L.off_Sc, L.off_dSc, L.off_dKh};
+    return chunk_bwd_bf16(q, k, v, log_alpha, b, w, nullptr, dout, dS_final, dq, dk, dv, dlog_alpha,
+                          db, dw, dS0, cu_seqlens, N, B, T, H, Dk, L.fwd, sl,
+                          static_cast<char *>(workspace), false, stream_ptr);
 }
 
 int gdn2_step(const void *q, const void *k, const void *v, const float *log_alpha, const float *b,

@@ -251,15 +251,18 @@ __device__ __forceinline__ float sigmoid1(float x) {
 
 // kBwd: also write the transposed factors a backward call needs (a.ws_Mt,
 // ws_Qt, ws_Tt), and not Qhat or M, which only o needs (its kernels read
-// Khat and W^T from Khat^T and W with transposing LDS reads).
+// Khat and W^T from Khat^T and W with transposing LDS reads).  kBoth (with
+// kBwd): write both sets, for a forward whose factors a later backward reuses.
 // kLogits: the gates arrive as bf16 -- log alpha itself and the logits of b
 // and w, whose sigmoid is taken here.  kAlphaLogit (with kLogits): log_alpha
 // holds logits too, and log alpha = logsigmoid(logit + a.alpha_bias).
 // Two workgroups per CU where their LDS fits (fp32 with 128-wide heads needs
 // over 80 KB, so one workgroup runs per CU and may use all of its registers).
-template <typename E, int DK, bool kBwd, bool kLogits = false, bool kAlphaLogit = false>
+template <typename E, int DK, bool kBwd, bool kLogits = false, bool kAlphaLogit = false, bool kBoth = false>
 __global__ __launch_bounds__(kThreads, (PrepCfg<E, DK>::SMEM <= 80 * 1024 ? 2 : 1)) void chunk_prep_kernel(ChunkArgs a) {
     using C = PrepCfg<E, DK>;
+    constexpr bool kFwdOut = !kBwd || kBoth;  // Qhat and M (for o)
+    constexpr bool kBwdOut = kBwd || kBoth;   // M^T, Qhat^T, T^T (for a backward)
     using M = Mma<E>;
     constexpr int TPG = C::TPG, LDT = C::LDT, LDC = C::LDC, LDA = C::LDA, LDX = C::LDX;
     __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
@@ -372,7 +375,7 @@ __global__ __launch_bounds__(kThreads, (PrepCfg<E, DK>::SMEM <= 80 * 1024 ? 2 : 
     for (int c = 0; c < 4; ++c) egr[c] = __expf(gr[c]);
 
     // ---- scaled tiles --------------------------------------------------------
-    E *Qh = kBwd ? nullptr : reinterpret_cast<E *>(a.ws_Qh) + ch * kChunk * DK;
+    E *Qh = kFwdOut ? reinterpret_cast<E *>(a.ws_Qh) + ch * kChunk * DK : nullptr;
     E *KhT = reinterpret_cast<E *>(a.ws_KhT) + ch * DK * kChunk;
     Vec4<E> qp[TPG], qh[TPG];
 #pragma unroll
@@ -409,7 +412,7 @@ __global__ __launch_bounds__(kThreads, (PrepCfg<E, DK>::SMEM <= 80 * 1024 ? 2 : 
         for (int j = 0; j < TPG; ++j) et[j] = bk[j][c];
         store_run_et<E, TPG>(sEt + (c0 + c) * LDC, c0 + c, tg * TPG, et);
     }
-    if constexpr (kBwd) {  // backward calls: Qhat^T, fragment order
+    if constexpr (kBwdOut) {  // backward calls: Qhat^T, fragment order
         E *QtG = reinterpret_cast<E *>(a.ws_Qt) + ch * DK * kChunk;
 #pragma unroll
         for (int c = 0; c < 4; ++c)
@@ -483,7 +486,7 @@ __global__ __launch_bounds__(kThreads, (PrepCfg<E, DK>::SMEM <= 80 * 1024 ? 2 : 
 #pragma unroll
     for (int j = 0; j < TPG; ++j) *reinterpret_cast<Vec4<E> *>(sX + (tg * TPG + j) * LDT + c0) = qp[j];
     // (A backward call needs neither Qhat nor M: its propagation forms no o.)
-    if constexpr (kBwd) {
+    if constexpr (!kFwdOut) {
     } else if constexpr (sizeof(E) == 2) {  // a granule is 8 channels of one token
 #pragma unroll
         for (int j = 0; j < TPG; ++j)
@@ -497,15 +500,15 @@ __global__ __launch_bounds__(kThreads, (PrepCfg<E, DK>::SMEM <= 80 * 1024 ? 2 : 
                     f32x4{qh[m][c], qh[m + 1][c], qh[m + 2][c], qh[m + 3][c]};
     }
     __syncthreads();
-    if constexpr (!kBwd) stage_copy_out<E, C::NG>(Qh, sStg, tid);
-    E *Mg = kBwd ? nullptr : reinterpret_cast<E *>(a.ws_M) + ch * kChunk * kChunk;
+    if constexpr (kFwdOut) stage_copy_out<E, C::NG>(Qh, sStg, tid);
+    E *Mg = kFwdOut ? reinterpret_cast<E *>(a.ws_M) + ch * kChunk * kChunk : nullptr;
 #pragma unroll
     for (int u = 0; u < 3; ++u) {
         const int t = wave + 4 * u;
         if (t < 10) {
             int I, J;
             lower_tile(t, I, J);
-            if constexpr (!kBwd) {
+            if constexpr (kFwdOut) {
                 f32x4 acc = mma_tile<E, DK>(zero4(), sKp + 16 * J * LDT, LDT, sX + 16 * I * LDT, LDT,
                                             lane);
                 const int i = 16 * I + (lane & 15);
@@ -515,7 +518,8 @@ __global__ __launch_bounds__(kThreads, (PrepCfg<E, DK>::SMEM <= 80 * 1024 ? 2 : 
                     acc[r] = j <= i ? acc[r] : 0.0f;
                 }
                 store4_frag_nt<E>(Mg, kChunk, i, 16 * J + 4 * (lane >> 4), acc);
-            } else {  // M^T[j][i] = M[i][j]: the same tile with the operands swapped
+            }
+            if constexpr (kBwdOut) {  // M^T[j][i] = M[i][j]: the same tile with the operands swapped
                 f32x4 t = mma_tile<E, DK>(zero4(), sX + 16 * I * LDT, LDT, sKp + 16 * J * LDT, LDT, lane);
                 const int jj = 16 * J + (lane & 15);
 #pragma unroll
@@ -534,7 +538,7 @@ __global__ __launch_bounds__(kThreads, (PrepCfg<E, DK>::SMEM <= 80 * 1024 ? 2 : 
             // Only the zero blocks inside an operand fragment that also holds
             // elements on or below the diagonal are written (and read): the
             // fragments wholly above it are skipped by the propagation.
-            if constexpr (!kBwd) {
+            if constexpr (kFwdOut) {
                 if (m_frag_used<E>(I, 16 * J)) {
                     // A zero made here: a loop-invariant zero register would be
                     // spilled, and its reload waits for every load in flight.
@@ -543,7 +547,8 @@ __global__ __launch_bounds__(kThreads, (PrepCfg<E, DK>::SMEM <= 80 * 1024 ? 2 : 
                     store4_frag<E>(Mg, kChunk, 16 * I + (lane & 15), 16 * J + 4 * (lane >> 4),
                                    f32x4{z, z, z, z});
                 }
-            } else {  // the zero lower blocks of M^T
+            }
+            if constexpr (kBwdOut) {  // the zero lower blocks of M^T
                 store4_frag<E>(reinterpret_cast<E *>(a.ws_Mt) + ch * kChunk * kChunk, kChunk,
                                16 * J + (lane & 15), 16 * I + 4 * (lane >> 4), zero4());
             }
@@ -656,7 +661,7 @@ __global__ __launch_bounds__(kThreads, (PrepCfg<E, DK>::SMEM <= 80 * 1024 ? 2 : 
         for (int j = 0; j < 16; j += 4)
             *reinterpret_cast<Vec4<E> *>(Tg + j) = *reinterpret_cast<const Vec4<E> *>(sTb + row * LDC + col0 + j);
     }
-    if constexpr (kBwd && sizeof(E) == 2) {  // T^T in fragment order: rows i, columns j = T[j][i]
+    if constexpr (kBwdOut && sizeof(E) == 2) {  // T^T in fragment order: rows i, columns j = T[j][i]
         E *TtG = reinterpret_cast<E *>(a.ws_Tt) + ch * kChunk * kChunk;
         for (int gi = tid; gi < kChunk * kChunk / 8; gi += kThreads) {
             const int blk = gi >> 6, lp = gi & 63;
@@ -735,6 +740,9 @@ hipError_t launch_chunk_prep(const ChunkArgs &a, int Dk, bool bf16_io, hipStream
     } else if (bf16_io && a.gate_logits) {  // bf16 gates, sigmoid in the kernel (forward only)
         if (Dk == 128) hipLaunchKernelGGL((chunk_prep_kernel<bf16, 128, false, true>), grid, block, 0, stream, a);
         else hipLaunchKernelGGL((chunk_prep_kernel<bf16, 64, false, true>), grid, block, 0, stream, a);
+    } else if (bf16_io && a.ws_Mt && a.ws_Qh) {  // forward for a later backward: both factor sets
+        if (Dk == 128) hipLaunchKernelGGL((chunk_prep_kernel<bf16, 128, true, false, false, true>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((chunk_prep_kernel<bf16, 64, true, false, false, true>), grid, block, 0, stream, a);
     } else if (bf16_io && a.ws_Mt) {  // backward calls (bf16 only)
         if (Dk == 128) hipLaunchKernelGGL((chunk_prep_kernel<bf16, 128, true>), grid, block, 0, stream, a);
         else hipLaunchKernelGGL((chunk_prep_kernel<bf16, 64, true>), grid, block, 0, stream, a);

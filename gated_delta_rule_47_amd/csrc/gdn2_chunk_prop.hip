@@ -312,6 +312,19 @@ __device__ __forceinline__ int sr_index(int c, int v) {
 
 // Accumulator tile (state rows 16 cblk.., columns 16 colb.. of the slab) into
 // that order.
+// kSaveSc: state tile (rows 16 cblk.., columns 16 colb.. of the slab) of a
+// chunk's incoming state straight to its workspace copy, as 8-byte row pieces
+// after a quad transpose (row 16 cblk + 4 (lane/16) + lane%4, four
+// consecutive columns), in the sc_index layout.
+template <int DK>
+__device__ __forceinline__ void store_state_pieces(bf16 *Sc, int cblk, int colb, int col0, f32x4 acc,
+                                                   int lane) {
+    const f32x4 t = quad_transpose(acc, lane);
+    const int c = 16 * cblk + 4 * (lane >> 4) + (lane & 3), v = col0 + 16 * colb + 4 * ((lane >> 2) & 3);
+    *reinterpret_cast<bf16x4 *>(Sc + sc_index(c, v, DK)) =
+        bf16x4{static_cast<bf16>(t[0]), static_cast<bf16>(t[1]), static_cast<bf16>(t[2]), static_cast<bf16>(t[3])};
+}
+
 template <int DVS>
 __device__ __forceinline__ void store_state_rows(bf16 *sSr, int cblk, int colb, f32x4 acc, int lane) {
     const int v = 16 * colb + (lane & 15);
@@ -379,9 +392,12 @@ __device__ __forceinline__ void ws_store_o(const ChunkArgs &a, const bf16 *sO, i
 }
 
 // kStates: also store every chunk's incoming state in a.ws_Sc (for the
-// backward) and write no o.
-template <int DK, int DV, int DVS, bool kStates>
+// backward) and write no o.  kSaveSc (without kStates): write o and also
+// store every chunk's incoming state in a.ws_Sc, from the compute waves'
+// accumulators (the stage region that kStates uses for them holds Qhat).
+template <int DK, int DV, int DVS, bool kStates, bool kSaveSc = false>
 __global__ __launch_bounds__(2 * kThreads, 1) void chunk_prop_ws_kernel(ChunkArgs a) {
+    static_assert(!(kStates && kSaveSc), "one way of storing the chunk states");
     using C = WsCfg<DK, DVS>;
     using M = Mma<bf16>;
     constexpr int NS = DV / DVS, LDS_ = C::LDS_, LDU = C::LDU, NCB = C::NCB;
@@ -525,6 +541,8 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_prop_ws_kernel(ChunkArg
         const int cblk = wave * C::KB_W + u / NCB, colb = u % NCB;
         store_tile_t<bf16>(sS + 16 * colb * LDS_ + 16 * cblk, LDS_, Sacc[u], lane);
         if constexpr (kStates) store_state_rows<DVS>(sSr, cblk, colb, Sacc[u], lane);
+        if constexpr (kSaveSc)
+            store_state_pieces<DK>(a.ws_Sc + ((size_t)cbeg * H + h) * DK * DV, cblk, colb, col0, Sacc[u], lane);
     }
     // The loader's steps 0 and 1 (the first chunk reaches stage 0).
 #pragma unroll
@@ -614,6 +632,11 @@ __global__ __launch_bounds__(2 * kThreads, 1) void chunk_prop_ws_kernel(ChunkArg
                 store_tile_t<bf16>(sS + 16 * colb * LDS_ + 16 * (wave * C::KB_W + b), LDS_, Sacc[u],
                                    lane);
                 if constexpr (kStates) store_state_rows<DVS>(sSr, wave * C::KB_W + b, colb, Sacc[u], lane);
+                if constexpr (kSaveSc) {  // the incoming state of the next chunk
+                    if (cid + 1 < cend)
+                        store_state_pieces<DK>(a.ws_Sc + ((size_t)(cid + 1) * H + h) * DK * DV,
+                                               wave * C::KB_W + b, colb, col0, Sacc[u], lane);
+                }
             }
         }
         __syncthreads();
@@ -655,7 +678,17 @@ static void launch_prop_d(const ChunkArgs &a, int dvs, hipStream_t stream) {
     const int groups = (chains + 7) / 8;
     if constexpr (sizeof(E) == 2) {  // compute + loader waves
         const dim3 block(2 * kThreads);
-        if (a.ws_Sc) {
+        if (a.ws_Sc && a.o) {  // o and every chunk's incoming state (a forward for a later backward)
+            if (dvs == 64)
+                hipLaunchKernelGGL((chunk_prop_ws_kernel<D, D, 64, false, true>), dim3(groups * 8 * (D / 64)),
+                                   block, 0, stream, a);
+            else if (dvs == 32)
+                hipLaunchKernelGGL((chunk_prop_ws_kernel<D, D, 32, false, true>), dim3(groups * 8 * (D / 32)),
+                                   block, 0, stream, a);
+            else
+                hipLaunchKernelGGL((chunk_prop_ws_kernel<D, D, 16, false, true>), dim3(groups * 8 * (D / 16)),
+                                   block, 0, stream, a);
+        } else if (a.ws_Sc) {
             if (dvs == 64)
                 hipLaunchKernelGGL((chunk_prop_ws_kernel<D, D, 64, true>), dim3(groups * 8 * (D / 64)),
                                    block, 0, stream, a);

@@ -83,6 +83,20 @@ struct BwdLayout {
 bool bwd_layout(int N, int B, int T, int H, int Dk, int Dv, size_t io_bytes, bool varlen,
                 BwdLayout *out);
 
+// The workspace of a forward whose chunk factors and chunk states a later
+// backward reuses (gdn2_chunk_fwd_train, then gdn2_chunk_bwd_saved): the
+// forward's layout without T, then the backward's slots as in BwdLayout,
+// with dKhat in a slot of its own so that the saved data outlive a backward.
+struct TrainLayout {
+    WorkspaceLayout fwd;
+    size_t off_Mt = 0, off_Qt = 0, off_Tt = 0;
+    size_t off_Sc = 0, off_dSc = 0, off_dKh = 0;
+    size_t total = 0;
+};
+
+bool train_layout(int N, int B, int T, int H, int Dk, int Dv, size_t io_bytes, bool varlen,
+                  TrainLayout *out);
+
 struct BwdArgs {
     ChunkArgs c;          // forward arguments and chunk factors (c.o unused)
     const void *dout;

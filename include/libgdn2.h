@@ -269,7 +269,7 @@ size_t gdn2_chunk_bwd_workspace_bytes(int N, int B, int T, int H, int Dk, int Dv
  * gdn2_chunk_bwd_workspace_bytes(...) bytes, 256-byte aligned) holds the
  * chunk factors, every chunk's incoming state and state gradient, and the
  * per-chunk partial gradients.  io = GDN2_BF16 runs the fast bf16-MFMA
- * kernels (bf16 factors and intermediates, fp32 accumulation; about 157 KiB
+ * kernels (bf16 factors and intermediates, fp32 accumulation; about 145 KiB
  * of workspace per chunk-head at Dk = 128); io = GDN2_F32
  * computes every product and intermediate in fp32 (fp32 MFMA), the precision
  * reference of the same chain rule, with a larger workspace (about 1 MiB per
@@ -283,6 +283,52 @@ int gdn2_chunk_bwd(const void *q, const void *k, const void *v,
                    const int32_t *cu_seqlens, int N,
                    int B, int T, int H, int Dk, int Dv, int io,
                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * A training step's forward and backward without recomputing the forward in
+ * the backward (the same chain rule as gdn2_chunk_bwd, same citations): the
+ * forward keeps, in a workspace the caller holds until the backward, what
+ * gdn2_chunk_bwd would otherwise rebuild first -- the chunk table, the chunk
+ * factors with their transposes and every chunk's incoming state.  This
+ * trades HBM (about 184.5 KiB per chunk-head at Dk = 128, 1.55 GB for
+ * B = 8, H = 16, T = 4096) for the recomputation.  bf16 I/O only
+ * (io = GDN2_F32 returns GDN2_ERR_UNSUPPORTED; gdn2_*_workspace_bytes
+ * returns 0 for it).
+ *
+ * gdn2_chunk_train_workspace_bytes: bytes of that workspace for a call with
+ * these sizes (arguments as for gdn2_chunk_fwd_workspace_bytes).
+ *
+ * gdn2_chunk_fwd_train: gdn2_chunk_fwd (same arguments, outputs and results,
+ * bitwise) on such a workspace (>= gdn2_chunk_train_workspace_bytes(...)
+ * bytes, 256-byte aligned), which it also fills for the backward.
+ *
+ * gdn2_chunk_bwd_saved: gdn2_chunk_bwd's gradients (bitwise the same) from a
+ * workspace a gdn2_chunk_fwd_train call filled, with the same q, k, v,
+ * log_alpha, b, w, cu_seqlens and sizes (S0 entered through the saved
+ * states, so it is not passed; the library cannot check that the inputs
+ * match, and gradients of other inputs are meaningless).  Its other
+ * arguments are those of gdn2_chunk_bwd.  It writes only the backward's own
+ * slots of the workspace, so the saved data stay valid: several backward
+ * calls may follow one forward.
+ */
+size_t gdn2_chunk_train_workspace_bytes(int N, int B, int T, int H, int Dk, int Dv,
+                                        int io, int varlen);
+
+int gdn2_chunk_fwd_train(const void *q, const void *k, const void *v,
+                         const float *log_alpha, const float *b, const float *w,
+                         const float *S0, void *o, float *S_final,
+                         const int32_t *cu_seqlens, int N, int B, int T, int H,
+                         int Dk, int Dv, int io, void *workspace,
+                         size_t workspace_bytes, void *stream);
+
+int gdn2_chunk_bwd_saved(const void *q, const void *k, const void *v,
+                         const float *log_alpha, const float *b, const float *w,
+                         const void *dout, const float *dS_final,
+                         void *dq, void *dk, void *dv,
+                         float *dlog_alpha, float *db, float *dw, float *dS0,
+                         const int32_t *cu_seqlens, int N,
+                         int B, int T, int H, int Dk, int Dv, int io,
+                         void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * One recurrent decode token for B independent sequences (constant-memory

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert g.gdn2_abi_version() == 2
+    assert g.gdn2_abi_version() == 3
     assert g.gdn2_status_string(g.GDN2_OK) == "GDN2_OK"
     assert g.gdn2_status_string(g.GDN2_ERR_WORKSPACE) == "GDN2_ERR_WORKSPACE"
     assert g.gdn2_status_string(99) == "GDN2_ERR_UNKNOWN"
@@ -104,6 +104,58 @@ def test_chunk_fwd_empty_call_without_buffers():
     assert _chunk(T=0, S_final=None, **none) in (g.GDN2_OK, g.GDN2_ERR_HIP)
     # a non-empty call still needs every token pointer
     assert _chunk(T=64, S_final=P16 + 8192, **none) == g.GDN2_ERR_INVALID_ARGUMENT
+
+
+def _bwd(fn, **kw):
+    args = dict(q=P16, k=P16, v=P16, log_alpha=P16, b=P16, w=P16, dout=P16, dS_final=None,
+                dq=P16 + 4096, dk=P16 + 8192, dv=P16 + 12288, dlog_alpha=P16 + 16384,
+                db=P16 + 20480, dw=P16 + 24576, dS0=None, cu_seqlens=None, N=1, B=1, T=64, H=1,
+                Dk=128, Dv=128, io=g.GDN2_BF16, workspace=None, workspace_bytes=0, stream=None)
+    if fn is g.gdn2_chunk_bwd:
+        args["S0"] = None
+    args.update(kw)
+    return fn(**args)
+
+
+def test_chunk_bwd_validation():
+    """gdn2_chunk_bwd and gdn2_chunk_bwd_saved reject bad arguments before any launch."""
+    sizes = (1, 1, 64, 1, 128, 128, g.GDN2_BF16, 0)
+    for fn, need in ((g.gdn2_chunk_bwd, g.gdn2_chunk_bwd_workspace_bytes(*sizes)),
+                     (g.gdn2_chunk_bwd_saved, g.gdn2_chunk_train_workspace_bytes(*sizes))):
+        assert _bwd(fn, q=None) == g.GDN2_ERR_INVALID_ARGUMENT
+        assert _bwd(fn, dout=None) == g.GDN2_ERR_INVALID_ARGUMENT
+        assert _bwd(fn, dq=P16 + 4104) == g.GDN2_ERR_INVALID_ARGUMENT      # misaligned
+        assert _bwd(fn, dk=P16 + 4096) == g.GDN2_ERR_INVALID_ARGUMENT      # dk aliases dq
+        assert _bwd(fn, dq=P16) == g.GDN2_ERR_INVALID_ARGUMENT             # dq aliases the inputs
+        assert _bwd(fn, Dk=96, Dv=96) == g.GDN2_ERR_UNSUPPORTED
+        assert _bwd(fn, N=2, B=1) == g.GDN2_ERR_INVALID_ARGUMENT
+        assert _bwd(fn) == g.GDN2_ERR_WORKSPACE                          # workspace missing
+        assert _bwd(fn, workspace=P16, workspace_bytes=need - 1) == g.GDN2_ERR_WORKSPACE
+        assert _bwd(fn, workspace=P16 + 16, workspace_bytes=need) == g.GDN2_ERR_WORKSPACE
+        assert _bwd(fn, N=0, B=0) == g.GDN2_OK and _bwd(fn, H=0) == g.GDN2_OK
+    # the saved-state backward is bf16 only
+    assert _bwd(g.gdn2_chunk_bwd_saved, io=g.GDN2_F32) == g.GDN2_ERR_UNSUPPORTED
+
+
+def test_chunk_fwd_train_validation_and_workspace():
+    """The training forward's workspace is the forward's (without T) plus the
+    backward's slots and a dKhat slot of its own; bf16 only."""
+    fwd = g.gdn2_chunk_fwd_workspace_bytes(8, 8, 4096, 16, 128, 128, g.GDN2_BF16, 0)
+    tr = g.gdn2_chunk_train_workspace_bytes(8, 8, 4096, 16, 128, 128, g.GDN2_BF16, 0)
+    chd = 8 * 64 * 16
+    # M^T, Qhat^T, T^T, Sc, dSc, dKhat (bf16) per chunk-head
+    assert tr == fwd + chd * 2 * (64 * 64 + 128 * 64 + 64 * 64 + 128 * 128 + 128 * 128 + 64 * 128)
+    assert g.gdn2_chunk_train_workspace_bytes(8, 8, 4096, 16, 128, 128, g.GDN2_F32, 0) == 0
+    args = dict(q=P16, k=P16, v=P16, log_alpha=P16, b=P16, w=P16, S0=None, o=P16 + 4096,
+                S_final=None, cu_seqlens=None, N=1, B=1, T=64, H=1, Dk=128, Dv=128,
+                io=g.GDN2_BF16, workspace=None, workspace_bytes=0, stream=None)
+    call = lambda **kw: g.gdn2_chunk_fwd_train(**dict(args, **kw))
+    need = g.gdn2_chunk_train_workspace_bytes(1, 1, 64, 1, 128, 128, g.GDN2_BF16, 0)
+    assert call(io=g.GDN2_F32) == g.GDN2_ERR_UNSUPPORTED
+    assert call(q=None) == g.GDN2_ERR_INVALID_ARGUMENT
+    assert call() == g.GDN2_ERR_WORKSPACE
+    assert call(workspace=P16, workspace_bytes=need - 1) == g.GDN2_ERR_WORKSPACE
+    assert call(N=0, B=0) == g.GDN2_OK
 
 
 def _step(**kw):
