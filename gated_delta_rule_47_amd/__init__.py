@@ -23,6 +23,8 @@ GDN2_ERR_HIP = 4
 GDN2_F32 = 0
 GDN2_BF16 = 1
 CHUNK = 64
+# The ABI revision these argument lists are written for (gdn2_abi_version()).
+ABI_VERSION = 3
 
 GDN2_STAGE_PLAN = 1
 GDN2_STAGE_FACTORS = 2
@@ -76,6 +78,10 @@ def load_library(path=LIB_PATH):
     P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     lib.gdn2_abi_version.restype = I
     lib.gdn2_abi_version.argtypes = []
+    if lib.gdn2_abi_version() != ABI_VERSION:
+        raise ImportError("%s reports ABI %d, this binding expects %d; rebuild it with "
+                          "`python -m gated_delta_rule_47_amd.build`"
+                          % (path, lib.gdn2_abi_version(), ABI_VERSION))
     lib.gdn2_status_string.restype = ctypes.c_char_p
     lib.gdn2_status_string.argtypes = [I]
     lib.gdn2_device_info.restype = I

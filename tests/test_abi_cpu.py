@@ -31,7 +31,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert g.gdn2_abi_version() == 3
+    assert g.gdn2_abi_version() == g.ABI_VERSION == 3
     assert g.gdn2_status_string(g.GDN2_OK) == "GDN2_OK"
     assert g.gdn2_status_string(g.GDN2_ERR_WORKSPACE) == "GDN2_ERR_WORKSPACE"
     assert g.gdn2_status_string(99) == "GDN2_ERR_UNKNOWN"
