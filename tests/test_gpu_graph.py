@@ -1,16 +1,17 @@
-"""The chunk forward under HIP graph capture: gdn2_chunk_fwd (dense and packed,
-the packed call's chunk table built by its own kernel) and
-gdn2_chunk_fwd_noalloc, each captured once on torch's capture stream and
-replayed three times, with other eager library calls and synchronisations
-between the replays.  Every replay must reproduce the eager result bitwise
-(the same kernels on the same inputs): the calls issue only kernel launches,
-no memset or copy nodes."""
+"""The library's calls under HIP graph capture: gdn2_chunk_fwd (dense and
+packed, the packed call's chunk table built by its own kernel),
+gdn2_chunk_fwd_noalloc, gdn2_chunk_bwd, the training pair
+gdn2_chunk_fwd_train + gdn2_chunk_bwd_saved, and a run of gdn2_step calls,
+each captured once on torch's capture stream and replayed three times, with
+other eager library calls and synchronisations between the replays.  Every
+replay must reproduce the eager result bitwise (the same kernels on the same
+inputs): the calls issue only kernel launches, no memset or copy nodes."""
 
 import pytest
 
 import gated_delta_rule_47_amd as g
 import workloads as W
-from gpu_util import log, upload_chunk
+from gpu_util import dev, log, upload_chunk
 
 pytestmark = pytest.mark.gpu
 
@@ -96,3 +97,87 @@ def test_chunk_fwd_noalloc_graph_replays():
     with torch.cuda.graph(graph):
         call(o, S)
     _replay_and_check(graph, (o, S), (o_ref, S_ref), "graph noalloc")
+
+
+GRADS = ("dq", "dk", "dv", "dlog_alpha", "db", "dw", "dS0")
+
+
+def _bwd_case(inp, seed, label, train=False):
+    import torch
+    grads = W.make_chunk_grads(inp, seed)
+    d = upload_chunk(inp)
+    x = (d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"])
+    dout = dev(grads["dout"], inp["io"])
+    dSf = dev(grads["dS_final"])
+    kw = dict(cu_seqlens=d["cu_seqlens"])
+    if train:
+        o_r, S_r, ws_r = g.chunk_fwd_train(*x, S0=d["S0"], **kw)
+        ref = g.chunk_bwd_saved(*x, dout, ws_r, dS_final=dSf, **kw)
+        refs = [o_r, S_r] + [ref[n] for n in GRADS]
+    else:
+        ref = g.chunk_bwd(*x, dout, S0=d["S0"], dS_final=dSf, **kw)
+        refs = [ref[n] for n in GRADS]
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        if train:
+            o, S, ws = g.chunk_fwd_train(*x, S0=d["S0"], **kw)
+            out = g.chunk_bwd_saved(*x, dout, ws, dS_final=dSf, **kw)
+            outs = [o, S] + [out[n] for n in GRADS]
+        else:
+            out = g.chunk_bwd(*x, dout, S0=d["S0"], dS_final=dSf, **kw)
+            outs = [out[n] for n in GRADS]
+    _replay_and_check(graph, outs, refs, label)
+
+
+def test_chunk_bwd_dense_graph_replays():
+    """gdn2_chunk_bwd on B=2, T=150, H=2, d=128, bf16, S0 and dS_final != 0."""
+    wl = W.ChunkWorkload("graph_bwd", 2, 150, 2, 128, 128, W.BF16, 6404, with_S0=True)
+    _bwd_case(W.make_chunk_inputs(wl), 41, "graph bwd dense")
+
+
+def test_chunk_bwd_packed_graph_replays():
+    """gdn2_chunk_bwd on packed lengths 1, 63, 64, 65, 130, 0 and 7."""
+    wl = W.ChunkWorkload("graph_bwd_varlen", 1, 0, 2, 128, 128, W.BF16, 6505, with_S0=True, n_seqs=7)
+    _bwd_case(W.make_chunk_inputs(wl, lengths=[1, 63, 64, 65, 130, 0, 7]), 42, "graph bwd packed")
+
+
+def test_training_pair_graph_replays():
+    """gdn2_chunk_fwd_train and gdn2_chunk_bwd_saved captured together, on
+    B=2, T=200, H=4, d=128, bf16."""
+    wl = W.ChunkWorkload("graph_train", 2, 200, 4, 128, 128, W.BF16, 6606, with_S0=True)
+    _bwd_case(W.make_chunk_inputs(wl), 43, "graph training pair", train=True)
+
+
+def test_decode_steps_graph_replays():
+    """Four consecutive gdn2_step calls on one state (B=4, H=2, d=128, bf16),
+    captured once; before each replay the state is reset to its initial
+    value, and every step's output and the final state must equal the eager
+    run's."""
+    import torch
+    dw = W.DecodeWorkload("graph_decode", 4, 2, 128, 128, W.BF16, 6707, 4)
+    S_init = dev(W.make_decode_state(dw))
+    names = ("q", "k", "v", "log_alpha", "b", "w")
+    xs = []
+    for t in range(dw.steps):
+        x = W.make_decode_step(dw, t)
+        xs.append([dev(x[n], dw.io if n in ("q", "k", "v") else None) for n in names])
+    S_e = S_init.clone()
+    o_ref = [g.step(*xs[t], S_e) for t in range(dw.steps)]
+    torch.cuda.synchronize()
+    S_g = S_init.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        outs = [g.step(*xs[t], S_g) for t in range(dw.steps)]
+    for rep in range(REPLAYS):
+        S_g.copy_(S_init)
+        for t in outs:
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for t in range(dw.steps):
+            assert torch.equal(outs[t], o_ref[t]), ("decode step", t, rep)
+        assert torch.equal(S_g, S_e), ("decode state", rep)
+        log("graph decode: replay %d matches the eager steps bitwise" % rep)
+        _other_work(950 + rep)
