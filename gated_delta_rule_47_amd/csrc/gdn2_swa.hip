@@ -114,7 +114,11 @@ template <int D>
 __global__ __launch_bounds__(kThreads, 2) void swa_fwd_kernel(SwaArgs a) {
     using C = SwaCfg<D>;
     using MB = Mma<bf16>;
-    __shared__ __attribute__((aligned(16))) bf16 smem[4 * C::SZ];  // 2 x (K tile, V tile)
+    // two stages, each a K tile followed by a V tile, as distinct arrays so
+    // that the compiler can tell the stage being read from the one the direct
+    // loads write
+    __shared__ __attribute__((aligned(16))) bf16 smemA[2 * C::SZ];
+    __shared__ __attribute__((aligned(16))) bf16 smemB[2 * C::SZ];
     // (the wave index as a uniform value: the LDS addresses of the direct
     // loads are then formed in scalar registers)
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -156,9 +160,6 @@ __global__ __launch_bounds__(kThreads, 2) void swa_fwd_kernel(SwaArgs a) {
     const int kstart = max(s0, q0 - W + 1), kend = qlast;
     const int ntiles = (kend - kstart) / C::BN + 1;
 
-    // buffer b: K tile at smem + 2 b SZ, V tile right after it
-    constexpr int BUF = 2 * C::SZ;
-
     // Q fragments (B operand of S^T = K Q^T): lane holds query col of tile rt,
     // dims 32c + 8 grp .. + 8
     const bf16 *Q = reinterpret_cast<const bf16 *>(a.q);
@@ -182,14 +183,15 @@ __global__ __launch_bounds__(kThreads, 2) void swa_fwd_kernel(SwaArgs a) {
     const float cs = a.scale * kLog2eF;  // scores in base-2 units
 
     const SwaFeed<D> feed = swa_feed<D>(a, h, wave, lane);
-    swa_issue<D>(a, feed, h, s0, s1, kstart, smem, smem + C::SZ, wave, lane);
+    swa_issue<D>(a, feed, h, s0, s1, kstart, smemA, smemA + C::SZ, wave, lane);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     const int wq_hi = min(wq0 + 31, s1 - 1);
-    for (int j = 0; j < ntiles; ++j) {
+    // one key tile: read stage cK, fill stage nK with the next tile
+    auto tile = [&](int j, const bf16 *cK, bf16 *nK) {
         const int k0 = kstart + j * C::BN;
-        const bf16 *cK = smem + (j & 1) * BUF, *cV = cK + C::SZ;
+        const bf16 *cV = cK + C::SZ;
 
         // ---- S^T = K Q^T: s[rt][kt] = [key 16 kt + 4 grp + r][query col] ----
         // Contraction chunk c outermost: the 8 accumulators advance together,
@@ -247,14 +249,15 @@ __global__ __launch_bounds__(kThreads, 2) void swa_fwd_kernel(SwaArgs a) {
         MB::frag vf[2][VGRP];
 #pragma unroll
         for (int u = 0; u < VGRP; ++u) vf[0][u] = load_v(u, 0);
-        // The next tile's direct loads go out only now: the compiler makes every
-        // transposing LDS read wait for all outstanding direct loads, so they
-        // are issued after the first group of V^T reads and land during the
-        // softmax and the first group of MFMAs.
-        if (j + 1 < ntiles) {
-            bf16 *nK = smem + ((j + 1) & 1) * BUF;
-            swa_issue<D>(a, feed, h, s0, s1, k0 + C::BN, nK, nK + C::SZ, wave, lane);
-        }
+        // The next tile's direct loads go out now, into the other stage's
+        // array: they land during the softmax and the V^T P^T products.  The
+        // two stages are distinct arrays and the tile loop is unrolled by two,
+        // so every LDS read names its stage and the compiler's wait
+        // insertion can tell it apart from the direct loads in flight (with
+        // one array and a runtime stage offset, every read after the issue
+        // waited for all of them).  Issuing before the S^T products, or
+        // before the first V^T reads, measured slower.
+        if (j + 1 < ntiles) swa_issue<D>(a, feed, h, s0, s1, k0 + C::BN, nK, nK + C::SZ, wave, lane);
         // mask the tile unless every key is inside every query's window
         const bool full = (k0 + C::BN - 1 <= wq0) && (k0 > wq_hi - W);
         if (!full) {
@@ -338,6 +341,10 @@ __global__ __launch_bounds__(kThreads, 2) void swa_fwd_kernel(SwaArgs a) {
         }
         __builtin_amdgcn_s_waitcnt(0);  // this wave's part of the next tile has landed
         __syncthreads();
+    };
+    for (int j = 0; j < ntiles; j += 2) {
+        tile(j, smemA, smemB);
+        if (j + 1 < ntiles) tile(j + 1, smemB, smemA);
     }
 
     // ---- normalise and store: lane holds dims 16 dt + 4 grp .. +3 of query col ----
