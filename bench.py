@@ -14,7 +14,10 @@ Also measured in the same run (each in its own object of the JSON line):
   context_sweep: the same 16K tokens as B x T = 8 x 2K, 4 x 4K, 2 x 8K, 1 x 16K;
   decode: gdn2_step on B=256, H=16, d=128 (fp32 state, in place) over 1024
           distinct pre-generated steps, GB/s of its algorithmic traffic;
-  varlen, gate_logits, backward, layer, swa (see the design doc's measurement section).
+  varlen: the 32-sequence packed workload; gate_logits: the batch workload with
+          bf16 gate logits; training_step: the recomputing and the saved-state
+          backward after their forwards; backward, layer, swa: the backward, the
+          token-mixer layer and the sliding-window attention (and its layer).
 cpu_baseline: the fp64 numpy oracle over the whole batch workload, its
 (sequence, head) chains spread over a process pool on this host's cores, plus
 one-core figures for the tiny and single-sequence workloads.  Work that starts
